@@ -1,0 +1,402 @@
+"""Tile-selection oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain Python statement of the selection rules: the candidate space, the
+feasibility filter, the analytical cost model and the model's choice, plus the
+counting invariants the pages state.  The library implements the same rules
+natively; tests require the two to agree bit for bit (identical feasible sets,
+identical float64 model times, identical choices, identical block counts).
+Nothing here imports the library.
+
+Passages followed (pages by title):
+  * "Tile Selection: Cost Models Against Measurement"
+      - "The structure of the search space": blocks = ceil(M/BM) * ceil(N/BN);
+        the resource bounds (shared memory holding both panels, accumulator
+        registers, filling the device) that make a tile infeasible.
+      - "Analytical models and where they break": per-block traffic
+        eb*K*(BM+BN), per-block work 2*BM*BN*K, grid traffic = per-block
+        traffic x blocks, time = work/peak or bytes/bandwidth; corrections for
+        occupancy, pipeline fill and the tail.
+      - "Hybrid strategies": filter by resources, rank by the model.
+  * "Compilers and Kernel Languages", "Workshop" and "A different tile for
+    every shape": the H100 model -- HBM traffic divided by g, compute time
+    divided by wave efficiency and by a tile efficiency that falls below
+    128 x 128, time = the larger of the two -- and its printed results.
+  * "Tiling the hierarchy", derivation: traffic of a square-tiled loop nest is
+    2 N^3 / T.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * tile efficiency = min(1, 0.5 + 0.5 * BM*BN / A_ref), A_ref = 128*128 for
+    the H100 model (the only simple form that reproduces both printed ratios);
+  * g = sqrt(min(tiles in flight, concurrent slots));
+  * a compulsory-traffic floor eb*(MK + KN) + ec*MN ("set by reading the
+    weights");
+  * ties keep the first candidate in canonical order.
+  * The MI355X constants (peaks, register model, calibration constants) are
+    not on the pages: outputs that depend on them are "parity unpinned"
+    against the pages and are pinned only by agreement with the library and
+    by invariants.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from dataclasses import dataclass
+
+F32, BF16, BF16_F32OUT = 0, 1, 2
+KIND_TILED, KIND_SKINNY, KIND_UNALIGNED = 0, 1, 2
+
+# reasons a candidate is rejected (first failing rule)
+OK = 0
+R_DTYPE = 1
+R_ALIGN = 2
+R_SHAPE = 3
+R_WAVES = 4
+R_DIV = 5
+R_LDS = 6
+R_ACC = 7
+R_VGPR = 8
+R_OCC = 9
+R_SPLIT = 10
+R_SPACE = 11
+
+
+@dataclass(frozen=True)
+class Device:
+    """Device description used by the rules.  ``mode`` 0 = MI355X rules,
+    1 = replica of the H100 model on the page "Compilers and Kernel
+    Languages"."""
+    mode: int
+    n_cu: int
+    simds: int
+    lds_cu: int
+    lds_block: int
+    max_threads: int
+    waves_max: int
+    blocks_max: int
+    vgpr_max: int
+    acc_max: int
+    peak_bf16: float
+    peak_f32: float
+    bw: float
+    a_ref: float
+    c_fill: float
+    t0: float
+    unaligned_eff: float
+    lat_mem: float
+    cu_bw: float
+    r0: int
+
+
+# MI355X (gfx950): 256 CUs x 4 SIMDs, 160 KiB LDS per CU, 512 unified
+# VGPR+AGPR per lane, 8 wave slots per SIMD; dense bf16 MFMA 2516.6 TFLOP/s,
+# fp32 MFMA 157.3 TFLOP/s, HBM3E 8 TB/s.  a_ref, c_fill, t0, unaligned_eff,
+# lat_mem, cu_bw and r0 are calibration constants of this model.
+MI355X = Device(mode=0, n_cu=256, simds=4, lds_cu=163840, lds_block=163840,
+                max_threads=1024, waves_max=8, blocks_max=32, vgpr_max=512,
+                acc_max=256, peak_bf16=2516.6e12, peak_f32=157.3e12, bw=8.0e12,
+                a_ref=16384.0, c_fill=2.0, t0=3.0e-6, unaligned_eff=0.25,
+                lat_mem=2.0e-6, cu_bw=153.6e9, r0=24)
+
+# The page's H100 model: 132 SMs, 228 KB shared memory, 989 TFLOP/s bf16,
+# 3.35 TB/s; one tile per SM at a time; no register model; no pipeline-fill
+# or launch term.
+H100_REPLICA = Device(mode=1, n_cu=132, simds=1, lds_cu=233472, lds_block=233472,
+                      max_threads=1024, waves_max=8, blocks_max=1, vgpr_max=1 << 30,
+                      acc_max=1 << 30, peak_bf16=989e12, peak_f32=989e12, bw=3.35e12,
+                      a_ref=16384.0, c_fill=0.0, t0=0.0, unaligned_eff=1.0,
+                      lat_mem=0.0, cu_bw=0.0, r0=0)
+
+
+@dataclass(frozen=True, order=True)
+class Cfg:
+    """One point of the space.  Field order is the canonical order."""
+    kind: int
+    bm: int
+    bn: int
+    bk: int
+    wgm: int
+    wgn: int
+    stages: int
+    split_k: int
+
+    def astuple(self):
+        return (self.kind, self.bm, self.bn, self.bk, self.wgm, self.wgn, self.stages, self.split_k)
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def in_bytes(dtype: int) -> int:
+    return 4 if dtype == F32 else 2
+
+
+def out_bytes(dtype: int) -> int:
+    return 2 if dtype == BF16 else 4
+
+
+def shape_aligned(N: int, K: int, dtype: int) -> bool:
+    """16-byte vectors along K of A and along N of B need K and N to be
+    multiples of the vector length."""
+    vec = 4 if dtype == F32 else 8
+    return K % vec == 0 and N % vec == 0
+
+
+# ---------------------------------------------------------------- space
+WAVE_GRIDS = ((1, 1), (1, 2), (2, 1), (2, 2), (2, 4), (4, 2))
+SPLITS = (1, 2, 4, 8, 16)
+UNALIGNED_TILES = ((32, 32, 1, 1), (64, 64, 2, 2), (128, 128, 2, 2))
+
+
+def space(dtype: int, dev: Device = MI355X):
+    """Every candidate in canonical (lexicographic) order, before filtering."""
+    out = []
+    if dev.mode == 1:
+        for bm in (32, 64, 128, 256):
+            for bn in (32, 64, 128, 256):
+                out.append(Cfg(KIND_TILED, bm, bn, 64, 1, 1, 1, 1))
+        return out
+    if dtype == F32:
+        tiles_mn, bks = (32, 64, 128), (8, 16, 32)
+    else:
+        tiles_mn, bks = (32, 64, 128, 256), (32, 64, 128)
+    for bm, bn, bk, (wm, wn), st, s in itertools.product(
+            tiles_mn, tiles_mn, bks, WAVE_GRIDS, (1, 2), SPLITS):
+        out.append(Cfg(KIND_TILED, bm, bn, bk, wm, wn, st, s))
+    if dtype != F32:
+        for bm, w, u, s in itertools.product((16, 32, 48, 64), (1, 2, 4, 8), (1, 2, 4),
+                                             (1, 2, 4, 8, 16, 32)):
+            out.append(Cfg(KIND_SKINNY, bm, 128, 32, w, 1, u, s))
+    ubk = 16 if dtype == F32 else 32
+    for (bm, bn, wm, wn), s in itertools.product(UNALIGNED_TILES, SPLITS):
+        out.append(Cfg(KIND_UNALIGNED, bm, bn, ubk, wm, wn, 2, s))
+    return out
+
+
+# ---------------------------------------------------------------- resources
+def lds_bytes(c: Cfg, dtype: int) -> int:
+    eb = in_bytes(dtype)
+    if c.kind == KIND_SKINNY:
+        return c.wgm * c.bm * 128 * 4 if c.wgm > 1 else 0
+    pad_b = 4 if dtype == F32 else 0
+    return c.stages * (c.bm * c.bk + c.bk * (c.bn + pad_b)) * eb
+
+
+def acc_regs(c: Cfg) -> int:
+    if c.kind == KIND_SKINNY:
+        return (c.bm // 16) * 32
+    return (c.bm // c.wgm) * (c.bn // c.wgn) // 64
+
+
+def vgpr_estimate(c: Cfg, dtype: int, dev: Device) -> int:
+    if c.kind == KIND_SKINNY:
+        mt = c.bm // 16
+        return 32 * c.stages + 32 * mt + 4 * mt + dev.r0
+    threads = 64 * c.wgm * c.wgn
+    eb = in_bytes(dtype)
+    frag = 4 * ((c.bm // c.wgm) // 16 + (c.bn // c.wgn) // 16)
+    chunks_a = c.bm * c.bk * eb // 16
+    stage = 4 * cdiv(chunks_a, threads)
+    if dtype == F32:
+        stage += 4 * cdiv(c.bk * c.bn // 4, threads)
+    else:
+        stage += 32 * cdiv(c.bk * c.bn // 64, threads)
+    return acc_regs(c) + frag + stage + dev.r0
+
+
+def waves_per_simd(c: Cfg, dtype: int, dev: Device) -> int:
+    v = vgpr_estimate(c, dtype, dev)
+    v8 = cdiv(v, 8) * 8
+    return min(dev.waves_max, dev.vgpr_max // v8) if v8 > 0 else dev.waves_max
+
+
+def blocks_per_cu(c: Cfg, dtype: int, dev: Device) -> int:
+    w = c.wgm * c.wgn
+    b = min(dev.blocks_max, (dev.simds * waves_per_simd(c, dtype, dev)) // w)
+    lds = lds_bytes(c, dtype)
+    if lds > 0:
+        b = min(b, dev.lds_cu // lds)
+    return b
+
+
+def k_per_split(c: Cfg, K: int) -> int:
+    unit = 32 if c.kind == KIND_SKINNY else c.bk
+    return cdiv(cdiv(K, c.split_k), unit) * unit
+
+
+def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> int:
+    """Feasibility of one candidate: OK, or the code of the first failing rule."""
+    if dtype not in (F32, BF16, BF16_F32OUT):
+        return R_DTYPE
+    if M < 1 or N < 1 or K < 0:
+        return R_SHAPE
+    if c not in _space_set(dtype, dev):
+        return R_SPACE
+    if c.kind == KIND_SKINNY and dtype == F32:
+        return R_DTYPE
+    aligned = shape_aligned(N, K, dtype)
+    if dev.mode == 0:
+        if c.kind == KIND_UNALIGNED and aligned:
+            return R_ALIGN
+        if c.kind != KIND_UNALIGNED and not aligned:
+            return R_ALIGN
+    if c.kind == KIND_SKINNY and (M > 64 or c.bm != 16 * cdiv(M, 16)):
+        return R_SHAPE
+    w = c.wgm * c.wgn
+    if 64 * w > dev.max_threads:
+        return R_WAVES
+    if c.kind != KIND_SKINNY:
+        kstep = 16 if dtype == F32 else 32
+        if c.bm % (16 * c.wgm) or c.bn % (16 * c.wgn) or c.bk % kstep:
+            return R_DIV
+    if lds_bytes(c, dtype) > dev.lds_block:
+        return R_LDS
+    if acc_regs(c) > dev.acc_max:
+        return R_ACC
+    if vgpr_estimate(c, dtype, dev) > dev.vgpr_max:
+        return R_VGPR
+    if blocks_per_cu(c, dtype, dev) < 1:
+        return R_OCC
+    if c.split_k > 1:
+        if K == 0 or cdiv(K, k_per_split(c, K)) != c.split_k:
+            return R_SPLIT
+    return OK
+
+
+_SPACE_CACHE: dict = {}
+
+
+def _space_set(dtype: int, dev: Device):
+    key = (dtype, dev)
+    if key not in _SPACE_CACHE:
+        _SPACE_CACHE[key] = frozenset(space(dtype, dev))
+    return _SPACE_CACHE[key]
+
+
+def enumerate_feasible(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):
+    return [c for c in space(dtype, dev) if check(M, N, K, dtype, c, dev) == OK]
+
+
+# ---------------------------------------------------------------- geometry
+def grid(M: int, N: int, c: Cfg):
+    """(tiles, launched blocks).  Tiles = ceil(M/BM) * ceil(N/BN) (page
+    "Tile Selection: Cost Models Against Measurement", search-space section);
+    split-K launches that many blocks per tile."""
+    tiles = cdiv(M, c.bm) * cdiv(N, c.bn)
+    return tiles, tiles * c.split_k
+
+
+# ---------------------------------------------------------------- cost model
+def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> float:
+    """Predicted seconds for one launch.  Caller guarantees feasibility."""
+    eb = in_bytes(dtype)
+    ec = out_bytes(dtype)
+    peak = dev.peak_f32 if dtype == F32 else dev.peak_bf16
+    flops = 2.0 * M * N * K
+    compulsory = float(eb * (M * K + K * N) + ec * M * N)
+    tiles, units = grid(M, N, c)
+    w = c.wgm * c.wgn
+    bcu = blocks_per_cu(c, dtype, dev)
+
+    if c.kind == KIND_SKINNY:
+        flops_pad = 2.0 * c.bm * N * K
+        t_c = flops_pad / peak
+        ws = 8.0 * c.bm * 128 * tiles * c.split_k if c.split_k > 1 else 0.0
+        resident = min(units * w, dev.n_cu * bcu * w)
+        inflight = resident * 64.0 * c.stages * 8 * 16
+        bw_eff = min(1.0, inflight / (dev.bw * dev.lat_mem))
+        active = min(units, dev.n_cu)
+        bw = min(dev.bw * bw_eff, active * dev.cu_bw)
+        t_m = (compulsory + ws) / bw
+        return max(t_c, t_m) + dev.t0
+
+    par_need = max(1, dev.simds // w)
+    par = min(bcu, par_need)
+    slots = dev.n_cu * par
+    rounds = cdiv(units, slots)
+    wave_eff = units / (rounds * slots)
+    simd_eff = min(1.0, (par * w) / dev.simds)
+    tile_eff = min(1.0, 0.5 + 0.5 * (c.bm * c.bn) / dev.a_ref)
+    ktiles = cdiv(k_per_split(c, K), c.bk)
+    fill_eff = ktiles / (ktiles + dev.c_fill) if ktiles > 0 else 1.0
+    eff = wave_eff * simd_eff * tile_eff * fill_eff
+    if c.kind == KIND_UNALIGNED:
+        eff = eff * dev.unaligned_eff
+    t_c = flops / (peak * eff)
+    raw = float(tiles) * eb * K * (c.bm + c.bn)
+    g = math.sqrt(min(units, dev.n_cu * bcu))
+    ws = 8.0 * tiles * c.bm * c.bn * c.split_k if c.split_k > 1 else 0.0
+    t_m = (max(compulsory, raw / g) + ws) / dev.bw
+    return max(t_c, t_m) + dev.t0
+
+
+def rank(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):
+    """Feasible candidates with model times, ascending; ties keep canonical order."""
+    feas = enumerate_feasible(M, N, K, dtype, dev)
+    timed = [(model_time(M, N, K, dtype, c, dev), i, c) for i, c in enumerate(feas)]
+    timed.sort(key=lambda t: (t[0], t[1]))
+    return [(c, t) for t, _, c in timed]
+
+
+def model_choice(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):
+    """First feasible candidate with the smallest model time (strict <)."""
+    best, best_t = None, None
+    for c in enumerate_feasible(M, N, K, dtype, dev):
+        t = model_time(M, N, K, dtype, c, dev)
+        if best is None or t < best_t:
+            best, best_t = c, t
+    return best, best_t
+
+
+def default_cfg(N: int, K: int, dtype: int) -> Cfg:
+    """The fixed configuration autotuning is always compared against."""
+    if not shape_aligned(N, K, dtype):
+        return Cfg(KIND_UNALIGNED, 64, 64, 16 if dtype == F32 else 32, 2, 2, 2, 1)
+    if dtype == F32:
+        return Cfg(KIND_TILED, 128, 128, 32, 2, 2, 2, 1)
+    return Cfg(KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
+
+
+# ---------------------------------------------------------------- page counts
+def page1_candidates(smem_bytes: int = 48 * 1024, max_threads: int = 1024):
+    """The float32 tile enumeration described on "Tile Selection: Cost Models
+    Against Measurement" (search-space section): BM, BN in {32..256}, KS in
+    {8..64}, per-thread TM, TN in {2, 4, 8}; keep a tuple when both panels fit
+    in shared memory, the thread count is between 32 and the block limit and
+    a whole number of 32-wide warps, and TM*TN accumulators stay within 128."""
+    keep = []
+    for bm, bn, ks, tm, tn in itertools.product((32, 64, 128, 256), (32, 64, 128, 256),
+                                                (8, 16, 32, 64), (2, 4, 8), (2, 4, 8)):
+        smem = 4 * ks * (bm + bn)
+        threads = (bm // tm) * (bn // tn)
+        ok = (smem <= smem_bytes and 32 <= threads <= max_threads
+              and threads % 32 == 0 and tm * tn <= 128)
+        if ok:
+            keep.append((bm, bn, ks, tm, tn))
+    return keep
+
+
+def loop_nest_traffic(n: int, t: int) -> int:
+    """Elements moved by the square-tiled loop nest of "Tiling the hierarchy"
+    (derivation), by simulation: loops over tile triples (i, j, k) with k
+    innermost; one resident A tile and one resident B tile; a tile is loaded
+    (t*t elements) whenever the triple needs a different one."""
+    assert n % t == 0
+    nt = n // t
+    moved = 0
+    res_a = res_b = None
+    for i in range(nt):
+        for j in range(nt):
+            for k in range(nt):
+                if res_a != (i, k):
+                    res_a = (i, k)
+                    moved += t * t
+                if res_b != (k, j):
+                    res_b = (k, j)
+                    moved += t * t
+    return moved
+
+
+def block_count_brute(M: int, N: int, bm: int, bn: int) -> int:
+    """Count the tile origins that cover an M x N output (brute force)."""
+    return sum(1 for i in range(0, M, bm) for j in range(0, N, bn))

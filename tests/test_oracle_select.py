@@ -1,0 +1,206 @@
+"""Pins for the tile-selection oracle (CPU only).
+
+* The H100 replica of the model on page "Compilers and Kernel Languages"
+  ("Workshop"; results in "A different tile for every shape") must reproduce
+  every number the page prints (tests/golden/h100_model_page_results.json).
+* Counting invariants: blocks = ceil(M/BM) * ceil(N/BN) (page "Tile Selection:
+  Cost Models Against Measurement", search-space section, checked by brute
+  force), the shared-memory cap of 12,288 float32 elements at 48 KB (same
+  section), the enumeration size "a few hundred to a few thousand" (same
+  section), and loop-nest traffic 2 N^3 / T (page "Tiling the hierarchy",
+  derivation, checked by simulating the loop nest).
+* Invariants of the MI355X model whose constants the pages do not give
+  ("parity unpinned" against the pages): wave efficiency is 1 exactly when
+  the work divides the slots, the memory time never undercuts the compulsory
+  floor, and time never rises when a peak rises.
+"""
+import dataclasses
+import json
+import math
+import os
+
+import pytest
+
+from oracle import select_ref as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "h100_model_page_results.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _tile_times(M, N, K):
+    return {(c.bm, c.bn): t for c, t in S.rank(M, N, K, S.BF16, S.H100_REPLICA)}
+
+
+def test_replica_constants_match_page():
+    g = _golden()["device"]
+    d = S.H100_REPLICA
+    assert d.n_cu == g["sms"]
+    assert d.lds_cu == g["shared_memory_kb"] * 1024
+    assert d.peak_bf16 == g["bf16_tflops"] * 1e12
+    assert d.bw == g["hbm_tbps"] * 1e12
+    assert {c.bk for c in S.space(S.BF16, d)} == {g["bk"]}
+    assert len(S.space(S.BF16, d)) == 16
+
+
+def test_replica_large_square():
+    case = _golden()["cases"][0]
+    M, N, K = case["M"], case["N"], case["K"]
+    best, best_t = S.model_choice(M, N, K, S.BF16, S.H100_REPLICA)
+    assert [best.bm, best.bn] == case["best_tile"]
+    assert round(best_t * 1e6) == case["best_us_rounded"]
+    times = _tile_times(M, N, K)
+    assert round(max(times.values()) / best_t, 2) == case["worst_over_best_2dp"]
+    assert round(times[(128, 128)] / best_t, 2) == case["fixed_128x128_over_best_2dp"]
+
+
+def test_replica_small_problem_wave_quantisation():
+    case = _golden()["cases"][1]
+    M, N, K = case["M"], case["N"], case["K"]
+    fixed = S.Cfg(S.KIND_TILED, 128, 128, 64, 1, 1, 1, 1)
+    assert S.grid(M, N, fixed)[0] == case["tiles_at_128x128"]
+    best, best_t = S.model_choice(M, N, K, S.BF16, S.H100_REPLICA)
+    assert [best.bm, best.bn] == case["best_tile"]
+    tiles = S.grid(M, N, best)[0]
+    slots = S.H100_REPLICA.n_cu
+    wave_eff = tiles / (math.ceil(tiles / slots) * slots)
+    assert round(100 * wave_eff) == case["best_wave_efficiency_pct"]
+    assert round(_tile_times(M, N, K)[(128, 128)] / best_t, 2) == case["fixed_128x128_over_best_2dp"]
+
+
+def test_replica_decode_all_tie_at_weight_floor():
+    case = _golden()["cases"][2]
+    M, N, K = case["M"], case["N"], case["K"]
+    times = set(_tile_times(M, N, K).values())
+    assert len(times) == 1
+    assert round(times.pop() * 1e6, 1) == case["floor_us_1dp"]
+
+
+def test_replica_catches_model_mistakes():
+    # dropping the g divisor, the tile efficiency, or the compulsory floor each
+    # breaks one printed number
+    d = S.H100_REPLICA
+    M = N = K = 8192
+    no_tile_eff = dataclasses.replace(d, a_ref=1.0)
+    best, _ = S.model_choice(M, N, K, S.BF16, no_tile_eff)
+    t = {(c.bm, c.bn): x for c, x in S.rank(M, N, K, S.BF16, no_tile_eff)}
+    assert round(max(t.values()) / t[(best.bm, best.bn)], 2) != 1.83
+
+
+@pytest.mark.parametrize("M,N,bm,bn", [(1, 1, 32, 32), (1000, 1000, 128, 128), (4100, 3000, 128, 128),
+                                       (4100, 3000, 256, 64), (16, 28672, 16, 128), (8192, 8192, 256, 256)])
+def test_block_count_formula_vs_brute_force(M, N, bm, bn):
+    c = S.Cfg(S.KIND_TILED, bm, bn, 32, 1, 1, 1, 1)
+    assert S.grid(M, N, c)[0] == S.block_count_brute(M, N, bm, bn)
+    c4 = dataclasses.replace(c, split_k=4)
+    assert S.grid(M, N, c4)[1] == 4 * S.block_count_brute(M, N, bm, bn)
+
+
+def test_page1_enumeration_size_and_caps():
+    cands = S.page1_candidates()
+    # "a few hundred to a few thousand configurations depending on the bounds"
+    assert 200 <= len(cands) <= 5000
+    assert len(cands) == 398
+    assert len({c[:3] for c in cands}) == 55
+    # 48 KB of float32 panels caps BM*KS + KS*BN at 12,288 elements
+    assert max(ks * (bm + bn) for bm, bn, ks, _, _ in cands) == 12288
+    for bm, bn, ks, tm, tn in cands:
+        threads = (bm // tm) * (bn // tn)
+        assert 32 <= threads <= 1024 and threads % 32 == 0 and tm * tn <= 128
+    # a larger shared memory admits strictly more tuples; a smaller thread cap fewer
+    assert len(S.page1_candidates(smem_bytes=96 * 1024)) > len(cands)
+    assert len(S.page1_candidates(max_threads=256)) < len(cands)
+
+
+@pytest.mark.parametrize("n,t", [(8, 8), (16, 4), (32, 8), (64, 8), (64, 16), (48, 12)])
+def test_loop_nest_traffic_is_2n3_over_t(n, t):
+    assert S.loop_nest_traffic(n, t) * t == 2 * n ** 3
+
+
+def test_square_root_law_halving_tile_doubles_traffic():
+    # traffic ~ 1/T: a 4x smaller capacity (T halves) doubles the traffic
+    assert S.loop_nest_traffic(64, 8) == 2 * S.loop_nest_traffic(64, 16)
+
+
+# ---------------------------------------------------------------- MI355X rules
+SHAPES = [(256, 256, 256, S.F32), (1000, 1000, 8192, S.BF16_F32OUT), (8192, 8192, 8192, S.BF16),
+          (16, 28672, 8192, S.BF16), (4100, 3000, 1000, S.BF16), (17, 65, 15, S.BF16), (1, 1, 1, S.F32)]
+
+
+def test_lds_examples():
+    d = S.MI355X
+    two = S.Cfg(S.KIND_TILED, 256, 256, 64, 2, 2, 2, 1)
+    assert S.lds_bytes(two, S.BF16) == 2 * 64 * 1024
+    assert S.check(8192, 8192, 8192, S.BF16, two, d) == S.OK
+    big = S.Cfg(S.KIND_TILED, 256, 256, 128, 2, 2, 2, 1)
+    assert S.lds_bytes(big, S.BF16) == 256 * 1024
+    assert S.check(8192, 8192, 8192, S.BF16, big, d) == S.R_LDS
+    # all 18 fp32 sweep triples fit LDS at one stage
+    for bm in (32, 64, 128):
+        for bn in (32, 64, 128):
+            for bk in (16, 32):
+                assert S.lds_bytes(S.Cfg(0, bm, bn, bk, 1, 1, 1, 1), S.F32) <= d.lds_block
+
+
+def test_rejections_have_reasons():
+    d = S.MI355X
+    assert S.check(256, 256, 256, S.F32, S.Cfg(0, 64, 64, 8, 1, 1, 1, 1), d) == S.R_DIV
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 1, 4, 1, 1), d) == S.R_SPACE
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 2, 4, 1, 1), d) == S.R_DIV
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 256, 32, 1, 1, 1, 1), d) == S.R_ACC
+    assert S.check(256, 256, 15, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(2, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
+    assert S.check(256, 256, 64, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 4), d) == S.R_SPLIT
+    assert S.check(100, 256, 256, S.BF16, S.Cfg(1, 112, 128, 32, 1, 1, 1, 1), d) == S.R_SPACE
+    assert S.check(100, 256, 256, S.BF16, S.Cfg(1, 64, 128, 32, 1, 1, 1, 1), d) == S.R_SHAPE
+    assert S.check(20, 256, 256, S.BF16, S.Cfg(1, 16, 128, 32, 1, 1, 1, 1), d) == S.R_SHAPE
+    assert S.check(20, 256, 256, S.F32, S.Cfg(1, 32, 128, 32, 1, 1, 1, 1), d) in (S.R_SPACE, S.R_DTYPE)
+    assert S.check(0, 256, 256, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 1), d) == S.R_SHAPE
+
+
+@pytest.mark.parametrize("M,N,K,dt", SHAPES)
+def test_model_invariants(M, N, K, dt):
+    d = S.MI355X
+    floor = (S.in_bytes(dt) * (M * K + K * N) + S.out_bytes(dt) * M * N) / d.bw
+    faster = dataclasses.replace(d, peak_bf16=2 * d.peak_bf16, peak_f32=2 * d.peak_f32, bw=2 * d.bw)
+    feas = S.enumerate_feasible(M, N, K, dt, d)
+    assert feas, "every shape has at least one feasible candidate"
+    for c in feas[:: max(1, len(feas) // 150)]:
+        t = S.model_time(M, N, K, dt, c, d)
+        assert t >= floor + d.t0 - 1e-18
+        assert S.model_time(M, N, K, dt, c, faster) <= t
+    best, bt = S.model_choice(M, N, K, dt, d)
+    assert all(S.model_time(M, N, K, dt, c, d) >= bt for c in feas)
+    # the default is always feasible (so it can always be measured)
+    assert S.check(M, N, K, dt, S.default_cfg(N, K, dt), d) == S.OK
+
+
+def test_wave_efficiency_one_when_work_divides_slots():
+    d = S.MI355X
+    # 128x128 tiles, W = 4 (one block fills a CU): 2048x2048 -> 256 tiles = one full round
+    c = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
+    t256 = S.model_time(2048, 2048, 4096, S.BF16, c, d)
+    # one extra tile row adds a whole second round: time (compute part) doubles
+    t257 = S.model_time(2048 + 128, 2048, 4096, S.BF16, c, d)
+    assert t257 > 1.9 * (t256 - d.t0)
+
+
+def test_skinny_only_for_small_m_and_bf16():
+    for M, N, K, dt in SHAPES:
+        kinds = {c.kind for c in S.enumerate_feasible(M, N, K, dt)}
+        if M <= 64 and dt != S.F32 and S.shape_aligned(N, K, dt):
+            assert S.KIND_SKINNY in kinds
+        else:
+            assert S.KIND_SKINNY not in kinds
+        assert (S.KIND_UNALIGNED in kinds) == (not S.shape_aligned(N, K, dt))
+
+
+def test_choice_tie_break_is_first_in_canonical_order():
+    feas = S.enumerate_feasible(4100, 3000, 1000, S.BF16)
+    assert feas == sorted(feas)
+    best, bt = S.model_choice(4100, 3000, 1000, S.BF16)
+    ties = [c for c in feas if S.model_time(4100, 3000, 1000, S.BF16, c) == bt]
+    assert best == ties[0]
