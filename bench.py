@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the autotuned fused GEMM on one MI355X.
+
+A step is one call of gemm_bias_act (cached autotuned configuration: key
+lookup, launch geometry, one kernel) on inputs already resident in HBM.  The
+headline line times the 1000 x 1000 x 8192 bf16 workload (fp32 output, the
+wave-quantisation case); the other four workloads are reported under
+"shapes" with their own throughput and roofline fraction.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
+                  [--report]   # also measure every feasible configuration
+                               # (best/worst/fixed ratios, model hit rate)
+                  [--copy-calib BYTES]   # plain copy for the HBM counter scale
+                  [--only]     # time only the chosen workload (for profiling)
+
+Prints one JSON line.  Needs the built library; the oracle is used only for
+the CPU-baseline leg.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from tile_shape_autotuning_amd import workloads as wl  # noqa: E402
+
+PEAK = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA TFLOP/s, MI355X spec
+HBM_PEAK = 8000.0                       # GB/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _dev(x, torch):
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def bound_of(w):
+    """HBM-bound when the roofline time of the bytes exceeds that of the flops."""
+    prec = "f32" if w.dtype == wl.F32 else "bf16"
+    t_flop = w.flops / (PEAK[prec] * 1e12)
+    t_mem = w.compulsory_bytes / (HBM_PEAK * 1e9)
+    return ("hbm" if t_mem > t_flop else "mfma"), prec
+
+
+class Prepared:
+    def __init__(self, index, torch, rotate=1):
+        import tile_shape_autotuning_amd as tg
+        self.w = w = wl.WORKLOADS[index]
+        self.index = index
+        A, B, bias = wl.workload_inputs(index)
+        self.A, self.B, self.bias = _dev(A, torch), _dev(B, torch), _dev(bias, torch)
+        self.Bs = [self.B] + [self.B.clone() for _ in range(rotate - 1)]
+        self.act = ["none", "relu", "gelu"][w.act]
+        self.out_dtype = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
+        self.C = torch.empty((w.M, w.N), dtype=self.out_dtype, device="cuda")
+        self.tg = tg
+        self.i = 0
+
+    def step(self):
+        B = self.Bs[self.i % len(self.Bs)]
+        self.i += 1
+        self.tg.gemm_bias_act(self.A, B, self.bias, act=self.act, out=self.C)
+
+
+def time_steps(p, steps, torch):
+    """Average seconds per step over `steps`, timed with HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        p.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) * 1e-3 / steps, wall
+
+
+def shape_summary(p, sec):
+    w = p.w
+    bound, prec = bound_of(w)
+    tflops = w.flops / sec / 1e12
+    gbs = w.compulsory_bytes / sec / 1e9
+    frac = gbs / HBM_PEAK if bound == "hbm" else tflops / PEAK[prec]
+    cfg, meas = p.tg.cache_lookup(w.M, w.N, w.K, w.dtype)
+    return {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": wl.DTYPE_NAMES[w.dtype],
+            "act": p.act, "us": round(sec * 1e6, 3), "TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 1),
+            "bound": bound, "roofline_frac": round(frac, 4), "cfg": list(cfg.astuple()),
+            "tuned_us": round(meas, 3)}
+
+
+def cpu_baseline(index, target_s=12.0):
+    """The oracle on a bounded row sample of the workload (host cores)."""
+    from oracle import gemm_ref
+    w = wl.WORKLOADS[index]
+    A, B, bias = wl.workload_inputs(index)
+    act = ["none", "relu", "gelu"][w.act]
+    rows = 4
+    t0 = time.perf_counter()
+    gemm_ref.gemm(A[:rows], B, bias, act)
+    dt = time.perf_counter() - t0
+    rows2 = int(max(rows, min(w.M, rows * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    gemm_ref.gemm(A[:rows2], B, bias, act)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows2 * w.N * w.K / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": gemm_ref.num_threads(), "kind": "oracle",
+            "sample": f"first {rows2} of {w.M} rows of {w.name} (full K and N), fp64 oracle, {dt:.1f} s"}
+
+
+def report(indices, torch):
+    """Measure every feasible configuration per workload with the library's
+    exhaustive tuner: best/worst/fixed ratios and the cost model's hit rate."""
+    import tile_shape_autotuning_amd as tg
+    from tile_shape_autotuning_amd import _native as N
+    out = {}
+    hits = 0
+    for i in indices:
+        w = wl.WORKLOADS[i]
+        os.environ["TILEGEMM_TUNE_MODE"] = "exhaustive"
+        os.environ["TILEGEMM_TUNE_SAMPLES"] = "5"
+        tg.cache_clear()
+        t0 = time.perf_counter()
+        tg.gemm_autotune(w.M, w.N, w.K, w.dtype)
+        tune_s = time.perf_counter() - t0
+        rows = [(c.astuple(), pred, meas) for c, pred, meas in tg.autotune_table(w.M, w.N, w.K, w.dtype)
+                if meas > 0]
+        best = min(rows, key=lambda r: r[2])
+        worst = max(rows, key=lambda r: r[2])
+        fixed = [r for r in rows if r[0] == tuple(tg.default_cfg(w.M, w.N, w.K, w.dtype).astuple())]
+        model_cfg, _ = tg.model_choice(w.M, w.N, w.K, w.dtype)
+        model_rows = [r for r in rows if r[0] == tuple(model_cfg.astuple())]
+        hit = bool(model_rows) and model_rows[0][0] == best[0]
+        hits += hit
+        # rank correlation between predicted and measured times
+        pr = np.argsort(np.argsort([r[1] for r in rows]))
+        mr = np.argsort(np.argsort([r[2] for r in rows]))
+        rho = float(np.corrcoef(pr, mr)[0, 1]) if len(rows) > 2 else float("nan")
+        out[w.name] = {
+            "measured": len(rows), "tune_s": round(tune_s, 2),
+            "best": {"cfg": list(best[0]), "us": round(best[2], 3)},
+            "worst": {"cfg": list(worst[0]), "us": round(worst[2], 3)},
+            "worst_over_best": round(worst[2] / best[2], 3),
+            "fixed_over_best": round(fixed[0][2] / best[2], 3) if fixed else None,
+            "model_choice": list(model_cfg.astuple()),
+            "model_choice_over_best": round(model_rows[0][2] / best[2], 3) if model_rows else None,
+            "model_hit": hit, "rank_corr": round(rho, 3),
+        }
+        log(f"report {w.name}: {out[w.name]}")
+    os.environ["TILEGEMM_TUNE_MODE"] = "hybrid"
+    tg.cache_clear()
+    return out, hits
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--only", action="store_true")
+    ap.add_argument("--report", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import tile_shape_autotuning_amd as tg
+    tg._native.lib()   # fails loudly if the library is missing
+
+    if a.copy_calib:
+        n = a.copy_calib // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {a.copy_calib} bytes")
+
+    main_idx = a.workload
+    indices = [main_idx] if a.only else [main_idx] + [i for i in sorted(wl.WORKLOADS) if i != main_idx]
+    shapes = {}
+    main_res = None
+    for i in indices:
+        rotate = 2 if wl.WORKLOADS[i].M <= 64 else 1     # decode: stream distinct weights every call
+        log(f"workload {i}: preparing")
+        p = Prepared(i, torch, rotate=rotate)
+        for _ in range(max(1, a.warmup)):               # first call tunes and caches
+            p.step()
+        torch.cuda.synchronize()
+        steps = a.steps if i == main_idx else max(10, min(a.steps, int(0.3 / max(1e-6, p.tg.cache_lookup(
+            p.w.M, p.w.N, p.w.K, p.w.dtype)[1] * 1e-6))))
+        sec, wall = time_steps(p, steps, torch)
+        s = shape_summary(p, sec)
+        s["steps"] = steps
+        shapes[p.w.name] = s
+        log(f"workload {i}: {s}")
+        if i == main_idx:
+            main_res = (p, sec, wall, steps)
+        else:
+            del p
+            torch.cuda.empty_cache()
+
+    p, sec, wall, steps = main_res
+    w = p.w
+    bound, prec = bound_of(w)
+    achieved = w.flops / sec / 1e12 if bound == "mfma" else w.compulsory_bytes / sec / 1e9
+    peak = PEAK[prec] if bound == "mfma" else HBM_PEAK
+    line = {
+        "metric": "autotuned GEMM TFLOP/s (or GB/s) per shape and % of MI355X roofline",
+        "value": round(w.flops * steps / (sec * steps) / 1e12, 3) if bound == "mfma" else round(achieved, 1),
+        "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": prec, "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "dtype": wl.DTYPE_NAMES[w.dtype], "act": p.act,
+                   "cfg": shapes[w.name]["cfg"], "parallelism": "single-gpu"},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+        "shapes": shapes,
+    }
+    if a.report:
+        rep, hits = report([i for i in indices], torch)
+        line["report"] = rep
+        line["model_hit_rate"] = f"{hits}/{len(indices)}"
+    if not a.no_cpu:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(main_idx)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * tilegemm -- fused GEMM with per-shape tile selection for AMD MI355X (gfx950).
+ *
+ * Operation (page "Tile Selection: Cost Models Against Measurement", opening
+ * section and "The structure of the search space"; epilogue fusion per page
+ * "Tiling the hierarchy", fusion section):
+ *
+ *     C[i][j] = act( sum_k A[i][k] * B[k][j] + bias[j] )
+ *
+ * Layouts: A is M x K, B is K x N, C is M x N, all row-major with leading
+ * dimensions K, N and N; bias is N float32 values or NULL (= 0).
+ *
+ * Every function is extern "C", never throws and returns a tg_status
+ * (0 = success).  On failure a message is available from tg_last_error() on
+ * the calling thread.  Device pointers are caller-owned; the library never
+ * retains or frees them.  C must not overlap A, B or bias.
+ */
+#ifndef TILEGEMM_H
+#define TILEGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_VERSION 1
+
+typedef enum {
+    TG_OK = 0,
+    TG_E_INVAL = -1,        /* bad argument (size, pointer, code) */
+    TG_E_INFEASIBLE = -2,   /* the configuration fails the feasibility filter for this shape */
+    TG_E_UNSUPPORTED = -3,  /* shape beyond the supported limits, or no device */
+    TG_E_HIP = -4,          /* a HIP runtime call failed */
+    TG_E_NOMEM = -5,        /* device or host allocation failed */
+    TG_E_CACHE = -6         /* tuning-cache file missing, unreadable or malformed */
+} tg_status;
+
+/* input -> output element types; accumulation is always fp32 */
+typedef enum {
+    TG_F32 = 0,          /* fp32 in, fp32 out */
+    TG_BF16 = 1,         /* bf16 in, bf16 out (round to nearest even) */
+    TG_BF16_F32OUT = 2   /* bf16 in, fp32 out */
+} tg_dtype;
+
+typedef enum {
+    TG_ACT_NONE = 0,
+    TG_ACT_RELU = 1,     /* max(0, x) */
+    TG_ACT_GELU = 2      /* 0.5 x (1 + erf(x / sqrt 2)) */
+} tg_act;
+
+typedef enum {
+    TG_KIND_TILED = 0,     /* block-tiled MFMA kernel, 16-byte vector loads */
+    TG_KIND_SKINNY = 1,    /* M <= 64 weight-streaming kernel (bf16 only) */
+    TG_KIND_UNALIGNED = 2  /* block-tiled kernel with element loads, for K or N
+                              not a multiple of the 16-byte vector */
+} tg_kind;
+
+/*
+ * One point of the tile space ("The structure of the search space": block
+ * tile, reduction step, per-thread tile; page "Compilers and Kernel
+ * Languages": pipeline depth and split-K are further choices).
+ *   tiled / unaligned: bm x bn block tile, bk reduction step, wgm x wgn waves
+ *       (64 lanes each) per workgroup, stages = LDS buffers (1 or 2),
+ *       split_k = workgroups sharing one tile's K range.
+ *   skinny: bm = 16 * ceil(M / 16), bn = 128 columns per workgroup, bk = 32,
+ *       wgm = waves per workgroup (each takes interleaved 32-row chunks of
+ *       K), wgn = 1, stages = chunks per pipelined step, split_k as above.
+ * Field order is the canonical order used for ties.
+ */
+typedef struct {
+    int32_t kind, bm, bn, bk, wgm, wgn, stages, split_k;
+} tg_cfg;
+
+/* Device description the selection rules use.  mode 0 = MI355X rules,
+ * mode 1 = replica of the H100 model on page "Compilers and Kernel Languages"
+ * ("Workshop").  Peaks in FLOP/s and bytes/s, times in seconds. */
+typedef struct {
+    int32_t mode, n_cu, simds, lds_cu, lds_block, max_threads, waves_max, blocks_max,
+            vgpr_max, acc_max, r0, reserved;
+    double peak_bf16, peak_f32, bw, a_ref, c_fill, t0, unaligned_eff, lat_mem, cu_bw;
+} tg_device_desc;
+
+/* One row of an autotuning table. */
+typedef struct {
+    tg_cfg cfg;
+    double predicted_us;   /* cost-model time */
+    double measured_us;    /* median measured time per launch, or -1 if not measured */
+} tg_tune_row;
+
+/* ---------------------------------------------------------------- errors */
+const char *tg_last_error(void);    /* thread-local; valid until the next call on this thread */
+int tg_version(void);
+
+/* ---------------------------------------------------------------- compute */
+/*
+ * Stream for later launches on this thread (a hipStream_t; NULL = the null
+ * stream).
+ */
+int tg_set_stream(void *hip_stream);
+
+/*
+ * C = act(A . B + bias) on the device current for this thread, on the stream
+ * set with tg_set_stream.  Asynchronous: returns once the kernel is queued,
+ * except that cfg == NULL with a shape not yet in the tuning cache first runs
+ * gemm_autotune (blocking), or takes the cost model's choice when the
+ * environment variable TILEGEMM_DISABLE_AUTOTUNE=1 is set.
+ *   M, N >= 0, K >= 0 (M or N = 0: nothing to do; K = 0: C = act(bias)).
+ *   A, B, C: device pointers, 16-byte aligned for the tiled and skinny kinds.
+ *   bias: device pointer to N floats, or NULL.
+ *   dtype: tg_dtype; act: tg_act; cfg: explicit configuration or NULL.
+ * Limits: K <= 2^21, N <= 2^21, M <= 2^31 - 1 (TG_E_UNSUPPORTED beyond).
+ * Errors: TG_E_INVAL (NULL pointer with a non-empty operand, bad code,
+ * negative size, misaligned pointer for the chosen kind), TG_E_INFEASIBLE
+ * (cfg fails the filter: nothing is launched), TG_E_HIP, TG_E_NOMEM.
+ * Split-K configurations use a library-owned workspace per device; launches
+ * on one device that use split-K must not run concurrently on different
+ * streams.
+ */
+int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                  const float *bias, void *C, int dtype, int act, const tg_cfg *cfg);
+
+/*
+ * Choose a configuration for (M, N, K, dtype) on the current device and store
+ * it in the tuning cache (page "Tile Selection: Cost Models Against
+ * Measurement", "Measurement, and what it must control" and "Hybrid
+ * strategies"): the feasibility filter, then the cost model ranks the
+ * survivors, then the best top_k plus the fixed default configuration are
+ * timed on scratch inputs of the workload's distribution, interleaved over
+ * several rounds, and the smallest median wins.  A cache hit returns at once
+ * without measuring.  Blocking.  Mode and top_k come from
+ * TILEGEMM_TUNE_MODE = hybrid (default) | model | exhaustive and
+ * TILEGEMM_TUNE_TOPK (default 16, at most 30).
+ */
+int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out);
+
+/* ---------------------------------------------------------------- selection queries (host only) */
+/* Feasible configurations in canonical order; writes at most cap, reports the total. */
+int tg_enumerate(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, int cap, int *n_feasible);
+/* The whole candidate space before filtering, canonical order. */
+int tg_space(int dtype, tg_cfg *out, int cap, int *n_total);
+/* Feasibility of one configuration: *reason = 0 if feasible, else the first failing rule:
+ * 1 dtype, 2 alignment, 3 shape, 4 waves, 5 divisibility, 6 LDS, 7 accumulators,
+ * 8 VGPR estimate, 9 occupancy, 10 split-K, 11 not in the space. */
+int tg_check_cfg(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, int *reason);
+/* Cost-model time of a feasible configuration, in microseconds. */
+int tg_model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, double *us);
+/* First feasible configuration with the smallest model time. */
+int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, double *us);
+/* Output tiles ceil(M/bm) * ceil(N/bn) and launched workgroups (tiles * split_k). */
+int tg_grid(int64_t M, int64_t N, int64_t K, const tg_cfg *cfg, int64_t *tiles, int64_t *blocks);
+/* The configuration autotuning is always compared against for this shape. */
+int tg_default_cfg(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out);
+/* Resource estimates the filter uses: LDS bytes, VGPRs per lane, workgroups per CU. */
+int tg_resources(int dtype, const tg_cfg *cfg, int *lds_bytes, int *vgprs, int *blocks_per_cu);
+/* Use desc for every selection rule (NULL = the real device / MI355X defaults). */
+int tg_set_device_override(const tg_device_desc *desc);
+/* The description in force (override, else the current device's, else MI355X defaults). */
+int tg_get_device_desc(tg_device_desc *out);
+/* Built-in descriptions: which = 0 MI355X, 1 H100 replica. */
+int tg_builtin_device_desc(int which, tg_device_desc *out);
+
+/* ---------------------------------------------------------------- kernel registry (host only) */
+/* Number of compiled kernel instantiations. */
+int tg_kernel_count(void);
+/* 1 if a compiled kernel serves cfg for dtype, else 0. */
+int tg_has_kernel(int dtype, const tg_cfg *cfg);
+/* What the compiler allotted to the kernel serving cfg (from its resource
+ * report at build time): out[0..4] = VGPRs, AGPRs, scratch bytes per lane
+ * (register spills), LDS bytes, waves per SIMD; -1 where unknown.
+ * TG_E_INFEASIBLE if no kernel serves cfg.  The autotuner skips kernels that
+ * spill (set TILEGEMM_ALLOW_SPILLS=1 to keep them). */
+int tg_kernel_resources(int dtype, const tg_cfg *cfg, int *out5);
+
+/* ---------------------------------------------------------------- tuning cache */
+/* Table of the last tuning run for this key (GPU): every measured candidate
+ * plus the model's time; rows in measurement order. */
+int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, tg_tune_row *rows, int cap, int *n);
+/* Cached entry for the key on the current device: *hit = 1 and *out filled, or *hit = 0. */
+int tg_cache_lookup(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, double *measured_us, int *hit);
+/* Persist / restore the cache as text, one line per key (arch, CU count,
+ * library version, M, N, K, dtype -> cfg, measured and predicted us).
+ * Loading skips lines for another library version; a malformed file is
+ * TG_E_CACHE and leaves the cache unchanged. */
+int tg_cache_save(const char *path);
+int tg_cache_load(const char *path, int *n_loaded, int *n_skipped);
+void tg_cache_clear(void);
+int tg_cache_size(void);
+/* Counters: tuning runs, timed launches, cache hits served by gemm_bias_act. */
+int tg_stats(int64_t *n_tunes, int64_t *n_timed_launches, int64_t *n_cache_hits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEGEMM_H */

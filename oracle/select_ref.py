@@ -159,7 +159,7 @@ def space(dtype: int, dev: Device = MI355X):
     if dtype == F32:
         tiles_mn, bks = (32, 64, 128), (8, 16, 32)
     else:
-        tiles_mn, bks = (32, 64, 128, 256), (32, 64, 128)
+        tiles_mn, bks = (32, 64, 128, 256), (32, 64)
     for bm, bn, bk, (wm, wn), st, s in itertools.product(
             tiles_mn, tiles_mn, bks, WAVE_GRIDS, (1, 2), SPLITS):
         out.append(Cfg(KIND_TILED, bm, bn, bk, wm, wn, st, s))
@@ -191,7 +191,9 @@ def acc_regs(c: Cfg) -> int:
 def vgpr_estimate(c: Cfg, dtype: int, dev: Device) -> int:
     if c.kind == KIND_SKINNY:
         mt = c.bm // 16
-        return 32 * c.stages + 32 * mt + 4 * mt + dev.r0
+        # two register sets of in-flight B (8 x 16 B per chunk) and A (16 B per
+        # M tile) per chunk, U = stages chunks each, plus the accumulators
+        return 64 * c.stages + 8 * c.stages * mt + 32 * mt + dev.r0
     threads = 64 * c.wgm * c.wgn
     eb = in_bytes(dtype)
     frag = 4 * ((c.bm // c.wgm) // 16 + (c.bn // c.wgn) // 16)
@@ -224,6 +226,28 @@ def k_per_split(c: Cfg, K: int) -> int:
     return cdiv(cdiv(K, c.split_k), unit) * unit
 
 
+def check_static(dtype: int, c: Cfg, dev: Device = MI355X) -> int:
+    """The rules that do not depend on the shape: threads, whole MFMA tiles
+    per wave, LDS, accumulator and VGPR budgets, at least one resident
+    workgroup per CU."""
+    w = c.wgm * c.wgn
+    if 64 * w > dev.max_threads:
+        return R_WAVES
+    if c.kind != KIND_SKINNY:
+        kstep = 16 if dtype == F32 else 32
+        if c.bm % (16 * c.wgm) or c.bn % (16 * c.wgn) or c.bk % kstep:
+            return R_DIV
+    if lds_bytes(c, dtype) > dev.lds_block:
+        return R_LDS
+    if acc_regs(c) > dev.acc_max:
+        return R_ACC
+    if vgpr_estimate(c, dtype, dev) > dev.vgpr_max:
+        return R_VGPR
+    if blocks_per_cu(c, dtype, dev) < 1:
+        return R_OCC
+    return OK
+
+
 def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> int:
     """Feasibility of one candidate: OK, or the code of the first failing rule."""
     if dtype not in (F32, BF16, BF16_F32OUT):
@@ -242,21 +266,9 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
             return R_ALIGN
     if c.kind == KIND_SKINNY and (M > 64 or c.bm != 16 * cdiv(M, 16)):
         return R_SHAPE
-    w = c.wgm * c.wgn
-    if 64 * w > dev.max_threads:
-        return R_WAVES
-    if c.kind != KIND_SKINNY:
-        kstep = 16 if dtype == F32 else 32
-        if c.bm % (16 * c.wgm) or c.bn % (16 * c.wgn) or c.bk % kstep:
-            return R_DIV
-    if lds_bytes(c, dtype) > dev.lds_block:
-        return R_LDS
-    if acc_regs(c) > dev.acc_max:
-        return R_ACC
-    if vgpr_estimate(c, dtype, dev) > dev.vgpr_max:
-        return R_VGPR
-    if blocks_per_cu(c, dtype, dev) < 1:
-        return R_OCC
+    r = check_static(dtype, c, dev)
+    if r != OK:
+        return r
     if c.split_k > 1:
         if K == 0 or cdiv(K, k_per_split(c, K)) != c.split_k:
             return R_SPLIT

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+* Integer-exact inputs (entries in {-2..2}, integer bias, K small enough that
+  every partial sum is an integer below 2^24): fp32 accumulation is exact in
+  any order, so every feasible configuration -- every tile, wave grid,
+  pipeline depth, split-K and edge tile -- must match the oracle bitwise
+  (fp32 output) or be exactly the round-to-nearest-even bf16 of it.
+* The five workloads with the autotuned and the fixed default
+  configuration, within max|err| <= tol * max|C_ref| (tol 1e-4 for fp32
+  inputs, 1e-2 for bf16 inputs); the full output where the oracle is quick,
+  sampled entries (oracle computes them one by one) for the 8192^3 case.
+* Edge shapes, empty and K = 0 problems, determinism, maximum sizes.
+"""
+import numpy as np
+import pytest
+
+from oracle import gemm_ref
+from oracle import select_ref as S
+from tile_shape_autotuning_amd import workloads as wl
+
+from gpu_util import assert_close, mark, out_bits, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+tg = pytest.importorskip("tile_shape_autotuning_amd")
+
+ACT_NAMES = ["none", "relu", "gelu"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg._native.lib()
+    tg.set_device_override(None)
+    yield
+    torch.cuda.synchronize()
+
+
+def _int_inputs(M, N, K, dtype, seed):
+    return wl.make_inputs(M, N, K, dtype, wl.Dist("int", 2), wl.Dist("int", 2), wl.Dist("int", 4), seed)
+
+
+def _run(A_d, B_d, bias_d, act, dtype, cfg=None):
+    out_dtype = torch.float32 if dtype in (wl.F32, wl.BF16_F32OUT) else torch.bfloat16
+    return tg.gemm_bias_act(A_d, B_d, bias_d, act=act, out_dtype=out_dtype, cfg=cfg)
+
+
+def _exact_check(C, ref, dtype, what):
+    if dtype == wl.BF16:
+        want = wl.f32_to_bf16_bits(ref.astype(np.float32))
+        got = out_bits(C)
+        bad = np.count_nonzero(got != want)
+        assert bad == 0, f"{what}: {bad} of {want.size} bf16 outputs differ from RNE(exact)"
+    else:
+        got = out_f64(C)
+        bad = np.count_nonzero(got != ref)
+        assert bad == 0, f"{what}: {bad} of {ref.size} outputs differ from the exact result"
+
+
+def test_first_kernel_default_cfg_integer_exact():
+    for dtype in (wl.BF16, wl.F32, wl.BF16_F32OUT):
+        M = N = K = 256
+        A, B, bias = _int_inputs(M, N, K, dtype, 1)
+        ref = gemm_ref.gemm(A, B, bias, "relu")
+        cfg = S.default_cfg(N, K, dtype).astuple()
+        mark(f"default cfg {cfg} dtype {dtype} 256^3")
+        C = _run(to_dev(A), to_dev(B), to_dev(bias), "relu", dtype, cfg)
+        torch.cuda.synchronize()
+        _exact_check(C, ref, dtype, f"dtype {dtype} cfg {cfg}")
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [
+    (200, 136, 328, wl.BF16),         # ragged in M and N, K not a multiple of 64
+    (96, 264, 520, wl.BF16_F32OUT),
+    (130, 100, 260, wl.F32),          # fp32: ragged everywhere, K mod 16 = 4
+    (40, 200, 300, wl.F32),
+])
+def test_every_feasible_cfg_integer_exact(M, N, K, dtype):
+    A, B, bias = _int_inputs(M, N, K, dtype, 2)
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    feas = [c for c in tg.enumerate_feasible(M, N, K, dtype) if tg.has_kernel(dtype, c)]
+    assert len(feas) > 50
+    for c in feas:
+        mark(f"sweep {M}x{N}x{K} dt{dtype} {c.astuple()}")
+        C = _run(A_d, B_d, b_d, "relu", dtype, c)
+        torch.cuda.synchronize()
+        _exact_check(C, ref, dtype, f"{M}x{N}x{K} dt{dtype} {c.astuple()}")
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [
+    (17, 65, 15, wl.BF16), (63, 17, 1, wl.F32), (1, 1, 1, wl.BF16), (65, 33, 63, wl.BF16_F32OUT),
+    (300, 47, 129, wl.F32), (5, 1000, 77, wl.BF16),
+])
+def test_unaligned_shapes_integer_exact(M, N, K, dtype):
+    A, B, bias = _int_inputs(M, N, K, dtype, 3)
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    feas = tg.enumerate_feasible(M, N, K, dtype)
+    assert feas and all(c.kind == S.KIND_UNALIGNED for c in feas)
+    for c in feas:
+        mark(f"unaligned {M}x{N}x{K} dt{dtype} {c.astuple()}")
+        C = _run(A_d, B_d, b_d, "relu", dtype, c)
+        torch.cuda.synchronize()
+        _exact_check(C, ref, dtype, f"{M}x{N}x{K} {c.astuple()}")
+    mark(f"unaligned {M}x{N}x{K} dt{dtype} autotuned")
+    C = _run(A_d, B_d, b_d, "relu", dtype)
+    torch.cuda.synchronize()
+    _exact_check(C, ref, dtype, f"{M}x{N}x{K} autotuned")
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 31, 48, 64])
+def test_skinny_kernels_integer_exact(M):
+    N, K = 1032, 1064
+    for dtype in (wl.BF16, wl.BF16_F32OUT):
+        A, B, bias = _int_inputs(M, N, K, dtype, 4)
+        ref = gemm_ref.gemm(A, B, bias, "none")
+        A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+        feas = [c for c in tg.enumerate_feasible(M, N, K, dtype) if c.kind == S.KIND_SKINNY]
+        assert feas
+        for c in feas:
+            if not tg.has_kernel(dtype, c):
+                continue
+            mark(f"skinny M={M} dt{dtype} {c.astuple()}")
+            C = _run(A_d, B_d, b_d, "none", dtype, c)
+            torch.cuda.synchronize()
+            _exact_check(C, ref, dtype, f"skinny M={M} {c.astuple()}")
+
+
+@pytest.mark.parametrize("act", ACT_NAMES)
+def test_activations_random_inputs(act):
+    M, N, K = 333, 200, 512
+    for dtype in (wl.F32, wl.BF16):
+        A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("normal", 0.1), wl.Dist("normal", 0.1),
+                                    wl.Dist("normal", 0.5), 5)
+        ref = gemm_ref.gemm(A, B, bias, act)
+        mark(f"act {act} dt{dtype}")
+        C = _run(to_dev(A), to_dev(B), to_dev(bias), act, dtype, S.default_cfg(N, K, dtype).astuple())
+        torch.cuda.synchronize()
+        assert_close(out_f64(C), ref, dtype, f"act {act} dtype {dtype}")
+
+
+def test_empty_and_k_zero():
+    for dtype in (wl.F32, wl.BF16):
+        mark(f"K=0 dt{dtype}")
+        A, B, bias = _int_inputs(37, 24, 0, dtype, 6)
+        A_d = torch.zeros((37, 0), device="cuda", dtype=torch.float32 if dtype == wl.F32 else torch.bfloat16)
+        B_d = torch.zeros((0, 24), device="cuda", dtype=A_d.dtype)
+        C = _run(A_d, B_d, to_dev(bias), "relu", dtype)
+        torch.cuda.synchronize()
+        _exact_check(C, np.maximum(np.broadcast_to(bias.astype(np.float64), (37, 24)), 0.0), dtype, "K=0")
+        mark(f"M=0 dt{dtype}")
+        C = _run(torch.zeros((0, 8), device="cuda", dtype=A_d.dtype),
+                 torch.zeros((8, 16), device="cuda", dtype=A_d.dtype), None, "none", dtype)
+        assert C.shape == (0, 16)
+
+
+def test_split_k_deterministic_and_exact():
+    M, N, K = 256, 512, 4096
+    dtype = wl.BF16_F32OUT
+    A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("normal"), wl.Dist("normal"), wl.Dist("normal"), 7)
+    ref = gemm_ref.gemm(A, B, bias, "gelu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    for s in (1, 2, 4, 8, 16):
+        cfg = (0, 128, 128, 64, 2, 2, 2, s)
+        mark(f"split {s}")
+        C1 = _run(A_d, B_d, b_d, "gelu", dtype, cfg)
+        C2 = _run(A_d, B_d, b_d, "gelu", dtype, cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(C1, C2), f"split {s}: two runs differ"
+        assert_close(out_f64(C1), ref, dtype, f"split {s}")
+
+
+def _workload_parity(index, cfgs, sample=None):
+    w = wl.WORKLOADS[index]
+    A, B, bias = wl.workload_inputs(index)
+    act = ACT_NAMES[w.act]
+    if sample is None:
+        ref = gemm_ref.gemm(A, B, bias, act)
+    else:
+        rng = np.random.default_rng(100 + index)
+        rows = np.concatenate([rng.integers(0, w.M, sample), [0, w.M - 1, w.M - 1, 0]])
+        cols = np.concatenate([rng.integers(0, w.N, sample), [0, w.N - 1, 0, w.N - 1]])
+        ref = gemm_ref.gemm_entries(A, B, rows, cols, bias, act)
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    for cfg in cfgs:
+        mark(f"workload {index} cfg {cfg}")
+        C = _run(A_d, B_d, b_d, act, w.dtype, cfg)
+        torch.cuda.synchronize()
+        got = out_f64(C) if sample is None else out_f64(C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+        assert np.all(np.isfinite(got))
+        assert_close(got, ref, w.dtype, f"workload {index} cfg {cfg}")
+
+
+def test_workload1_fp32_every_feasible_cfg():
+    w = wl.WORKLOADS[1]
+    feas = [c.astuple() for c in tg.enumerate_feasible(w.M, w.N, w.K, w.dtype) if tg.has_kernel(w.dtype, c)]
+    _workload_parity(1, [None] + feas)
+
+
+def test_workload2_wave_quantisation():
+    w = wl.WORKLOADS[2]
+    _workload_parity(2, [None, S.default_cfg(w.N, w.K, w.dtype).astuple(), (0, 64, 64, 64, 2, 2, 2, 1),
+                         (0, 128, 128, 64, 2, 2, 2, 4)])
+
+
+def test_workload3_square_sampled():
+    w = wl.WORKLOADS[3]
+    _workload_parity(3, [None, S.default_cfg(w.N, w.K, w.dtype).astuple()], sample=3000)
+
+
+def test_workload4_decode():
+    _workload_parity(4, [None, (0, 128, 128, 64, 2, 2, 2, 1), (1, 16, 128, 32, 4, 1, 2, 4)])
+
+
+def test_workload5_ragged():
+    w = wl.WORKLOADS[5]
+    feas = [c.astuple() for c in tg.enumerate_feasible(w.M, w.N, w.K, w.dtype)
+            if tg.has_kernel(w.dtype, c) and c.split_k == 1]
+    _workload_parity(5, [None] + feas[::9])
+
+
+def test_max_sizes():
+    # K at its limit (2^21) with a skinny M; N at its limit; a tall M
+    for (M, N, K, dtype) in [(16, 64, 1 << 21, wl.BF16_F32OUT), (8, 1 << 21, 64, wl.BF16),
+                             (1 << 20, 64, 64, wl.BF16), (3, 1 << 20, 40, wl.F32)]:
+        mark(f"max size {M}x{N}x{K} dt{dtype}")
+        A, B, bias = _int_inputs(M, N, K, dtype, 8)
+        rng = np.random.default_rng(9)
+        rows = rng.integers(0, M, 512)
+        cols = rng.integers(0, N, 512)
+        ref = gemm_ref.gemm_entries(A, B, rows, cols, bias, "none")
+        C = _run(to_dev(A), to_dev(B), to_dev(bias), "none", dtype)
+        torch.cuda.synchronize()
+        got = out_f64(C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+        if dtype == wl.BF16:
+            want = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+            assert np.array_equal(got, want)
+        else:
+            assert np.array_equal(got, ref)
+    with pytest.raises(tg.TileGemmError):
+        tg._native.check(tg._native.gemm_bias_act_ptr(4, 4, (1 << 21) + 8, 256, 256, 0, 256, wl.BF16, 0))

@@ -1,0 +1,95 @@
+"""GPU tests of the measuring autotuner and the shape-keyed cache.
+
+Page "Tile Selection: Cost Models Against Measurement" ("Measurement, and
+what it must control"; cache keyed by shape, dtype, device and version) and
+page "CuTile Autotuning" (the fixed configuration is always measured, so
+tuning never loses to it; correctness with tuning on and off).
+"""
+import numpy as np
+import pytest
+
+from oracle import gemm_ref
+from oracle import select_ref as S
+from tile_shape_autotuning_amd import workloads as wl
+
+from gpu_util import assert_close, mark, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+tg = pytest.importorskip("tile_shape_autotuning_amd")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.set_device_override(None)
+
+
+def test_autotune_measures_default_and_picks_argmin(monkeypatch):
+    monkeypatch.setenv("TILEGEMM_TUNE_MODE", "hybrid")
+    M, N, K, dtype = 4100, 3000, 1000, wl.BF16
+    tg.cache_clear()
+    s0 = tg.stats()
+    mark("autotune 4100x3000x1000 bf16")
+    c = tg.gemm_autotune(M, N, K, dtype)
+    s1 = tg.stats()
+    assert s1["tunes"] == s0["tunes"] + 1 and s1["timed_launches"] > s0["timed_launches"]
+    table = tg.autotune_table(M, N, K, dtype)
+    measured = [(row[0].astuple(), row[2]) for row in table if row[2] > 0]
+    assert len(measured) >= 2
+    default = S.default_cfg(N, K, dtype).astuple()
+    assert default in [m[0] for m in measured], "the fixed default must be measured"
+    best = min(measured, key=lambda m: m[1])
+    assert c.astuple() == best[0]
+    assert best[1] <= dict(measured)[default]
+    # every measured candidate is feasible and has a kernel that does not spill
+    for cfg, _ in measured:
+        assert tg.check_cfg(M, N, K, dtype, cfg) == 0
+        assert tg.kernel_resources(dtype, cfg)[2] == 0
+    # second request: cache hit, no new tuning
+    assert tg.gemm_autotune(M, N, K, dtype).astuple() == c.astuple()
+    assert tg.stats()["tunes"] == s1["tunes"]
+    # gemm_bias_act without a cfg serves the cached choice and counts a hit
+    A, B, bias = wl.workload_inputs(5)
+    mark("cached launch 4100x3000x1000")
+    C = tg.gemm_bias_act(to_dev(A), to_dev(B), to_dev(bias), act="relu")
+    torch.cuda.synchronize()
+    assert tg.stats()["cache_hits"] == s1["cache_hits"] + 1
+    rng = np.random.default_rng(1)
+    rows, cols = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+    ref = gemm_ref.gemm_entries(A, B, rows, cols, bias, "relu")
+    got = out_f64(C)[rows, cols]
+    assert_close(got, ref, dtype, "cached choice")
+
+
+def test_disable_autotune_uses_model_choice(monkeypatch):
+    monkeypatch.setenv("TILEGEMM_DISABLE_AUTOTUNE", "1")
+    tg.cache_clear()
+    s0 = tg.stats()
+    M, N, K, dtype = 1000, 1000, 8192, wl.BF16_F32OUT
+    A, B, _ = wl.workload_inputs(2)
+    mark("disable-autotune 1000x1000x8192")
+    C = tg.gemm_bias_act(to_dev(A), to_dev(B), None, act="none", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert tg.stats()["tunes"] == s0["tunes"]
+    rng = np.random.default_rng(2)
+    rows, cols = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+    ref = gemm_ref.gemm_entries(A, B, rows, cols, None, "none")
+    assert_close(out_f64(C)[rows, cols], ref, dtype, "model choice")
+
+
+def test_cache_roundtrip_on_device(tmp_path, monkeypatch):
+    monkeypatch.setenv("TILEGEMM_TUNE_MODE", "hybrid")
+    monkeypatch.setenv("TILEGEMM_TUNE_TOPK", "4")
+    tg.cache_clear()
+    mark("autotune 256^3 f32 topk 4")
+    c = tg.gemm_autotune(256, 256, 256, wl.F32)
+    p = str(tmp_path / "tune.txt")
+    tg.cache_save(p)
+    tg.cache_clear()
+    assert tg.cache_lookup(256, 256, 256, wl.F32) is None
+    assert tg.cache_load(p) == (1, 0)
+    hit = tg.cache_lookup(256, 256, 256, wl.F32)
+    assert hit is not None and hit[0].astuple() == c.astuple() and hit[1] > 0

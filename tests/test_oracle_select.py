@@ -136,8 +136,11 @@ def test_lds_examples():
     assert S.lds_bytes(two, S.BF16) == 2 * 64 * 1024
     assert S.check(8192, 8192, 8192, S.BF16, two, d) == S.OK
     big = S.Cfg(S.KIND_TILED, 256, 256, 128, 2, 2, 2, 1)
-    assert S.lds_bytes(big, S.BF16) == 256 * 1024
-    assert S.check(8192, 8192, 8192, S.BF16, big, d) == S.R_LDS
+    assert S.lds_bytes(big, S.BF16) == 256 * 1024 > d.lds_block
+    assert S.check(8192, 8192, 8192, S.BF16, big, d) == S.R_SPACE   # bf16 BK is 32 or 64
+    # the largest bf16 tiles at one stage fit; fp32 128x128x32 two stages fit
+    assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 1, 1), d) == S.OK
+    assert S.lds_bytes(S.Cfg(0, 128, 128, 32, 2, 2, 2, 1), S.F32) == 2 * (128 * 32 + 32 * 132) * 4
     # all 18 fp32 sweep triples fit LDS at one stage
     for bm in (32, 64, 128):
         for bn in (32, 64, 128):

@@ -1,0 +1,484 @@
+// C ABI of the fused GEMM library: argument checking, device description,
+// launch geometry, split-K workspace, and the selection queries.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "registry.hpp"
+#include "runtime.hpp"
+#include "select.hpp"
+
+namespace tg {
+
+// ------------------------------------------------------------------ errors
+static thread_local std::string t_err;
+
+int set_error(int status, const std::string& msg)
+{
+    t_err = msg;
+    return status;
+}
+
+int set_hip_error(hipError_t e, const char* what)
+{
+    return set_error(TG_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------------ device description
+static std::mutex g_desc_mu;
+static bool g_override_set = false;
+static tg_device_desc g_override;
+
+struct DevInfo {
+    bool valid = false;
+    tg_device_desc desc{};
+    DeviceKey key;
+};
+static std::vector<DevInfo> g_devs;
+
+static int device_count()
+{
+    static int n = -1;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int c = 0;
+        if (hipGetDeviceCount(&c) != hipSuccess)
+            c = 0;
+        n = c;
+    });
+    return n;
+}
+
+bool have_device() { return device_count() > 0; }
+
+// caller holds g_desc_mu
+static const DevInfo* real_device_info()
+{
+    if (!have_device())
+        return nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    if ((int)g_devs.size() <= dev)
+        g_devs.resize(dev + 1);
+    DevInfo& di = g_devs[dev];
+    if (!di.valid) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess)
+            return nullptr;
+        di.desc = mi355x_desc();
+        di.desc.n_cu = p.multiProcessorCount;
+        if (p.maxSharedMemoryPerMultiProcessor > 0)
+            di.desc.lds_cu = (int32_t)p.maxSharedMemoryPerMultiProcessor;
+        if (p.sharedMemPerBlock > 0)
+            di.desc.lds_block = (int32_t)std::min<size_t>(p.sharedMemPerBlock, (size_t)di.desc.lds_cu);
+        std::string arch = p.gcnArchName;
+        const size_t colon = arch.find(':');
+        if (colon != std::string::npos)
+            arch = arch.substr(0, colon);
+        di.key = DeviceKey{arch, p.multiProcessorCount};
+        di.valid = true;
+    }
+    return &di;
+}
+
+tg_device_desc current_desc()
+{
+    std::lock_guard<std::mutex> lk(g_desc_mu);
+    if (g_override_set)
+        return g_override;
+    if (const DevInfo* di = real_device_info())
+        return di->desc;
+    return mi355x_desc();
+}
+
+DeviceKey current_key()
+{
+    std::lock_guard<std::mutex> lk(g_desc_mu);
+    if (g_override_set)
+        return DeviceKey{g_override.mode == 1 ? "h100-replica" : "gfx950-override", g_override.n_cu};
+    if (const DevInfo* di = real_device_info())
+        return di->key;
+    return DeviceKey{"gfx950-nodevice", 256};
+}
+
+// ------------------------------------------------------------------ stream
+static thread_local hipStream_t t_stream = nullptr;
+hipStream_t current_stream() { return t_stream; }
+
+// ------------------------------------------------------------------ workspace
+struct Workspace {
+    float* ws = nullptr;
+    size_t ws_bytes = 0;
+    unsigned* counters = nullptr;
+    size_t n_counters = 0;
+};
+static std::mutex g_ws_mu;
+static std::vector<Workspace> g_ws;
+
+size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& c)
+{
+    if (c.split_k <= 1)
+        return 0;
+    int64_t tiles, blocks;
+    grid(M, N, c, &tiles, &blocks);
+    return (size_t)blocks * (size_t)c.bm * (size_t)c.bn * sizeof(float);
+}
+
+int ensure_workspace(size_t ws_bytes, size_t n_counters, float** ws, unsigned** counters)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return set_hip_error(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if ((int)g_ws.size() <= dev)
+        g_ws.resize(dev + 1);
+    Workspace& w = g_ws[dev];
+    if (w.ws_bytes < ws_bytes || w.n_counters < n_counters) {
+        // the old buffers may still be in use by queued kernels
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess)
+            return set_hip_error(e, "hipDeviceSynchronize (workspace growth)");
+        const size_t nb = std::max(ws_bytes, w.ws_bytes);
+        const size_t nc = std::max(n_counters, w.n_counters);
+        if (w.ws_bytes < nb) {
+            if (w.ws)
+                (void)hipFree(w.ws);
+            w.ws = nullptr;
+            w.ws_bytes = 0;
+            e = hipMalloc(&w.ws, nb);
+            if (e != hipSuccess)
+                return set_error(TG_E_NOMEM, std::string("split-K workspace: ") + hipGetErrorString(e));
+            w.ws_bytes = nb;
+        }
+        if (w.n_counters < nc) {
+            if (w.counters)
+                (void)hipFree(w.counters);
+            w.counters = nullptr;
+            w.n_counters = 0;
+            e = hipMalloc(&w.counters, nc * sizeof(unsigned));
+            if (e != hipSuccess)
+                return set_error(TG_E_NOMEM, std::string("split-K counters: ") + hipGetErrorString(e));
+            e = hipMemset(w.counters, 0, nc * sizeof(unsigned));
+            if (e != hipSuccess)
+                return set_hip_error(e, "hipMemset (split-K counters)");
+            w.n_counters = nc;
+        }
+    }
+    *ws = w.ws;
+    *counters = w.counters;
+    return TG_OK;
+}
+
+// ------------------------------------------------------------------ launch
+static constexpr int64_t kMaxKN = int64_t(1) << 21;
+static constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
+
+int validate_problem(int64_t M, int64_t N, int64_t K, int dtype)
+{
+    if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_BF16_F32OUT)
+        return set_error(TG_E_INVAL, "unknown dtype " + std::to_string(dtype));
+    if (M < 0 || N < 0 || K < 0)
+        return set_error(TG_E_INVAL, "negative dimension");
+    if (K > kMaxKN || N > kMaxKN || M > kMaxM)
+        return set_error(TG_E_UNSUPPORTED, "shape beyond the supported limits (K, N <= 2^21, M < 2^31)");
+    return TG_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, void* C,
+               int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked)
+{
+    const tg_device_desc d = current_desc();
+    tg_cfg c = cfg;
+    bool misaligned = !(aligned16(A) && aligned16(B) && aligned16(C));
+    if (c.kind != TG_KIND_UNALIGNED && misaligned) {
+        if (!pointers_checked)
+            return set_error(TG_E_INVAL, "A, B and C must be 16-byte aligned for the tiled and skinny kinds");
+        // selection ran without knowing the pointers: fall back to the element-load kernel
+        c = tg_cfg{TG_KIND_UNALIGNED, 64, 64, dtype == TG_F32 ? 16 : 32, 2, 2, 2, 1};
+    } else {
+        const int r = check(M, N, K, dtype, c, d);
+        if (r != OK)
+            return set_error(TG_E_INFEASIBLE, "configuration infeasible for this shape (rule " +
+                                                  std::to_string(r) + ")");
+    }
+    if (bias && ((uintptr_t)bias & 3u))
+        return set_error(TG_E_INVAL, "bias must be 4-byte aligned");
+    if (c.kind == TG_KIND_SKINNY && bias && misaligned)
+        return set_error(TG_E_INVAL, "misaligned pointers");
+    const KernelEntry* ke = find_kernel(dtype, c);
+    if (!ke)
+        return set_error(TG_E_INFEASIBLE, "no compiled kernel for this configuration");
+
+    GemmParams p{};
+    p.A = A;
+    p.B = B;
+    p.bias = bias;
+    p.C = C;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.kps = (int)k_per_split(c, K);
+    p.split = c.split_k;
+    if (c.kind == TG_KIND_SKINNY) {
+        p.tiles_m = 1;
+        p.tiles_n = (int)((N + 127) / 128);
+    } else {
+        p.tiles_m = (int)((M + c.bm - 1) / c.bm);
+        p.tiles_n = (int)((N + c.bn - 1) / c.bn);
+    }
+    p.out_bf16 = dtype == TG_BF16 ? 1 : 0;
+    p.act = act;
+    static const int group_m = [] {
+        const char* s = std::getenv("TILEGEMM_GROUP_M");
+        const int v = s ? std::atoi(s) : 0;
+        return v > 0 ? v : 8;
+    }();
+    p.group_m = group_m;
+    int64_t tiles, blocks;
+    grid(M, N, c, &tiles, &blocks);
+    if (blocks > 0x7FFFFFFF)
+        return set_error(TG_E_UNSUPPORTED, "too many workgroups");
+    if (c.split_k > 1) {
+        const int st = ensure_workspace(workspace_bytes_for(M, N, c), (size_t)tiles, &p.ws, &p.counters);
+        if (st != TG_OK)
+            return st;
+    }
+    hipError_t e = ke->launch(p, (int)blocks, stream);
+    if (e != hipSuccess)
+        return set_hip_error(e, "kernel launch");
+    return TG_OK;
+}
+
+}  // namespace tg
+
+using namespace tg;
+
+extern "C" {
+
+const char* tg_last_error(void) { return t_err.c_str(); }
+
+int tg_version(void) { return TG_VERSION; }
+
+int tg_set_stream(void* hip_stream)
+{
+    t_stream = static_cast<hipStream_t>(hip_stream);
+    return TG_OK;
+}
+
+int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, void* C,
+                  int dtype, int act, const tg_cfg* cfg)
+{
+    int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    if (act < TG_ACT_NONE || act > TG_ACT_GELU)
+        return set_error(TG_E_INVAL, "unknown activation " + std::to_string(act));
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (!C || (K > 0 && (!A || !B)))
+        return set_error(TG_E_INVAL, "NULL pointer for a non-empty operand");
+    if (!have_device())
+        return set_error(TG_E_UNSUPPORTED, "no HIP device");
+    tg_cfg c;
+    bool from_selection = false;
+    if (cfg) {
+        c = *cfg;
+    } else {
+        from_selection = true;
+        double us;
+        if (cache_find(M, N, K, dtype, &c, &us)) {
+            count_cache_hit();
+        } else {
+            const char* dis = std::getenv("TILEGEMM_DISABLE_AUTOTUNE");
+            if (dis && std::strcmp(dis, "0") != 0 && dis[0]) {
+                if (!model_choice(M, N, K, dtype, current_desc(), &c, nullptr))
+                    return set_error(TG_E_INFEASIBLE, "no feasible configuration");
+            } else {
+                st = autotune(M, N, K, dtype, &c);
+                if (st != TG_OK)
+                    return st;
+            }
+        }
+    }
+    return launch_cfg(M, N, K, A, B, bias, C, dtype, act, c, current_stream(), from_selection);
+}
+
+int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
+{
+    if (!out)
+        return set_error(TG_E_INVAL, "out is NULL");
+    const int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return set_error(TG_E_INVAL, "empty problem has nothing to tune");
+    return autotune(M, N, K, dtype, out);
+}
+
+int tg_enumerate(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, int cap, int* n_feasible)
+{
+    const int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    if (cap < 0 || (cap > 0 && !out))
+        return set_error(TG_E_INVAL, "bad output buffer");
+    const std::vector<tg_cfg> v = enumerate_feasible(M, N, K, dtype, current_desc());
+    const int n = (int)std::min<size_t>(v.size(), (size_t)cap);
+    if (n > 0)
+        std::memcpy(out, v.data(), n * sizeof(tg_cfg));
+    if (n_feasible)
+        *n_feasible = (int)v.size();
+    return TG_OK;
+}
+
+int tg_space(int dtype, tg_cfg* out, int cap, int* n_total)
+{
+    if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_BF16_F32OUT)
+        return set_error(TG_E_INVAL, "unknown dtype");
+    if (cap < 0 || (cap > 0 && !out))
+        return set_error(TG_E_INVAL, "bad output buffer");
+    const auto& sp = space(dtype, current_desc());
+    const int n = (int)std::min<size_t>(sp.size(), (size_t)cap);
+    if (n > 0)
+        std::memcpy(out, sp.data(), n * sizeof(tg_cfg));
+    if (n_total)
+        *n_total = (int)sp.size();
+    return TG_OK;
+}
+
+int tg_check_cfg(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg* cfg, int* reason)
+{
+    if (!cfg || !reason)
+        return set_error(TG_E_INVAL, "NULL argument");
+    *reason = check(M, N, K, dtype, *cfg, current_desc());
+    return TG_OK;
+}
+
+int tg_model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg* cfg, double* us)
+{
+    if (!cfg || !us)
+        return set_error(TG_E_INVAL, "NULL argument");
+    const tg_device_desc d = current_desc();
+    const int r = check(M, N, K, dtype, *cfg, d);
+    if (r != OK)
+        return set_error(TG_E_INFEASIBLE, "configuration infeasible (rule " + std::to_string(r) + ")");
+    *us = model_time(M, N, K, dtype, *cfg, d) * 1e6;
+    return TG_OK;
+}
+
+int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* us)
+{
+    if (!out)
+        return set_error(TG_E_INVAL, "NULL argument");
+    const int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    double t = 0.0;
+    if (!model_choice(M, N, K, dtype, current_desc(), out, &t))
+        return set_error(TG_E_INFEASIBLE, "no feasible configuration");
+    if (us)
+        *us = t * 1e6;
+    return TG_OK;
+}
+
+int tg_grid(int64_t M, int64_t N, int64_t K, const tg_cfg* cfg, int64_t* tiles, int64_t* blocks)
+{
+    (void)K;
+    if (!cfg || !tiles || !blocks || cfg->bm <= 0 || cfg->bn <= 0 || cfg->split_k <= 0 || M < 0 || N < 0)
+        return set_error(TG_E_INVAL, "bad argument");
+    grid(M, N, *cfg, tiles, blocks);
+    return TG_OK;
+}
+
+int tg_default_cfg(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
+{
+    (void)M;
+    if (!out)
+        return set_error(TG_E_INVAL, "NULL argument");
+    const int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    *out = default_cfg(N, K, dtype);
+    return TG_OK;
+}
+
+int tg_resources(int dtype, const tg_cfg* cfg, int* lds, int* vgprs, int* bpc)
+{
+    if (!cfg)
+        return set_error(TG_E_INVAL, "NULL argument");
+    if (cfg->wgm <= 0 || cfg->wgn <= 0 || cfg->bm <= 0 || cfg->bn <= 0)
+        return set_error(TG_E_INVAL, "bad configuration");
+    const tg_device_desc d = current_desc();
+    if (lds)
+        *lds = (int)lds_bytes(*cfg, dtype);
+    if (vgprs)
+        *vgprs = (int)vgpr_estimate(*cfg, dtype, d);
+    if (bpc)
+        *bpc = (int)blocks_per_cu(*cfg, dtype, d);
+    return TG_OK;
+}
+
+int tg_set_device_override(const tg_device_desc* desc)
+{
+    std::lock_guard<std::mutex> lk(g_desc_mu);
+    if (desc) {
+        if (desc->n_cu <= 0 || desc->simds <= 0 || desc->bw <= 0 || desc->peak_bf16 <= 0 || desc->peak_f32 <= 0)
+            return set_error(TG_E_INVAL, "implausible device description");
+        g_override = *desc;
+        g_override_set = true;
+    } else {
+        g_override_set = false;
+    }
+    return TG_OK;
+}
+
+int tg_get_device_desc(tg_device_desc* out)
+{
+    if (!out)
+        return set_error(TG_E_INVAL, "NULL argument");
+    *out = current_desc();
+    return TG_OK;
+}
+
+int tg_builtin_device_desc(int which, tg_device_desc* out)
+{
+    if (!out || (which != 0 && which != 1))
+        return set_error(TG_E_INVAL, "bad argument");
+    *out = which == 0 ? mi355x_desc() : h100_replica_desc();
+    return TG_OK;
+}
+
+int tg_kernel_count(void) { return (int)(registry_end() - registry_begin()); }
+
+int tg_has_kernel(int dtype, const tg_cfg* cfg)
+{
+    if (!cfg)
+        return 0;
+    return find_kernel(dtype, *cfg) ? 1 : 0;
+}
+
+int tg_kernel_resources(int dtype, const tg_cfg* cfg, int* out5)
+{
+    if (!cfg || !out5)
+        return set_error(TG_E_INVAL, "NULL argument");
+    const KernelEntry* k = find_kernel(dtype, *cfg);
+    if (!k)
+        return set_error(TG_E_INFEASIBLE, "no compiled kernel for this configuration");
+    out5[0] = k->res.vgpr;
+    out5[1] = k->res.agpr;
+    out5[2] = k->res.scratch;
+    out5[3] = k->res.lds;
+    out5[4] = k->res.occupancy;
+    return TG_OK;
+}
+
+}  // extern "C"

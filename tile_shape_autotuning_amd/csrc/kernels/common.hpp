@@ -1,0 +1,144 @@
+// Device-side building blocks shared by the GEMM kernels (gfx950 / CDNA4).
+//
+// Everything here is written for 64-wide wavefronts and the CDNA4 matrix
+// cores.  Lane layouts of the MFMA operands used below (verified on gfx950):
+//   v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16) + e] and
+//     B[8*(l/16) + e][l%16], e = 0..7; result D[4*(l/16) + r][l%16], r = 0..3.
+//   v_mfma_f32_16x16x4_f32:   lane l holds A[l%16][l/16] and B[l/16][l%16];
+//     result as above.
+// Because the reduction index only has to agree between the two operands,
+// any fixed assignment of k values to (lane group, element) is valid as long
+// as A and B use the same one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Kernel parameters (passed by value).  Matrices are row-major with natural
+// leading dimensions: A [M][K], B [K][N], C [M][N]; bias [N] fp32 or null.
+struct GemmParams {
+    const void* A;
+    const void* B;
+    const float* bias;
+    void* C;
+    float* ws;            // split-K partial tiles (fp32), used when split > 1
+    unsigned* counters;   // one arrival counter per output tile; zero between launches
+    int M, N, K;
+    int kps;              // K elements per split (multiple of the kernel's k unit)
+    int split;            // number of K splits (grid blocks per output tile)
+    int tiles_m, tiles_n;
+    int out_bf16;         // 1: C is bf16, 0: C is fp32
+    int act;              // 0 none, 1 ReLU, 2 GELU (erf form)
+    int group_m;          // tile rows per scheduling group (>= 1)
+};
+
+// Buffer-resource word 3 for gfx9-family raw buffers (32-bit dwords, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+// A voffset no buffer below reaches: loads there return zero (range check).
+constexpr int kOOB = 0x7FFFFFF8;
+// Largest num_records used, kept below kOOB so OOB lanes always fail the check.
+constexpr int64_t kMaxRecords = 0x7FFFFF00;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    int64_t n = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ unsigned short load2(__amdgpu_buffer_rsrc_t r, int voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ unsigned load4(__amdgpu_buffer_rsrc_t r, int voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 8x8 transpose of 16-bit elements held as 8 rows x 4 dwords (dword d of a row
+// holds columns 2d, 2d+1).  Output column t (8 values, rows 0..7) goes to out[t].
+__device__ __forceinline__ void transpose8x8_b16(const u32x4_t (&rows)[8], u32x4_t (&out)[8])
+{
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const unsigned sel = (t & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            out[t][e] = __builtin_amdgcn_perm(rows[2 * e + 1][t >> 1], rows[2 * e][t >> 1], sel);
+    }
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS row of CPR chunks: row r, logical
+// chunk c lives at physical chunk c ^ swz(r).  Chosen so that 16 consecutive
+// rows at one logical chunk (an MFMA fragment read) hit distinct 16-byte bank
+// groups within both a 128-byte and a 256-byte window.
+template <int CPR>
+__device__ __forceinline__ int swz(int r)
+{
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
+    constexpr int s1 = (CPR == 4) ? 1 : 0;
+    constexpr int s2 = s1 + ((CPR == 4) ? 2 : (CPR == 8) ? 3 : 4);
+    return ((r >> s1) ^ (r >> s2)) & (CPR - 1);
+}
+
+__device__ __forceinline__ float apply_act(float v, int act)
+{
+    if (act == 1)
+        return v > 0.0f ? v : 0.0f;
+    if (act == 2)
+        return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    return v;
+}
+
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float v)
+{
+    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
+}
+
+// Block index -> (tile_m, tile_n, split).  The hardware hands consecutive
+// workgroups to the 8 XCDs round robin; the first step renumbers blocks so
+// that each XCD owns a contiguous range of logical ids (tiles that share A
+// rows and B columns then share that XCD's L2).  Logical ids enumerate tiles
+// split-major, and tiles in groups of group_m tile rows, column-major inside a
+// group.
+__device__ __forceinline__ void map_block(int bid, int total, int tiles_m, int tiles_n, int group_m,
+                                          int& tile, int& tm, int& tn, int& split)
+{
+    const int q = total >> 3, r = total & 7;
+    const int x = bid & 7, i = bid >> 3;
+    const int logical = x * q + (x < r ? x : r) + i;
+    const int tiles = tiles_m * tiles_n;
+    tile = logical % tiles;
+    split = logical / tiles;
+    const int per_group = group_m * tiles_n;
+    const int g = tile / per_group;
+    const int first_m = g * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int in_g = tile - g * per_group;
+    tm = first_m + in_g % gsize;
+    tn = in_g / gsize;
+}
+
+}  // namespace tg

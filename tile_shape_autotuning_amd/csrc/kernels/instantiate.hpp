@@ -1,0 +1,24 @@
+// Launch wrappers used by the generated instantiation units.
+#pragma once
+
+#include "gemm_skinny.hpp"
+#include "gemm_tiled.hpp"
+
+namespace tg {
+
+template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST, bool VEC>
+hipError_t launch_tiled(const GemmParams& p, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_tiled_kernel<BF, BM, BN, BK, WGM, WGN, ST, VEC>), dim3(blocks),
+                       dim3(64 * WGM * WGN), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int MT, int W, int U>
+hipError_t launch_skinny(const GemmParams& p, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_skinny_kernel<MT, W, U>), dim3(blocks), dim3(64 * W), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace tg

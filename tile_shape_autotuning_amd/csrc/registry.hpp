@@ -1,0 +1,31 @@
+// Kernel registry: one entry per compiled kernel instantiation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tilegemm.h"
+#include "kernels/common.hpp"
+
+namespace tg {
+
+typedef hipError_t (*LaunchFn)(const GemmParams& p, int blocks, hipStream_t stream);
+
+// What the compiler allotted (from its resource remarks at build time; -1 = unknown).
+struct KernelResources {
+    int vgpr, agpr, scratch, lds, occupancy;
+};
+
+struct KernelEntry {
+    int in_bf16;        // 1: bf16 operands, 0: fp32 operands
+    tg_cfg cfg;         // split_k is 0 here: it is a run-time value
+    LaunchFn launch;
+    int threads;
+    KernelResources res;
+};
+
+// all entries, sorted by (in_bf16, cfg)
+const KernelEntry* registry_begin();
+const KernelEntry* registry_end();
+const KernelEntry* find_kernel(int dtype, const tg_cfg& c);
+
+}  // namespace tg

@@ -1,0 +1,51 @@
+// Host runtime shared by the C ABI and the autotuner.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/tilegemm.h"
+#include "registry.hpp"
+
+namespace tg {
+
+int set_error(int status, const std::string& msg);   // returns status
+int set_hip_error(hipError_t e, const char* what);     // returns TG_E_HIP
+
+// identity of the device the selection rules and the cache are keyed on
+struct DeviceKey {
+    std::string arch;   // e.g. "gfx950", or "h100-replica" under that override
+    int n_cu;
+};
+
+// description in force: override if set, else the current HIP device's, else MI355X defaults
+tg_device_desc current_desc();
+DeviceKey current_key();
+bool have_device();
+
+hipStream_t current_stream();
+
+// Validates arguments and launches one configuration (no selection).
+// `allow_misaligned_unaligned_kind` lets an aligned shape with misaligned
+// pointers run the element-load kernel.
+int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias,
+               void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked);
+
+// Split-K workspace: grows to at least `ws_bytes` and `n_counters` zeroed counters.
+int ensure_workspace(size_t ws_bytes, size_t n_counters, float** ws, unsigned** counters);
+size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& cfg);
+
+// Argument validation shared by the entry points.
+int validate_problem(int64_t M, int64_t N, int64_t K, int dtype);
+
+// tuner
+int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out);
+bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us);
+void count_cache_hit();
+
+// fill kernels for tuning scratch (defined in tune_kernels.hip)
+hipError_t fill_uniform(void* p, int64_t n, int is_bf16, uint32_t seed, hipStream_t s);
+
+}  // namespace tg

@@ -1,0 +1,371 @@
+// Tile selection rules (host only).
+//
+// Candidate space and feasibility filter: page "Tile Selection: Cost Models
+// Against Measurement", "The structure of the search space" -- the block
+// tile, reduction step and per-thread (here per-wave) tile are the free
+// parameters; limits that are "checkable before any code is generated" bound
+// the space: both panels must fit in on-chip memory, the accumulators must
+// fit in registers, and the tile must leave the device filled.  On MI355X
+// these become: LDS per workgroup and per CU (160 KiB), 256 accumulator and
+// 512 unified VGPR+AGPR registers per lane, 8 wave slots per SIMD, whole
+// 16x16 MFMA tiles per wave, K step a multiple of the MFMA K.
+//
+// Cost model: same page, "Analytical models and where they break" (per-block
+// traffic eb*K*(BM+BN), work 2*BM*BN*K, grid traffic = per-block x blocks,
+// time bounded by the busier of compute and memory, with corrections for
+// occupancy, pipeline fill and the tail) and page "Compilers and Kernel
+// Languages", "Workshop" (HBM traffic divided by g, compute divided by wave
+// efficiency and tile efficiency, time = the larger).  The H100 replica mode
+// reproduces that page's model; the MI355X mode adds the CU/SIMD occupancy,
+// pipeline-fill and split-K workspace terms.  Every expression below is in
+// the same order as the selection rules the tests compare against.
+#include "select.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+
+namespace tg {
+
+tg_device_desc mi355x_desc()
+{
+    tg_device_desc d{};
+    d.mode = 0;
+    d.n_cu = 256;
+    d.simds = 4;
+    d.lds_cu = 163840;
+    d.lds_block = 163840;
+    d.max_threads = 1024;
+    d.waves_max = 8;
+    d.blocks_max = 32;
+    d.vgpr_max = 512;
+    d.acc_max = 256;
+    d.r0 = 24;
+    d.peak_bf16 = 2516.6e12;
+    d.peak_f32 = 157.3e12;
+    d.bw = 8.0e12;
+    d.a_ref = 16384.0;
+    d.c_fill = 2.0;
+    d.t0 = 3.0e-6;
+    d.unaligned_eff = 0.25;
+    d.lat_mem = 2.0e-6;
+    d.cu_bw = 153.6e9;
+    return d;
+}
+
+tg_device_desc h100_replica_desc()
+{
+    tg_device_desc d{};
+    d.mode = 1;
+    d.n_cu = 132;
+    d.simds = 1;
+    d.lds_cu = 233472;
+    d.lds_block = 233472;
+    d.max_threads = 1024;
+    d.waves_max = 8;
+    d.blocks_max = 1;
+    d.vgpr_max = 1 << 30;
+    d.acc_max = 1 << 30;
+    d.r0 = 0;
+    d.peak_bf16 = 989e12;
+    d.peak_f32 = 989e12;
+    d.bw = 3.35e12;
+    d.a_ref = 16384.0;
+    d.c_fill = 0.0;
+    d.t0 = 0.0;
+    d.unaligned_eff = 1.0;
+    d.lat_mem = 0.0;
+    d.cu_bw = 0.0;
+    return d;
+}
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool cfg_less(const tg_cfg& a, const tg_cfg& b)
+{
+    const int32_t x[8] = {a.kind, a.bm, a.bn, a.bk, a.wgm, a.wgn, a.stages, a.split_k};
+    const int32_t y[8] = {b.kind, b.bm, b.bn, b.bk, b.wgm, b.wgn, b.stages, b.split_k};
+    return std::lexicographical_compare(x, x + 8, y, y + 8);
+}
+
+bool cfg_equal(const tg_cfg& a, const tg_cfg& b)
+{
+    return a.kind == b.kind && a.bm == b.bm && a.bn == b.bn && a.bk == b.bk && a.wgm == b.wgm &&
+           a.wgn == b.wgn && a.stages == b.stages && a.split_k == b.split_k;
+}
+
+int in_bytes(int dtype) { return dtype == TG_F32 ? 4 : 2; }
+int out_bytes(int dtype) { return dtype == TG_BF16 ? 2 : 4; }
+
+bool shape_aligned(int64_t N, int64_t K, int dtype)
+{
+    const int64_t vec = dtype == TG_F32 ? 4 : 8;
+    return K % vec == 0 && N % vec == 0;
+}
+
+// ------------------------------------------------------------------ space
+static const int kWaveGrids[6][2] = {{1, 1}, {1, 2}, {2, 1}, {2, 2}, {2, 4}, {4, 2}};
+static const int kSplits[5] = {1, 2, 4, 8, 16};
+static const int kUnaligned[3][4] = {{32, 32, 1, 1}, {64, 64, 2, 2}, {128, 128, 2, 2}};
+
+static std::vector<tg_cfg> build_space(int dtype, int mode)
+{
+    std::vector<tg_cfg> out;
+    if (mode == 1) {
+        const int t[4] = {32, 64, 128, 256};
+        for (int bm : t)
+            for (int bn : t)
+                out.push_back(tg_cfg{TG_KIND_TILED, bm, bn, 64, 1, 1, 1, 1});
+        return out;
+    }
+    std::vector<int> mn, bks;
+    if (dtype == TG_F32) {
+        mn = {32, 64, 128};
+        bks = {8, 16, 32};
+    } else {
+        mn = {32, 64, 128, 256};
+        bks = {32, 64};
+    }
+    for (int bm : mn)
+        for (int bn : mn)
+            for (int bk : bks)
+                for (const auto& w : kWaveGrids)
+                    for (int st = 1; st <= 2; ++st)
+                        for (int s : kSplits)
+                            out.push_back(tg_cfg{TG_KIND_TILED, bm, bn, bk, w[0], w[1], st, s});
+    if (dtype != TG_F32) {
+        const int bms[4] = {16, 32, 48, 64}, ws[4] = {1, 2, 4, 8}, us[3] = {1, 2, 4};
+        const int ss[6] = {1, 2, 4, 8, 16, 32};
+        for (int bm : bms)
+            for (int w : ws)
+                for (int u : us)
+                    for (int s : ss)
+                        out.push_back(tg_cfg{TG_KIND_SKINNY, bm, 128, 32, w, 1, u, s});
+    }
+    const int ubk = dtype == TG_F32 ? 16 : 32;
+    for (const auto& t : kUnaligned)
+        for (int s : kSplits)
+            out.push_back(tg_cfg{TG_KIND_UNALIGNED, t[0], t[1], ubk, t[2], t[3], 2, s});
+    return out;
+}
+
+const std::vector<tg_cfg>& space(int dtype, const tg_device_desc& d)
+{
+    static std::once_flag once;
+    static std::vector<tg_cfg> spaces[2][3];
+    std::call_once(once, [] {
+        for (int m = 0; m < 2; ++m)
+            for (int dt = 0; dt < 3; ++dt)
+                spaces[m][dt] = build_space(dt, m);
+    });
+    const int m = d.mode == 1 ? 1 : 0;
+    const int dt = (dtype >= 0 && dtype <= 2) ? dtype : 0;
+    return spaces[m][dt];
+}
+
+bool in_space(int dtype, const tg_device_desc& d, const tg_cfg& c)
+{
+    const auto& sp = space(dtype, d);
+    return std::binary_search(sp.begin(), sp.end(), c, cfg_less);
+}
+
+// ------------------------------------------------------------------ resources
+int64_t lds_bytes(const tg_cfg& c, int dtype)
+{
+    const int64_t eb = in_bytes(dtype);
+    if (c.kind == TG_KIND_SKINNY)
+        return c.wgm > 1 ? (int64_t)c.wgm * c.bm * 128 * 4 : 0;
+    const int64_t pad_b = dtype == TG_F32 ? 4 : 0;
+    return (int64_t)c.stages * ((int64_t)c.bm * c.bk + (int64_t)c.bk * (c.bn + pad_b)) * eb;
+}
+
+int64_t acc_regs(const tg_cfg& c)
+{
+    if (c.kind == TG_KIND_SKINNY)
+        return (int64_t)(c.bm / 16) * 32;
+    return (int64_t)(c.bm / c.wgm) * (c.bn / c.wgn) / 64;
+}
+
+int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d)
+{
+    if (c.kind == TG_KIND_SKINNY) {
+        const int64_t mt = c.bm / 16;
+        return 64 * (int64_t)c.stages + 8 * (int64_t)c.stages * mt + 32 * mt + d.r0;
+    }
+    const int64_t threads = 64 * (int64_t)c.wgm * c.wgn;
+    const int64_t eb = in_bytes(dtype);
+    const int64_t frag = 4 * ((c.bm / c.wgm) / 16 + (c.bn / c.wgn) / 16);
+    const int64_t chunks_a = (int64_t)c.bm * c.bk * eb / 16;
+    int64_t stage = 4 * cdiv(chunks_a, threads);
+    if (dtype == TG_F32)
+        stage += 4 * cdiv((int64_t)c.bk * c.bn / 4, threads);
+    else
+        stage += 32 * cdiv((int64_t)c.bk * c.bn / 64, threads);
+    return acc_regs(c) + frag + stage + d.r0;
+}
+
+int64_t waves_per_simd(const tg_cfg& c, int dtype, const tg_device_desc& d)
+{
+    const int64_t v = vgpr_estimate(c, dtype, d);
+    const int64_t v8 = cdiv(v, 8) * 8;
+    return v8 > 0 ? std::min<int64_t>(d.waves_max, d.vgpr_max / v8) : d.waves_max;
+}
+
+int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d)
+{
+    const int64_t w = (int64_t)c.wgm * c.wgn;
+    int64_t b = std::min<int64_t>(d.blocks_max, (d.simds * waves_per_simd(c, dtype, d)) / w);
+    const int64_t lds = lds_bytes(c, dtype);
+    if (lds > 0)
+        b = std::min<int64_t>(b, d.lds_cu / lds);
+    return b;
+}
+
+int64_t k_per_split(const tg_cfg& c, int64_t K)
+{
+    const int64_t unit = c.kind == TG_KIND_SKINNY ? 32 : c.bk;
+    return cdiv(cdiv(K, c.split_k), unit) * unit;
+}
+
+int check_static(int dtype, const tg_cfg& c, const tg_device_desc& d)
+{
+    const int64_t w = (int64_t)c.wgm * c.wgn;
+    if (64 * w > d.max_threads)
+        return R_WAVES;
+    if (c.kind != TG_KIND_SKINNY) {
+        const int kstep = dtype == TG_F32 ? 16 : 32;
+        if (c.bm % (16 * c.wgm) || c.bn % (16 * c.wgn) || c.bk % kstep)
+            return R_DIV;
+    }
+    if (lds_bytes(c, dtype) > d.lds_block)
+        return R_LDS;
+    if (acc_regs(c) > d.acc_max)
+        return R_ACC;
+    if (vgpr_estimate(c, dtype, d) > d.vgpr_max)
+        return R_VGPR;
+    if (blocks_per_cu(c, dtype, d) < 1)
+        return R_OCC;
+    return OK;
+}
+
+int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d)
+{
+    if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_BF16_F32OUT)
+        return R_DTYPE;
+    if (M < 1 || N < 1 || K < 0)
+        return R_SHAPE;
+    if (!in_space(dtype, d, c))
+        return R_SPACE;
+    if (c.kind == TG_KIND_SKINNY && dtype == TG_F32)
+        return R_DTYPE;
+    const bool aligned = shape_aligned(N, K, dtype);
+    if (d.mode == 0) {
+        if (c.kind == TG_KIND_UNALIGNED && aligned)
+            return R_ALIGN;
+        if (c.kind != TG_KIND_UNALIGNED && !aligned)
+            return R_ALIGN;
+    }
+    if (c.kind == TG_KIND_SKINNY && (M > 64 || c.bm != 16 * cdiv(M, 16)))
+        return R_SHAPE;
+    const int st = check_static(dtype, c, d);
+    if (st != OK)
+        return st;
+    if (c.split_k > 1) {
+        if (K == 0 || cdiv(K, k_per_split(c, K)) != c.split_k)
+            return R_SPLIT;
+    }
+    return OK;
+}
+
+std::vector<tg_cfg> enumerate_feasible(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d)
+{
+    std::vector<tg_cfg> out;
+    for (const tg_cfg& c : space(dtype, d))
+        if (check(M, N, K, dtype, c, d) == OK)
+            out.push_back(c);
+    return out;
+}
+
+// ------------------------------------------------------------------ geometry
+void grid(int64_t M, int64_t N, const tg_cfg& c, int64_t* tiles, int64_t* blocks)
+{
+    const int64_t t = cdiv(M, c.bm) * cdiv(N, c.bn);
+    *tiles = t;
+    *blocks = t * c.split_k;
+}
+
+// ------------------------------------------------------------------ cost model
+double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d)
+{
+    const int64_t eb = in_bytes(dtype);
+    const int64_t ec = out_bytes(dtype);
+    const double peak = dtype == TG_F32 ? d.peak_f32 : d.peak_bf16;
+    const double flops = 2.0 * (double)M * (double)N * (double)K;
+    const double compulsory = (double)(eb * (M * K + K * N) + ec * M * N);
+    int64_t tiles, units;
+    grid(M, N, c, &tiles, &units);
+    const int64_t w = (int64_t)c.wgm * c.wgn;
+    const int64_t bcu = blocks_per_cu(c, dtype, d);
+
+    if (c.kind == TG_KIND_SKINNY) {
+        const double flops_pad = 2.0 * (double)c.bm * (double)N * (double)K;
+        const double t_c = flops_pad / peak;
+        const double ws = c.split_k > 1 ? 8.0 * (double)c.bm * 128.0 * (double)tiles * (double)c.split_k : 0.0;
+        const int64_t resident = std::min<int64_t>(units * w, (int64_t)d.n_cu * bcu * w);
+        const double inflight = (double)resident * 64.0 * (double)c.stages * 8.0 * 16.0;
+        const double bw_eff = std::min(1.0, inflight / (d.bw * d.lat_mem));
+        const int64_t active = std::min<int64_t>(units, d.n_cu);
+        const double bw = std::min(d.bw * bw_eff, (double)active * d.cu_bw);
+        const double t_m = (compulsory + ws) / bw;
+        return std::max(t_c, t_m) + d.t0;
+    }
+
+    const int64_t par_need = std::max<int64_t>(1, d.simds / w);
+    const int64_t par = std::min(bcu, par_need);
+    const int64_t slots = (int64_t)d.n_cu * par;
+    const int64_t rounds = cdiv(units, slots);
+    const double wave_eff = (double)units / (double)(rounds * slots);
+    const double simd_eff = std::min(1.0, (double)(par * w) / (double)d.simds);
+    const double tile_eff = std::min(1.0, 0.5 + 0.5 * (double)((int64_t)c.bm * c.bn) / d.a_ref);
+    const int64_t ktiles = cdiv(k_per_split(c, K), c.bk);
+    const double fill_eff = ktiles > 0 ? (double)ktiles / ((double)ktiles + d.c_fill) : 1.0;
+    double eff = wave_eff * simd_eff * tile_eff * fill_eff;
+    if (c.kind == TG_KIND_UNALIGNED)
+        eff = eff * d.unaligned_eff;
+    const double t_c = flops / (peak * eff);
+    const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
+    const double g = std::sqrt((double)std::min<int64_t>(units, (int64_t)d.n_cu * bcu));
+    const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
+    const double t_m = (std::max(compulsory, raw / g) + ws) / d.bw;
+    return std::max(t_c, t_m) + d.t0;
+}
+
+bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t)
+{
+    bool found = false;
+    double best = 0.0;
+    for (const tg_cfg& c : space(dtype, d)) {
+        if (check(M, N, K, dtype, c, d) != OK)
+            continue;
+        const double x = model_time(M, N, K, dtype, c, d);
+        if (!found || x < best) {
+            found = true;
+            best = x;
+            *out = c;
+        }
+    }
+    if (found && t)
+        *t = best;
+    return found;
+}
+
+tg_cfg default_cfg(int64_t N, int64_t K, int dtype)
+{
+    if (!shape_aligned(N, K, dtype))
+        return tg_cfg{TG_KIND_UNALIGNED, 64, 64, dtype == TG_F32 ? 16 : 32, 2, 2, 2, 1};
+    if (dtype == TG_F32)
+        return tg_cfg{TG_KIND_TILED, 128, 128, 32, 2, 2, 2, 1};
+    return tg_cfg{TG_KIND_TILED, 128, 128, 64, 2, 2, 2, 1};
+}
+
+}  // namespace tg

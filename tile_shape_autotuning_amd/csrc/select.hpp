@@ -1,0 +1,49 @@
+// Host-only tile selection: candidate space, feasibility filter, cost model.
+// Pure C++ (no HIP), compiled with -ffp-contract=off so that every float64
+// operation happens exactly in the order written.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/tilegemm.h"
+
+namespace tg {
+
+enum Reason {
+    OK = 0, R_DTYPE = 1, R_ALIGN = 2, R_SHAPE = 3, R_WAVES = 4, R_DIV = 5, R_LDS = 6,
+    R_ACC = 7, R_VGPR = 8, R_OCC = 9, R_SPLIT = 10, R_SPACE = 11
+};
+
+tg_device_desc mi355x_desc();
+tg_device_desc h100_replica_desc();
+
+bool cfg_less(const tg_cfg& a, const tg_cfg& b);
+bool cfg_equal(const tg_cfg& a, const tg_cfg& b);
+
+int in_bytes(int dtype);
+int out_bytes(int dtype);
+bool shape_aligned(int64_t N, int64_t K, int dtype);
+
+// canonical-order candidate space for a dtype
+const std::vector<tg_cfg>& space(int dtype, const tg_device_desc& d);
+bool in_space(int dtype, const tg_device_desc& d, const tg_cfg& c);
+
+int64_t lds_bytes(const tg_cfg& c, int dtype);
+int64_t acc_regs(const tg_cfg& c);
+int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d);
+int64_t waves_per_simd(const tg_cfg& c, int dtype, const tg_device_desc& d);
+int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d);
+int64_t k_per_split(const tg_cfg& c, int64_t K);
+
+// shape-independent rules only (waves, divisibility, LDS, registers, occupancy)
+int check_static(int dtype, const tg_cfg& c, const tg_device_desc& d);
+int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d);
+
+void grid(int64_t M, int64_t N, const tg_cfg& c, int64_t* tiles, int64_t* blocks);
+double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d);
+std::vector<tg_cfg> enumerate_feasible(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d);
+bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t);
+tg_cfg default_cfg(int64_t N, int64_t K, int dtype);
+
+}  // namespace tg

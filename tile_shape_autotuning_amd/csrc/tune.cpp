@@ -1,0 +1,444 @@
+// Measuring autotuner and the shape-keyed tuning cache.
+//
+// Page "Tile Selection: Cost Models Against Measurement":
+//   * "Hybrid strategies": the resource filter discards what cannot fit, the
+//     cost model ranks the rest, a handful of the best is measured;
+//   * "Measurement, and what it must control": candidates are interleaved
+//     (round robin over several rounds, so clock drift hits all of them), the
+//     inputs have the workload's kind of values, and each sample times many
+//     back-to-back launches so launch overhead is divided out;
+//   * the result is cached keyed by shape, dtype, device and library version
+//     and can be stored in a file that outlives the process.
+// Page "CuTile Autotuning" (rules): the fixed default configuration is always
+// among the measured candidates, so tuning never picks something slower than
+// the default it replaces; at most 30 candidates are measured in hybrid mode.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "runtime.hpp"
+#include "select.hpp"
+
+namespace tg {
+
+struct CacheKey {
+    std::string arch;
+    int n_cu;
+    int64_t M, N, K;
+    int dtype;
+    bool operator<(const CacheKey& o) const
+    {
+        return std::tie(arch, n_cu, M, N, K, dtype) < std::tie(o.arch, o.n_cu, o.M, o.N, o.K, o.dtype);
+    }
+};
+
+struct CacheEntry {
+    tg_cfg cfg;
+    double measured_us;
+    double predicted_us;
+    std::vector<tg_tune_row> table;
+};
+
+static std::mutex g_cache_mu;
+static std::map<CacheKey, CacheEntry> g_cache;
+static int64_t g_n_tunes = 0, g_n_timed = 0, g_n_hits = 0;
+
+static CacheKey make_key(int64_t M, int64_t N, int64_t K, int dtype)
+{
+    const DeviceKey dk = current_key();
+    return CacheKey{dk.arch, dk.n_cu, M, N, K, dtype};
+}
+
+bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us)
+{
+    const CacheKey k = make_key(M, N, K, dtype);
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    auto it = g_cache.find(k);
+    if (it == g_cache.end())
+        return false;
+    *out = it->second.cfg;
+    if (measured_us)
+        *measured_us = it->second.measured_us;
+    return true;
+}
+
+void count_cache_hit()
+{
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    ++g_n_hits;
+}
+
+static int env_int(const char* name, int def)
+{
+    const char* s = std::getenv(name);
+    if (!s || !*s)
+        return def;
+    return std::atoi(s);
+}
+
+static std::string env_str(const char* name, const char* def)
+{
+    const char* s = std::getenv(name);
+    return (s && *s) ? std::string(s) : std::string(def);
+}
+
+namespace {
+
+// Device scratch operands filled with uniform values in [-1, 1).
+struct Scratch {
+    void* A = nullptr;
+    void* B = nullptr;
+    void* C = nullptr;
+    float* bias = nullptr;
+    ~Scratch()
+    {
+        if (A) (void)hipFree(A);
+        if (B) (void)hipFree(B);
+        if (C) (void)hipFree(C);
+        if (bias) (void)hipFree(bias);
+    }
+};
+
+struct Timed {
+    tg_cfg cfg;
+    double predicted_us;
+    int reps = 1;
+    bool ok = true;
+    std::vector<double> samples;   // us per launch
+};
+
+}  // namespace
+
+int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
+{
+    const CacheKey key = make_key(M, N, K, dtype);
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        auto it = g_cache.find(key);
+        if (it != g_cache.end()) {
+            *out = it->second.cfg;
+            return TG_OK;
+        }
+    }
+    const tg_device_desc d = current_desc();
+    const std::string mode = env_str("TILEGEMM_TUNE_MODE", "hybrid");
+    int topk = env_int("TILEGEMM_TUNE_TOPK", 16);
+    topk = std::max(1, std::min(topk, 30));
+    const int rounds = std::max(3, std::min(env_int("TILEGEMM_TUNE_SAMPLES", 7), 51));
+    const bool log = env_int("TILEGEMM_LOG", 0) != 0;
+
+    // filter + rank (stable: equal model times keep canonical order)
+    std::vector<tg_cfg> feas = enumerate_feasible(M, N, K, dtype, d);
+    if (feas.empty())
+        return set_error(TG_E_INFEASIBLE, "no feasible configuration");
+    std::vector<std::pair<double, size_t>> ranked;
+    ranked.reserve(feas.size());
+    for (size_t i = 0; i < feas.size(); ++i)
+        ranked.emplace_back(model_time(M, N, K, dtype, feas[i], d), i);
+    std::stable_sort(ranked.begin(), ranked.end(),
+                     [](const auto& a, const auto& b) { return a.first < b.first; });
+
+    CacheEntry entry;
+    if (mode == "model") {
+        entry.cfg = feas[ranked[0].second];
+        entry.predicted_us = ranked[0].first * 1e6;
+        entry.measured_us = -1.0;
+        entry.table.push_back(tg_tune_row{entry.cfg, entry.predicted_us, -1.0});
+    } else {
+        if (!have_device())
+            return set_error(TG_E_UNSUPPORTED, "measured tuning needs a HIP device (TILEGEMM_TUNE_MODE=model does not)");
+        // only candidates with a compiled kernel can be measured; kernels the
+        // compiler had to spill sit past the register cliff and are skipped
+        const bool allow_spills = env_int("TILEGEMM_ALLOW_SPILLS", 0) != 0;
+        auto runnable = [&](const tg_cfg& c) {
+            const KernelEntry* k = find_kernel(dtype, c);
+            return k != nullptr && (allow_spills || k->res.scratch <= 0);
+        };
+        std::vector<Timed> cands;
+        const size_t take = mode == "exhaustive" ? ranked.size() : (size_t)topk;
+        for (size_t i = 0; i < ranked.size() && cands.size() < take; ++i)
+            if (runnable(feas[ranked[i].second]))
+                cands.push_back(Timed{feas[ranked[i].second], ranked[i].first * 1e6});
+        const tg_cfg def = default_cfg(N, K, dtype);
+        bool have_def = false;
+        for (const Timed& t : cands)
+            have_def = have_def || cfg_equal(t.cfg, def);
+        if (!have_def && check(M, N, K, dtype, def, d) == OK && find_kernel(dtype, def))
+            cands.push_back(Timed{def, model_time(M, N, K, dtype, def, d) * 1e6});
+        if (cands.empty())
+            return set_error(TG_E_INFEASIBLE, "no compiled kernel among the candidates");
+
+        // scratch operands of the problem's shape
+        const int eb = in_bytes(dtype), ec = out_bytes(dtype);
+        Scratch s;
+        hipStream_t st = current_stream();
+        hipError_t e = hipSuccess;
+        const size_t na = (size_t)std::max<int64_t>(M * K, 1), nb = (size_t)std::max<int64_t>(K * N, 1);
+        if ((e = hipMalloc(&s.A, na * eb)) != hipSuccess || (e = hipMalloc(&s.B, nb * eb)) != hipSuccess ||
+            (e = hipMalloc(&s.C, (size_t)M * N * ec)) != hipSuccess ||
+            (e = hipMalloc(&s.bias, (size_t)N * sizeof(float))) != hipSuccess)
+            return set_error(TG_E_NOMEM, std::string("tuning scratch: ") + hipGetErrorString(e));
+        if ((e = fill_uniform(s.A, (int64_t)na, dtype != TG_F32, 0x1234u, st)) != hipSuccess ||
+            (e = fill_uniform(s.B, (int64_t)nb, dtype != TG_F32, 0x5678u, st)) != hipSuccess ||
+            (e = fill_uniform(s.bias, N, 0, 0x9abcu, st)) != hipSuccess)
+            return set_hip_error(e, "tuning scratch fill");
+        // workspace for the largest split-K candidate, allocated before timing
+        size_t wsb = 0, nct = 0;
+        for (const Timed& t : cands) {
+            wsb = std::max(wsb, workspace_bytes_for(M, N, t.cfg));
+            int64_t tiles, blocks;
+            grid(M, N, t.cfg, &tiles, &blocks);
+            if (t.cfg.split_k > 1)
+                nct = std::max(nct, (size_t)tiles);
+        }
+        if (wsb > 0) {
+            float* w;
+            unsigned* c;
+            const int r = ensure_workspace(wsb, nct, &w, &c);
+            if (r != TG_OK)
+                return r;
+        }
+        hipEvent_t e0, e1;
+        if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
+            return set_hip_error(e, "hipEventCreate");
+        auto run = [&](Timed& t, int reps) -> bool {
+            for (int r = 0; r < reps; ++r) {
+                if (launch_cfg(M, N, K, s.A, s.B, s.bias, s.C, dtype, TG_ACT_NONE, t.cfg, st, false) != TG_OK)
+                    return false;
+            }
+            return true;
+        };
+        // warm-up and a single-launch estimate to size each sample (~200 us)
+        for (Timed& t : cands) {
+            if (!run(t, 1)) {
+                t.ok = false;
+                continue;
+            }
+            hipEventRecord(e0, st);
+            t.ok = run(t, 1);
+            hipEventRecord(e1, st);
+            hipEventSynchronize(e1);
+            float ms = 0.f;
+            hipEventElapsedTime(&ms, e0, e1);
+            const double us = std::max(1.0, (double)ms * 1e3);
+            t.reps = (int)std::max(1.0, std::min(200.0, std::ceil(200.0 / us)));
+        }
+        int64_t timed = 0;
+        for (int r = 0; r < rounds; ++r) {
+            const size_t n = cands.size();
+            for (size_t j = 0; j < n; ++j) {
+                Timed& t = cands[(j + (size_t)r) % n];   // rotate the order every round
+                if (!t.ok)
+                    continue;
+                hipEventRecord(e0, st);
+                t.ok = run(t, t.reps);
+                hipEventRecord(e1, st);
+                e = hipEventSynchronize(e1);
+                if (e != hipSuccess) {
+                    hipEventDestroy(e0);
+                    hipEventDestroy(e1);
+                    return set_hip_error(e, "timing");
+                }
+                float ms = 0.f;
+                hipEventElapsedTime(&ms, e0, e1);
+                t.samples.push_back((double)ms * 1e3 / t.reps);
+                timed += t.reps;
+            }
+        }
+        hipEventDestroy(e0);
+        hipEventDestroy(e1);
+        int best = -1;
+        double best_us = 0.0;
+        for (size_t i = 0; i < cands.size(); ++i) {
+            Timed& t = cands[i];
+            double med = -1.0;
+            if (t.ok && !t.samples.empty()) {
+                std::vector<double> v = t.samples;
+                std::sort(v.begin(), v.end());
+                med = v[v.size() / 2];
+                if (best < 0 || med < best_us || (med == best_us && cfg_less(t.cfg, cands[best].cfg))) {
+                    best = (int)i;
+                    best_us = med;
+                }
+            }
+            entry.table.push_back(tg_tune_row{t.cfg, t.predicted_us, med});
+            if (log)
+                std::fprintf(stderr,
+                             "[tilegemm] %lldx%lldx%lld dt%d kind%d %dx%dx%d w%dx%d st%d sk%d: model %.2f us, measured %.2f us\n",
+                             (long long)M, (long long)N, (long long)K, dtype, t.cfg.kind, t.cfg.bm, t.cfg.bn, t.cfg.bk,
+                             t.cfg.wgm, t.cfg.wgn, t.cfg.stages, t.cfg.split_k, t.predicted_us, med);
+        }
+        if (best < 0)
+            return set_error(TG_E_HIP, "every candidate failed to launch: " + std::string(tg_last_error()));
+        entry.cfg = cands[best].cfg;
+        entry.measured_us = best_us;
+        entry.predicted_us = cands[best].predicted_us;
+        e = hipStreamSynchronize(st);
+        if (e != hipSuccess)
+            return set_hip_error(e, "hipStreamSynchronize");
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        g_n_timed += timed;
+    }
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    ++g_n_tunes;
+    *out = entry.cfg;
+    g_cache[key] = std::move(entry);
+    return TG_OK;
+}
+
+}  // namespace tg
+
+using namespace tg;
+
+static const char* kHeader = "# tilegemm tuning cache v1";
+
+extern "C" {
+
+int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, tg_tune_row* rows, int cap, int* n)
+{
+    if (cap < 0 || (cap > 0 && !rows))
+        return set_error(TG_E_INVAL, "bad output buffer");
+    const CacheKey k = make_key(M, N, K, dtype);
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    auto it = g_cache.find(k);
+    if (it == g_cache.end()) {
+        if (n)
+            *n = 0;
+        return TG_OK;
+    }
+    const auto& t = it->second.table;
+    const int m = (int)std::min<size_t>(t.size(), (size_t)cap);
+    for (int i = 0; i < m; ++i)
+        rows[i] = t[i];
+    if (n)
+        *n = (int)t.size();
+    return TG_OK;
+}
+
+int tg_cache_lookup(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us, int* hit)
+{
+    if (!out || !hit)
+        return set_error(TG_E_INVAL, "NULL argument");
+    *hit = cache_find(M, N, K, dtype, out, measured_us) ? 1 : 0;
+    return TG_OK;
+}
+
+int tg_cache_save(const char* path)
+{
+    if (!path)
+        return set_error(TG_E_INVAL, "NULL path");
+    std::ostringstream os;
+    os << kHeader << "\n";
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        char buf[512];
+        for (const auto& kv : g_cache) {
+            const CacheKey& k = kv.first;
+            const CacheEntry& e = kv.second;
+            std::snprintf(buf, sizeof buf, "%s %d %d %lld %lld %lld %d %d %d %d %d %d %d %d %d %.17g %.17g\n",
+                          k.arch.c_str(), k.n_cu, TG_VERSION, (long long)k.M, (long long)k.N, (long long)k.K,
+                          k.dtype, e.cfg.kind, e.cfg.bm, e.cfg.bn, e.cfg.bk, e.cfg.wgm, e.cfg.wgn, e.cfg.stages,
+                          e.cfg.split_k, e.measured_us, e.predicted_us);
+            os << buf;
+        }
+    }
+    std::ofstream f(path, std::ios::out | std::ios::trunc);
+    if (!f)
+        return set_error(TG_E_CACHE, std::string("cannot write ") + path);
+    f << os.str();
+    f.close();
+    if (!f)
+        return set_error(TG_E_CACHE, std::string("write failed: ") + path);
+    return TG_OK;
+}
+
+int tg_cache_load(const char* path, int* n_loaded, int* n_skipped)
+{
+    if (!path)
+        return set_error(TG_E_INVAL, "NULL path");
+    std::ifstream f(path);
+    if (!f)
+        return set_error(TG_E_CACHE, std::string("cannot read ") + path);
+    std::string line;
+    if (!std::getline(f, line) || line != kHeader)
+        return set_error(TG_E_CACHE, "not a tilegemm tuning cache (bad header)");
+    std::vector<std::pair<CacheKey, CacheEntry>> parsed;
+    int skipped = 0, lineno = 1;
+    while (std::getline(f, line)) {
+        ++lineno;
+        if (line.empty() || line[0] == '#')
+            continue;
+        std::istringstream is(line);
+        CacheKey k;
+        CacheEntry e{};
+        int ver;
+        long long M, N, K;
+        if (!(is >> k.arch >> k.n_cu >> ver >> M >> N >> K >> k.dtype >> e.cfg.kind >> e.cfg.bm >> e.cfg.bn >>
+              e.cfg.bk >> e.cfg.wgm >> e.cfg.wgn >> e.cfg.stages >> e.cfg.split_k >> e.measured_us >>
+              e.predicted_us))
+            return set_error(TG_E_CACHE, "malformed cache line " + std::to_string(lineno));
+        std::string rest;
+        if (is >> rest)
+            return set_error(TG_E_CACHE, "trailing fields on cache line " + std::to_string(lineno));
+        k.M = M;
+        k.N = N;
+        k.K = K;
+        if (ver != TG_VERSION || validate_problem(M, N, K, k.dtype) != TG_OK) {
+            ++skipped;   // another library version, or not a valid problem
+            continue;
+        }
+        // a configuration that this build cannot run is stale
+        const tg_device_desc d = k.arch == "h100-replica" ? h100_replica_desc() : mi355x_desc();
+        if (check(M, N, K, k.dtype, e.cfg, d) != OK) {
+            ++skipped;
+            continue;
+        }
+        e.table.push_back(tg_tune_row{e.cfg, e.predicted_us, e.measured_us});
+        parsed.emplace_back(k, e);
+    }
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (auto& kv : parsed)
+        g_cache[kv.first] = kv.second;
+    if (n_loaded)
+        *n_loaded = (int)parsed.size();
+    if (n_skipped)
+        *n_skipped = skipped;
+    return TG_OK;
+}
+
+void tg_cache_clear(void)
+{
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache.clear();
+}
+
+int tg_cache_size(void)
+{
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    return (int)g_cache.size();
+}
+
+int tg_stats(int64_t* n_tunes, int64_t* n_timed_launches, int64_t* n_cache_hits)
+{
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    if (n_tunes)
+        *n_tunes = g_n_tunes;
+    if (n_timed_launches)
+        *n_timed_launches = g_n_timed;
+    if (n_cache_hits)
+        *n_cache_hits = g_n_hits;
+    return TG_OK;
+}
+
+}  // extern "C"
