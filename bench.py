@@ -69,11 +69,16 @@ class Prepared:
         self.C = torch.empty((w.M, w.N), dtype=self.out_dtype, device="cuda")
         self.tg = tg
         self.i = 0
+        self.calls = None
 
     def step(self):
-        B = self.Bs[self.i % len(self.Bs)]
+        if self.calls is None:
+            # first call tunes and caches; then bind the C-ABI call once per weight copy
+            self.tg.gemm_bias_act(self.A, self.B, self.bias, act=self.act, out=self.C)
+            self.calls = [self.tg.BoundGemm(self.A, B, self.bias, act=self.act, out=self.C) for B in self.Bs]
+            return
+        self.calls[self.i % len(self.calls)]()
         self.i += 1
-        self.tg.gemm_bias_act(self.A, B, self.bias, act=self.act, out=self.C)
 
 
 def time_steps(p, steps, torch):
@@ -116,12 +121,20 @@ def cpu_baseline(index, target_s=12.0):
     gemm_ref.gemm(A[:rows], B, bias, act)
     dt = time.perf_counter() - t0
     rows2 = int(max(rows, min(w.M, rows * target_s / max(dt, 1e-3))))
+    reps = 1
     t0 = time.perf_counter()
     gemm_ref.gemm(A[:rows2], B, bias, act)
     dt = time.perf_counter() - t0
+    if rows2 == w.M and dt < target_s:          # the whole workload is quick: repeat it
+        reps = max(1, int(target_s / max(dt, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            gemm_ref.gemm(A, B, bias, act)
+        dt = (time.perf_counter() - t0) / reps
     return {"value": round(2.0 * rows2 * w.N * w.K / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": gemm_ref.num_threads(), "kind": "oracle",
-            "sample": f"first {rows2} of {w.M} rows of {w.name} (full K and N), fp64 oracle, {dt:.1f} s"}
+            "sample": f"first {rows2} of {w.M} rows of {w.name} (full K and N), fp64 oracle, "
+                      f"{dt:.2f} s per pass x {reps} pass(es)"}
 
 
 def report(indices, torch):
@@ -135,6 +148,9 @@ def report(indices, torch):
         w = wl.WORKLOADS[i]
         os.environ["TILEGEMM_TUNE_MODE"] = "exhaustive"
         os.environ["TILEGEMM_TUNE_SAMPLES"] = "5"
+        os.environ["TILEGEMM_PROGRESS"] = "1"
+        # split-K cannot help a problem with thousands of tiles; keep its sweep short
+        os.environ["TILEGEMM_TUNE_MAX_SPLIT"] = "1" if w.flops > 1e12 else "64"
         tg.cache_clear()
         t0 = time.perf_counter()
         tg.gemm_autotune(w.M, w.N, w.K, w.dtype)

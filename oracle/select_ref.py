@@ -160,8 +160,10 @@ def space(dtype: int, dev: Device = MI355X):
         tiles_mn, bks = (32, 64, 128), (8, 16, 32)
     else:
         tiles_mn, bks = (32, 64, 128, 256), (32, 64)
+    # fp32 kernel: 1 or 2 LDS buffers; bf16 kernel: 2 to 4 stages in flight
+    stages = (1, 2) if dtype == F32 else (2, 3, 4)
     for bm, bn, bk, (wm, wn), st, s in itertools.product(
-            tiles_mn, tiles_mn, bks, WAVE_GRIDS, (1, 2), SPLITS):
+            tiles_mn, tiles_mn, bks, WAVE_GRIDS, stages, SPLITS):
         out.append(Cfg(KIND_TILED, bm, bn, bk, wm, wn, st, s))
     if dtype != F32:
         for bm, w, u, s in itertools.product((16, 32, 48, 64), (1, 2, 4, 8), (1, 2, 4),
@@ -197,6 +199,9 @@ def vgpr_estimate(c: Cfg, dtype: int, dev: Device) -> int:
     threads = 64 * c.wgm * c.wgn
     eb = in_bytes(dtype)
     frag = 4 * ((c.bm // c.wgm) // 16 + (c.bn // c.wgn) // 16)
+    if c.kind == KIND_TILED and dtype != F32:
+        # the bf16 tiled kernel loads panels straight into LDS: no staging registers
+        return acc_regs(c) + frag + dev.r0
     chunks_a = c.bm * c.bk * eb // 16
     stage = 4 * cdiv(chunks_a, threads)
     if dtype == F32:

@@ -139,7 +139,9 @@ def test_lds_examples():
     assert S.lds_bytes(big, S.BF16) == 256 * 1024 > d.lds_block
     assert S.check(8192, 8192, 8192, S.BF16, big, d) == S.R_SPACE   # bf16 BK is 32 or 64
     # the largest bf16 tiles at one stage fit; fp32 128x128x32 two stages fit
-    assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 1, 1), d) == S.OK
+    assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 2, 1), d) == S.OK
+    assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 3, 1), d) == S.R_LDS
+    assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 1, 1), d) == S.R_SPACE
     assert S.lds_bytes(S.Cfg(0, 128, 128, 32, 2, 2, 2, 1), S.F32) == 2 * (128 * 32 + 32 * 132) * 4
     # all 18 fp32 sweep triples fit LDS at one stage
     for bm in (32, 64, 128):
@@ -152,8 +154,8 @@ def test_rejections_have_reasons():
     d = S.MI355X
     assert S.check(256, 256, 256, S.F32, S.Cfg(0, 64, 64, 8, 1, 1, 1, 1), d) == S.R_DIV
     assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 1, 4, 1, 1), d) == S.R_SPACE
-    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 2, 4, 1, 1), d) == S.R_DIV
-    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 256, 32, 1, 1, 1, 1), d) == S.R_ACC
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 2, 4, 2, 1), d) == S.R_DIV
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 256, 32, 1, 1, 2, 1), d) == S.R_ACC
     assert S.check(256, 256, 15, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
     assert S.check(256, 256, 256, S.BF16, S.Cfg(2, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
     assert S.check(256, 256, 64, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 4), d) == S.R_SPLIT

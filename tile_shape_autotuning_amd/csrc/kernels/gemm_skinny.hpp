@@ -49,7 +49,8 @@ gemm_skinny_kernel(GemmParams p)
     __shared__ f32x4_t red[Cf::RED_BYTES / 16];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: scalar registers
     const int l16 = lane & 15, g = lane >> 4;
 
     int tile, tm, tn, split;

@@ -66,10 +66,12 @@ gemm_tiled_kernel(GemmParams p)
     constexpr int T = Cf::T, CPR = Cf::CPR, EB = Cf::EB, EPC = Cf::EPC;
     constexpr int FM = Cf::FM, FN = Cf::FN;
     __shared__ u32x4_t lds[ST * Cf::STAGE_SLOTS];
-    __shared__ int s_last;
+    // split-K arrival flag: lives in the (then idle) panel buffers
+    int& s_last = *reinterpret_cast<int*>(lds);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: scalar registers
     const int l16 = lane & 15, g = lane >> 4;
     const int wm = wave / WGN, wn = wave % WGN;
 

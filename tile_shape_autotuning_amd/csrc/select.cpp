@@ -126,11 +126,14 @@ static std::vector<tg_cfg> build_space(int dtype, int mode)
         mn = {32, 64, 128, 256};
         bks = {32, 64};
     }
+    // fp32: register-staged kernel, 1 or 2 LDS buffers; bf16: direct-to-LDS
+    // kernel, 2 to 4 stages in flight
+    const int st_lo = dtype == TG_F32 ? 1 : 2, st_hi = dtype == TG_F32 ? 2 : 4;
     for (int bm : mn)
         for (int bn : mn)
             for (int bk : bks)
                 for (const auto& w : kWaveGrids)
-                    for (int st = 1; st <= 2; ++st)
+                    for (int st = st_lo; st <= st_hi; ++st)
                         for (int s : kSplits)
                             out.push_back(tg_cfg{TG_KIND_TILED, bm, bn, bk, w[0], w[1], st, s});
     if (dtype != TG_F32) {
@@ -195,6 +198,8 @@ int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d)
     const int64_t threads = 64 * (int64_t)c.wgm * c.wgn;
     const int64_t eb = in_bytes(dtype);
     const int64_t frag = 4 * ((c.bm / c.wgm) / 16 + (c.bn / c.wgn) / 16);
+    if (c.kind == TG_KIND_TILED && dtype != TG_F32)
+        return acc_regs(c) + frag + d.r0;   // panels go global -> LDS directly: no staging registers
     const int64_t chunks_a = (int64_t)c.bm * c.bk * eb / 16;
     int64_t stage = 4 * cdiv(chunks_a, threads);
     if (dtype == TG_F32)

@@ -161,15 +161,37 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
         // only candidates with a compiled kernel can be measured; kernels the
         // compiler had to spill sit past the register cliff and are skipped
         const bool allow_spills = env_int("TILEGEMM_ALLOW_SPILLS", 0) != 0;
+        const int max_split = env_int("TILEGEMM_TUNE_MAX_SPLIT", 1 << 30);
         auto runnable = [&](const tg_cfg& c) {
             const KernelEntry* k = find_kernel(dtype, c);
-            return k != nullptr && (allow_spills || k->res.scratch <= 0);
+            return k != nullptr && (allow_spills || k->res.scratch <= 0) && c.split_k <= max_split;
         };
         std::vector<Timed> cands;
         const size_t take = mode == "exhaustive" ? ranked.size() : (size_t)topk;
+        std::vector<char> picked(ranked.size(), 0);
         for (size_t i = 0; i < ranked.size() && cands.size() < take; ++i)
-            if (runnable(feas[ranked[i].second]))
+            if (runnable(feas[ranked[i].second])) {
                 cands.push_back(Timed{feas[ranked[i].second], ranked[i].first * 1e6});
+                picked[i] = 1;
+            }
+        // the model cannot rank across kernel kinds reliably (kinds often tie
+        // at the memory floor), so the best few of every kind are measured too
+        if (mode != "exhaustive") {
+            const size_t per_kind = std::max<size_t>(2, (size_t)topk / 4);
+            for (int kind = 0; kind <= 2; ++kind) {
+                size_t have = 0;
+                for (size_t i = 0; i < ranked.size() && have < per_kind; ++i) {
+                    const tg_cfg& c = feas[ranked[i].second];
+                    if (c.kind != kind || !runnable(c))
+                        continue;
+                    ++have;
+                    if (!picked[i]) {
+                        picked[i] = 1;
+                        cands.push_back(Timed{c, ranked[i].first * 1e6});
+                    }
+                }
+            }
+        }
         const tg_cfg def = default_cfg(N, K, dtype);
         bool have_def = false;
         for (const Timed& t : cands)
@@ -219,8 +241,15 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
             }
             return true;
         };
+        const bool progress = env_int("TILEGEMM_PROGRESS", 0) != 0;
+        if (progress)
+            std::fprintf(stderr, "[tilegemm] tuning %lldx%lldx%lld dt%d: %zu candidates, %d rounds\n",
+                         (long long)M, (long long)N, (long long)K, dtype, cands.size(), rounds);
         // warm-up and a single-launch estimate to size each sample (~200 us)
+        size_t done = 0;
         for (Timed& t : cands) {
+            if (progress && ++done % 100 == 0)
+                std::fprintf(stderr, "[tilegemm]   warm-up %zu/%zu\n", done, cands.size());
             if (!run(t, 1)) {
                 t.ok = false;
                 continue;
@@ -255,6 +284,8 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
                 t.samples.push_back((double)ms * 1e3 / t.reps);
                 timed += t.reps;
             }
+            if (progress)
+                std::fprintf(stderr, "[tilegemm]   round %d/%d done\n", r + 1, rounds);
         }
         hipEventDestroy(e0);
         hipEventDestroy(e1);
