@@ -70,12 +70,14 @@ class Prepared:
         self.tg = tg
         self.i = 0
         self.calls = None
+        self.cfg = None          # None: autotuned; else a forced configuration
 
     def step(self):
         if self.calls is None:
             # first call tunes and caches; then bind the C-ABI call once per weight copy
-            self.tg.gemm_bias_act(self.A, self.B, self.bias, act=self.act, out=self.C)
-            self.calls = [self.tg.BoundGemm(self.A, B, self.bias, act=self.act, out=self.C) for B in self.Bs]
+            self.tg.gemm_bias_act(self.A, self.B, self.bias, act=self.act, out=self.C, cfg=self.cfg)
+            self.calls = [self.tg.BoundGemm(self.A, B, self.bias, act=self.act, out=self.C, cfg=self.cfg)
+                          for B in self.Bs]
             return
         self.calls[self.i % len(self.calls)]()
         self.i += 1
@@ -103,7 +105,10 @@ def shape_summary(p, sec):
     tflops = w.flops / sec / 1e12
     gbs = w.compulsory_bytes / sec / 1e9
     frac = gbs / HBM_PEAK if bound == "hbm" else tflops / PEAK[prec]
-    cfg, meas = p.tg.cache_lookup(w.M, w.N, w.K, w.dtype)
+    if p.cfg is not None:
+        cfg, meas = p.tg.Cfg.of(p.cfg), float("nan")
+    else:
+        cfg, meas = p.tg.cache_lookup(w.M, w.N, w.K, w.dtype)
     return {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": wl.DTYPE_NAMES[w.dtype],
             "act": p.act, "us": round(sec * 1e6, 3), "TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 1),
             "bound": bound, "roofline_frac": round(frac, 4), "cfg": list(cfg.astuple()),
@@ -194,6 +199,8 @@ def main():
     ap.add_argument("--report", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0)
+    ap.add_argument("--cfg", type=str, default="",
+                    help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -223,6 +230,8 @@ def main():
         rotate = 2 if wl.WORKLOADS[i].M <= 64 else 1     # decode: stream distinct weights every call
         log(f"workload {i}: preparing")
         p = Prepared(i, torch, rotate=rotate)
+        if i == main_idx and a.cfg:
+            p.cfg = tuple(int(x) for x in a.cfg.split(","))
         for _ in range(max(1, a.warmup)):               # first call tunes and caches
             p.step()
         torch.cuda.synchronize()

@@ -18,7 +18,9 @@
 //     chunk a lane fetches decides the LDS layout, so the XOR swizzles below
 //     cost nothing; out-of-range lanes (M, N, K edges) write zeros;
 //   * completion is tracked with s_waitcnt vmcnt(n) per wave followed by a
-//     plain s_barrier: no fence, so loads of later stages stay in flight;
+//     plain s_barrier: no fence, so loads of later stages stay in flight (the
+//     loads are issued as inline assembly so that the compiler does not add
+//     its own full drain before the LDS reads);
 //   * A [BM][BK] is K-contiguous in LDS and read with ds_read_b128 (8 k values
 //     of one row per lane = the A operand of v_mfma_f32_16x16x32_bf16);
 //   * B [BK][BN] stays N-contiguous (as in memory) and is read with
@@ -69,6 +71,28 @@ __device__ __forceinline__ int swz_b(int r)
     return (2 * ((r & 3) + 4 * ((r >> 3) & 1))) & (CPRB - 1) & ~1;
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource words (base, 32-bit num_records, gfx9 raw-buffer flags).
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes)
+{
+    const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)n, kRsrcWord3};
+}
+
+// One wave-wide load of 16 bytes per lane from a buffer straight into LDS
+// (lane l writes LDS bytes lds_addr + 16 l .. + 15; out-of-range offsets
+// write zeros).  Issued as inline assembly on purpose: the compiler's
+// wait-count insertion would otherwise treat every later LDS read as
+// dependent on all outstanding transfers and drain the whole pipeline before
+// it; completion is tracked explicitly with wait_vmcnt<> instead.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, unsigned lds_addr)
+{
+    __asm__ __volatile__("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+                         : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -112,49 +136,48 @@ gemm_tiled_dma_kernel(GemmParams p)
     const char* Bb = static_cast<const char*>(p.B);
     const int64_t a_total = (int64_t)M * K, b_total = (int64_t)K * N;
 
-    // per-lane source of each DMA instruction this wave issues (fixed over K)
-    int voff[Cf::LPW_MAX];   // byte offset in the rebased panel, or -1 if the lane is out of range in M/N
-    int kpos[Cf::LPW_MAX];   // k (relative to the tile start) the lane's chunk begins at
+    // per-lane source of each DMA instruction this wave issues (fixed over K):
+    // byte offset in the panel rebased at each K step, or kOOB when the lane's
+    // row (A) or columns (B) lie outside the matrix
+    int voff[Cf::LPW_MAX];
 #pragma unroll
     for (int q = 0; q < Cf::LPW_MAX; ++q) {
         const int j = wave + q * W;
-        voff[q] = -1;
-        kpos[q] = 0;
+        voff[q] = kOOB;
         if (j < Cf::A_INST) {
             const int s = j * 64 + lane;
-            const int row = s / CPRA, pc = s % CPRA;
-            const int c = pc ^ swz<CPRA>(row);
-            kpos[q] = c * 8;
+            const int row = s / CPRA, c = (s % CPRA) ^ swz<CPRA>(s / CPRA);
             if (m0 + row < M)
                 voff[q] = row * K * 2 + c * 16;
         } else if (j < Cf::INST) {
             const int s = (j - Cf::A_INST) * 64 + lane;
-            const int krow = s / CPRB, pcn = s % CPRB;
-            const int cn = pcn ^ swz_b<CPRB>(krow);
-            kpos[q] = krow;
+            const int krow = s / CPRB, cn = (s % CPRB) ^ swz_b<CPRB>(s / CPRB);
             if (n0 + cn * 8 < N)
                 voff[q] = krow * N * 2 + cn * 16;
         }
     }
+    const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) u32x4_t*)lds;
 
     auto issue = [&](int t, int buf) {
         const int k0 = kbeg + t * BK;
-        const int klim = kend - k0;   // chunks / rows at k >= klim are outside this split
+        const int klim = kend - k0;   // k >= klim (relative) lies outside this split
         const int64_t a_off = (int64_t)m0 * K + k0;
         const int64_t b_off = (int64_t)k0 * N + n0;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab + a_off * 2, (a_total - a_off) * 2);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bb + b_off * 2, (b_total - b_off) * 2);
-        u32x4_t* L = lds + buf * Cf::STAGE_SLOTS;
+        const i32x4_t rA = rsrc_words(Ab + a_off * 2, (a_total - a_off) * 2);
+        const i32x4_t rB = rsrc_words(Bb + b_off * 2, (b_total - b_off) * 2);
+        const unsigned dst0 = lds_base + (unsigned)(buf * Cf::STAGE_SLOTS * 16);
+        const bool tail = klim < BK;
 #pragma unroll
         for (int q = 0; q < Cf::LPW_MAX; ++q) {
             const int j = wave + q * W;
             if (j < Cf::INST) {
-                const int vo = (voff[q] >= 0 && kpos[q] < klim) ? voff[q] : kOOB;
-                void* dst = L + j * 64;   // wave-uniform: lanes write slots j*64 + lane
-                if (j < Cf::A_INST)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, TG_LDS(dst), 16, vo, 0, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, TG_LDS(dst), 16, vo, 0, 0, 0);
+                int vo = voff[q];
+                if (tail) {   // last, partial K step: mask the chunks (A) / rows (B) past the end
+                    const int s = (j < Cf::A_INST ? j : j - Cf::A_INST) * 64 + lane;
+                    const int kp = j < Cf::A_INST ? ((s % CPRA) ^ swz<CPRA>(s / CPRA)) * 8 : s / CPRB;
+                    vo = kp < klim ? vo : kOOB;
+                }
+                dma16(j < Cf::A_INST ? rA : rB, vo, dst0 + (unsigned)(j * 64 * 16));
             }
         }
     };
@@ -166,17 +189,21 @@ gemm_tiled_dma_kernel(GemmParams p)
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // ---- MFMA work on one LDS stage.  Fragment reads run one step ahead of
+    // the MFMAs that consume them: the A fragment of row-tile i+1 is read
+    // while row-tile i multiplies, and the B fragments of the next 32-wide k
+    // slice while the last row-tile of this one multiplies.  sched_barrier
+    // pins that order (left alone, the scheduler sinks every read next to its
+    // first use and the matrix core waits on each LDS round trip).
     auto compute = [&](int buf) {
         const u32x4_t* LA = lds + buf * Cf::STAGE_SLOTS;
         const char* LB = reinterpret_cast<const char*>(LA + Cf::A_SLOTS);
-#pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            u32x4_t a[FM], b[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * Cf::WM + i * 16 + l16;
-                a[i] = LA[row * CPRA + ((kk * 4 + g) ^ swz<CPRA>(row))];
-            }
+        constexpr int KK = BK / 32;
+        auto read_a = [&](int i, int kk) {
+            const int row = wm * Cf::WM + i * 16 + l16;
+            return LA[row * CPRA + ((kk * 4 + g) ^ swz<CPRA>(row))];
+        };
+        auto read_b = [&](int kk, u32x4_t(&b)[FN]) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int n = wn * Cf::WN + j * 16 + 4 * (l16 & 3);
@@ -192,11 +219,33 @@ gemm_tiled_dma_kernel(GemmParams p)
                     b[j][2 * h + 1] = w.y;
                 }
             }
+        };
+        u32x4_t b_cur[FN], b_nxt[FN];
+        read_b(0, b_cur);
+        u32x4_t a_cur = read_a(0, 0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+        for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                u32x4_t a_nxt = a_cur;
+                if (i + 1 < FM)
+                    a_nxt = read_a(i + 1, kk);
+                else if (kk + 1 < KK)
+                    a_nxt = read_a(0, kk + 1);
+                if (kk + 1 < KK && i == FM - 1)
+                    read_b(kk + 1, b_nxt);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+                    acc[i][j] = mfma_bf16(a_cur, b_cur[j], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+                a_cur = a_nxt;
+            }
+            if (kk + 1 < KK) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    b_cur[j] = b_nxt[j];
+            }
         }
     };
 
