@@ -142,7 +142,7 @@ def cpu_baseline(index, target_s=12.0):
                       f"{dt:.2f} s per pass x {reps} pass(es)"}
 
 
-def report(indices, torch):
+def report(indices, torch, dump_dir=None):
     """Measure every feasible configuration per workload with the library's
     exhaustive tuner: best/worst/fixed ratios and the cost model's hit rate."""
     import tile_shape_autotuning_amd as tg
@@ -162,6 +162,11 @@ def report(indices, torch):
         tune_s = time.perf_counter() - t0
         rows = [(c.astuple(), pred, meas) for c, pred, meas in tg.autotune_table(w.M, w.N, w.K, w.dtype)
                 if meas > 0]
+        if dump_dir:
+            os.makedirs(dump_dir, exist_ok=True)
+            with open(os.path.join(dump_dir, f"table_{w.name}.json"), "w") as f:
+                json.dump({"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype,
+                           "rows": [[list(c), pred, meas] for c, pred, meas in rows]}, f)
         best = min(rows, key=lambda r: r[2])
         worst = max(rows, key=lambda r: r[2])
         fixed = [r for r in rows if r[0] == tuple(tg.default_cfg(w.M, w.N, w.K, w.dtype).astuple())]
@@ -199,6 +204,7 @@ def main():
     ap.add_argument("--report", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0)
+    ap.add_argument("--dump", type=str, default="", help="with --report: write every measured row here")
     ap.add_argument("--cfg", type=str, default="",
                     help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
@@ -270,7 +276,7 @@ def main():
         "shapes": shapes,
     }
     if a.report:
-        rep, hits = report([i for i in indices], torch)
+        rep, hits = report([i for i in indices], torch, a.dump)
         line["report"] = rep
         line["model_hit_rate"] = f"{hits}/{len(indices)}"
     if not a.no_cpu:
