@@ -78,7 +78,9 @@ typedef struct {
 typedef struct {
     int32_t mode, n_cu, simds, lds_cu, lds_block, max_threads, waves_max, blocks_max,
             vgpr_max, acc_max, r0, reserved;
-    double peak_bf16, peak_f32, bw, a_ref, c_fill, t0, unaligned_eff, lat_mem, cu_bw;
+    double peak_bf16, peak_f32, bw, a_ref, c_fill, t0, unaligned_eff, lat_mem, cu_bw,
+           lds_bw_cu,   /* LDS bytes/s per CU (0 = no LDS term) */
+           lat_step;    /* memory latency a K step waits for, divided by the pipeline depth (s) */
 } tg_device_desc;
 
 /* One row of an autotuning table. */

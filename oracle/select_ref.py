@@ -85,17 +85,20 @@ class Device:
     lat_mem: float
     cu_bw: float
     r0: int
+    lds_bw_cu: float = 0.0
+    lat_step: float = 0.0
 
 
 # MI355X (gfx950): 256 CUs x 4 SIMDs, 160 KiB LDS per CU, 512 unified
 # VGPR+AGPR per lane, 8 wave slots per SIMD; dense bf16 MFMA 2516.6 TFLOP/s,
-# fp32 MFMA 157.3 TFLOP/s, HBM3E 8 TB/s.  a_ref, c_fill, t0, unaligned_eff,
-# lat_mem, cu_bw and r0 are calibration constants of this model.
+# fp32 MFMA 157.3 TFLOP/s, HBM3E 8 TB/s, LDS 128 B/clk per CU at 2.4 GHz.
+# a_ref, c_fill, t0, unaligned_eff, lat_mem, cu_bw, lat_step and r0 are
+# calibration constants of this model.
 MI355X = Device(mode=0, n_cu=256, simds=4, lds_cu=163840, lds_block=163840,
                 max_threads=1024, waves_max=8, blocks_max=32, vgpr_max=512,
                 acc_max=256, peak_bf16=2516.6e12, peak_f32=157.3e12, bw=8.0e12,
                 a_ref=16384.0, c_fill=2.0, t0=3.0e-6, unaligned_eff=0.25,
-                lat_mem=2.0e-6, cu_bw=153.6e9, r0=24)
+                lat_mem=2.0e-6, cu_bw=153.6e9, r0=24, lds_bw_cu=307.2e9, lat_step=2.0e-6)
 
 # The page's H100 model: 132 SMs, 228 KB shared memory, 989 TFLOP/s bf16,
 # 3.35 TB/s; one tile per SM at a time; no register model; no pipeline-fill
@@ -344,7 +347,18 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
     g = math.sqrt(min(units, dev.n_cu * bcu))
     ws = 8.0 * tiles * c.bm * c.bn * c.split_k if c.split_k > 1 else 0.0
     t_m = (max(compulsory, raw / g) + ws) / dev.bw
-    return max(t_c, t_m) + dev.t0
+    # LDS traffic: every wave reads its A and B fragments once per K step and
+    # the panels are written once; a CU moves the bytes of its blocks in turn
+    # (the register-level reuse of "Tiling the hierarchy", multi-level coupling)
+    t_lds = 0.0
+    if dev.lds_bw_cu > 0.0:
+        per_unit = float(k_per_split(c, K)) * eb * (w * (c.bm // c.wgm + c.bn // c.wgn) + c.bm + c.bn)
+        t_lds = cdiv(units, dev.n_cu) * per_unit / dev.lds_bw_cu
+    # pipeline fill per K step ("Analytical models and where they break"): a step
+    # cannot finish before its transfers land; depth - 1 later steps are in flight
+    depth = max(1, c.stages - 1) if (c.kind == KIND_TILED and dtype != F32) else 1
+    t_lat = cdiv(units, dev.n_cu * bcu) * (ktiles + 1) * dev.lat_step / depth
+    return max(t_c, t_m, t_lds, t_lat) + dev.t0
 
 
 def rank(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):

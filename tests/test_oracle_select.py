@@ -184,7 +184,8 @@ def test_model_invariants(M, N, K, dt):
 
 
 def test_wave_efficiency_one_when_work_divides_slots():
-    d = S.MI355X
+    # compute term alone (no LDS or pipeline-latency term)
+    d = dataclasses.replace(S.MI355X, lds_bw_cu=0.0, lat_step=0.0)
     # 128x128 tiles, W = 4 (one block fills a CU): 2048x2048 -> 256 tiles = one full round
     c = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
     t256 = S.model_time(2048, 2048, 4096, S.BF16, c, d)

@@ -61,7 +61,7 @@ class DeviceDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("mode", "n_cu", "simds", "lds_cu", "lds_block", "max_threads",
                                               "waves_max", "blocks_max", "vgpr_max", "acc_max", "r0", "reserved")] + \
                [(n, ctypes.c_double) for n in ("peak_bf16", "peak_f32", "bw", "a_ref", "c_fill", "t0",
-                                               "unaligned_eff", "lat_mem", "cu_bw")]
+                                               "unaligned_eff", "lat_mem", "cu_bw", "lds_bw_cu", "lat_step")]
 
 
 class TuneRow(ctypes.Structure):

@@ -109,10 +109,14 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes)
 // write zeros).  Issued as inline assembly on purpose: the compiler's
 // wait-count insertion would otherwise treat every later LDS read as
 // dependent on all outstanding transfers and drain the whole pipeline before
-// it; completion is tracked explicitly with wait_vmcnt<> instead.
+// it; completion is tracked explicitly with wait_vmcnt<> instead.  The
+// compiler writes M0 (the LDS destination) just before the statement but
+// cannot see that the load reads it, so the wait states an LDS-DMA load needs
+// after an M0 write are provided here (without them the transfer can land at
+// the previous M0 address).
 __device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, int soff, unsigned lds_addr)
 {
-    __asm__ __volatile__("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+    __asm__ __volatile__("s_nop 1\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                          "{m0}"(lds_addr)
                          : "memory");
 }

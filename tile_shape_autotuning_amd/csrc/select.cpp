@@ -50,6 +50,8 @@ tg_device_desc mi355x_desc()
     d.unaligned_eff = 0.25;
     d.lat_mem = 2.0e-6;
     d.cu_bw = 153.6e9;
+    d.lds_bw_cu = 307.2e9;
+    d.lat_step = 2.0e-6;
     return d;
 }
 
@@ -76,6 +78,8 @@ tg_device_desc h100_replica_desc()
     d.unaligned_eff = 1.0;
     d.lat_mem = 0.0;
     d.cu_bw = 0.0;
+    d.lds_bw_cu = 0.0;
+    d.lat_step = 0.0;
     return d;
 }
 
@@ -342,7 +346,17 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     const double g = std::sqrt((double)std::min<int64_t>(units, (int64_t)d.n_cu * bcu));
     const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
     const double t_m = (std::max(compulsory, raw / g) + ws) / d.bw;
-    return std::max(t_c, t_m) + d.t0;
+    // LDS traffic: fragment reads of every wave plus the panel writes, per CU in turn
+    double t_lds = 0.0;
+    if (d.lds_bw_cu > 0.0) {
+        const int64_t frag_rows = w * (c.bm / c.wgm + c.bn / c.wgn) + c.bm + c.bn;
+        const double per_unit = (double)k_per_split(c, K) * (double)eb * (double)frag_rows;
+        t_lds = (double)cdiv(units, d.n_cu) * per_unit / d.lds_bw_cu;
+    }
+    // pipeline fill: a K step waits for its transfers; depth - 1 later steps are in flight
+    const int64_t depth = (c.kind == TG_KIND_TILED && dtype != TG_F32) ? std::max<int64_t>(1, c.stages - 1) : 1;
+    const double t_lat = (double)(cdiv(units, (int64_t)d.n_cu * bcu) * (ktiles + 1)) * d.lat_step / (double)depth;
+    return std::max(std::max(std::max(t_c, t_m), t_lds), t_lat) + d.t0;
 }
 
 bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t)

@@ -1,0 +1,154 @@
+"""rocprofv3 harness: commands and summaries for the GEMM kernels.
+
+The measurement side of the method (page "Tile Selection: Cost Models Against
+Measurement", "Measurement, and what it must control") reports what the
+hardware did: per-kernel average duration from a kernel trace, matrix-core
+utilisation and LDS bank conflicts from SQ counters, and HBM traffic from the
+L2 fetch/write counters, scaled by what the same counters read for a plain
+copy of known size.
+
+    python -m tile_shape_autotuning_amd.rocprof_report commands [bench args...]
+    python -m tile_shape_autotuning_amd.rocprof_report summary --trace DIR [--pmc DIR ...]
+        [--fetch DIR --write DIR --copy-bytes N] [--kernel SUBSTR] [--flops F] [--bytes B]
+
+rocprofv3 writes SQLite databases (`*_results.db`); this module reads them
+with the standard library only.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import glob
+import json
+import os
+import sqlite3
+import sys
+
+MFMA_PASS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+             "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY",
+             "GRBM_GUI_ACTIVE"]
+SIMDS_PER_CU = 4
+MFMA_FLOPS_PER_MOP = 512        # SQ_INSTS_VALU_MFMA_MOPS_* counts 512-flop units
+
+
+def commands(bench_args, outdir="gpurun_out/prof"):
+    """The rocprofv3 invocations that produce the summaries (one pass each)."""
+    b = " ".join(["python3", "bench.py"] + list(bench_args))
+    return [
+        f"rocprofv3 --kernel-trace --stats -d {outdir}/trace -o run -- {b}",
+        f"rocprofv3 --pmc {' '.join(MFMA_PASS)} -d {outdir}/pmc -o run -- {b}",
+        f"rocprofv3 --pmc FETCH_SIZE -d {outdir}/fetch -o run -- {b} --copy-calib 1073741824",
+        f"rocprofv3 --pmc WRITE_SIZE -d {outdir}/write -o run -- {b} --copy-calib 1073741824",
+    ]
+
+
+def _dbs(d):
+    out = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not out:
+        raise FileNotFoundError(f"no *_results.db under {d}")
+    return out
+
+
+def kernel_times(trace_dir):
+    """{kernel name: (calls, average ns)} from a kernel trace."""
+    acc = collections.defaultdict(lambda: [0, 0.0])
+    for db in _dbs(trace_dir):
+        c = sqlite3.connect(db)
+        for name, dur in c.execute("select name, duration from kernels"):
+            acc[name][0] += 1
+            acc[name][1] += float(dur)
+    return {k: (n, s / n) for k, (n, s) in acc.items()}
+
+
+def counters(pmc_dir):
+    """{kernel name: {counter: mean value per dispatch}}."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for db in _dbs(pmc_dir):
+        c = sqlite3.connect(db)
+        q = "select kernel_name, dispatch_id, counter_name, value from counters_collection"
+        for name, disp, ctr, val in c.execute(q):
+            acc[name][ctr][(db, disp)] = acc[name][ctr].get((db, disp), 0.0) + float(val)
+    return {k: {ctr: sum(v.values()) / len(v) for ctr, v in d.items()} for k, d in acc.items()}
+
+
+def _pick(d, sub):
+    keys = [k for k in d if sub in k]
+    if not keys:
+        raise KeyError(f"no kernel matching {sub!r}; have {list(d)[:5]}")
+    return max(keys, key=lambda k: d[k][0] if isinstance(d[k], tuple) else 0)
+
+
+def summary(trace_dir, pmc_dirs=(), fetch_dir=None, write_dir=None, copy_bytes=0, kernel="gemm",
+            flops=None, nbytes=None):
+    times = kernel_times(trace_dir)
+    kname = _pick(times, kernel)
+    calls, avg_ns = times[kname]
+    out = {"kernel": kname, "calls": calls, "avg_us": avg_ns / 1e3}
+    if flops:
+        out["TFLOP/s"] = flops / (avg_ns * 1e-9) / 1e12
+    if nbytes:
+        out["GB/s"] = nbytes / (avg_ns * 1e-9) / 1e9
+    for d in pmc_dirs:
+        cs = counters(d)
+        k = next((n for n in cs if kernel in n), None)
+        if k is None:
+            continue
+        s = cs[k]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in s and s.get("SQ_BUSY_CU_CYCLES"):
+            out["mfma_util"] = s["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS_PER_CU * s["SQ_BUSY_CU_CYCLES"])
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in s:
+            out["mfma_flops_per_dispatch"] = s["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * MFMA_FLOPS_PER_MOP
+        if s.get("SQ_INSTS_LDS"):
+            out["lds_conflict_cycles_per_lds_inst"] = s.get("SQ_LDS_BANK_CONFLICT", 0.0) / s["SQ_INSTS_LDS"]
+        if s.get("SQ_WAVE_CYCLES"):
+            out["wait_any_frac"] = s.get("SQ_WAIT_ANY", 0.0) / s["SQ_WAVE_CYCLES"]
+            out["wait_lds_frac"] = s.get("SQ_WAIT_INST_LDS", 0.0) / s["SQ_WAVE_CYCLES"]
+        out.setdefault("counters", {}).update({c: s[c] for c in s})
+    if fetch_dir and write_dir and copy_bytes:
+        out["traffic"] = hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel)
+    return out
+
+
+def hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel="gemm"):
+    """HBM bytes per dispatch of the kernel, from FETCH_SIZE and WRITE_SIZE (KiB),
+    each scaled so that a plain copy of copy_bytes reads and writes exactly
+    copy_bytes."""
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        cs = counters(d)
+        k = next((n for n in cs if kernel in n), None)
+        copy = [n for n in cs if "copy" in n.lower() or "elementwise" in n.lower()]
+        if k is None or not copy:
+            raise KeyError(f"{name}: kernel or copy calibration missing")
+        copy_kib = max(cs[n].get(name, 0.0) for n in copy)
+        scale = (copy_bytes / 1024.0) / copy_kib if copy_kib > 0 else float("nan")
+        res[name] = {"kib_raw": cs[k].get(name, 0.0), "copy_kib_raw": copy_kib, "scale": scale,
+                     "bytes": cs[k].get(name, 0.0) * 1024.0 * scale}
+    res["bytes"] = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("commands")
+    c.add_argument("bench_args", nargs=argparse.REMAINDER)
+    s = sub.add_parser("summary")
+    s.add_argument("--trace", required=True)
+    s.add_argument("--pmc", action="append", default=[])
+    s.add_argument("--fetch")
+    s.add_argument("--write")
+    s.add_argument("--copy-bytes", type=int, default=0)
+    s.add_argument("--kernel", default="gemm")
+    s.add_argument("--flops", type=float)
+    s.add_argument("--bytes", type=float)
+    a = ap.parse_args(argv)
+    if a.cmd == "commands":
+        print("\n".join(commands(a.bench_args)))
+    else:
+        print(json.dumps(summary(a.trace, a.pmc, a.fetch, a.write, a.copy_bytes, a.kernel, a.flops, a.bytes),
+                         indent=1))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
