@@ -110,13 +110,15 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes)
 // wait-count insertion would otherwise treat every later LDS read as
 // dependent on all outstanding transfers and drain the whole pipeline before
 // it; completion is tracked explicitly with wait_vmcnt<> instead.  The
-// compiler writes M0 (the LDS destination) just before the statement but
-// cannot see that the load reads it, so the wait states an LDS-DMA load needs
-// after an M0 write are provided here (without them the transfer can land at
-// the previous M0 address).
+// compiler does not insert hazard wait states in front of an asm statement
+// for the registers it reads, so the statement carries its own: a vector
+// memory instruction that reads an SGPR written by a VALU instruction needs
+// 5 wait states on this chip family (the compiler reloads spilled SGPRs with
+// v_readlane, and without the wait the load takes a stale offset or
+// descriptor word), and an LDS-DMA load needs 1 after M0 is written.
 __device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, int soff, unsigned lds_addr)
 {
-    __asm__ __volatile__("s_nop 1\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+    __asm__ __volatile__("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                          "{m0}"(lds_addr)
                          : "memory");
 }
@@ -162,7 +164,9 @@ gemm_tiled_dma_kernel(GemmParams p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: scalar registers
+    // uniform per wave (scalar registers); a constant for one-wave blocks, so
+    // that the transfer schedule below is resolved at compile time
+    const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int wm = wave / WGN, wn = wave % WGN;
 
