@@ -117,6 +117,52 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float v)
     return __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
 }
 
+// ---- split-K workspace
+// The fp32 partial tiles of one output tile come from workgroups that may run
+// on different XCDs, whose L2 caches are not coherent with one another.  Every
+// workspace access therefore carries the agent-scope cache policy (sc1: stores
+// write through, loads never return a stale L2 copy) -- the same instructions
+// the compiler emits for relaxed agent-scope atomic loads and stores.  A
+// partial is published by waiting for its stores to complete and then bumping
+// the tile's arrival counter (a relaxed agent-scope atomic); the last arriving
+// workgroup issues its loads only after it has seen the counter.  Agent-scope
+// release/acquire fences would do the same job as a writeback plus an
+// invalidate of the whole L2 of the XCD, evicting the operand panels of every
+// other workgroup there -- that made split-K several times slower than no split.
+constexpr int kCpolSc1 = 16;
+
+// Workspace region of one tile: `split` slots of `tile_vecs` 16-byte values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(void* ws, int tile, int split, int tile_vecs)
+{
+    const int64_t slot_bytes = (int64_t)tile_vecs * 16;
+    return make_rsrc(static_cast<char*>(ws) + (int64_t)tile * split * slot_bytes, split * slot_bytes);
+}
+
+__device__ __forceinline__ void ws_store(__amdgpu_buffer_rsrc_t r, int vec, f32x4_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, vec * 16, 0, kCpolSc1);
+}
+
+__device__ __forceinline__ f32x4_t ws_load(__amdgpu_buffer_rsrc_t r, int vec)
+{
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vec * 16, 0, kCpolSc1));
+}
+
+// Wait until every vector memory access this wave issued has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Arrival of one split at `tile`; returns how many arrived before.
+__device__ __forceinline__ unsigned ws_arrive(unsigned* counters, int tile)
+{
+    return __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The reducer leaves the counter at zero for the next launch.
+__device__ __forceinline__ void ws_reset(unsigned* counters, int tile)
+{
+    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Block index -> (tile_m, tile_n, split).  The hardware hands consecutive
 // workgroups to the 8 XCDs round robin; the first step renumbers blocks so
 // that each XCD owns a contiguous range of logical ids (tiles that share A

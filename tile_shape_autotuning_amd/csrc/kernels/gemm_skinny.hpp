@@ -160,36 +160,34 @@ gemm_skinny_kernel(GemmParams p)
 
     // ---- split-K across workgroups
     if (p.split > 1) {
-        f32x4_t* wsp = reinterpret_cast<f32x4_t*>(p.ws) + (int64_t)tile * p.split * (MT * 8 * 64);
-        f32x4_t* mine = wsp + (int64_t)split * (MT * 8 * 64);
+        constexpr int TV = MT * 8 * 64;            // 16-byte values per partial slice
+        const __amdgpu_buffer_rsrc_t ws = ws_rsrc(p.ws, tile, p.split, TV);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                mine[(m * 8 + t) * 64 + lane] = acc[m][t];
-        __threadfence();
+                ws_store(ws, split * TV + (m * 8 + t) * 64 + lane, acc[m][t]);
+        wait_vm_all();
         unsigned prev = 0;
         if (lane == 0)
-            prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            prev = ws_arrive(p.counters, tile);
         prev = __shfl(prev, 0);
         if (prev != (unsigned)(p.split - 1))
             return;
-        __threadfence();
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < p.split; ++sp) {
-            const f32x4_t* part = wsp + (int64_t)sp * (MT * 8 * 64);
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    acc[m][t] += part[(m * 8 + t) * 64 + lane];
+                    acc[m][t] += ws_load(ws, sp * TV + (m * 8 + t) * 64 + lane);
         }
         if (lane == 0)
-            __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ws_reset(p.counters, tile);
     }
 
     // ---- epilogue: lane owns rows 16m + 4g + r, columns n0 + 8*l16 + t (t = 0..7)

@@ -319,39 +319,34 @@ gemm_tiled_dma_kernel(GemmParams p)
 
     // ---- split-K: publish the partial tile; the last arriving block reduces
     if (p.split > 1) {
-        f32x4_t* wsp = reinterpret_cast<f32x4_t*>(p.ws) + (int64_t)tile * p.split * (BM * BN / 4);
-        f32x4_t* mine = wsp + (int64_t)split * (BM * BN / 4);
+        constexpr int TV = BM * BN / 4;            // 16-byte values per partial tile
+        const __amdgpu_buffer_rsrc_t ws = ws_rsrc(p.ws, tile, p.split, TV);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                mine[(i * FN + j) * T + tid] = acc[i][j];
-        __threadfence();
+                ws_store(ws, split * TV + (i * FN + j) * T + tid, acc[i][j]);
+        wait_vm_all();
         __syncthreads();
-        if (tid == 0) {
-            const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (prev == (unsigned)(p.split - 1));
-        }
+        if (tid == 0)
+            s_last = (ws_arrive(p.counters, tile) == (unsigned)(p.split - 1));
         __syncthreads();
         if (!s_last)
             return;
-        __threadfence();
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < p.split; ++s) {
-            const f32x4_t* part = wsp + (int64_t)s * (BM * BN / 4);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] += part[(i * FN + j) * T + tid];
+                    acc[i][j] += ws_load(ws, s * TV + (i * FN + j) * T + tid);
         }
         if (tid == 0)
-            __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ws_reset(p.counters, tile);
     }
 
     // ---- epilogue: bias, activation, convert, store
