@@ -5,12 +5,24 @@
 // Against Measurement", "The structure of the search space": BM x BN block
 // tile, BK reduction step, WGM x WGN waves each owning a (BM/WGM) x (BN/WGN)
 // tile), but the panels travel global -> LDS without passing through
-// registers, so the pipeline can be ST stages deep: tiles t+1 .. t+ST-1 are in
-// flight while the matrix cores work on tile t.  Page "Tiling the hierarchy"
-// (double buffering): the overlap has to be asynchronous to exist at all, a
-// compute-bound tile wants at least two stages and a latency-bound one wants
-// more; on MI355X one K step of even a 256 x 256 tile is shorter than the
-// memory latency under load, so depth is what hides it.
+// registers, so the pipeline can be ST stages deep (page "Tiling the
+// hierarchy", double buffering: the overlap must be asynchronous to exist,
+// and a latency-bound tile wants more than two stages; on MI355X one K step
+// of even a 256 x 256 tile is shorter than the memory latency under load).
+//
+// Schedule.  A stage (one BK step) is KK = BK/32 slices of 32 k; a wave's
+// fragment registers are double buffered per slice, and while the matrix
+// core works through the FM x FN MFMAs of slice s the wave reads slice s+1's
+// fragments and, in the last slice of a stage, issues the transfers of the
+// tile ST steps ahead -- one or two such instructions after each MFMA, in an
+// order pinned with sched_barrier, so the matrix core is never left waiting
+// on an instruction burst.  There is one block barrier per stage, at the
+// start of its last slice: by then every read of the stage's buffer has
+// returned (its fragments are in registers) and the next tile has landed, so
+// after the barrier the buffer can be refilled and the next stage's first
+// fragments read while the last slice multiplies.  Tiles past the end of the
+// K range are issued as fully out-of-range transfers (they write zeros that
+// nothing reads), which keeps every stage -- and every wait count -- the same.
 //
 // gfx950 specifics:
 //   * buffer_load_dwordx4 ... lds: every lane of a wave fetches 16 bytes into
@@ -59,16 +71,20 @@ struct TiledDma {
     static constexpr int A_INST = A_BYTES / 1024;       // wave-wide 1 KiB transfers
     static constexpr int B_INST = B_BYTES / 1024;
     static constexpr int INST = A_INST + B_INST;
-    static constexpr int LPW_MAX = (INST + W - 1) / W;
+    static constexpr int LPW_MAX = (INST + W - 1) / W;   // transfers per wave per stage
     static constexpr int LPW_MIN = INST / W;
-    static constexpr int WAIT_N = (ST - 2) * LPW_MIN > 63 ? 63 : (ST - 2) * LPW_MIN;
+    static constexpr int cap63(int n) { return n > 63 ? 63 : n; }
+    // outstanding transfers a wave may still have when tile t+1 must have
+    // landed (tiles t+2 .. t+ST-1), and after the prologue (tiles 1 .. ST-1)
+    static constexpr int WAIT_N = cap63((ST - 2) * LPW_MIN);
+    static constexpr int WAIT_P = cap63((ST - 1) * LPW_MIN);
     static constexpr int PPI = 1024 / RB;               // B rows per transfer (8 or 16)
     static constexpr int SLOTS_PER_ROW = RB / 16;       // 16-byte slots per B block row
-    // Read the next k slice's B fragments during the last row-tile of the
-    // current one only when the extra FN x 4 registers fit next to the
-    // accumulators (at W waves a lane has 512 / max(1, W/4) registers).
-    static constexpr int REGS = W <= 4 ? 512 : 512 / (W / 4);
-    static constexpr bool PREFETCH_B = KK > 1 && FM * FN * 4 + 8 * FN + 8 + 64 <= REGS;
+    static constexpr int NMF = FM * FN;                 // MFMAs per wave per slice
+    static constexpr int NRD = FM + 2 * FN;             // LDS reads per wave per slice
+    // every wave's transfers split into A and B ones the same way: which
+    // operand a transfer loads is then known at compile time
+    static constexpr bool STATIC_AB = A_INST % W == 0 && B_INST % W == 0;
 
     static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "whole 16x16 tiles per wave");
     static_assert(BK % 32 == 0, "BK is a multiple of the MFMA K (32)");
@@ -116,9 +132,9 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes)
 // 5 wait states on this chip family (the compiler reloads spilled SGPRs with
 // v_readlane, and without the wait the load takes a stale offset or
 // descriptor word), and an LDS-DMA load needs 1 after M0 is written.
-__device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, int soff, unsigned lds_addr)
+__device__ __forceinline__ void dma16(i32x4_t rsrc, int voff, unsigned lds_addr)
 {
-    __asm__ __volatile__("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+    __asm__ __volatile__("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
                          "{m0}"(lds_addr)
                          : "memory");
 }
@@ -130,6 +146,14 @@ __device__ __forceinline__ void wait_vmcnt()
     // expcnt and lgkmcnt at their maxima: wait on vector memory only
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+
+// Wait until every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
 
 __device__ __forceinline__ void block_barrier()
 {
@@ -188,6 +212,7 @@ gemm_tiled_dma_kernel(GemmParams p)
     // physical chunk lane%4 holding logical chunk (lane%4) ^ swz_a(row).
     const int a_row = lane >> 2;
     const int a_chunk = (lane & 3) ^ swz_a(a_row);
+    const int a_k8 = a_chunk * 8;                     // first k of the lane's chunk
     const int voA = a_row * K * 2 + a_chunk * 16;
     // B transfer: PPI block rows x RB bytes; lane -> block row p_l, 16-byte slot
     // s16 (unit s16/2 ^ swz_b, half s16%2).
@@ -197,33 +222,60 @@ gemm_tiled_dma_kernel(GemmParams p)
     const int b_krow_lane = b_pos_to_row(b_pl);       // row bits coming from the lane
     const int voB = b_krow_lane * N * 2 + b_col * 2;
 
+    // Transfer q of this wave is number j = wave + q W of the stage: A
+    // transfers first (row block rb, k slice kk), then B (block blk, row group
+    // pblk).  Its lane offset within the tile, with the M / N edge folded in,
+    // does not change from stage to stage; only the K edge is checked per stage.
+    auto is_a = [&](int q) { return Cf::STATIC_AB ? q < Cf::A_INST / W : wave + q * W < Cf::A_INST; };
+    auto exists = [&](int q) { return Cf::STATIC_AB || wave + q * W < Cf::INST; };
+    int vo[Cf::LPW_MAX];
+#pragma unroll
+    for (int q = 0; q < Cf::LPW_MAX; ++q) {
+        const int j = wave + q * W;
+        if (is_a(q)) {
+            const int kk = j / (BM / 16), rb = j % (BM / 16);
+            vo[q] = (rb * 16 + a_row < rows_left) ? voA + (rb * 16 * K + kk * 32) * 2 : kOOB;
+        } else {
+            const int jb = j - Cf::A_INST;
+            const int blk = jb / (BK / Cf::PPI), pblk = jb % (BK / Cf::PPI);
+            const int krow_unif = b_pos_to_row(pblk * Cf::PPI);    // disjoint from the lane's row bits
+            vo[q] = (blk * QW + b_col < cols_left) ? voB + (krow_unif * N + blk * QW) * 2 : kOOB;
+        }
+    }
+
     const unsigned lds_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) u32x4_t*)lds;
 
-    auto issue = [&](int t, int buf) {
+    // Everything the transfers of tile t need: buffer descriptors whose base is
+    // the tile's corner (so lane offsets stay small), its LDS buffer, and how
+    // many k of it lie inside this split's K range (<= 0 past the end).
+    struct Tile {
+        i32x4_t rA, rB;
+        unsigned dst;
+        int klim;
+    };
+    auto tile_desc = [&](int t, int buf) {
+        Tile d;
         const int k0 = kbeg + t * BK;
-        const int klim = kend - k0;   // k >= klim (relative) lies outside this split
+        d.klim = kend - k0;
         const int64_t a_off = (int64_t)m0 * K + k0;
         const int64_t b_off = (int64_t)k0 * N + n0;
-        const i32x4_t rA = rsrc_words(Ab + a_off * 2, (a_total - a_off) * 2);
-        const i32x4_t rB = rsrc_words(Bb + b_off * 2, (b_total - b_off) * 2);
-        const unsigned dst0 = lds_base + (unsigned)(buf * Cf::STAGE_BYTES);
-#pragma unroll
-        for (int q = 0; q < Cf::LPW_MAX; ++q) {
-            const int j = wave + q * W;
-            if (j < Cf::A_INST) {
-                // rows rb*16 .. +15 of k slice kk
-                const int kk = j / (BM / 16), rb = j % (BM / 16);
-                const bool ok = (rb * 16 + a_row < rows_left) && (kk * 32 + a_chunk * 8 < klim);
-                dma16(rA, ok ? voA : kOOB, (rb * 16 * K + kk * 32) * 2, dst0 + (unsigned)(j * 1024));
-            } else if (j < Cf::INST) {
-                const int jb = j - Cf::A_INST;
-                const int blk = jb / (BK / Cf::PPI), pblk = jb % (BK / Cf::PPI);
-                const int p_unif = pblk * Cf::PPI;                   // block-row bits from the transfer index
-                const int krow_unif = b_pos_to_row(p_unif);           // disjoint from the lane's row bits
-                const bool ok = (blk * QW + b_col < cols_left) && (krow_unif + b_krow_lane < klim);
-                dma16(rB, ok ? voB : kOOB, krow_unif * N * 2 + blk * QW * 2,
-                      dst0 + (unsigned)(Cf::A_BYTES + jb * 1024));
-            }
+        d.rA = rsrc_words(Ab + a_off * 2, (a_total - a_off) * 2);
+        d.rB = rsrc_words(Bb + b_off * 2, (b_total - b_off) * 2);
+        d.dst = lds_base + (unsigned)(buf * Cf::STAGE_BYTES);
+        return d;
+    };
+    auto dma_op = [&](int q, const Tile& d) {
+        if (!exists(q))
+            return;
+        const int j = wave + q * W;
+        if (is_a(q)) {
+            const int kk = j / (BM / 16);
+            dma16(d.rA, (a_k8 < d.klim - kk * 32) ? vo[q] : kOOB, d.dst + (unsigned)(j * 1024));
+        } else {
+            const int jb = j - Cf::A_INST;
+            const int krow_unif = b_pos_to_row((jb % (BK / Cf::PPI)) * Cf::PPI);
+            dma16(d.rB, (b_krow_lane < d.klim - krow_unif) ? vo[q] : kOOB,
+                  d.dst + (unsigned)(Cf::A_BYTES + jb * 1024));
         }
     };
 
@@ -242,80 +294,119 @@ gemm_tiled_dma_kernel(GemmParams p)
                             (l16 & 3) * 8);
     }
 
+    // Accumulators live in AGPRs from here to the end of the K loop: the
+    // empty asm statements pin them there at both ends (left alone, the
+    // register allocator splits them between AGPRs and VGPRs and shuffles
+    // them on every iteration).
     f32x4_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            __asm__ __volatile__("" : "+a"(acc[i][j]));
+        }
 
-    // ---- MFMA work on one LDS stage.  Fragment reads run one step ahead of
-    // the MFMAs that consume them: the A fragment of row-tile i+1 is read
-    // while row-tile i multiplies, and the B fragments of the next 32-wide k
-    // slice while the last row-tile of this one multiplies.  sched_barrier
-    // pins that order (left alone, the scheduler sinks every read next to its
-    // first use and the matrix core waits on each LDS round trip).
-    auto compute = [&](int buf) {
+    // fragment registers of two slices
+    u32x4_t a[2][FM], b[2][FN];
+    // read o of a slice, in the order its MFMAs first need them: A row-tile 0,
+    // the B halves, then the other A row-tiles
+    auto read_op = [&](unsigned st, int kk, int par, int o) {
+        if (o == 0) {
+            a[par][0] = lds_read_b128(st + rdA + (unsigned)(kk * BM * 64));
+        } else if (o <= 2 * FN) {
+            const int j = (o - 1) >> 1, h = (o - 1) & 1;
+            const u32x2_t w = lds_read_tr(st + rdB[j] + (unsigned)((kk * 32 + h * 16) * RB));
+            b[par][j][2 * h] = w.x;
+            b[par][j][2 * h + 1] = w.y;
+        } else {
+            const int i = o - 2 * FN;
+            a[par][i] = lds_read_b128(st + rdA + (unsigned)(kk * BM * 64 + i * 1024));
+        }
+    };
+    // The MFMAs of one slice with NOPS other instructions spread among them.
+    // Op o goes right after MFMA (o NMF) / NOPS.
+    auto slice = [&](int par, auto NOPS, auto&& op) {
+        constexpr int nops = decltype(NOPS)::value;
+#pragma unroll
+        for (int m = 0; m < Cf::NMF; ++m) {
+            const int i = m / FN, j = m % FN;
+            acc[i][j] = mfma_bf16(a[par][i], b[par][j], acc[i][j]);
+#pragma unroll
+            for (int o = (m * nops + Cf::NMF - 1) / Cf::NMF; o < ((m + 1) * nops + Cf::NMF - 1) / Cf::NMF; ++o)
+                op(o);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // One stage: tile t in buffer buf, its first slice in fragment set PAR0.
+    auto stage = [&](int t, int buf, auto PAR0) {
+        constexpr int par0 = decltype(PAR0)::value;
         const unsigned st = lds_base + (unsigned)(buf * Cf::STAGE_BYTES);
-        const unsigned a0 = st + rdA;
-        auto read_a = [&](int i, int kk) { return lds_read_b128(a0 + (unsigned)(kk * BM * 64 + i * 1024)); };
-        auto read_b = [&](int kk, u32x4_t(&b)[FN]) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x2_t w = lds_read_tr(st + rdB[j] + (unsigned)((kk * 32 + h * 16) * RB));
-                    b[j][2 * h] = w.x;
-                    b[j][2 * h + 1] = w.y;
-                }
-            }
-        };
-        u32x4_t b_cur[FN], b_nxt[FN];
-        read_b(0, b_cur);
-        u32x4_t a_cur = read_a(0, 0);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            if (!Cf::PREFETCH_B && kk > 0)
-                read_b(kk, b_cur);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                u32x4_t a_nxt = a_cur;
-                if (i + 1 < FM)
-                    a_nxt = read_a(i + 1, kk);
-                else if (kk + 1 < KK)
-                    a_nxt = read_a(0, kk + 1);
-                if (Cf::PREFETCH_B && kk + 1 < KK && i == FM - 1)
-                    read_b(kk + 1, b_nxt);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma_bf16(a_cur, b_cur[j], acc[i][j]);
-                __builtin_amdgcn_sched_barrier(0);
-                a_cur = a_nxt;
-            }
-            if (Cf::PREFETCH_B && kk + 1 < KK) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    b_cur[j] = b_nxt[j];
+            const int par = (par0 + kk) & 1;
+            if (kk + 1 < KK) {
+                slice(par, IntC<Cf::NRD>{}, [&](int o) { read_op(st, kk + 1, par ^ 1, o); });
+            } else {
+                // all reads of this buffer have returned, tile t+1 has landed
+                wait_lgkm0();
+                wait_vmcnt<Cf::WAIT_N>();
+                block_barrier();
+                const int nbuf = buf + 1 == ST ? 0 : buf + 1;
+                const unsigned nst = lds_base + (unsigned)(nbuf * Cf::STAGE_BYTES);
+                const Tile d = tile_desc(t + ST, buf);
+                slice(par, IntC<Cf::NRD + Cf::LPW_MAX>{}, [&](int o) {
+                    if (o < Cf::NRD)
+                        read_op(nst, 0, par ^ 1, o);
+                    else
+                        dma_op(o - Cf::NRD, d);
+                });
             }
         }
     };
 
-    // ---- pipeline: tile t lives in buffer t % ST
+    // ---- prologue: tiles 0 .. ST-1 in flight, slice 0 of tile 0 in registers
 #pragma unroll
-    for (int t = 0; t < ST - 1; ++t)
-        if (t < nk)
-            issue(t, t);
-    for (int t = 0; t < nk; ++t) {
-        if (t + ST - 2 < nk)
-            wait_vmcnt<Cf::WAIT_N>();     // this wave's loads of tile t have landed
-        else
-            wait_vmcnt<0>();
-        block_barrier();                  // ... and every wave's; tile t-1's buffer is free
-        if (t + ST - 1 < nk)
-            issue(t + ST - 1, (t + ST - 1) % ST);
-        compute(t % ST);
+    for (int t = 0; t < ST; ++t) {
+        const Tile d = tile_desc(t, t);
+#pragma unroll
+        for (int q = 0; q < Cf::LPW_MAX; ++q)
+            dma_op(q, d);
     }
+    wait_vmcnt<Cf::WAIT_P>();
+    block_barrier();
+#pragma unroll
+    for (int o = 0; o < Cf::NRD; ++o)
+        read_op(lds_base, 0, 0, o);
+
+    // ---- main loop; with an odd number of slices per stage the fragment set
+    // of a stage's first slice alternates, so stages go in pairs
+    if constexpr (KK % 2 == 0) {
+        int buf = 0;
+        for (int t = 0; t < nk; ++t) {
+            stage(t, buf, IntC<0>{});
+            buf = buf + 1 == ST ? 0 : buf + 1;
+        }
+    } else {
+        int buf = 0;
+        for (int t = 0; t < nk; t += 2) {
+            stage(t, buf, IntC<0>{});
+            buf = buf + 1 == ST ? 0 : buf + 1;
+            if (t + 1 >= nk)
+                break;
+            stage(t + 1, buf, IntC<1>{});
+            buf = buf + 1 == ST ? 0 : buf + 1;
+        }
+    }
+    // the zero-filling transfers of tiles past the end may still be in flight:
+    // they must land before LDS is reused or released
+    wait_vm_all();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            __asm__ __volatile__("" : "+a"(acc[i][j]));
 
     // ---- split-K: publish the partial tile; the last arriving block reduces
     if (p.split > 1) {
@@ -349,17 +440,25 @@ gemm_tiled_dma_kernel(GemmParams p)
             ws_reset(p.counters, tile);
     }
 
-    // ---- epilogue: bias, activation, convert, store
+    // ---- epilogue: bias, activation, convert, store.  The lane coordinates
+    // are derived afresh from an opaque copy of the thread index, so that
+    // nothing the epilogue needs is computed before the K loop and held in
+    // registers across it.
+    int tid_e = tid;
+    __asm__ __volatile__("" : "+v"(tid_e));
+    const int l16e = tid_e & 15, ge = (tid_e >> 4) & 3;
+    const int wave_e = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid_e >> 6);
+    const int wme = wave_e / WGN, wne = wave_e % WGN;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * Cf::WN + j * 16 + l16;
+        const int col = n0 + wne * Cf::WN + j * 16 + l16e;
         const bool cv = col < N;
         const float bj = (p.bias && cv) ? p.bias[col] : 0.0f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * Cf::WM + i * 16 + g * 4 + r;
+                const int row = m0 + wme * Cf::WM + i * 16 + ge * 4 + r;
                 if (cv && row < M) {
                     const float v = apply_act(acc[i][j][r] + bj, p.act);
                     const int64_t idx = (int64_t)row * N + col;
