@@ -85,6 +85,8 @@ struct TiledDma {
     // every wave's transfers split into A and B ones the same way: which
     // operand a transfer loads is then known at compile time
     static constexpr bool STATIC_AB = A_INST % W == 0 && B_INST % W == 0;
+    // the epilogue stages one 16-row slab per wave through LDS when it fits
+    static constexpr bool EPI_LDS = W * 16 * (WN + 4) * 4 <= ST * STAGE_BYTES;
 
     static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "whole 16x16 tiles per wave");
     static_assert(BK % 32 == 0, "BK is a multiple of the MFMA K (32)");
@@ -446,26 +448,85 @@ gemm_tiled_dma_kernel(GemmParams p)
     // registers across it.
     int tid_e = tid;
     __asm__ __volatile__("" : "+v"(tid_e));
-    const int l16e = tid_e & 15, ge = (tid_e >> 4) & 3;
+    const int lane_e = tid_e & 63;
+    const int l16e = lane_e & 15, ge = lane_e >> 4;
     const int wave_e = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid_e >> 6);
     const int wme = wave_e / WGN, wne = wave_e % WGN;
+    const int row_w = m0 + wme * Cf::WM;          // first output row of the wave tile
+    const int col_w = n0 + wne * Cf::WN;          // first output column
+
+    if constexpr (Cf::EPI_LDS) {
+        // Each wave turns its accumulators, one 16-row slab at a time, into
+        // whole rows through a private LDS slab (row stride WN + 4 floats keeps
+        // the four row groups of a write in different banks), then every lane
+        // stores 8 consecutive outputs with one 16-byte (bf16) or two (fp32)
+        // stores.  A lane always owns the same 8 columns, so it loads their
+        // bias once.
+        constexpr int RS = Cf::WN + 4;                 // slab row stride, floats
+        constexpr int CPR = Cf::WN / 8;                // 8-column chunks per row
+        constexpr int PASSES = (16 * CPR + 63) / 64;   // 64-chunk rounds per slab
+        float* slab = reinterpret_cast<float*>(lds) + wave_e * 16 * RS;
+        const int c8 = lane_e % CPR;                   // the lane's column chunk
+        const int col0 = col_w + c8 * 8;
+        const bool col_ok = col0 < N;                  // N is a multiple of 8
+        float bias8[8];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wne * Cf::WN + j * 16 + l16e;
-        const bool cv = col < N;
-        const float bj = (p.bias && cv) ? p.bias[col] : 0.0f;
+        for (int e = 0; e < 8; ++e)
+            bias8[e] = (p.bias && col_ok) ? p.bias[col0 + e] : 0.0f;
+        __syncthreads();   // every wave's last transfers and reads are done: LDS is free
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wme * Cf::WM + i * 16 + ge * 4 + r;
-                if (cv && row < M) {
-                    const float v = apply_act(acc[i][j][r] + bj, p.act);
-                    const int64_t idx = (int64_t)row * N + col;
-                    if (p.out_bf16)
-                        static_cast<unsigned short*>(p.C)[idx] = f32_to_bf16_rne(v);
-                    else
-                        static_cast<float*>(p.C)[idx] = v;
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    slab[(ge * 4 + r) * RS + j * 16 + l16e] = acc[i][j][r];
+#pragma unroll
+            for (int ps = 0; ps < PASSES; ++ps) {
+                const int c = ps * 64 + lane_e;
+                const int r = c / CPR;
+                const int row = row_w + i * 16 + r;
+                if (c < 16 * CPR && row < M && col_ok) {
+                    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(slab + r * RS + c8 * 8);
+                    const f32x4_t v0 = src[0], v1 = src[1];
+                    float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        o[e] = apply_act(o[e] + bias8[e], p.act);
+                    const int64_t idx = (int64_t)row * N + col0;
+                    if (p.out_bf16) {
+                        u32x4_t w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            w[e] = (unsigned)f32_to_bf16_rne(o[2 * e]) | ((unsigned)f32_to_bf16_rne(o[2 * e + 1]) << 16);
+                        *reinterpret_cast<u32x4_t*>(static_cast<unsigned short*>(p.C) + idx) = w;
+                    } else {
+                        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx);
+                        dst[0] = f32x4_t{o[0], o[1], o[2], o[3]};
+                        dst[1] = f32x4_t{o[4], o[5], o[6], o[7]};
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = col_w + j * 16 + l16e;
+            const bool cv = col < N;
+            const float bj = (p.bias && cv) ? p.bias[col] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row_w + i * 16 + ge * 4 + r;
+                    if (cv && row < M) {
+                        const float v = apply_act(acc[i][j][r] + bj, p.act);
+                        const int64_t idx = (int64_t)row * N + col;
+                        if (p.out_bf16)
+                            static_cast<unsigned short*>(p.C)[idx] = f32_to_bf16_rne(v);
+                        else
+                            static_cast<float*>(p.C)[idx] = v;
+                    }
                 }
             }
         }
