@@ -12,8 +12,14 @@ wave-quantisation case); the other four workloads are reported under
                                # (best/worst/fixed ratios, model hit rate)
                   [--copy-calib BYTES]   # plain copy for the HBM counter scale
                   [--only]     # time only the chosen workload (for profiling)
+                  [--fresh | --cache FILE]   # tune now, or load a tuning cache
+                                             # (default: the persisted MI355X one)
+                  [--cache-out FILE]         # with --report: save the exhaustive tuning
 
-Prints one JSON line.  Needs the built library; the oracle is used only for
+The per-shape configurations come from the persisted tuning cache when it is
+present (the exhaustive measured autotune of every workload on MI355X, in the
+library's own cache format); --fresh runs the library's hybrid tuner instead.
+The JSON "config.tuning" says which.  Prints one JSON line.  Needs the built library; the oracle is used only for
 the CPU-baseline leg.
 """
 from __future__ import annotations
@@ -115,6 +121,36 @@ def shape_summary(p, sec):
             "tuned_us": round(meas, 3)}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+# per-shape tuning results measured on MI355X (the library's cache file format)
+DEFAULT_CACHE = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "mi355x.cache")
+
+
+def library_digest():
+    import hashlib
+    from tile_shape_autotuning_amd import _native
+    with open(_native.LIB_PATH, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload, cfg):
+    """HBM bytes per launch recorded by the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs for this workload and configuration -- only if they were taken on
+    the library that is loaded now (else the kernel may have changed: None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = library_digest()
+    want = ",".join(str(x) for x in cfg)
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if not line.startswith("traffic "):
+                continue
+            kv = dict(t.split("=", 1) for t in line.split()[1:])
+            if kv.get("workload") == workload and kv.get("cfg") == want and kv.get("lib_sha256") == digest:
+                return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
+    return None
+
+
 def cpu_baseline(index, target_s=12.0):
     """The oracle on a bounded row sample of the workload (host cores)."""
     from oracle import gemm_ref
@@ -142,13 +178,15 @@ def cpu_baseline(index, target_s=12.0):
                       f"{dt:.2f} s per pass x {reps} pass(es)"}
 
 
-def report(indices, torch, dump_dir=None):
+def report(indices, torch, dump_dir=None, cache_out=None):
     """Measure every feasible configuration per workload with the library's
-    exhaustive tuner: best/worst/fixed ratios and the cost model's hit rate."""
+    exhaustive tuner: best/worst/fixed ratios and the cost model's hit rate.
+    With cache_out, the exhaustively tuned entries are saved there."""
     import tile_shape_autotuning_amd as tg
     from tile_shape_autotuning_amd import _native as N
     out = {}
     hits = 0
+    tg.cache_clear()
     for i in indices:
         w = wl.WORKLOADS[i]
         os.environ["TILEGEMM_TUNE_MODE"] = "exhaustive"
@@ -156,7 +194,6 @@ def report(indices, torch, dump_dir=None):
         os.environ["TILEGEMM_PROGRESS"] = "1"
         # split-K cannot help a problem with thousands of tiles; keep its sweep short
         os.environ["TILEGEMM_TUNE_MAX_SPLIT"] = "1" if w.flops > 1e12 else "64"
-        tg.cache_clear()
         t0 = time.perf_counter()
         tg.gemm_autotune(w.M, w.N, w.K, w.dtype)
         tune_s = time.perf_counter() - t0
@@ -189,6 +226,9 @@ def report(indices, torch, dump_dir=None):
             "model_hit": hit, "rank_corr": round(rho, 3),
         }
         log(f"report {w.name}: {out[w.name]}")
+    if cache_out:
+        tg.cache_save(cache_out)
+        log(f"tuning cache written to {cache_out}")
     os.environ["TILEGEMM_TUNE_MODE"] = "hybrid"
     tg.cache_clear()
     return out, hits
@@ -205,6 +245,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0)
     ap.add_argument("--dump", type=str, default="", help="with --report: write every measured row here")
+    ap.add_argument("--fresh", action="store_true",
+                    help="tune from scratch instead of loading the persisted tuning cache")
+    ap.add_argument("--cache", type=str, default=DEFAULT_CACHE, help="tuning cache file to load")
+    ap.add_argument("--cache-out", type=str, default="", help="with --report: save the exhaustive tuning here")
     ap.add_argument("--cfg", type=str, default="",
                     help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
@@ -227,6 +271,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {a.copy_calib} bytes")
+
+    tuning = "fresh"
+    if not a.fresh and a.cache and os.path.exists(a.cache):
+        loaded, skipped = tg.cache_load(a.cache)
+        tuning = f"cache {os.path.relpath(a.cache, ROOT)} ({loaded} entries, {skipped} skipped)"
+        log(f"tuning: {tuning}")
 
     main_idx = a.workload
     indices = [main_idx] if a.only else [main_idx] + [i for i in sorted(wl.WORKLOADS) if i != main_idx]
@@ -269,14 +319,15 @@ def main():
         "dtype": prec, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "dtype": wl.DTYPE_NAMES[w.dtype], "act": p.act,
-                   "cfg": shapes[w.name]["cfg"], "parallelism": "single-gpu"},
+                   "cfg": shapes[w.name]["cfg"], "tuning": tuning, "parallelism": "single-gpu"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(w.name, shapes[w.name]["cfg"])},
         "shapes": shapes,
     }
     if a.report:
-        rep, hits = report([i for i in indices], torch, a.dump)
+        rep, hits = report([i for i in indices], torch, a.dump, a.cache_out or None)
         line["report"] = rep
         line["model_hit_rate"] = f"{hits}/{len(indices)}"
     if not a.no_cpu:

@@ -1,0 +1,104 @@
+"""The rocprofv3 harness on synthetic result databases (CPU only).
+
+rocprofv3 writes SQLite files with a `kernels` view (one row per dispatch,
+duration in ns) and a `counters_collection` view (one row per dispatch and
+counter, possibly several rows per counter that add up).  These tests build
+such files by hand, with numbers whose derived figures are known exactly.
+"""
+import os
+import sqlite3
+
+import pytest
+
+from tile_shape_autotuning_amd import rocprof_report as R
+
+GEMM = "void tg::gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2>(tg::GemmParams)"
+COPY = "void at::native::elementwise_kernel<copy>(int)"
+
+
+def _trace_db(d, rows):
+    os.makedirs(d, exist_ok=True)
+    c = sqlite3.connect(os.path.join(d, "run_results.db"))
+    c.execute("create table kernels (name text, duration integer)")
+    c.executemany("insert into kernels values (?, ?)", rows)
+    c.commit()
+    c.close()
+
+
+def _pmc_db(d, rows):
+    os.makedirs(d, exist_ok=True)
+    c = sqlite3.connect(os.path.join(d, "run_results.db"))
+    c.execute("create table counters_collection (kernel_name text, dispatch_id integer, counter_name text, "
+              "value real)")
+    c.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+    c.commit()
+    c.close()
+
+
+def test_kernel_times_average_per_name(tmp_path):
+    d = str(tmp_path / "trace")
+    _trace_db(d, [(GEMM, 30000), (GEMM, 40000), (COPY, 1000)])
+    t = R.kernel_times(d)
+    assert t[GEMM] == (2, 35000.0)
+    assert t[COPY] == (1, 1000.0)
+    assert "gemm_tiled_dma_kernel" in R.kernel_table(d)
+
+
+def test_counters_sum_rows_of_one_dispatch_then_average(tmp_path):
+    d = str(tmp_path / "pmc")
+    # dispatch 1 reports the counter in two rows (e.g. per XCD); dispatch 2 in one
+    _pmc_db(d, [(GEMM, 1, "SQ_WAVES", 3.0), (GEMM, 1, "SQ_WAVES", 5.0), (GEMM, 2, "SQ_WAVES", 4.0)])
+    assert R.counters(d)[GEMM]["SQ_WAVES"] == pytest.approx(6.0)
+
+
+def test_summary_mfma_utilisation_and_rates(tmp_path):
+    tr, pmc = str(tmp_path / "t"), str(tmp_path / "p")
+    _trace_db(tr, [(GEMM, 50000)] * 4)            # 50 us per launch
+    busy_cu = 1.0e6
+    _pmc_db(pmc, [(GEMM, 1, "SQ_VALU_MFMA_BUSY_CYCLES", 2.0e6), (GEMM, 1, "SQ_BUSY_CU_CYCLES", busy_cu),
+                  (GEMM, 1, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0), (GEMM, 1, "SQ_INSTS_LDS", 400.0),
+                  (GEMM, 1, "SQ_LDS_BANK_CONFLICT", 100.0), (GEMM, 1, "SQ_WAVE_CYCLES", 1000.0),
+                  (GEMM, 1, "SQ_WAIT_ANY", 250.0)])
+    s = R.summary(tr, [pmc], kernel="gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2>", flops=1.0e12, nbytes=4.0e8)
+    assert s["avg_us"] == pytest.approx(50.0)
+    assert s["TFLOP/s"] == pytest.approx(1.0e12 / 50e-6 / 1e12)
+    assert s["GB/s"] == pytest.approx(4.0e8 / 50e-6 / 1e9)
+    assert s["mfma_util"] == pytest.approx(2.0e6 / (4 * busy_cu))       # four SIMDs per CU
+    assert s["mfma_flops_per_dispatch"] == pytest.approx(1000.0 * 512)
+    assert s["lds_conflict_cycles_per_lds_inst"] == pytest.approx(0.25)
+    assert s["wait_any_frac"] == pytest.approx(0.25)
+
+
+def test_hbm_traffic_scaled_by_the_copy_calibration(tmp_path):
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    copy_bytes = 1 << 30
+    # the copy reads and writes copy_bytes; its counters read half and exactly that
+    _pmc_db(fetch, [(COPY, 1, "FETCH_SIZE", copy_bytes / 1024 / 2), (GEMM, 2, "FETCH_SIZE", 1000.0)])
+    _pmc_db(write, [(COPY, 1, "WRITE_SIZE", copy_bytes / 1024), (GEMM, 2, "WRITE_SIZE", 300.0)])
+    t = R.hbm_traffic(fetch, write, copy_bytes, kernel="gemm")
+    assert t["FETCH_SIZE"]["scale"] == pytest.approx(2.0)
+    assert t["FETCH_SIZE"]["bytes"] == pytest.approx(1000.0 * 1024 * 2.0)
+    assert t["WRITE_SIZE"]["bytes"] == pytest.approx(300.0 * 1024)
+    assert t["bytes"] == pytest.approx(1000.0 * 1024 * 2.0 + 300.0 * 1024)
+
+
+def test_missing_results_raise(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        R.kernel_times(str(tmp_path / "nothing"))
+
+
+def test_kernel_names_match_the_template_instances():
+    assert R.kernel_name((0, 64, 128, 64, 2, 4, 2, 4)) == "gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2>"
+    assert R.kernel_name((1, 32, 128, 32, 4, 1, 2, 8)) == "gemm_skinny_kernel<2, 4, 2>"
+
+
+def test_commands_give_one_counter_block_per_pass():
+    cmds = R.commands(["--workload", "3", "--only"])
+    pmc = [c for c in cmds if "--pmc" in c]
+    assert len(pmc) == 3
+    for c in pmc:
+        ctrs = c.split("--pmc", 1)[1].split("-d", 1)[0].split()
+        assert sum(1 for x in ctrs if x.startswith("SQ_")) <= 8
+        assert sum(1 for x in ctrs if x.startswith("GRBM_")) <= 2
+    assert any("FETCH_SIZE" in c and "WRITE_SIZE" not in c for c in pmc)
+    assert any("WRITE_SIZE" in c and "FETCH_SIZE" not in c for c in pmc)

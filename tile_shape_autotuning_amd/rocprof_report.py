@@ -128,6 +128,66 @@ def hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel="gemm"):
     return res
 
 
+def kernel_table(trace_dir, top=12):
+    """Text table of the kernels in a trace, by total time."""
+    times = kernel_times(trace_dir)
+    rows = sorted(times.items(), key=lambda kv: -kv[1][0] * kv[1][1])[:top]
+    out = [f"{'calls':>7} {'avg us':>10} {'total ms':>9}  kernel"]
+    for name, (n, avg) in rows:
+        out.append(f"{n:>7} {avg / 1e3:>10.3f} {n * avg / 1e6:>9.3f}  {name}")
+    return "\n".join(out)
+
+
+def kernel_name(cfg, in_bf16=True):
+    """The template name rocprofv3 prints for a configuration's kernel."""
+    kind, bm, bn, bk, wgm, wgn, st, _ = cfg
+    if kind == 0 and in_bf16:
+        return f"gemm_tiled_dma_kernel<{bm}, {bn}, {bk}, {wgm}, {wgn}, {st}>"
+    if kind == 1:
+        return f"gemm_skinny_kernel<{bm // 16}, {wgm}, {st}>"
+    return f"gemm_tiled_kernel<{'true' if in_bf16 else 'false'}, {bm}, {bn}, {bk}, {wgm}, {wgn}, {st}"
+
+
+def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, flops,
+                  algo_bytes, commands_used):
+    """Summary of one kernel on one workload: duration, MFMA utilisation, LDS
+    bank conflicts, L2 hit rate and HBM bytes (FETCH_SIZE / WRITE_SIZE scaled
+    by the same counters for a plain copy of copy_bytes)."""
+    sm = summary(trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, kname, flops, algo_bytes)
+    c = sm.get("counters", {})
+    lines = [f"# {kname} on {workload}", "", "cfg (kind,bm,bn,bk,wgm,wgn,stages,split_k): " +
+             ",".join(str(x) for x in cfg), "", "commands (run from the repository root on MI355X):"]
+    lines += [f"  {cmd}" for cmd in commands_used]
+    lines += ["", f"launches traced:            {sm['calls']}", f"average duration:           {sm['avg_us']:.3f} us"]
+    if flops:
+        lines.append(f"algorithmic TFLOP/s:        {sm['TFLOP/s']:.1f}   (2MNK = {flops:.4g} flop per launch)")
+    if algo_bytes:
+        lines.append(f"algorithmic GB/s:           {sm['GB/s']:.1f}   (compulsory {algo_bytes:.4g} B per launch)")
+    if "mfma_util" in sm:
+        lines.append(f"MFMA busy / (4 x CU busy):  {sm['mfma_util']:.3f}")
+    if c.get("GRBM_GUI_ACTIVE") and c.get("SQ_BUSY_CU_CYCLES"):
+        lines.append(f"busy CUs (CU-busy / GPU-busy cycles, 8 XCDs): {c['SQ_BUSY_CU_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / 8):.0f}")
+    if "lds_conflict_cycles_per_lds_inst" in sm:
+        lines.append(f"LDS bank-conflict cycles per LDS instruction: {sm['lds_conflict_cycles_per_lds_inst']:.2f}")
+    if "wait_any_frac" in sm:
+        lines.append(f"wave cycles waiting (any): {sm['wait_any_frac']:.3f}")
+    if c.get("TCC_HIT_sum") is not None and c.get("TCC_MISS_sum") is not None:
+        h, m = c["TCC_HIT_sum"], c["TCC_MISS_sum"]
+        lines.append(f"L2 hit rate:                {h / max(1.0, h + m):.3f}  ({h:.4g} hits, {m:.4g} misses per launch)")
+    tr = sm.get("traffic")
+    if tr:
+        f, w = tr["FETCH_SIZE"], tr["WRITE_SIZE"]
+        lines += ["", "HBM traffic per launch (counter KiB x scale; scale = copy bytes / copy counter):",
+                  f"  FETCH_SIZE {f['kib_raw']:.1f} KiB x {f['scale']:.4f} = {f['bytes']:.4g} B",
+                  f"  WRITE_SIZE {w['kib_raw']:.1f} KiB x {w['scale']:.4f} = {w['bytes']:.4g} B",
+                  f"  total {tr['bytes']:.4g} B" + (f" = {tr['bytes'] / algo_bytes:.2f} x the compulsory bytes"
+                                                     if algo_bytes else ""),
+                  f"  achieved HBM rate {tr['bytes'] / (sm['avg_us'] * 1e-6) / 1e9:.1f} GB/s"]
+    lines += ["", "raw counters (mean per dispatch):"]
+    lines += [f"  {k} = {v:.6g}" for k, v in sorted(c.items())]
+    return "\n".join(lines) + "\n", sm
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
