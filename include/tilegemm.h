@@ -143,7 +143,8 @@ int tg_enumerate(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, int ca
 int tg_space(int dtype, tg_cfg *out, int cap, int *n_total);
 /* Feasibility of one configuration: *reason = 0 if feasible, else the first failing rule:
  * 1 dtype, 2 alignment, 3 shape, 4 waves, 5 divisibility, 6 LDS, 7 accumulators,
- * 8 VGPR estimate, 9 occupancy, 10 split-K, 11 not in the space. */
+ * 8 VGPR estimate, 9 occupancy, 10 split-K, 11 not in the space, 12 more transfers in flight per
+ * wave than the memory counter tracks (63; bf16 tiled kind, ST x transfers per wave and stage). */
 int tg_check_cfg(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, int *reason);
 /* Cost-model time of a feasible configuration, in microseconds. */
 int tg_model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, double *us);

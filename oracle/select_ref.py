@@ -58,6 +58,7 @@ R_VGPR = 8
 R_OCC = 9
 R_SPLIT = 10
 R_SPACE = 11
+R_INFLIGHT = 12
 
 
 @dataclass(frozen=True)
@@ -160,13 +161,16 @@ def space(dtype: int, dev: Device = MI355X):
                 out.append(Cfg(KIND_TILED, bm, bn, 64, 1, 1, 1, 1))
         return out
     if dtype == F32:
-        tiles_mn, bks = (32, 64, 128), (8, 16, 32)
+        tiles_m, tiles_n, bks = (32, 64, 128), (32, 64, 128), (8, 16, 32)
     else:
-        tiles_mn, bks = (32, 64, 128, 256), (32, 64)
-    # fp32 kernel: 1 or 2 LDS buffers; bf16 kernel: 2 to 4 stages in flight
-    stages = (1, 2) if dtype == F32 else (2, 3, 4)
+        # 16-row tiles for the bf16 kernel: a 16-row decode wastes no MFMA rows
+        tiles_m, tiles_n, bks = (16, 32, 64, 128, 256), (32, 64, 128, 256), (32, 64)
+    # fp32 kernel: 1 or 2 LDS buffers; bf16 kernel: 2 to 8 stages in flight
+    # (page "Tiling the hierarchy", double buffering: a latency-bound tile wants
+    # a deeper pipeline; the LDS rule keeps the deep ones to small tiles)
+    stages = (1, 2) if dtype == F32 else (2, 3, 4, 6, 8)
     for bm, bn, bk, (wm, wn), st, s in itertools.product(
-            tiles_mn, tiles_mn, bks, WAVE_GRIDS, stages, SPLITS):
+            tiles_m, tiles_n, bks, WAVE_GRIDS, stages, SPLITS):
         out.append(Cfg(KIND_TILED, bm, bn, bk, wm, wn, st, s))
     if dtype != F32:
         for bm, w, u, s in itertools.product((16, 32, 48, 64), (1, 2, 4, 8), (1, 2, 4),
@@ -229,6 +233,13 @@ def blocks_per_cu(c: Cfg, dtype: int, dev: Device) -> int:
     return b
 
 
+def transfers_per_wave(c: Cfg, dtype: int) -> int:
+    """16-byte-per-lane (1 KiB) transfers a wave issues per stage in the bf16
+    tiled kernel: the A and B panels of one stage spread over the waves."""
+    inst = (c.bm + c.bn) * c.bk * in_bytes(dtype) // 1024
+    return cdiv(inst, c.wgm * c.wgn)
+
+
 def k_per_split(c: Cfg, K: int) -> int:
     unit = 32 if c.kind == KIND_SKINNY else c.bk
     return cdiv(cdiv(K, c.split_k), unit) * unit
@@ -247,6 +258,11 @@ def check_static(dtype: int, c: Cfg, dev: Device = MI355X) -> int:
             return R_DIV
     if lds_bytes(c, dtype) > dev.lds_block:
         return R_LDS
+    # the bf16 tiled kernel keeps ST stages of transfers in flight after its
+    # prologue; a wave's memory counter tracks at most 63 (MI355X only)
+    if (dev.mode == 0 and c.kind == KIND_TILED and dtype != F32
+            and c.stages * transfers_per_wave(c, dtype) > 63):
+        return R_INFLIGHT
     if acc_regs(c) > dev.acc_max:
         return R_ACC
     if vgpr_estimate(c, dtype, dev) > dev.vgpr_max:

@@ -155,7 +155,17 @@ def test_rejections_have_reasons():
     assert S.check(256, 256, 256, S.F32, S.Cfg(0, 64, 64, 8, 1, 1, 1, 1), d) == S.R_DIV
     assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 1, 4, 1, 1), d) == S.R_SPACE
     assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 2, 4, 2, 1), d) == S.R_DIV
-    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 256, 32, 1, 1, 2, 1), d) == S.R_ACC
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 128, 32, 1, 1, 2, 1), d) == S.R_ACC
+    # 64x256x64 panels are 40 one-KiB transfers per stage; one wave, 4 stages
+    # in flight = 160 outstanding > 63 (the 160 KiB of LDS would fit)
+    assert S.lds_bytes(S.Cfg(0, 64, 256, 64, 1, 1, 4, 1), S.BF16) == 4 * 40 * 1024
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 64, 256, 64, 1, 1, 4, 1), d) == S.R_INFLIGHT
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 64, 256, 64, 2, 4, 4, 1), d) == S.OK    # 5 per wave
+    assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 256, 32, 1, 1, 2, 1), d) == S.R_INFLIGHT
+    # a 16-row decode tile: 9 transfers per wave and stage; 6 stages fit, 8 do not
+    assert S.transfers_per_wave(S.Cfg(0, 16, 128, 64, 1, 2, 8, 1), S.BF16) == 9
+    assert S.check(16, 28672, 8192, S.BF16, S.Cfg(0, 16, 128, 64, 1, 2, 6, 1), d) == S.OK
+    assert S.check(16, 28672, 8192, S.BF16, S.Cfg(0, 16, 128, 64, 1, 2, 8, 1), d) == S.R_INFLIGHT
     assert S.check(256, 256, 15, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
     assert S.check(256, 256, 256, S.BF16, S.Cfg(2, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
     assert S.check(256, 256, 64, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 4), d) == S.R_SPLIT

@@ -91,7 +91,7 @@ struct TiledDma {
     static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "whole 16x16 tiles per wave");
     static_assert(BK % 32 == 0, "BK is a multiple of the MFMA K (32)");
     static_assert(BM % 16 == 0 && BN % 32 == 0, "tile sizes");
-    static_assert(ST >= 2 && ST <= 4, "pipeline depth");
+    static_assert(ST >= 2 && ST <= 8, "pipeline depth");
 };
 
 // A: 64-byte rows (4 chunks of 8 k); chunk c of row r sits at c ^ swz_a(r).

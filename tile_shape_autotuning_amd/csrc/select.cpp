@@ -122,22 +122,23 @@ static std::vector<tg_cfg> build_space(int dtype, int mode)
                 out.push_back(tg_cfg{TG_KIND_TILED, bm, bn, 64, 1, 1, 1, 1});
         return out;
     }
-    std::vector<int> mn, bks;
+    std::vector<int> ms, ns, bks, sts;
     if (dtype == TG_F32) {
-        mn = {32, 64, 128};
+        ms = {32, 64, 128};
+        ns = {32, 64, 128};
         bks = {8, 16, 32};
+        sts = {1, 2};               // register-staged kernel: 1 or 2 LDS buffers
     } else {
-        mn = {32, 64, 128, 256};
+        ms = {16, 32, 64, 128, 256};   // 16-row tiles: a 16-row decode wastes no MFMA rows
+        ns = {32, 64, 128, 256};
         bks = {32, 64};
+        sts = {2, 3, 4, 6, 8};      // direct-to-LDS kernel: stages in flight
     }
-    // fp32: register-staged kernel, 1 or 2 LDS buffers; bf16: direct-to-LDS
-    // kernel, 2 to 4 stages in flight
-    const int st_lo = dtype == TG_F32 ? 1 : 2, st_hi = dtype == TG_F32 ? 2 : 4;
-    for (int bm : mn)
-        for (int bn : mn)
+    for (int bm : ms)
+        for (int bn : ns)
             for (int bk : bks)
                 for (const auto& w : kWaveGrids)
-                    for (int st = st_lo; st <= st_hi; ++st)
+                    for (int st : sts)
                         for (int s : kSplits)
                             out.push_back(tg_cfg{TG_KIND_TILED, bm, bn, bk, w[0], w[1], st, s});
     if (dtype != TG_F32) {
@@ -230,6 +231,12 @@ int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d)
     return b;
 }
 
+int64_t transfers_per_wave(const tg_cfg& c, int dtype)
+{
+    const int64_t inst = ((int64_t)c.bm + c.bn) * c.bk * in_bytes(dtype) / 1024;
+    return cdiv(inst, (int64_t)c.wgm * c.wgn);
+}
+
 int64_t k_per_split(const tg_cfg& c, int64_t K)
 {
     const int64_t unit = c.kind == TG_KIND_SKINNY ? 32 : c.bk;
@@ -248,6 +255,10 @@ int check_static(int dtype, const tg_cfg& c, const tg_device_desc& d)
     }
     if (lds_bytes(c, dtype) > d.lds_block)
         return R_LDS;
+    // the direct-to-LDS kernel keeps ST stages of transfers in flight after its
+    // prologue; a wave's memory counter tracks at most 63 (MI355X only)
+    if (d.mode == 0 && c.kind == TG_KIND_TILED && dtype != TG_F32 && c.stages * transfers_per_wave(c, dtype) > 63)
+        return R_INFLIGHT;
     if (acc_regs(c) > d.acc_max)
         return R_ACC;
     if (vgpr_estimate(c, dtype, d) > d.vgpr_max)

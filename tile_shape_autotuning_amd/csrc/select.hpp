@@ -12,7 +12,7 @@ namespace tg {
 
 enum Reason {
     OK = 0, R_DTYPE = 1, R_ALIGN = 2, R_SHAPE = 3, R_WAVES = 4, R_DIV = 5, R_LDS = 6,
-    R_ACC = 7, R_VGPR = 8, R_OCC = 9, R_SPLIT = 10, R_SPACE = 11
+    R_ACC = 7, R_VGPR = 8, R_OCC = 9, R_SPLIT = 10, R_SPACE = 11, R_INFLIGHT = 12
 };
 
 tg_device_desc mi355x_desc();
@@ -34,6 +34,7 @@ int64_t acc_regs(const tg_cfg& c);
 int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d);
 int64_t waves_per_simd(const tg_cfg& c, int dtype, const tg_device_desc& d);
 int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d);
+int64_t transfers_per_wave(const tg_cfg& c, int dtype);
 int64_t k_per_split(const tg_cfg& c, int64_t K);
 
 // shape-independent rules only (waves, divisibility, LDS, registers, occupancy)
