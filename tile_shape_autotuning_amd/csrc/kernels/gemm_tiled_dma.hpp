@@ -33,7 +33,8 @@
 //     plain s_barrier: no fence, so loads of later stages stay in flight (the
 //     loads are issued as inline assembly so that the compiler does not add
 //     its own full drain before the LDS reads);
-//   * A sits in LDS as 32-wide k sub-panels [BK/32][BM][4 x 16 B], K-contiguous,
+//   * A sits in LDS as whole rows [BM][2 BK bytes], K-contiguous (a transfer
+//     carries 8 or 16 complete rows, so BK = 64 requests whole 128-byte lines),
 //     and is read with ds_read_b128 (8 k values of one row per lane = the A
 //     operand of v_mfma_f32_16x16x32_bf16);
 //   * B stays N-contiguous in 64-column blocks [BN/64][BK][128 B] whose rows
@@ -41,10 +42,11 @@
 //     lane L names 4 consecutive columns of row base + L/4 and lane i receives
 //     column i of those four rows) touches 16 consecutive LDS rows; two such
 //     reads give the 8 k values of one column that the B operand wants;
-//   * 16-byte chunks are XOR-swizzled by row bits that come from the lane
-//     index only, so every fragment read is one per-lane base register plus an
-//     immediate offset, every transfer one per-lane register plus a scalar
-//     offset, and the reads of a half-wave hit 64 distinct banks.
+//   * 16-byte chunks are XOR-swizzled by row bits 1..3, which for fragment
+//     reads come from the lane index only: every fragment read is a per-lane
+//     base register (one per 32-k slice) plus an immediate offset, and the
+//     reads of a half-wave hit 64 distinct banks; every transfer is a per-lane
+//     offset register fixed for the whole K loop.
 #pragma once
 
 #include "common.hpp"
@@ -63,6 +65,9 @@ struct TiledDma {
     static constexpr int FM = WM / 16, FN = WN / 16;
     static constexpr int KK = BK / 32;                  // 32-wide k slices per step
     static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int ROWB = BK * 2;                 // bytes of one A row in LDS (all KK slices)
+    static constexpr int RPA = 1024 / ROWB;             // A rows per transfer (16 or 8)
+    static constexpr int LPR = ROWB / 16;               // lanes per A row
     static constexpr int QW = BN < 64 ? BN : 64;        // columns per B block
     static constexpr int U = QW / 16;                   // 16-column units per B row
     static constexpr int RB = QW * 2;                   // bytes per B block row
@@ -94,10 +99,19 @@ struct TiledDma {
     static_assert(ST >= 2 && ST <= 8, "pipeline depth");
 };
 
-// A: 64-byte rows (4 chunks of 8 k); chunk c of row r sits at c ^ swz_a(r).
-// Uses row bits 1..3 only: 16 consecutive rows read one chunk each without
-// bank conflicts (within 128- and 256-byte windows).
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// A: rows of 2 BK bytes (all k of the stage, 4 KK chunks of 8 k); chunk c of
+// row r sits at c ^ swz_a<KK>(r).  Uses row bits 1..3 only: 16 consecutive
+// rows reading one logical chunk land in 16 distinct 16-byte slots of a
+// 256-byte window (no bank conflicts).  With BK = 64 a row is a whole
+// 128-byte line, so every A transfer requests whole lines (half-line requests
+// halve what the L2 delivers per request).
+template <int KK>
+__device__ __forceinline__ int swz_a(int r)
+{
+    static_assert(KK == 1 || KK == 2, "BK is 32 or 64");
+    r &= 15;   // a function of the row within its 16-row group (what a fragment read sees)
+    return KK == 1 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r >> 1) & 7);
+}
 
 // B: 32-byte unit u (16 columns) of block row p sits at u ^ swz_b(p).
 template <int RB>
@@ -210,12 +224,10 @@ gemm_tiled_dma_kernel(GemmParams p)
     const int cols_left = N - n0;      // valid B columns in this tile
 
     // ---- per-lane parts of the transfers (fixed for the whole K loop)
-    // A transfer: 16 rows x 64 bytes of one 32-wide k slice; lane -> row lane/4,
-    // physical chunk lane%4 holding logical chunk (lane%4) ^ swz_a(row).
-    const int a_row = lane >> 2;
-    const int a_chunk = (lane & 3) ^ swz_a(a_row);
-    const int a_k8 = a_chunk * 8;                     // first k of the lane's chunk
-    const int voA = a_row * K * 2 + a_chunk * 16;
+    // A transfer: RPA whole rows (2 BK bytes each); lane -> row lane / LPR,
+    // physical chunk lane % LPR holding logical chunk (lane % LPR) ^ swz_a(row).
+    const int a_row = lane / Cf::LPR;
+    const int a_p = lane % Cf::LPR;
     // B transfer: PPI block rows x RB bytes; lane -> block row p_l, 16-byte slot
     // s16 (unit s16/2 ^ swz_b, half s16%2).
     const int b_pl = lane / Cf::SLOTS_PER_ROW;
@@ -225,18 +237,22 @@ gemm_tiled_dma_kernel(GemmParams p)
     const int voB = b_krow_lane * N * 2 + b_col * 2;
 
     // Transfer q of this wave is number j = wave + q W of the stage: A
-    // transfers first (row block rb, k slice kk), then B (block blk, row group
-    // pblk).  Its lane offset within the tile, with the M / N edge folded in,
-    // does not change from stage to stage; only the K edge is checked per stage.
+    // transfers first (rows j RPA ..), then B (block blk, row group pblk).  Its
+    // lane offset within the tile, with the M / N edge folded in, does not
+    // change from stage to stage; only the K edge is checked per stage (ak8:
+    // first k of the lane's A chunk).
     auto is_a = [&](int q) { return Cf::STATIC_AB ? q < Cf::A_INST / W : wave + q * W < Cf::A_INST; };
     auto exists = [&](int q) { return Cf::STATIC_AB || wave + q * W < Cf::INST; };
-    int vo[Cf::LPW_MAX];
+    int vo[Cf::LPW_MAX], ak8[Cf::LPW_MAX];
 #pragma unroll
     for (int q = 0; q < Cf::LPW_MAX; ++q) {
         const int j = wave + q * W;
+        ak8[q] = 0;
         if (is_a(q)) {
-            const int kk = j / (BM / 16), rb = j % (BM / 16);
-            vo[q] = (rb * 16 + a_row < rows_left) ? voA + (rb * 16 * K + kk * 32) * 2 : kOOB;
+            const int row = j * Cf::RPA + a_row;
+            const int c = a_p ^ swz_a<KK>(row);
+            ak8[q] = c * 8;
+            vo[q] = (row < rows_left) ? (row * K + c * 8) * 2 : kOOB;
         } else {
             const int jb = j - Cf::A_INST;
             const int blk = jb / (BK / Cf::PPI), pblk = jb % (BK / Cf::PPI);
@@ -271,8 +287,7 @@ gemm_tiled_dma_kernel(GemmParams p)
             return;
         const int j = wave + q * W;
         if (is_a(q)) {
-            const int kk = j / (BM / 16);
-            dma16(d.rA, (a_k8 < d.klim - kk * 32) ? vo[q] : kOOB, d.dst + (unsigned)(j * 1024));
+            dma16(d.rA, (ak8[q] < d.klim) ? vo[q] : kOOB, d.dst + (unsigned)(j * 1024));
         } else {
             const int jb = j - Cf::A_INST;
             const int krow_unif = b_pos_to_row((jb % (BK / Cf::PPI)) * Cf::PPI);
@@ -282,8 +297,12 @@ gemm_tiled_dma_kernel(GemmParams p)
     };
 
     // ---- per-lane LDS read bases (bytes within a stage)
-    // A fragment (row-tile i, k slice kk): row wm*WM + 16 i + l16, chunk g.
-    const unsigned rdA = (unsigned)((wm * Cf::WM + l16) * 64 + ((g ^ swz_a(l16)) * 16));
+    // A fragment (row-tile i, k slice kk): row wm*WM + 16 i + l16, logical
+    // chunk 4 kk + g; the swizzle only sees row bits 1..3, i.e. l16.
+    unsigned rdA[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        rdA[kk] = (unsigned)((wm * Cf::WM + l16) * Cf::ROWB + (((kk * 4 + g) ^ swz_a<KK>(l16)) * 16));
     // B fragment (column tile j, k slice kk, half h): block row 16h + 4g + l16/4
     // of slice kk, columns 4 (l16 % 4) .. +3 of the 16-column unit.
     const int b_prow = 4 * g + (l16 >> 2);
@@ -315,7 +334,7 @@ gemm_tiled_dma_kernel(GemmParams p)
     // the B halves, then the other A row-tiles
     auto read_op = [&](unsigned st, int kk, int par, int o) {
         if (o == 0) {
-            a[par][0] = lds_read_b128(st + rdA + (unsigned)(kk * BM * 64));
+            a[par][0] = lds_read_b128(st + rdA[kk]);
         } else if (o <= 2 * FN) {
             const int j = (o - 1) >> 1, h = (o - 1) & 1;
             const u32x2_t w = lds_read_tr(st + rdB[j] + (unsigned)((kk * 32 + h * 16) * RB));
@@ -323,7 +342,7 @@ gemm_tiled_dma_kernel(GemmParams p)
             b[par][j][2 * h + 1] = w.y;
         } else {
             const int i = o - 2 * FN;
-            a[par][i] = lds_read_b128(st + rdA + (unsigned)(kk * BM * 64 + i * 1024));
+            a[par][i] = lds_read_b128(st + rdA[kk] + (unsigned)(i * 16 * Cf::ROWB));
         }
     };
     // The MFMAs of one slice with NOPS other instructions spread among them.
