@@ -353,6 +353,9 @@ gemm_tiled_dma_kernel(GemmParams p)
         for (int m = 0; m < Cf::NMF; ++m) {
             const int i = m / FN, j = m % FN;
             acc[i][j] = mfma_bf16(a[par][i], b[par][j], acc[i][j]);
+            // the MFMA goes first: a read hoisted above it would make the
+            // MFMA's own wait for older fragments wait for this read as well
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int o = (m * nops + Cf::NMF - 1) / Cf::NMF; o < ((m + 1) * nops + Cf::NMF - 1) / Cf::NMF; ++o)
                 op(o);
