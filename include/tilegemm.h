@@ -79,8 +79,16 @@ typedef struct {
     int32_t mode, n_cu, simds, lds_cu, lds_block, max_threads, waves_max, blocks_max,
             vgpr_max, acc_max, r0, reserved;
     double peak_bf16, peak_f32, bw, a_ref, c_fill, t0, unaligned_eff, lat_mem, cu_bw,
-           lds_bw_cu,   /* LDS bytes/s per CU (0 = no LDS term) */
-           lat_step;    /* memory latency a K step waits for, divided by the pipeline depth (s) */
+           lds_bw_cu,   /* LDS bytes/s per CU */
+           lat_step,    /* memory latency a K step waits for, divided by the pipeline depth (s) */
+           lat_l2,      /* the same when the problem's compulsory bytes fit in l2_bytes (s) */
+           l2_bytes,
+           w1_eff,      /* issue efficiency of a lone wave on a SIMD */
+           skinny_eff,  /* achievable fraction of the decode kernel's streaming model */
+           hbm_eff;     /* achievable fraction of the HBM peak */
+/* The MI355X mode prices a K step per CU (MFMA, LDS, L2-to-CU, latency /
+ * depth) over rounds of resident blocks; the replica mode is the page's
+ * formula and ignores lds_bw_cu .. hbm_eff. */
 } tg_device_desc;
 
 /* One row of an autotuning table. */

@@ -117,7 +117,8 @@ def test_builtin_descriptions_match_oracle_constants():
         d = N.builtin_device_desc(which)
         for f in ("mode", "n_cu", "simds", "lds_cu", "lds_block", "max_threads", "waves_max", "blocks_max",
                   "vgpr_max", "acc_max", "r0", "peak_bf16", "peak_f32", "bw", "a_ref", "c_fill", "t0",
-                  "unaligned_eff", "lat_mem", "cu_bw", "lds_bw_cu", "lat_step"):
+                  "unaligned_eff", "lat_mem", "cu_bw", "lds_bw_cu", "lat_step", "lat_l2", "l2_bytes", "w1_eff",
+                  "skinny_eff", "hbm_eff"):
             assert getattr(d, f) == getattr(ref, f), f
 
 

@@ -193,15 +193,51 @@ def test_model_invariants(M, N, K, dt):
     assert S.check(M, N, K, dt, S.default_cfg(N, K, dt), d) == S.OK
 
 
-def test_wave_efficiency_one_when_work_divides_slots():
-    # compute term alone (no LDS or pipeline-latency term)
-    d = dataclasses.replace(S.MI355X, lds_bw_cu=0.0, lat_step=0.0)
-    # 128x128 tiles, W = 4 (one block fills a CU): 2048x2048 -> 256 tiles = one full round
+def test_wave_quantisation_in_the_per_cu_model():
+    # compute alone: LDS, L2 and latency terms made negligible, no lone-wave penalty
+    d = dataclasses.replace(S.MI355X, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0)
+    # 128x128 tiles, W = 4, two blocks fit a CU (64 KiB of LDS each): 256 tiles are one
+    # partial round with one block per CU
     c = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
-    t256 = S.model_time(2048, 2048, 4096, S.BF16, c, d)
-    # one extra tile row adds a whole second round: time (compute part) doubles
-    t257 = S.model_time(2048 + 128, 2048, 4096, S.BF16, c, d)
-    assert t257 > 1.9 * (t256 - d.t0)
+    assert S.blocks_per_cu(c, S.BF16, d) == 2
+    t256 = S.model_time(2048, 2048, 4096, S.BF16, c, d) - d.t0
+    flops = 2.0 * 2048 * 2048 * 4096
+    assert t256 == pytest.approx(flops / d.peak_bf16)            # every SIMD busy: the roofline
+    # 272 tiles: the round holds two blocks on some CUs, which then take twice as long
+    t272 = S.model_time(2048 + 128, 2048, 4096, S.BF16, c, d) - d.t0
+    assert t272 == pytest.approx(2 * t256)
+    # 512 tiles: exactly one full round of two blocks per CU, no waste
+    t512 = S.model_time(4096, 2048, 4096, S.BF16, c, d) - d.t0
+    assert t512 == pytest.approx(2 * flops / d.peak_bf16)
+    # one-wave blocks occupy as many SIMDs as there are blocks on the CU
+    c1 = S.Cfg(S.KIND_TILED, 128, 128, 64, 1, 2, 2, 1)
+    b1 = S.blocks_per_cu(c1, S.BF16, d)
+    busy = min(4, 2 * b1)
+    t1 = S.model_time(4096, 4096, 4096, S.BF16, c1, d) - d.t0
+    assert t1 >= (2.0 * 4096 ** 3 / d.peak_bf16) * 4 / busy * (1 - 1e-12)
+    if busy < 4:
+        assert t1 > 1.5 * (2.0 * 4096 ** 3 / d.peak_bf16)
+
+
+def test_per_cu_model_terms():
+    d = S.MI355X
+    c = S.Cfg(S.KIND_TILED, 256, 256, 64, 2, 4, 2, 1)
+    # a half-line A row (BK = 32 bf16) costs a whole line: more L2 time per byte than BK = 64
+    assert S._line(32 * 2) == 128 and S._line(64 * 2) == 128 and S._line(16 * 4) == 128
+    # a deeper pipeline never makes the latency-bound step slower
+    base = S.Cfg(S.KIND_TILED, 64, 64, 32, 2, 2, 2, 1)
+    deeper = S.Cfg(S.KIND_TILED, 64, 64, 32, 2, 2, 4, 1)
+    assert S.model_time(1000, 1000, 8192, S.BF16, deeper, d) <= S.model_time(1000, 1000, 8192, S.BF16, base, d)
+    # split-K costs the reducer's reads and a round trip through memory
+    s1 = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
+    s2 = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 2)
+    t_no = S.model_time(8192, 8192, 8192, S.BF16, s1, d)
+    t_sk = S.model_time(8192, 8192, 8192, S.BF16, s2, d)
+    assert t_sk > t_no          # 4096 tiles already fill the chip: splitting only adds work
+    # the HBM floor binds the 16-row decode
+    dec = S.model_time(16, 28672, 8192, S.BF16, S.Cfg(S.KIND_TILED, 32, 128, 64, 1, 2, 4, 1), d)
+    floor = (2 * (16 * 8192 + 8192 * 28672) + 2 * 16 * 28672) / (d.bw * d.hbm_eff)
+    assert dec >= floor + d.t0
 
 
 def test_skinny_only_for_small_m_and_bf16():

@@ -29,10 +29,12 @@ import sys
 from . import _native as N
 
 GRID = {
-    "lat_step": [0.5e-6, 1.0e-6, 1.5e-6, 2.0e-6, 3.0e-6],
-    "lds_bw_cu": [153.6e9, 230.4e9, 307.2e9, 460.8e9, 614.4e9],
-    "a_ref": [4096.0, 16384.0, 65536.0],
-    "c_fill": [0.0, 2.0, 8.0],
+    "lds_bw_cu": [153.6e9, 230.0e9, 307.2e9],
+    "cu_bw": [45.0e9, 60.0e9, 90.0e9],
+    "lat_step": [1.0e-6, 1.5e-6, 2.0e-6],
+    "lat_l2": [0.2e-6, 0.3e-6, 0.5e-6],
+    "w1_eff": [0.6, 0.75, 0.9],
+    "t0": [3.0e-6, 4.0e-6],
 }
 
 
@@ -67,12 +69,13 @@ def _rank_stats(tab, desc, topk):
     rm = {i: r for r, i in enumerate(sorted(range(len(meas)), key=lambda i: meas[i]))}
     n = len(meas)
     rho = 1 - 6 * sum((rp[i] - rm[i]) ** 2 for i in range(n)) / (n * (n * n - 1)) if n > 2 else float("nan")
-    return err, best in top, choice_ratio, rho
+    return err, best in top, choice_ratio, rho, order[0] == best
 
 
 def evaluate(tabs, desc, topk):
     stats = [_rank_stats(t, desc, topk) for t in tabs]
     return {"msle": sum(s[0] for s in stats) / len(stats),
+            "model_hits": sum(s[4] for s in stats),
             "best_in_topk": sum(s[1] for s in stats),
             "choice_over_best": [round(s[2], 3) for s in stats],
             "rank_corr": [round(s[3], 3) for s in stats]}
@@ -86,7 +89,7 @@ def fit(tabs, topk=16, grid=GRID):
         for k, v in zip(grid, vals):
             setattr(d, k, v)
         e = evaluate(tabs, d, topk)
-        key = (e["msle"], -e["best_in_topk"])
+        key = (-e["model_hits"], -e["best_in_topk"], e["msle"])
         if best is None or key < best[0]:
             best = (key, dict(zip(grid, vals)), e)
     N.set_device_override(None)

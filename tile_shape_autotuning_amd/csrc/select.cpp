@@ -46,12 +46,17 @@ tg_device_desc mi355x_desc()
     d.bw = 8.0e12;
     d.a_ref = 16384.0;
     d.c_fill = 2.0;
-    d.t0 = 3.0e-6;
+    d.t0 = 4.0e-6;
     d.unaligned_eff = 0.25;
     d.lat_mem = 2.0e-6;
-    d.cu_bw = 153.6e9;
-    d.lds_bw_cu = 307.2e9;
-    d.lat_step = 2.0e-6;
+    d.cu_bw = 45.0e9;
+    d.lds_bw_cu = 153.6e9;
+    d.lat_step = 1.5e-6;
+    d.lat_l2 = 0.2e-6;
+    d.l2_bytes = 32.0e6;
+    d.w1_eff = 0.75;
+    d.skinny_eff = 0.75;
+    d.hbm_eff = 0.9125;
     return d;
 }
 
@@ -80,6 +85,9 @@ tg_device_desc h100_replica_desc()
     d.cu_bw = 0.0;
     d.lds_bw_cu = 0.0;
     d.lat_step = 0.0;
+    d.w1_eff = 1.0;
+    d.skinny_eff = 1.0;
+    d.hbm_eff = 1.0;
     return d;
 }
 
@@ -315,6 +323,84 @@ void grid(int64_t M, int64_t N, const tg_cfg& c, int64_t* tiles, int64_t* blocks
 }
 
 // ------------------------------------------------------------------ cost model
+static int64_t line_bytes(int64_t x) { return cdiv(x, (int64_t)128) * 128; }
+
+// The roofline model of page "Compilers and Kernel Languages" ("Workshop"):
+// the larger of the compute time at the wave, SIMD, tile and fill
+// efficiencies and the memory time of the traffic, plus split-K workspace.
+static double model_page(int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d, int64_t eb, double peak,
+                         double flops, double compulsory, int64_t tiles, int64_t units, int64_t w, int64_t bcu)
+{
+    const int64_t par_need = std::max<int64_t>(1, d.simds / w);
+    const int64_t par = std::min(bcu, par_need);
+    const int64_t slots = (int64_t)d.n_cu * par;
+    const int64_t rounds = cdiv(units, slots);
+    const double wave_eff = (double)units / (double)(rounds * slots);
+    const double simd_eff = std::min(1.0, (double)(par * w) / (double)d.simds);
+    const double tile_eff = std::min(1.0, 0.5 + 0.5 * (double)((int64_t)c.bm * c.bn) / d.a_ref);
+    const int64_t ktiles = cdiv(k_per_split(c, K), c.bk);
+    const double fill_eff = ktiles > 0 ? (double)ktiles / ((double)ktiles + d.c_fill) : 1.0;
+    double eff = wave_eff * simd_eff * tile_eff * fill_eff;
+    if (c.kind == TG_KIND_UNALIGNED)
+        eff = eff * d.unaligned_eff;
+    const double t_c = flops / (peak * eff);
+    const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
+    const double g = std::sqrt((double)std::min<int64_t>(units, (int64_t)d.n_cu * bcu));
+    const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
+    const double t_m = (std::max(compulsory, raw / g) + ws) / d.bw;
+    return std::max(t_c, t_m) + d.t0;
+}
+
+// MI355X: the roofline of "Analytical models and where they break" per CU and
+// per K step.  One K step of the blocks resident on a CU takes the longest of
+// their MFMA work on the SIMDs their waves occupy, their LDS traffic, their
+// L2-to-CU traffic (rows narrower than a cache line cost a line) and the
+// memory latency over the pipeline depth; a lone wave on a SIMD issues all of
+// it in order (w1_eff).  Blocks run in rounds of n_cu x resident, the partial
+// last round spread out, each round starting with one latency; the HBM time of
+// the traffic bounds it from below; split-K adds the reducer reading every
+// partial and a store -> count -> load chain through memory.
+static double model_cu(int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d, int64_t eb, double peak,
+                       double compulsory, int64_t tiles, int64_t units, int64_t w, int64_t bcu)
+{
+    const int64_t ktiles = cdiv(k_per_split(c, K), c.bk);
+    const int64_t wm = c.bm / c.wgm, wn = c.bn / c.wgn;
+    const double simd_peak = peak / (double)((int64_t)d.n_cu * d.simds);
+    const double f_step = 2.0 * (double)c.bm * (double)c.bn * (double)c.bk;
+    const double lds_step = (double)(c.bk * eb * (w * (wm + wn) + c.bm + c.bn));
+    const int64_t qw = (c.kind == TG_KIND_TILED && dtype != TG_F32) ? std::min<int64_t>(c.bn, 64) : c.bn;
+    double l2_step = (double)(c.bm * line_bytes(c.bk * eb) + c.bk * (c.bn / qw) * line_bytes(qw * eb));
+    if (c.kind == TG_KIND_UNALIGNED)
+        l2_step = l2_step / d.unaligned_eff;
+    const int64_t depth = (c.kind == TG_KIND_TILED && dtype != TG_F32) ? std::max<int64_t>(1, c.stages - 1) : 1;
+    const double lat = compulsory > d.l2_bytes ? d.lat_step : d.lat_l2;
+
+    auto step = [&](int64_t res) {
+        const int64_t busy = std::min<int64_t>(d.simds, res * w);
+        double t = (double)res * f_step / (simd_peak * (double)busy);
+        t = std::max(t, (double)res * lds_step / d.lds_bw_cu);
+        t = std::max(t, (double)res * l2_step / d.cu_bw);
+        t = std::max(t, lat / (double)depth);
+        return res * w <= d.simds ? t / d.w1_eff : t;
+    };
+    const int64_t slots = (int64_t)d.n_cu * bcu;
+    const int64_t full = units / slots;
+    const int64_t rem = units - full * slots;
+    double t_cu = (double)(full * ktiles) * step(bcu);
+    if (rem > 0)
+        t_cu = t_cu + (double)ktiles * step(cdiv(rem, (int64_t)d.n_cu));
+    const int64_t rounds = full + (rem > 0 ? 1 : 0);
+    t_cu = t_cu + (double)rounds * lat;
+    const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
+    const double g = std::sqrt((double)std::min<int64_t>(units, slots));
+    const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
+    const double t_hbm = (std::max(compulsory, raw / g) + ws) / (d.bw * d.hbm_eff);
+    double t_red = 0.0;
+    if (c.split_k > 1)
+        t_red = (double)(cdiv(tiles, (int64_t)d.n_cu) * c.split_k * c.bm * c.bn) * 4.0 / d.cu_bw + 2.0 * d.lat_step;
+    return std::max(t_cu, t_hbm) + t_red + d.t0;
+}
+
 double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d)
 {
     const int64_t eb = in_bytes(dtype);
@@ -337,37 +423,14 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
         const int64_t active = std::min<int64_t>(units, d.n_cu);
         const double bw = std::min(d.bw * bw_eff, (double)active * d.cu_bw);
         const double t_m = (compulsory + ws) / bw;
-        return std::max(t_c, t_m) + d.t0;
+        double t = std::max(t_c, t_m);
+        if (d.mode == 0)
+            t = t / d.skinny_eff;
+        return t + d.t0;
     }
-
-    const int64_t par_need = std::max<int64_t>(1, d.simds / w);
-    const int64_t par = std::min(bcu, par_need);
-    const int64_t slots = (int64_t)d.n_cu * par;
-    const int64_t rounds = cdiv(units, slots);
-    const double wave_eff = (double)units / (double)(rounds * slots);
-    const double simd_eff = std::min(1.0, (double)(par * w) / (double)d.simds);
-    const double tile_eff = std::min(1.0, 0.5 + 0.5 * (double)((int64_t)c.bm * c.bn) / d.a_ref);
-    const int64_t ktiles = cdiv(k_per_split(c, K), c.bk);
-    const double fill_eff = ktiles > 0 ? (double)ktiles / ((double)ktiles + d.c_fill) : 1.0;
-    double eff = wave_eff * simd_eff * tile_eff * fill_eff;
-    if (c.kind == TG_KIND_UNALIGNED)
-        eff = eff * d.unaligned_eff;
-    const double t_c = flops / (peak * eff);
-    const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
-    const double g = std::sqrt((double)std::min<int64_t>(units, (int64_t)d.n_cu * bcu));
-    const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
-    const double t_m = (std::max(compulsory, raw / g) + ws) / d.bw;
-    // LDS traffic: fragment reads of every wave plus the panel writes, per CU in turn
-    double t_lds = 0.0;
-    if (d.lds_bw_cu > 0.0) {
-        const int64_t frag_rows = w * (c.bm / c.wgm + c.bn / c.wgn) + c.bm + c.bn;
-        const double per_unit = (double)k_per_split(c, K) * (double)eb * (double)frag_rows;
-        t_lds = (double)cdiv(units, d.n_cu) * per_unit / d.lds_bw_cu;
-    }
-    // pipeline fill: a K step waits for its transfers; depth - 1 later steps are in flight
-    const int64_t depth = (c.kind == TG_KIND_TILED && dtype != TG_F32) ? std::max<int64_t>(1, c.stages - 1) : 1;
-    const double t_lat = (double)(cdiv(units, (int64_t)d.n_cu * bcu) * (ktiles + 1)) * d.lat_step / (double)depth;
-    return std::max(std::max(std::max(t_c, t_m), t_lds), t_lat) + d.t0;
+    if (d.mode == 1)
+        return model_page(K, dtype, c, d, eb, peak, flops, compulsory, tiles, units, w, bcu);
+    return model_cu(K, dtype, c, d, eb, peak, compulsory, tiles, units, w, bcu);
 }
 
 bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t)
