@@ -283,7 +283,11 @@ def main():
     shapes = {}
     main_res = None
     for i in indices:
-        rotate = 2 if wl.WORKLOADS[i].M <= 64 else 1     # decode: stream distinct weights every call
+        # decode: stream distinct weights every call (copies together exceed the 256 MiB
+        # last-level cache twice over, as the library's tuner times it)
+        wi = wl.WORKLOADS[i]
+        b_bytes = wi.K * wi.N * (4 if wi.dtype == wl.F32 else 2)
+        rotate = min(8, max(2, -(-(512 << 20) // b_bytes))) if wi.M <= 64 else 1
         log(f"workload {i}: preparing")
         p = Prepared(i, torch, rotate=rotate)
         if i == main_idx and a.cfg:

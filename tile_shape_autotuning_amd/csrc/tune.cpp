@@ -98,17 +98,33 @@ namespace {
 // Device scratch operands filled with uniform values in [-1, 1).
 struct Scratch {
     void* A = nullptr;
-    void* B = nullptr;
+    std::vector<void*> B;   // one or more copies of B (see b_copies)
     void* C = nullptr;
     float* bias = nullptr;
     ~Scratch()
     {
         if (A) (void)hipFree(A);
-        if (B) (void)hipFree(B);
+        for (void* b : B)
+            if (b) (void)hipFree(b);
         if (C) (void)hipFree(C);
         if (bias) (void)hipFree(bias);
     }
 };
+
+// Page "Tile Selection: Cost Models Against Measurement", "Measurement, and
+// what it must control": the timed runs must see the cache state the real
+// calls see.  A problem with at most 64 rows is a decode step streaming
+// weights that no cache holds between calls (each layer has its own), so its
+// candidates are timed rotating through copies of B that together exceed the
+// 256 MiB last-level cache twice over; larger problems reuse their operands
+// call after call and are timed warm.
+static int b_copies(int64_t M, int64_t b_bytes)
+{
+    if (M > 64 || b_bytes <= 0)
+        return 1;
+    const int64_t need = (int64_t)512 << 20;
+    return (int)std::min<int64_t>(8, std::max<int64_t>(2, (need + b_bytes - 1) / b_bytes));
+}
 
 struct Timed {
     tg_cfg cfg;
@@ -207,14 +223,20 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
         hipStream_t st = current_stream();
         hipError_t e = hipSuccess;
         const size_t na = (size_t)std::max<int64_t>(M * K, 1), nb = (size_t)std::max<int64_t>(K * N, 1);
-        if ((e = hipMalloc(&s.A, na * eb)) != hipSuccess || (e = hipMalloc(&s.B, nb * eb)) != hipSuccess ||
-            (e = hipMalloc(&s.C, (size_t)M * N * ec)) != hipSuccess ||
+        const int nbc = b_copies(M, (int64_t)(nb * eb));
+        s.B.assign(nbc, nullptr);
+        if ((e = hipMalloc(&s.A, na * eb)) != hipSuccess || (e = hipMalloc(&s.C, (size_t)M * N * ec)) != hipSuccess ||
             (e = hipMalloc(&s.bias, (size_t)N * sizeof(float))) != hipSuccess)
             return set_error(TG_E_NOMEM, std::string("tuning scratch: ") + hipGetErrorString(e));
+        for (int i = 0; i < nbc; ++i)
+            if ((e = hipMalloc(&s.B[i], nb * eb)) != hipSuccess)
+                return set_error(TG_E_NOMEM, std::string("tuning scratch: ") + hipGetErrorString(e));
         if ((e = fill_uniform(s.A, (int64_t)na, dtype != TG_F32, 0x1234u, st)) != hipSuccess ||
-            (e = fill_uniform(s.B, (int64_t)nb, dtype != TG_F32, 0x5678u, st)) != hipSuccess ||
             (e = fill_uniform(s.bias, N, 0, 0x9abcu, st)) != hipSuccess)
             return set_hip_error(e, "tuning scratch fill");
+        for (int i = 0; i < nbc; ++i)
+            if ((e = fill_uniform(s.B[i], (int64_t)nb, dtype != TG_F32, 0x5678u + (uint32_t)i, st)) != hipSuccess)
+                return set_hip_error(e, "tuning scratch fill");
         // workspace for the largest split-K candidate, allocated before timing
         size_t wsb = 0, nct = 0;
         for (const Timed& t : cands) {
@@ -234,9 +256,11 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
         hipEvent_t e0, e1;
         if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess)
             return set_hip_error(e, "hipEventCreate");
+        size_t launches = 0;
         auto run = [&](Timed& t, int reps) -> bool {
             for (int r = 0; r < reps; ++r) {
-                if (launch_cfg(M, N, K, s.A, s.B, s.bias, s.C, dtype, TG_ACT_NONE, t.cfg, st, false) != TG_OK)
+                const void* b = s.B[launches++ % s.B.size()];
+                if (launch_cfg(M, N, K, s.A, b, s.bias, s.C, dtype, TG_ACT_NONE, t.cfg, st, false) != TG_OK)
                     return false;
             }
             return true;
