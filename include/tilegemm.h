@@ -140,7 +140,11 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
  * several rounds, and the smallest median wins.  A cache hit returns at once
  * without measuring.  Blocking.  Mode and top_k come from
  * TILEGEMM_TUNE_MODE = hybrid (default) | model | exhaustive and
- * TILEGEMM_TUNE_TOPK (default 16, at most 30).
+ * TILEGEMM_TUNE_TOPK (default 16, at most 30).  Each sample is about
+ * TILEGEMM_TUNE_SAMPLE_US (default 2000) of back-to-back launches; problems
+ * with at most 64 rows rotate through copies of B that exceed the last-level
+ * cache (weights streamed from HBM, as in a decode step).  Scratch memory:
+ * A, C, bias and one to eight copies of B, freed before returning.
  */
 int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out);
 

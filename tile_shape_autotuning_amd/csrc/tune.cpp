@@ -269,7 +269,11 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
         if (progress)
             std::fprintf(stderr, "[tilegemm] tuning %lldx%lldx%lld dt%d: %zu candidates, %d rounds\n",
                          (long long)M, (long long)N, (long long)K, dtype, cands.size(), rounds);
-        // warm-up and a single-launch estimate to size each sample (~200 us)
+        // warm-up and a single-launch estimate to size each sample: long enough
+        // (2 ms by default) for the clock to settle where back-to-back calls run
+        // it -- a configuration that burns more matrix-core power than it needs
+        // looks fast in short bursts and slows down when sustained
+        const double sample_us = (double)std::max(50, env_int("TILEGEMM_TUNE_SAMPLE_US", 2000));
         size_t done = 0;
         for (Timed& t : cands) {
             if (progress && ++done % 100 == 0)
@@ -285,7 +289,7 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
             float ms = 0.f;
             hipEventElapsedTime(&ms, e0, e1);
             const double us = std::max(1.0, (double)ms * 1e3);
-            t.reps = (int)std::max(1.0, std::min(200.0, std::ceil(200.0 / us)));
+            t.reps = (int)std::max(1.0, std::min(2000.0, std::ceil(sample_us / us)));
         }
         int64_t timed = 0;
         for (int r = 0; r < rounds; ++r) {
