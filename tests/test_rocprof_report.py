@@ -19,8 +19,8 @@ COPY = "void at::native::elementwise_kernel<copy>(int)"
 def _trace_db(d, rows):
     os.makedirs(d, exist_ok=True)
     c = sqlite3.connect(os.path.join(d, "run_results.db"))
-    c.execute("create table kernels (name text, duration integer)")
-    c.executemany("insert into kernels values (?, ?)", rows)
+    c.execute("create table kernels (name text, duration integer, grid_x integer)")
+    c.executemany("insert into kernels values (?, ?, ?)", [r if len(r) == 3 else (r[0], r[1], 1024) for r in rows])
     c.commit()
     c.close()
 
@@ -42,6 +42,15 @@ def test_kernel_times_average_per_name(tmp_path):
     assert t[GEMM] == (2, 35000.0)
     assert t[COPY] == (1, 1000.0)
     assert "gemm_tiled_dma_kernel" in R.kernel_table(d)
+
+
+def test_kernel_times_split_one_template_by_grid(tmp_path):
+    d = str(tmp_path / "trace")
+    # the same kernel serving a big and a small problem in one run
+    _trace_db(d, [(GEMM, 900000, 524288), (GEMM, 910000, 524288), (GEMM, 40000, 104448)])
+    assert R.kernel_times(d, grid=524288)[GEMM] == (2, 905000.0)
+    assert R.kernel_times(d, grid=104448)[GEMM] == (1, 40000.0)
+    assert R.kernel_times(d)[GEMM][0] == 3
 
 
 def test_counters_sum_rows_of_one_dispatch_then_average(tmp_path):

@@ -49,12 +49,16 @@ def _dbs(d):
     return out
 
 
-def kernel_times(trace_dir):
-    """{kernel name: (calls, average ns)} from a kernel trace."""
+def kernel_times(trace_dir, grid=None):
+    """{kernel name: (calls, average ns)} from a kernel trace; with grid, only
+    the dispatches of that many work-items (one template can serve several
+    problems in one run)."""
     acc = collections.defaultdict(lambda: [0, 0.0])
     for db in _dbs(trace_dir):
         c = sqlite3.connect(db)
-        for name, dur in c.execute("select name, duration from kernels"):
+        for name, dur, gx in c.execute("select name, duration, grid_x from kernels"):
+            if grid is not None and int(gx) != int(grid):
+                continue
             acc[name][0] += 1
             acc[name][1] += float(dur)
     return {k: (n, s / n) for k, (n, s) in acc.items()}
@@ -79,8 +83,8 @@ def _pick(d, sub):
 
 
 def summary(trace_dir, pmc_dirs=(), fetch_dir=None, write_dir=None, copy_bytes=0, kernel="gemm",
-            flops=None, nbytes=None):
-    times = kernel_times(trace_dir)
+            flops=None, nbytes=None, grid=None):
+    times = kernel_times(trace_dir, grid)
     kname = _pick(times, kernel)
     calls, avg_ns = times[kname]
     out = {"kernel": kname, "calls": calls, "avg_us": avg_ns / 1e3}
@@ -129,12 +133,18 @@ def hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel="gemm"):
 
 
 def kernel_table(trace_dir, top=12):
-    """Text table of the kernels in a trace, by total time."""
-    times = kernel_times(trace_dir)
-    rows = sorted(times.items(), key=lambda kv: -kv[1][0] * kv[1][1])[:top]
-    out = [f"{'calls':>7} {'avg us':>10} {'total ms':>9}  kernel"]
-    for name, (n, avg) in rows:
-        out.append(f"{n:>7} {avg / 1e3:>10.3f} {n * avg / 1e6:>9.3f}  {name}")
+    """Text table of the kernels in a trace (one row per kernel and grid
+    size), by total time."""
+    acc = collections.defaultdict(lambda: [0, 0.0])
+    for db in _dbs(trace_dir):
+        c = sqlite3.connect(db)
+        for name, dur, gx in c.execute("select name, duration, grid_x from kernels"):
+            acc[(name, int(gx))][0] += 1
+            acc[(name, int(gx))][1] += float(dur)
+    rows = sorted(acc.items(), key=lambda kv: -kv[1][1])[:top]
+    out = [f"{'calls':>7} {'avg us':>10} {'total ms':>9} {'work-items':>10}  kernel"]
+    for (name, gx), (n, tot) in rows:
+        out.append(f"{n:>7} {tot / n / 1e3:>10.3f} {tot / 1e6:>9.3f} {gx:>10}  {name}")
     return "\n".join(out)
 
 
@@ -149,16 +159,17 @@ def kernel_name(cfg, in_bf16=True):
 
 
 def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, flops,
-                  algo_bytes, commands_used):
+                  algo_bytes, commands_used, grid=None):
     """Summary of one kernel on one workload: duration, MFMA utilisation, LDS
     bank conflicts, L2 hit rate and HBM bytes (FETCH_SIZE / WRITE_SIZE scaled
     by the same counters for a plain copy of copy_bytes)."""
-    sm = summary(trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, kname, flops, algo_bytes)
+    sm = summary(trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, kname, flops, algo_bytes, grid)
     c = sm.get("counters", {})
     lines = [f"# {kname} on {workload}", "", "cfg (kind,bm,bn,bk,wgm,wgn,stages,split_k): " +
              ",".join(str(x) for x in cfg), "", "commands (run from the repository root on MI355X):"]
     lines += [f"  {cmd}" for cmd in commands_used]
-    lines += ["", f"launches traced:            {sm['calls']}", f"average duration:           {sm['avg_us']:.3f} us"]
+    lines += ["", f"launches traced:            {sm['calls']}" + (f" (dispatches of {grid} work-items)" if grid else ""),
+              f"average duration:           {sm['avg_us']:.3f} us"]
     if flops:
         lines.append(f"algorithmic TFLOP/s:        {sm['TFLOP/s']:.1f}   (2MNK = {flops:.4g} flop per launch)")
     if algo_bytes:
