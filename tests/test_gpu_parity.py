@@ -142,6 +142,29 @@ def test_activations_random_inputs(act):
         assert_close(out_f64(C), ref, dtype, f"act {act} dtype {dtype}")
 
 
+def test_gelu_epilogue_accuracy_over_its_range():
+    # A = 0, so C = GELU(bias): the epilogue's GELU alone, at pre-activation
+    # values across [-12, 12], against the oracle's fp64 erf, for the bf16
+    # direct-to-LDS kernel, the fp32 kernel and the element-load kind
+    M, N = 48, 4096
+    bias = np.linspace(-12.0, 12.0, N).astype(np.float32)
+    # K = 60 is not a multiple of 8: the element-load kind; M = 48 also admits the decode kernel
+    cases = [(wl.BF16_F32OUT, 64, (0, 32, 128, 64, 1, 2, 2, 1)), (wl.F32, 64, (0, 32, 32, 32, 2, 2, 1, 1)),
+             (wl.BF16_F32OUT, 60, None), (wl.BF16_F32OUT, 64, (1, 48, 128, 32, 2, 1, 2, 1))]
+    for dtype, K, cfg in cases:
+        if cfg is not None and not tg.has_kernel(dtype, cfg):
+            continue
+        A = np.zeros((M, K), np.float32 if dtype == wl.F32 else np.uint16)
+        B = np.zeros((K, N), A.dtype)
+        ref = gemm_ref.gemm(A, B, bias, "gelu")
+        mark(f"gelu range dt{dtype} {cfg}")
+        C = _run(to_dev(A), to_dev(B), to_dev(bias), "gelu", dtype, cfg)
+        torch.cuda.synchronize()
+        err = np.abs(out_f64(C) - ref)
+        bound = 2e-6 * np.maximum(1.0, np.abs(bias.astype(np.float64)))[None, :]
+        assert np.all(err <= bound), f"dt{dtype} {cfg}: worst {float(np.max(err / bound)):.3g} x the bound"
+
+
 def test_empty_and_k_zero():
     for dtype in (wl.F32, wl.BF16):
         mark(f"K=0 dt{dtype}")
