@@ -380,11 +380,16 @@ gemm_tiled_dma_kernel(GemmParams p)
                 const int nbuf = buf + 1 == ST ? 0 : buf + 1;
                 const unsigned nst = lds_base + (unsigned)(nbuf * Cf::STAGE_BYTES);
                 const Tile d = tile_desc(t + ST, buf);
-                slice(par, IntC<Cf::NRD + Cf::LPW_MAX>{}, [&](int o) {
-                    if (o < Cf::NRD)
-                        read_op(nst, 0, par ^ 1, o);
+                // transfers spaced evenly among the reads: issued in a burst
+                // they back up in the address unit (one 1 KiB transfer takes
+                // 16 cycles there) and stall the issuing waves' MFMAs
+                constexpr int NOPS = Cf::NRD + Cf::LPW_MAX;
+                slice(par, IntC<NOPS>{}, [&](int o) {
+                    const int before = o * Cf::LPW_MAX / NOPS;          // transfers among ops 0 .. o-1
+                    if ((o + 1) * Cf::LPW_MAX / NOPS > before)
+                        dma_op(before, d);
                     else
-                        dma_op(o - Cf::NRD, d);
+                        read_op(nst, 0, par ^ 1, o - before);
                 });
             }
         }
