@@ -354,7 +354,10 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
     if c.kind == KIND_SKINNY:
         flops_pad = 2.0 * c.bm * N * K
         t_c = flops_pad / peak
-        ws = 8.0 * c.bm * 128 * tiles * c.split_k if c.split_k > 1 else 0.0
+        if dev.mode == 0:
+            ws = _splitk_slabs(M, N, c)
+        else:
+            ws = 8.0 * c.bm * 128 * tiles * c.split_k if c.split_k > 1 else 0.0
         resident = min(units * w, dev.n_cu * bcu * w)
         inflight = resident * 64.0 * c.stages * 8 * 16
         bw_eff = min(1.0, inflight / (dev.bw * dev.lat_mem))
@@ -363,11 +366,27 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
         t_m = (compulsory + ws) / bw
         t = max(t_c, t_m)
         if dev.mode == 0:
-            t = t / dev.skinny_eff
+            return t / dev.skinny_eff + _splitk_pass(M, N, ec, c, dev) + dev.t0
         return t + dev.t0
     if dev.mode == 1:
         return _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, units, w, bcu)
-    return _model_cu(K, dtype, c, dev, eb, peak, compulsory, tiles, units, w, bcu)
+    return _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w, bcu)
+
+
+def _splitk_slabs(M: int, N: int, c: Cfg) -> float:
+    """Bytes of the fp32 partial-sum slabs split-K leaves in memory: one
+    M x N slab per split (my reading of split-K, page "Compilers and Kernel
+    Languages", "A different tile for a different shape": the partial sums
+    of the K ranges have to meet before the non-linear epilogue)."""
+    return 4.0 * c.split_k * M * N if c.split_k > 1 else 0.0
+
+
+def _splitk_pass(M: int, N: int, ec: int, c: Cfg, dev: Device) -> float:
+    """The second split-K pass: one more launch that reads every slab once
+    and writes C, at the HBM rate."""
+    if c.split_k <= 1:
+        return 0.0
+    return (_splitk_slabs(M, N, c) + float(ec) * M * N) / (dev.bw * dev.hbm_eff) + dev.t0
 
 
 def _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, units, w, bcu) -> float:
@@ -396,7 +415,7 @@ def _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, unit
     return max(t_c, t_m) + dev.t0
 
 
-def _model_cu(K, dtype, c, dev, eb, peak, compulsory, tiles, units, w, bcu) -> float:
+def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w, bcu) -> float:
     """MI355X: the roofline of "Analytical models and where they break" taken
     per CU and per K step.  The blocks resident on a CU advance together; one
     K step of all of them takes the longest of
@@ -410,9 +429,8 @@ def _model_cu(K, dtype, c, dev, eb, peak, compulsory, tiles, units, w, bcu) -> f
     and a lone wave on a SIMD issues everything in order (w1_eff).  Blocks run
     in rounds of n_cu x resident (wave quantisation; the partial last round
     spreads its blocks); each round starts with one latency.  The chip-wide
-    HBM time of the traffic bounds it from below; split-K adds the reducer
-    reading every partial of its tile and a store -> count -> load chain that
-    goes to memory."""
+    HBM time of the traffic bounds it from below (with split-K that traffic
+    includes writing the partial-sum slabs); split-K adds the second pass."""
     ktiles = cdiv(k_per_split(c, K), c.bk)
     wm, wn = c.bm // c.wgm, c.bn // c.wgn
     simd_peak = peak / (dev.n_cu * dev.simds)
@@ -441,12 +459,8 @@ def _model_cu(K, dtype, c, dev, eb, peak, compulsory, tiles, units, w, bcu) -> f
     t_cu = t_cu + rounds * lat
     raw = float(tiles) * eb * K * (c.bm + c.bn)
     g = math.sqrt(min(units, slots))
-    ws = 8.0 * tiles * c.bm * c.bn * c.split_k if c.split_k > 1 else 0.0
-    t_hbm = (max(compulsory, raw / g) + ws) / (dev.bw * dev.hbm_eff)
-    t_red = 0.0
-    if c.split_k > 1:
-        t_red = cdiv(tiles, dev.n_cu) * c.split_k * c.bm * c.bn * 4.0 / dev.cu_bw + 2.0 * dev.lat_step
-    return max(t_cu, t_hbm) + t_red + dev.t0
+    t_hbm = (max(compulsory, raw / g) + _splitk_slabs(M, N, c)) / (dev.bw * dev.hbm_eff)
+    return max(t_cu, t_hbm) + _splitk_pass(M, N, ec, c, dev) + dev.t0
 
 
 def rank(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):

@@ -234,6 +234,12 @@ def test_per_cu_model_terms():
     t_no = S.model_time(8192, 8192, 8192, S.BF16, s1, d)
     t_sk = S.model_time(8192, 8192, 8192, S.BF16, s2, d)
     assert t_sk > t_no          # 4096 tiles already fill the chip: splitting only adds work
+    # the second split-K pass is a launch of its own that reads every fp32 slab once and writes C
+    M, Nn, K = 1000, 1000, 8192
+    c4 = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 4, 3, 4)
+    assert S.model_time(M, Nn, K, S.BF16_F32OUT, c4, d) >= (4 * 4 * M * Nn + 4 * M * Nn) / d.bw + 2 * d.t0
+    sk = S.Cfg(S.KIND_SKINNY, 16, 128, 32, 4, 1, 2, 2)
+    assert S.model_time(16, 28672, 8192, S.BF16, sk, d) >= (4 * 2 * 16 * 28672 + 2 * 16 * 28672) / d.bw + 2 * d.t0
     # the HBM floor binds the 16-row decode
     dec = S.model_time(16, 28672, 8192, S.BF16, S.Cfg(S.KIND_TILED, 32, 128, 64, 1, 2, 4, 1), d)
     floor = (2 * (16 * 8192 + 8192 * 28672) + 2 * 16 * 28672) / (d.bw * d.hbm_eff)

@@ -115,8 +115,6 @@ hipStream_t current_stream() { return t_stream; }
 struct Workspace {
     float* ws = nullptr;
     size_t ws_bytes = 0;
-    unsigned* counters = nullptr;
-    size_t n_counters = 0;
 };
 static std::mutex g_ws_mu;
 static std::vector<Workspace> g_ws;
@@ -125,12 +123,10 @@ size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& c)
 {
     if (c.split_k <= 1)
         return 0;
-    int64_t tiles, blocks;
-    grid(M, N, c, &tiles, &blocks);
-    return (size_t)blocks * (size_t)c.bm * (size_t)c.bn * sizeof(float);
+    return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
 }
 
-int ensure_workspace(size_t ws_bytes, size_t n_counters, float** ws, unsigned** counters)
+int ensure_workspace(size_t ws_bytes, float** ws)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -140,39 +136,21 @@ int ensure_workspace(size_t ws_bytes, size_t n_counters, float** ws, unsigned** 
     if ((int)g_ws.size() <= dev)
         g_ws.resize(dev + 1);
     Workspace& w = g_ws[dev];
-    if (w.ws_bytes < ws_bytes || w.n_counters < n_counters) {
-        // the old buffers may still be in use by queued kernels
+    if (w.ws_bytes < ws_bytes) {
+        // the old buffer may still be in use by queued kernels
         e = hipDeviceSynchronize();
         if (e != hipSuccess)
             return set_hip_error(e, "hipDeviceSynchronize (workspace growth)");
-        const size_t nb = std::max(ws_bytes, w.ws_bytes);
-        const size_t nc = std::max(n_counters, w.n_counters);
-        if (w.ws_bytes < nb) {
-            if (w.ws)
-                (void)hipFree(w.ws);
-            w.ws = nullptr;
-            w.ws_bytes = 0;
-            e = hipMalloc(&w.ws, nb);
-            if (e != hipSuccess)
-                return set_error(TG_E_NOMEM, std::string("split-K workspace: ") + hipGetErrorString(e));
-            w.ws_bytes = nb;
-        }
-        if (w.n_counters < nc) {
-            if (w.counters)
-                (void)hipFree(w.counters);
-            w.counters = nullptr;
-            w.n_counters = 0;
-            e = hipMalloc(&w.counters, nc * sizeof(unsigned));
-            if (e != hipSuccess)
-                return set_error(TG_E_NOMEM, std::string("split-K counters: ") + hipGetErrorString(e));
-            e = hipMemset(w.counters, 0, nc * sizeof(unsigned));
-            if (e != hipSuccess)
-                return set_hip_error(e, "hipMemset (split-K counters)");
-            w.n_counters = nc;
-        }
+        if (w.ws)
+            (void)hipFree(w.ws);
+        w.ws = nullptr;
+        w.ws_bytes = 0;
+        e = hipMalloc(&w.ws, ws_bytes);
+        if (e != hipSuccess)
+            return set_error(TG_E_NOMEM, std::string("split-K workspace: ") + hipGetErrorString(e));
+        w.ws_bytes = ws_bytes;
     }
     *ws = w.ws;
-    *counters = w.counters;
     return TG_OK;
 }
 
@@ -248,13 +226,19 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     if (blocks > 0x7FFFFFFF)
         return set_error(TG_E_UNSUPPORTED, "too many workgroups");
     if (c.split_k > 1) {
-        const int st = ensure_workspace(workspace_bytes_for(M, N, c), (size_t)tiles, &p.ws, &p.counters);
+        const int st = ensure_workspace(workspace_bytes_for(M, N, c), &p.ws);
         if (st != TG_OK)
             return st;
+        p.slab = splitk_slab(M, N);
     }
     hipError_t e = ke->launch(p, (int)blocks, stream);
     if (e != hipSuccess)
         return set_hip_error(e, "kernel launch");
+    if (c.split_k > 1) {
+        e = splitk_reduce(p.ws, c.split_k, M, N, bias, C, p.out_bf16, act, stream);
+        if (e != hipSuccess)
+            return set_hip_error(e, "split-K reduction launch");
+    }
     return TG_OK;
 }
 

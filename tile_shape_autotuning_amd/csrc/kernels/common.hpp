@@ -27,8 +27,8 @@ struct GemmParams {
     const void* B;
     const float* bias;
     void* C;
-    float* ws;            // split-K partial tiles (fp32), used when split > 1
-    unsigned* counters;   // one arrival counter per output tile; zero between launches
+    float* ws;            // split-K: fp32 partial sums, one [M x N] slab per split
+    int64_t slab;         // floats from one split's slab to the next
     int M, N, K;
     int kps;              // K elements per split (multiple of the kernel's k unit)
     int split;            // number of K splits (grid blocks per output tile)
@@ -136,51 +136,28 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float v)
     return __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
 }
 
-// ---- split-K workspace
-// The fp32 partial tiles of one output tile come from workgroups that may run
-// on different XCDs, whose L2 caches are not coherent with one another.  Every
-// workspace access therefore carries the agent-scope cache policy (sc1: stores
-// write through, loads never return a stale L2 copy) -- the same instructions
-// the compiler emits for relaxed agent-scope atomic loads and stores.  A
-// partial is published by waiting for its stores to complete and then bumping
-// the tile's arrival counter (a relaxed agent-scope atomic); the last arriving
-// workgroup issues its loads only after it has seen the counter.  Agent-scope
-// release/acquire fences would do the same job as a writeback plus an
-// invalidate of the whole L2 of the XCD, evicting the operand panels of every
-// other workgroup there -- that made split-K several times slower than no split.
-constexpr int kCpolSc1 = 16;
+// ---- split-K
+// With split > 1 a block's sums skip bias, activation and conversion and go,
+// as fp32, to its split's slab of the workspace (row-major, row stride N like
+// C); a second kernel adds the slabs in split order and applies the rest.
+// Kernel boundaries order the two passes, so no flags or cache control are
+// needed between them.
+struct OutSpec {
+    void* dst;
+    const float* bias;
+    int act;
+    int bf16;
+};
 
-// Workspace region of one tile: `split` slots of `tile_vecs` 16-byte values.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(void* ws, int tile, int split, int tile_vecs)
+__device__ __forceinline__ OutSpec out_spec(const GemmParams& p, int split)
 {
-    const int64_t slot_bytes = (int64_t)tile_vecs * 16;
-    return make_rsrc(static_cast<char*>(ws) + (int64_t)tile * split * slot_bytes, split * slot_bytes);
-}
-
-__device__ __forceinline__ void ws_store(__amdgpu_buffer_rsrc_t r, int vec, f32x4_t v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, vec * 16, 0, kCpolSc1);
-}
-
-__device__ __forceinline__ f32x4_t ws_load(__amdgpu_buffer_rsrc_t r, int vec)
-{
-    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, vec * 16, 0, kCpolSc1));
+    if (p.split > 1)
+        return OutSpec{p.ws + (int64_t)split * p.slab, nullptr, 0, 0};
+    return OutSpec{p.C, p.bias, p.act, p.out_bf16};
 }
 
 // Wait until every vector memory access this wave issued has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Arrival of one split at `tile`; returns how many arrived before.
-__device__ __forceinline__ unsigned ws_arrive(unsigned* counters, int tile)
-{
-    return __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The reducer leaves the counter at zero for the next launch.
-__device__ __forceinline__ void ws_reset(unsigned* counters, int tile)
-{
-    __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Block index -> (tile_m, tile_n, split).  The hardware hands consecutive
 // workgroups to the 8 XCDs round robin; the first step renumbers blocks so

@@ -19,10 +19,10 @@
 //     all 8 and comes from L2;
 //   * U chunks are issued per step and the next step's loads are issued
 //     before the current step's MFMAs (software pipelining);
-//   * the W per-wave partials are summed through LDS, then split-K partials
-//     (run-time `split` workgroups per slice) are summed in split order by the
-//     last workgroup to arrive, which also runs the bias/activation epilogue
-//     and writes 8 consecutive outputs per lane.
+//   * the W per-wave partials are summed through LDS; wave 0 runs the
+//     bias/activation epilogue and writes 8 consecutive outputs per lane (with
+//     split-K, run-time `split` workgroups per slice, it writes raw fp32 sums
+//     to the split's workspace slab instead, for the second pass).
 #pragma once
 
 #include "common.hpp"
@@ -149,46 +149,21 @@ gemm_skinny_kernel(GemmParams p)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                f32x4_t v = red[((0 * MT + m) * 8 + t) * 64 + lane];
-                for (int w = 1; w < W; ++w)
-                    v += red[((w * MT + m) * 8 + t) * 64 + lane];
-                acc[m][t] = v;
-            }
-    }
-    // from here on only wave 0 is active
-
-    // ---- split-K across workgroups
-    if (p.split > 1) {
-        constexpr int TV = MT * 8 * 64;            // 16-byte values per partial slice
-        const __amdgpu_buffer_rsrc_t ws = ws_rsrc(p.ws, tile, p.split, TV);
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
             for (int t = 0; t < 8; ++t)
-                ws_store(ws, split * TV + (m * 8 + t) * 64 + lane, acc[m][t]);
-        wait_vm_all();
-        unsigned prev = 0;
-        if (lane == 0)
-            prev = ws_arrive(p.counters, tile);
-        prev = __shfl(prev, 0);
-        if (prev != (unsigned)(p.split - 1))
-            return;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < p.split; ++sp) {
+                acc[m][t] = red[((0 * MT + m) * 8 + t) * 64 + lane];
+        // one wave's partials at a time (unrolled, the compiler would load
+        // all of them before the first add and spill)
+#pragma unroll 1
+        for (int w = 1; w < W; ++w)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    acc[m][t] += ws_load(ws, sp * TV + (m * 8 + t) * 64 + lane);
-        }
-        if (lane == 0)
-            ws_reset(p.counters, tile);
+                    acc[m][t] += red[((w * MT + m) * 8 + t) * 64 + lane];
     }
+    // from here on only wave 0 is active
+
+    const OutSpec out = out_spec(p, split);
 
     // ---- epilogue: lane owns rows 16m + 4g + r, columns n0 + 8*l16 + t (t = 0..7)
     if (!col_ok)
@@ -197,7 +172,7 @@ gemm_skinny_kernel(GemmParams p)
     float bv[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-        bv[t] = p.bias ? p.bias[col0 + t] : 0.0f;
+        bv[t] = out.bias ? out.bias[col0 + t] : 0.0f;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -208,16 +183,16 @@ gemm_skinny_kernel(GemmParams p)
             float v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                v[t] = apply_act(acc[m][t][r] + bv[t], p.act);
+                v[t] = apply_act(acc[m][t][r] + bv[t], out.act);
             const int64_t idx = (int64_t)row * N + col0;
-            if (p.out_bf16) {
+            if (out.bf16) {
                 u32x4_t o;
 #pragma unroll
                 for (int d = 0; d < 4; ++d)
                     o[d] = (unsigned)f32_to_bf16_rne(v[2 * d]) | ((unsigned)f32_to_bf16_rne(v[2 * d + 1]) << 16);
-                *reinterpret_cast<u32x4_t*>(static_cast<unsigned short*>(p.C) + idx) = o;
+                *reinterpret_cast<u32x4_t*>(static_cast<unsigned short*>(out.dst) + idx) = o;
             } else {
-                f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx);
+                f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out.dst) + idx);
                 dst[0] = f32x4_t{v[0], v[1], v[2], v[3]};
                 dst[1] = f32x4_t{v[4], v[5], v[6], v[7]};
             }

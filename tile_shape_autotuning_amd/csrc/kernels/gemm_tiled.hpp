@@ -10,9 +10,9 @@
 // pipeline depth: 1 = one panel buffer, 2 = double buffering, where the loads
 // of step t+1 are in flight while the matrix cores work on step t (page
 // "Tiling the hierarchy", double-buffering section).  Split-K (a run-time
-// value) gives each of `split` workgroups a contiguous K range; the last one
-// to finish a tile sums the fp32 partials in split order and runs the
-// epilogue, so no extra launch is needed and results are deterministic.
+// value) gives each of `split` workgroups a contiguous K range; each writes
+// its fp32 sums to its split's workspace slab and a second kernel adds the
+// slabs in split order and runs the epilogue (deterministic results).
 //
 // gfx950 specifics:
 //   * global loads are 16-byte buffer loads (out-of-range lanes read zero, so
@@ -66,8 +66,6 @@ gemm_tiled_kernel(GemmParams p)
     constexpr int T = Cf::T, CPR = Cf::CPR, EB = Cf::EB, EPC = Cf::EPC;
     constexpr int FM = Cf::FM, FN = Cf::FN;
     __shared__ u32x4_t lds[ST * Cf::STAGE_SLOTS];
-    // split-K arrival flag: lives in the (then idle) panel buffers
-    int& s_last = *reinterpret_cast<int*>(lds);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -282,56 +280,26 @@ gemm_tiled_kernel(GemmParams p)
         }
     }
 
-    // ---- split-K: publish the partial tile; the last arriving block reduces
-    if (p.split > 1) {
-        constexpr int TV = BM * BN / 4;            // 16-byte values per partial tile
-        const __amdgpu_buffer_rsrc_t ws = ws_rsrc(p.ws, tile, p.split, TV);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                ws_store(ws, split * TV + (i * FN + j) * T + tid, acc[i][j]);
-        wait_vm_all();
-        __syncthreads();
-        if (tid == 0)
-            s_last = (ws_arrive(p.counters, tile) == (unsigned)(p.split - 1));
-        __syncthreads();
-        if (!s_last)
-            return;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < p.split; ++s) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] += ws_load(ws, s * TV + (i * FN + j) * T + tid);
-        }
-        if (tid == 0)
-            ws_reset(p.counters, tile);
-    }
+    const OutSpec out = out_spec(p, split);
 
     // ---- epilogue: bias, activation, convert, store
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int col = n0 + wn * Cf::WN + j * 16 + l16;
         const bool cv = col < N;
-        const float bj = (p.bias && cv) ? p.bias[col] : 0.0f;
+        const float bj = (out.bias && cv) ? out.bias[col] : 0.0f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + wm * Cf::WM + i * 16 + g * 4 + r;
                 if (cv && row < M) {
-                    const float v = apply_act(acc[i][j][r] + bj, p.act);
+                    const float v = apply_act(acc[i][j][r] + bj, out.act);
                     const int64_t idx = (int64_t)row * N + col;
-                    if (p.out_bf16)
-                        static_cast<unsigned short*>(p.C)[idx] = f32_to_bf16_rne(v);
+                    if (out.bf16)
+                        static_cast<unsigned short*>(out.dst)[idx] = f32_to_bf16_rne(v);
                     else
-                        static_cast<float*>(p.C)[idx] = v;
+                        static_cast<float*>(out.dst)[idx] = v;
                 }
             }
         }

@@ -129,11 +129,17 @@ __device__ __forceinline__ int b_pos_to_row(int p)
 }
 
 // Buffer resource words (base, 32-bit num_records, gfx9 raw-buffer flags).
+// Uniform by construction; readfirstlane states it, so the words always land
+// in the scalar registers the transfer instruction takes (where the
+// compiler's uniformity analysis loses track of them it would otherwise pick
+// vector registers, which the instruction cannot encode).
 __device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes)
 {
     const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : bytes);
     const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)n, kRsrcWord3};
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu)),
+                   __builtin_amdgcn_readfirstlane((int)n), kRsrcWord3};
 }
 
 // One wave-wide load of 16 bytes per lane from a buffer straight into LDS
@@ -198,9 +204,6 @@ gemm_tiled_dma_kernel(GemmParams p)
     constexpr int T = Cf::T, FM = Cf::FM, FN = Cf::FN, W = Cf::W, KK = Cf::KK;
     constexpr int RB = Cf::RB, U = Cf::U, QW = Cf::QW;
     __shared__ u32x4_t lds[ST * Cf::STAGE_BYTES / 16];
-    // split-K arrival flag: lives in the (then idle) panel buffers, so the
-    // LDS footprint is exactly ST panels
-    int& s_last = *reinterpret_cast<int*>(lds);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -437,38 +440,6 @@ gemm_tiled_dma_kernel(GemmParams p)
         for (int j = 0; j < FN; ++j)
             __asm__ __volatile__("" : "+a"(acc[i][j]));
 
-    // ---- split-K: publish the partial tile; the last arriving block reduces
-    if (p.split > 1) {
-        constexpr int TV = BM * BN / 4;            // 16-byte values per partial tile
-        const __amdgpu_buffer_rsrc_t ws = ws_rsrc(p.ws, tile, p.split, TV);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                ws_store(ws, split * TV + (i * FN + j) * T + tid, acc[i][j]);
-        wait_vm_all();
-        __syncthreads();
-        if (tid == 0)
-            s_last = (ws_arrive(p.counters, tile) == (unsigned)(p.split - 1));
-        __syncthreads();
-        if (!s_last)
-            return;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < p.split; ++s) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] += ws_load(ws, s * TV + (i * FN + j) * T + tid);
-        }
-        if (tid == 0)
-            ws_reset(p.counters, tile);
-    }
-
     // ---- epilogue: bias, activation, convert, store.  The lane coordinates
     // are derived afresh from an opaque copy of the thread index, so that
     // nothing the epilogue needs is computed before the K loop and held in
@@ -481,6 +452,7 @@ gemm_tiled_dma_kernel(GemmParams p)
     const int wme = wave_e / WGN, wne = wave_e % WGN;
     const int row_w = m0 + wme * Cf::WM;          // first output row of the wave tile
     const int col_w = n0 + wne * Cf::WN;          // first output column
+    const OutSpec out = out_spec(p, split);
 
     if constexpr (Cf::EPI_LDS) {
         // Each wave turns its accumulators, one 16-row slab at a time, into
@@ -499,7 +471,7 @@ gemm_tiled_dma_kernel(GemmParams p)
         float bias8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            bias8[e] = (p.bias && col_ok) ? p.bias[col0 + e] : 0.0f;
+            bias8[e] = (out.bias && col_ok) ? out.bias[col0 + e] : 0.0f;
         __syncthreads();   // every wave's last transfers and reads are done: LDS is free
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -519,16 +491,16 @@ gemm_tiled_dma_kernel(GemmParams p)
                     float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        o[e] = apply_act(o[e] + bias8[e], p.act);
+                        o[e] = apply_act(o[e] + bias8[e], out.act);
                     const int64_t idx = (int64_t)row * N + col0;
-                    if (p.out_bf16) {
+                    if (out.bf16) {
                         u32x4_t w;
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             w[e] = (unsigned)f32_to_bf16_rne(o[2 * e]) | ((unsigned)f32_to_bf16_rne(o[2 * e + 1]) << 16);
-                        *reinterpret_cast<u32x4_t*>(static_cast<unsigned short*>(p.C) + idx) = w;
+                        *reinterpret_cast<u32x4_t*>(static_cast<unsigned short*>(out.dst) + idx) = w;
                     } else {
-                        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(p.C) + idx);
+                        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out.dst) + idx);
                         dst[0] = f32x4_t{o[0], o[1], o[2], o[3]};
                         dst[1] = f32x4_t{o[4], o[5], o[6], o[7]};
                     }
@@ -540,19 +512,19 @@ gemm_tiled_dma_kernel(GemmParams p)
         for (int j = 0; j < FN; ++j) {
             const int col = col_w + j * 16 + l16e;
             const bool cv = col < N;
-            const float bj = (p.bias && cv) ? p.bias[col] : 0.0f;
+            const float bj = (out.bias && cv) ? out.bias[col] : 0.0f;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = row_w + i * 16 + ge * 4 + r;
                     if (cv && row < M) {
-                        const float v = apply_act(acc[i][j][r] + bj, p.act);
+                        const float v = apply_act(acc[i][j][r] + bj, out.act);
                         const int64_t idx = (int64_t)row * N + col;
-                        if (p.out_bf16)
-                            static_cast<unsigned short*>(p.C)[idx] = f32_to_bf16_rne(v);
+                        if (out.bf16)
+                            static_cast<unsigned short*>(out.dst)[idx] = f32_to_bf16_rne(v);
                         else
-                            static_cast<float*>(p.C)[idx] = v;
+                            static_cast<float*>(out.dst)[idx] = v;
                     }
                 }
             }

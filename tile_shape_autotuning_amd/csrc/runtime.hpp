@@ -33,9 +33,15 @@ hipStream_t current_stream();
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias,
                void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked);
 
-// Split-K workspace: grows to at least `ws_bytes` and `n_counters` zeroed counters.
-int ensure_workspace(size_t ws_bytes, size_t n_counters, float** ws, unsigned** counters);
+// Split-K workspace: grows to at least `ws_bytes`.
+int ensure_workspace(size_t ws_bytes, float** ws);
 size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& cfg);
+
+// Split-K second pass (splitk_reduce.hip): C = act(sum of the split slabs +
+// bias), slabs `splitk_slab(M, N)` floats apart.
+int64_t splitk_slab(int64_t M, int64_t N);
+hipError_t splitk_reduce(const float* ws, int split, int64_t M, int64_t N, const float* bias, void* C,
+                         int out_bf16, int act, hipStream_t stream);
 
 // Argument validation shared by the entry points.
 int validate_problem(int64_t M, int64_t N, int64_t K, int dtype);

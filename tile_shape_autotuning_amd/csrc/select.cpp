@@ -351,6 +351,22 @@ static double model_page(int64_t K, int dtype, const tg_cfg& c, const tg_device_
     return std::max(t_c, t_m) + d.t0;
 }
 
+// Split-K (page "Compilers and Kernel Languages", "A different tile for a
+// different shape"): the fp32 partial-sum slabs, one M x N slab per split ...
+static double splitk_slabs(int64_t M, int64_t N, const tg_cfg& c)
+{
+    return c.split_k > 1 ? 4.0 * (double)c.split_k * (double)M * (double)N : 0.0;
+}
+
+// ... and the second pass: one more launch reading every slab once and
+// writing C at the HBM rate.
+static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, const tg_device_desc& d)
+{
+    if (c.split_k <= 1)
+        return 0.0;
+    return (splitk_slabs(M, N, c) + (double)ec * (double)M * (double)N) / (d.bw * d.hbm_eff) + d.t0;
+}
+
 // MI355X: the roofline of "Analytical models and where they break" per CU and
 // per K step.  One K step of the blocks resident on a CU takes the longest of
 // their MFMA work on the SIMDs their waves occupy, their LDS traffic, their
@@ -358,10 +374,11 @@ static double model_page(int64_t K, int dtype, const tg_cfg& c, const tg_device_
 // memory latency over the pipeline depth; a lone wave on a SIMD issues all of
 // it in order (w1_eff).  Blocks run in rounds of n_cu x resident, the partial
 // last round spread out, each round starting with one latency; the HBM time of
-// the traffic bounds it from below; split-K adds the reducer reading every
-// partial and a store -> count -> load chain through memory.
-static double model_cu(int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d, int64_t eb, double peak,
-                       double compulsory, int64_t tiles, int64_t units, int64_t w, int64_t bcu)
+// the traffic bounds it from below (with split-K that traffic includes
+// writing the partial-sum slabs); split-K adds the second pass.
+static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d,
+                       int64_t eb, int64_t ec, double peak, double compulsory, int64_t tiles, int64_t units,
+                       int64_t w, int64_t bcu)
 {
     const int64_t ktiles = cdiv(k_per_split(c, K), c.bk);
     const int64_t wm = c.bm / c.wgm, wn = c.bn / c.wgn;
@@ -393,12 +410,8 @@ static double model_cu(int64_t K, int dtype, const tg_cfg& c, const tg_device_de
     t_cu = t_cu + (double)rounds * lat;
     const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
     const double g = std::sqrt((double)std::min<int64_t>(units, slots));
-    const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
-    const double t_hbm = (std::max(compulsory, raw / g) + ws) / (d.bw * d.hbm_eff);
-    double t_red = 0.0;
-    if (c.split_k > 1)
-        t_red = (double)(cdiv(tiles, (int64_t)d.n_cu) * c.split_k * c.bm * c.bn) * 4.0 / d.cu_bw + 2.0 * d.lat_step;
-    return std::max(t_cu, t_hbm) + t_red + d.t0;
+    const double t_hbm = (std::max(compulsory, raw / g) + splitk_slabs(M, N, c)) / (d.bw * d.hbm_eff);
+    return std::max(t_cu, t_hbm) + splitk_pass(M, N, ec, c, d) + d.t0;
 }
 
 double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d)
@@ -416,21 +429,22 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     if (c.kind == TG_KIND_SKINNY) {
         const double flops_pad = 2.0 * (double)c.bm * (double)N * (double)K;
         const double t_c = flops_pad / peak;
-        const double ws = c.split_k > 1 ? 8.0 * (double)c.bm * 128.0 * (double)tiles * (double)c.split_k : 0.0;
+        const double ws = d.mode == 0 ? splitk_slabs(M, N, c)
+                          : (c.split_k > 1 ? 8.0 * (double)c.bm * 128.0 * (double)tiles * (double)c.split_k : 0.0);
         const int64_t resident = std::min<int64_t>(units * w, (int64_t)d.n_cu * bcu * w);
         const double inflight = (double)resident * 64.0 * (double)c.stages * 8.0 * 16.0;
         const double bw_eff = std::min(1.0, inflight / (d.bw * d.lat_mem));
         const int64_t active = std::min<int64_t>(units, d.n_cu);
         const double bw = std::min(d.bw * bw_eff, (double)active * d.cu_bw);
         const double t_m = (compulsory + ws) / bw;
-        double t = std::max(t_c, t_m);
+        const double t = std::max(t_c, t_m);
         if (d.mode == 0)
-            t = t / d.skinny_eff;
+            return t / d.skinny_eff + splitk_pass(M, N, ec, c, d) + d.t0;
         return t + d.t0;
     }
     if (d.mode == 1)
         return model_page(K, dtype, c, d, eb, peak, flops, compulsory, tiles, units, w, bcu);
-    return model_cu(K, dtype, c, d, eb, peak, compulsory, tiles, units, w, bcu);
+    return model_cu(M, N, K, dtype, c, d, eb, ec, peak, compulsory, tiles, units, w, bcu);
 }
 
 bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t)

@@ -1,0 +1,96 @@
+// Second pass of split-K (page "Compilers and Kernel Languages", "A different
+// tile for a different shape": split-K is one of the choices real kernels add
+// for skinny problems).  The GEMM kernels leave one fp32 slab of raw sums per
+// split in the workspace, row-major like C; this kernel adds the slabs in
+// split order 0 .. S-1, then adds the bias, applies the activation, converts
+// and stores C.  The activation is not linear, so it can only follow the
+// complete sum.
+//
+// The pass is elementwise over the flattened M x N array: each thread owns
+// four consecutive elements (one 16-byte load per slab), so every access is
+// coalesced whatever the GEMM's tile shape was.  It reads S x M x N x 4 bytes
+// and writes M x N elements: HBM-bound.
+#include <hip/hip_runtime.h>
+
+#include "kernels/common.hpp"
+#include "runtime.hpp"
+
+namespace tg {
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* ws, int split, int64_t slab, int64_t mn, int n, const float* bias, void* C,
+                     int out_bf16, int act, int vec_out)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < mn; i += stride) {
+        const int cnt = mn - i < 4 ? (int)(mn - i) : 4;
+        float v[4];
+        if (cnt == 4) {
+            f32x4_t s = *reinterpret_cast<const f32x4_t*>(ws + i);
+            for (int k = 1; k < split; ++k)
+                s += *reinterpret_cast<const f32x4_t*>(ws + k * slab + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = s[e];
+        } else {
+            for (int e = 0; e < cnt; ++e) {
+                float s = ws[i + e];
+                for (int k = 1; k < split; ++k)
+                    s += ws[k * slab + i + e];
+                v[e] = s;
+            }
+        }
+        int col = (int)(i % n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e < cnt)
+                v[e] = apply_act(v[e] + (bias ? bias[col] : 0.0f), act);
+            col = col + 1 == n ? 0 : col + 1;
+        }
+        if (out_bf16) {
+            unsigned short* c = static_cast<unsigned short*>(C) + i;
+            if (cnt == 4 && vec_out) {
+                const u32x2_t w = {(unsigned)f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16),
+                                   (unsigned)f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16)};
+                *reinterpret_cast<u32x2_t*>(c) = w;
+            } else {
+                for (int e = 0; e < cnt; ++e)
+                    c[e] = f32_to_bf16_rne(v[e]);
+            }
+        } else {
+            float* c = static_cast<float*>(C) + i;
+            if (cnt == 4 && vec_out) {
+                *reinterpret_cast<f32x4_t*>(c) = f32x4_t{v[0], v[1], v[2], v[3]};
+            } else {
+                for (int e = 0; e < cnt; ++e)
+                    c[e] = v[e];
+            }
+        }
+    }
+}
+
+int64_t splitk_slab(int64_t M, int64_t N)
+{
+    // each slab starts 256-byte aligned, so 16-byte loads stay aligned
+    return (M * N + 63) / 64 * 64;
+}
+
+hipError_t splitk_reduce(const float* ws, int split, int64_t M, int64_t N, const float* bias, void* C,
+                         int out_bf16, int act, hipStream_t stream)
+{
+    const int64_t mn = M * N;
+    if (mn <= 0)
+        return hipSuccess;
+    const int64_t want = (mn + 1023) / 1024;      // 256 threads x 4 elements per block
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    // four outputs per store where C's alignment allows it (the element-load
+    // kind accepts any C)
+    const int vec_out = ((uintptr_t)C & (out_bf16 ? 7u : 15u)) == 0;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, ws, split, splitk_slab(M, N), mn,
+                       (int)N, bias, C, out_bf16, act, vec_out);
+    return hipGetLastError();
+}
+
+}  // namespace tg

@@ -238,18 +238,12 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
             if ((e = fill_uniform(s.B[i], (int64_t)nb, dtype != TG_F32, 0x5678u + (uint32_t)i, st)) != hipSuccess)
                 return set_hip_error(e, "tuning scratch fill");
         // workspace for the largest split-K candidate, allocated before timing
-        size_t wsb = 0, nct = 0;
-        for (const Timed& t : cands) {
+        size_t wsb = 0;
+        for (const Timed& t : cands)
             wsb = std::max(wsb, workspace_bytes_for(M, N, t.cfg));
-            int64_t tiles, blocks;
-            grid(M, N, t.cfg, &tiles, &blocks);
-            if (t.cfg.split_k > 1)
-                nct = std::max(nct, (size_t)tiles);
-        }
         if (wsb > 0) {
             float* w;
-            unsigned* c;
-            const int r = ensure_workspace(wsb, nct, &w, &c);
+            const int r = ensure_workspace(wsb, &w);
             if (r != TG_OK)
                 return r;
         }
