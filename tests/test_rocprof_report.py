@@ -111,3 +111,27 @@ def test_commands_give_one_counter_block_per_pass():
         assert sum(1 for x in ctrs if x.startswith("GRBM_")) <= 2
     assert any("FETCH_SIZE" in c and "WRITE_SIZE" not in c for c in pmc)
     assert any("WRITE_SIZE" in c and "FETCH_SIZE" not in c for c in pmc)
+
+
+RED = "tg::splitk_reduce_kernel(float const*, int, long, long, int, float const*, void*, int, int, int)"
+
+
+def test_split_k_calls_count_both_launches(tmp_path):
+    tr, fetch, write = str(tmp_path / "t"), str(tmp_path / "f"), str(tmp_path / "w")
+    # every call: the GEMM (30 us) then the second pass (5 us, its own grid)
+    _trace_db(tr, [(GEMM, 30000, 131072), (RED, 5000, 250112)] * 3 + [(RED, 9000, 4096)])
+    copy_bytes = 1 << 30
+    _pmc_db(fetch, [(COPY, 1, "FETCH_SIZE", copy_bytes / 1024), (GEMM, 2, "FETCH_SIZE", 1000.0),
+                    (RED, 3, "FETCH_SIZE", 400.0)])
+    _pmc_db(write, [(COPY, 1, "WRITE_SIZE", copy_bytes / 1024), (GEMM, 2, "WRITE_SIZE", 400.0),
+                    (RED, 3, "WRITE_SIZE", 100.0)])
+    s = R.summary(tr, [], fetch, write, copy_bytes, kernel="gemm_tiled_dma_kernel", flops=1.0e12, grid=131072,
+                  second=("splitk_reduce", 250112))
+    assert s["avg_us"] == pytest.approx(30.0)
+    assert s["second"]["avg_us"] == pytest.approx(5.0) and s["second"]["calls"] == 3
+    assert s["call_us"] == pytest.approx(35.0)
+    assert s["TFLOP/s"] == pytest.approx(1.0e12 / 35e-6 / 1e12)
+    assert s["traffic"]["bytes"] == pytest.approx((1000.0 + 400.0 + 400.0 + 100.0) * 1024)
+    text, _ = R.counters_text("w", (0, 128, 64, 64, 2, 2, 3, 4), "gemm_tiled_dma_kernel", tr, [], fetch, write,
+                              copy_bytes, 1.0e12, 0, ["cmd"], 131072, ("splitk_reduce", 250112))
+    assert "per call (both launches):   35.000 us" in text

@@ -83,11 +83,21 @@ def _pick(d, sub):
 
 
 def summary(trace_dir, pmc_dirs=(), fetch_dir=None, write_dir=None, copy_bytes=0, kernel="gemm",
-            flops=None, nbytes=None, grid=None):
+            flops=None, nbytes=None, grid=None, second=None):
+    """Figures of one kernel.  `second` = (name substring, grid) of a kernel
+    that every call launches after it (the split-K second pass): its average
+    duration and HBM bytes are reported too, and the per-call figures cover
+    both launches."""
     times = kernel_times(trace_dir, grid)
     kname = _pick(times, kernel)
     calls, avg_ns = times[kname]
-    out = {"kernel": kname, "calls": calls, "avg_us": avg_ns / 1e3}
+    out = {"kernel": kname, "calls": calls, "avg_us": avg_ns / 1e3, "call_us": avg_ns / 1e3}
+    if second:
+        t2 = kernel_times(trace_dir, second[1])
+        k2 = _pick(t2, second[0])
+        out["second"] = {"kernel": k2, "calls": t2[k2][0], "avg_us": t2[k2][1] / 1e3}
+        out["call_us"] = out["avg_us"] + out["second"]["avg_us"]
+        avg_ns = out["call_us"] * 1e3
     if flops:
         out["TFLOP/s"] = flops / (avg_ns * 1e-9) / 1e12
     if nbytes:
@@ -110,6 +120,13 @@ def summary(trace_dir, pmc_dirs=(), fetch_dir=None, write_dir=None, copy_bytes=0
         out.setdefault("counters", {}).update({c: s[c] for c in s})
     if fetch_dir and write_dir and copy_bytes:
         out["traffic"] = hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel)
+        if second:
+            t2 = hbm_traffic(fetch_dir, write_dir, copy_bytes, second[0])
+            out["second"]["traffic"] = t2
+            tr = out["traffic"]
+            out["traffic"] = {n: {"kib_raw": tr[n]["kib_raw"] + t2[n]["kib_raw"], "scale": tr[n]["scale"],
+                                  "bytes": tr[n]["bytes"] + t2[n]["bytes"]} for n in ("FETCH_SIZE", "WRITE_SIZE")}
+            out["traffic"]["bytes"] = tr["bytes"] + t2["bytes"]
     return out
 
 
@@ -159,21 +176,27 @@ def kernel_name(cfg, in_bf16=True):
 
 
 def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, flops,
-                  algo_bytes, commands_used, grid=None):
+                  algo_bytes, commands_used, grid=None, second=None):
     """Summary of one kernel on one workload: duration, MFMA utilisation, LDS
     bank conflicts, L2 hit rate and HBM bytes (FETCH_SIZE / WRITE_SIZE scaled
-    by the same counters for a plain copy of copy_bytes)."""
-    sm = summary(trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, kname, flops, algo_bytes, grid)
+    by the same counters for a plain copy of copy_bytes).  With `second` (the
+    split-K second pass) the rates and bytes are per call, both launches."""
+    sm = summary(trace_dir, pmc_dirs, fetch_dir, write_dir, copy_bytes, kname, flops, algo_bytes, grid, second)
     c = sm.get("counters", {})
     lines = [f"# {kname} on {workload}", "", "cfg (kind,bm,bn,bk,wgm,wgn,stages,split_k): " +
              ",".join(str(x) for x in cfg), "", "commands (run from the repository root on MI355X):"]
     lines += [f"  {cmd}" for cmd in commands_used]
     lines += ["", f"launches traced:            {sm['calls']}" + (f" (dispatches of {grid} work-items)" if grid else ""),
               f"average duration:           {sm['avg_us']:.3f} us"]
+    if second:
+        s2 = sm["second"]
+        lines += [f"second pass {s2['kernel']}: {s2['calls']} launches, average {s2['avg_us']:.3f} us",
+                  f"per call (both launches):   {sm['call_us']:.3f} us"]
+    per = "call" if second else "launch"
     if flops:
-        lines.append(f"algorithmic TFLOP/s:        {sm['TFLOP/s']:.1f}   (2MNK = {flops:.4g} flop per launch)")
+        lines.append(f"algorithmic TFLOP/s:        {sm['TFLOP/s']:.1f}   (2MNK = {flops:.4g} flop per {per})")
     if algo_bytes:
-        lines.append(f"algorithmic GB/s:           {sm['GB/s']:.1f}   (compulsory {algo_bytes:.4g} B per launch)")
+        lines.append(f"algorithmic GB/s:           {sm['GB/s']:.1f}   (compulsory {algo_bytes:.4g} B per {per})")
     if "mfma_util" in sm:
         lines.append(f"MFMA busy / (4 x CU busy):  {sm['mfma_util']:.3f}")
     if c.get("GRBM_GUI_ACTIVE") and c.get("SQ_BUSY_CU_CYCLES"):
@@ -188,12 +211,12 @@ def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_di
     tr = sm.get("traffic")
     if tr:
         f, w = tr["FETCH_SIZE"], tr["WRITE_SIZE"]
-        lines += ["", "HBM traffic per launch (counter KiB x scale; scale = copy bytes / copy counter):",
+        lines += ["", f"HBM traffic per {per} (counter KiB x scale; scale = copy bytes / copy counter):",
                   f"  FETCH_SIZE {f['kib_raw']:.1f} KiB x {f['scale']:.4f} = {f['bytes']:.4g} B",
                   f"  WRITE_SIZE {w['kib_raw']:.1f} KiB x {w['scale']:.4f} = {w['bytes']:.4g} B",
                   f"  total {tr['bytes']:.4g} B" + (f" = {tr['bytes'] / algo_bytes:.2f} x the compulsory bytes"
                                                      if algo_bytes else ""),
-                  f"  achieved HBM rate {tr['bytes'] / (sm['avg_us'] * 1e-6) / 1e9:.1f} GB/s"]
+                  f"  achieved HBM rate {tr['bytes'] / (sm['call_us'] * 1e-6) / 1e9:.1f} GB/s"]
     lines += ["", "raw counters (mean per dispatch):"]
     lines += [f"  {k} = {v:.6g}" for k, v in sorted(c.items())]
     return "\n".join(lines) + "\n", sm
