@@ -430,7 +430,9 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
     in rounds of n_cu x resident (wave quantisation; the partial last round
     spreads its blocks); each round starts with one latency.  The chip-wide
     HBM time of the traffic bounds it from below (with split-K that traffic
-    includes writing the partial-sum slabs); split-K adds the second pass."""
+    includes writing the partial-sum slabs).  The output stores come after
+    each block's K loop and add their HBM time to the per-CU time; split-K
+    adds the second pass."""
     ktiles = cdiv(k_per_split(c, K), c.bk)
     wm, wn = c.bm // c.wgm, c.bn // c.wgn
     simd_peak = peak / (dev.n_cu * dev.simds)
@@ -460,6 +462,10 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
     raw = float(tiles) * eb * K * (c.bm + c.bn)
     g = math.sqrt(min(units, slots))
     t_hbm = (max(compulsory, raw / g) + _splitk_slabs(M, N, c)) / (dev.bw * dev.hbm_eff)
+    # every block stores its outputs (C, or its split-K slab) after its K
+    # loop: those stores do not overlap the loop
+    stores = _splitk_slabs(M, N, c) if c.split_k > 1 else float(ec) * M * N
+    t_cu = t_cu + stores / (dev.bw * dev.hbm_eff)
     return max(t_cu, t_hbm) + _splitk_pass(M, N, ec, c, dev) + dev.t0
 
 

@@ -194,8 +194,8 @@ def test_model_invariants(M, N, K, dt):
 
 
 def test_wave_quantisation_in_the_per_cu_model():
-    # compute alone: LDS, L2 and latency terms made negligible, no lone-wave penalty
-    d = dataclasses.replace(S.MI355X, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0)
+    # compute alone: LDS, L2, latency and output-store terms made negligible, no lone-wave penalty
+    d = dataclasses.replace(S.MI355X, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0, bw=1e30)
     # 128x128 tiles, W = 4, two blocks fit a CU (64 KiB of LDS each): 256 tiles are one
     # partial round with one block per CU
     c = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
@@ -217,6 +217,22 @@ def test_wave_quantisation_in_the_per_cu_model():
     assert t1 >= (2.0 * 4096 ** 3 / d.peak_bf16) * 4 / busy * (1 - 1e-12)
     if busy < 4:
         assert t1 > 1.5 * (2.0 * 4096 ** 3 / d.peak_bf16)
+
+
+def test_output_stores_follow_the_k_loop():
+    # compute-bound 2048x2048x4096 on 128x128 tiles: the C stores (bf16) add their HBM time
+    fast = dataclasses.replace(S.MI355X, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0, bw=1e30)
+    real_bw = dataclasses.replace(fast, bw=S.MI355X.bw)
+    c = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
+    t_inf = S.model_time(2048, 2048, 4096, S.BF16, c, fast)
+    t_bw = S.model_time(2048, 2048, 4096, S.BF16, c, real_bw)
+    assert t_bw - t_inf == pytest.approx(2 * 2048 * 2048 / (S.MI355X.bw * S.MI355X.hbm_eff))
+    # with split-K the stores are the fp32 slabs, and the second pass reads them and writes C
+    c2 = dataclasses.replace(c, split_k=2)
+    t2_inf = S.model_time(2048, 2048, 4096, S.BF16, c2, fast)
+    t2_bw = S.model_time(2048, 2048, 4096, S.BF16, c2, real_bw)
+    bw = S.MI355X.bw * S.MI355X.hbm_eff
+    assert t2_bw - t2_inf == pytest.approx((2 * 4 * 2048 * 2048 + (2 * 4 + 2) * 2048 * 2048) / bw)
 
 
 def test_per_cu_model_terms():

@@ -375,7 +375,9 @@ static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, con
 // it in order (w1_eff).  Blocks run in rounds of n_cu x resident, the partial
 // last round spread out, each round starting with one latency; the HBM time of
 // the traffic bounds it from below (with split-K that traffic includes
-// writing the partial-sum slabs); split-K adds the second pass.
+// writing the partial-sum slabs). The output stores come after each block's
+// K loop and add their HBM time to the per-CU time; split-K adds the second
+// pass.
 static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d,
                        int64_t eb, int64_t ec, double peak, double compulsory, int64_t tiles, int64_t units,
                        int64_t w, int64_t bcu)
@@ -411,6 +413,10 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
     const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
     const double g = std::sqrt((double)std::min<int64_t>(units, slots));
     const double t_hbm = (std::max(compulsory, raw / g) + splitk_slabs(M, N, c)) / (d.bw * d.hbm_eff);
+    // every block stores its outputs (C, or its split-K slab) after its K
+    // loop: those stores do not overlap the loop
+    const double stores = c.split_k > 1 ? splitk_slabs(M, N, c) : (double)ec * (double)M * (double)N;
+    t_cu = t_cu + stores / (d.bw * d.hbm_eff);
     return std::max(t_cu, t_hbm) + splitk_pass(M, N, ec, c, d) + d.t0;
 }
 
