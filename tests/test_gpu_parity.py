@@ -196,6 +196,31 @@ def test_split_k_deterministic_and_exact():
         assert_close(out_f64(C1), ref, dtype, f"split {s}")
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])
+def test_split_k_second_pass_edges(dtype):
+    # an unaligned shape (N = 33) runs the element-load kind, which takes any C: the second pass
+    # then writes element by element into a C shifted off 16-byte alignment, and M x N = 2145
+    # leaves a ragged tail after the four-element groups
+    M, N, K = 65, 33, 630
+    A, B, bias = _int_inputs(M, N, K, dtype, 8)
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    feas = [c for c in tg.enumerate_feasible(M, N, K, dtype) if c.split_k > 1 and tg.has_kernel(dtype, c)]
+    assert feas and all(c.kind == S.KIND_UNALIGNED for c in feas)
+    odt = torch.bfloat16 if dtype == wl.BF16 else torch.float32
+    for shift in (0, 1):
+        buf = torch.zeros(M * N + 1, dtype=odt, device="cuda")
+        out = buf[shift:shift + M * N].view(M, N)
+        for c in feas:
+            mark(f"split-K second pass dt{dtype} shift {shift} {c.astuple()}")
+            out.fill_(0)
+            tg.gemm_bias_act(A_d, B_d, b_d, act="relu", out=out, cfg=c)
+            torch.cuda.synchronize()
+            _exact_check(out, ref, dtype, f"second pass dt{dtype} shift {shift} {c.astuple()}")
+            if shift:
+                assert float(buf[0]) == 0.0, "the second pass wrote before C"
+
+
 def _workload_parity(index, cfgs, sample=None):
     w = wl.WORKLOADS[index]
     A, B, bias = wl.workload_inputs(index)
