@@ -15,6 +15,8 @@ wave-quantisation case); the other four workloads are reported under
                   [--fresh | --cache FILE]   # tune now, or load a tuning cache
                                              # (default: the persisted MI355X one)
                   [--cache-out FILE]         # with --report: save the exhaustive tuning
+                  [--buckets]  # also: shape-bucket dispatch against per-M tuning
+                               # on the decode weights (M = 1 .. 256)
 
 The per-shape configurations come from the persisted tuning cache when it is
 present (the exhaustive measured autotune of every workload on MI355X, in the
@@ -234,6 +236,62 @@ def report(indices, torch, dump_dir=None, cache_out=None):
     return out, hits
 
 
+BUCKET_MS = (1, 2, 3, 5, 8, 13, 16, 17, 24, 32, 40, 48, 56, 64, 80, 100, 128, 160, 200, 256)
+
+
+def bucket_report(torch, steps):
+    """Run-time dispatch over shape buckets on the decode weights (N = 28672,
+    K = 8192, bf16): for each M, the time per call with the configuration of
+    M's bucket (tuned once per bucket, at its largest M) and with a
+    configuration tuned for M itself, and how many tuning runs each needed.
+    Weights rotate through two copies, as in the decode workload."""
+    import tile_shape_autotuning_amd as tg
+    N, K = 28672, 8192
+    A, B, bias = wl.make_inputs(max(BUCKET_MS), N, K, wl.BF16, wl.Dist("normal"), wl.Dist("normal"),
+                                wl.Dist("normal"), 5)
+    A_d, bias_d = _dev(A, torch), _dev(bias, torch)
+    Bs = [_dev(B, torch)]
+    Bs.append(Bs[0].clone())
+    rows = {M: {"M": M, "key": None} for M in BUCKET_MS}
+    tunes = {}
+    try:
+        for mode in ("bucketed", "exact"):
+            tg.set_shape_buckets(mode == "bucketed")
+            tg.cache_clear()
+            t0 = tg.stats()["tunes"]
+            for M in BUCKET_MS:
+                a = A_d[:M]
+                C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                calls = [tg.BoundGemm(a, b, bias_d, act="none", out=C) for b in Bs]   # the first tunes
+                for c in calls:
+                    c()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(steps):
+                    calls[i % 2]()
+                e1.record()
+                torch.cuda.synchronize()
+                key = tg.dispatch_m(M)
+                cfg = tg.cache_lookup(key, N, K, wl.BF16)[0].astuple()
+                rows[M][mode + "_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 3)
+                rows[M][mode + "_cfg"] = list(cfg)
+                if mode == "bucketed":
+                    rows[M]["key"] = key
+                log(f"buckets {mode} M={M}: {rows[M][mode + '_us']} us cfg {cfg}")
+            tunes[mode] = tg.stats()["tunes"] - t0
+    finally:
+        tg.set_shape_buckets(True)
+        tg.cache_clear()
+    out = list(rows.values())
+    for r in out:
+        r["bucketed_over_exact"] = round(r["bucketed_us"] / r["exact_us"], 3)
+    ratios = [r["bucketed_over_exact"] for r in out]
+    return {"shape": f"M x {N} x {K} bf16", "tunings": tunes, "rows": out,
+            "geomean_bucketed_over_exact": round(float(np.exp(np.mean(np.log(ratios)))), 4),
+            "max_bucketed_over_exact": max(ratios)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +307,8 @@ def main():
                     help="tune from scratch instead of loading the persisted tuning cache")
     ap.add_argument("--cache", type=str, default=DEFAULT_CACHE, help="tuning cache file to load")
     ap.add_argument("--cache-out", type=str, default="", help="with --report: save the exhaustive tuning here")
+    ap.add_argument("--buckets", action="store_true",
+                    help="also report shape-bucket dispatch against per-M tuning on the decode weights")
     ap.add_argument("--cfg", type=str, default="",
                     help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
@@ -334,6 +394,8 @@ def main():
         rep, hits = report([i for i in indices], torch, a.dump, a.cache_out or None)
         line["report"] = rep
         line["model_hit_rate"] = f"{hits}/{len(indices)}"
+    if a.buckets:
+        line["buckets"] = bucket_report(torch, 100)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(main_idx)

@@ -114,7 +114,9 @@ int tg_set_stream(void *hip_stream);
  * set with tg_set_stream.  Asynchronous: returns once the kernel is queued,
  * except that cfg == NULL with a shape not yet in the tuning cache first runs
  * gemm_autotune (blocking), or takes the cost model's choice when the
- * environment variable TILEGEMM_DISABLE_AUTOTUNE=1 is set.
+ * environment variable TILEGEMM_DISABLE_AUTOTUNE=1 is set.  With cfg == NULL
+ * the cache is keyed on M's shape bucket (tg_dispatch_m): one tuning serves
+ * every M of the bucket.
  *   M, N >= 0, K >= 0 (M or N = 0: nothing to do; K = 0: C = act(bias)).
  *   A, B, C: device pointers, 16-byte aligned for the tiled and skinny kinds.
  *   bias: device pointer to N floats, or NULL.
@@ -132,6 +134,24 @@ int tg_set_stream(void *hip_stream);
  */
 int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   const float *bias, void *C, int dtype, int act, const tg_cfg *cfg);
+
+/*
+ * Run-time dispatch over shape buckets (page "Tile Selection: Cost Models
+ * Against Measurement", "Hybrid strategies": a few tuned variants selected at
+ * launch from the actual extents, so that a varying batch does not make every
+ * request a new cache key, a miss and a re-tune).  With buckets on (the
+ * default; TILEGEMM_SHAPE_BUCKETS=0 starts the process with them off), a
+ * gemm_bias_act call without cfg uses the cache entry of key_m: M rounded up
+ * to a multiple of 16 for 1 <= M <= 64, to 128 for 64 < M <= 128, to 256 for
+ * 128 < M <= 256, M itself otherwise; that entry is tuned at key_m, the
+ * bucket's largest M, whose configuration is feasible for every M of the
+ * bucket.  gemm_autotune and explicit cfgs are not affected.
+ * tg_set_shape_buckets: on != 0 switches buckets on, 0 off (process-wide).
+ * tg_dispatch_m: the M a call without cfg is keyed on now; TG_E_INVAL for
+ * M < 0 or a NULL key_m.
+ */
+int tg_set_shape_buckets(int on);
+int tg_dispatch_m(int64_t M, int64_t *key_m);
 
 /*
  * Choose a configuration for (M, N, K, dtype) on the current device and store

@@ -487,6 +487,21 @@ def model_choice(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):
     return best, best_t
 
 
+def bucket_m(M: int) -> int:
+    """The M a dispatch without an explicit configuration is keyed and tuned
+    on (page "Tile Selection: Cost Models Against Measurement", "Hybrid
+    strategies": a few tuned variants picked at launch from the real extents;
+    "Selection is per device, and devices change": small batches need their
+    own tiles).  My reading: row counts up to 64 round up to the 16-row MFMA
+    tile, 65..128 share 128, 129..256 share 256, larger M are their own key."""
+    if M < 1 or M > 256:
+        return M
+    for top in (16, 32, 48, 64, 128, 256):
+        if M <= top:
+            return top
+    raise AssertionError("unreachable")
+
+
 def default_cfg(N: int, K: int, dtype: int) -> Cfg:
     """The fixed configuration autotuning is always compared against."""
     if not shape_aligned(N, K, dtype):

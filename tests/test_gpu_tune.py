@@ -93,3 +93,43 @@ def test_cache_roundtrip_on_device(tmp_path, monkeypatch):
     assert tg.cache_load(p) == (1, 0)
     hit = tg.cache_lookup(256, 256, 256, wl.F32)
     assert hit is not None and hit[0].astuple() == c.astuple() and hit[1] > 0
+
+
+def test_shape_buckets_one_tuning_per_bucket(monkeypatch):
+    # page "Tile Selection: Cost Models Against Measurement", "Hybrid strategies": a varying
+    # batch is served by a few tuned variants picked from the real extents, not re-tuned per M
+    monkeypatch.setenv("TILEGEMM_TUNE_MODE", "hybrid")
+    monkeypatch.setenv("TILEGEMM_TUNE_TOPK", "4")
+    N, K, dtype = 2048, 1024, wl.BF16
+    rng_seed = 11
+
+    def run(M):
+        A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("normal"), wl.Dist("normal"), wl.Dist("normal"),
+                                    rng_seed + M)
+        mark(f"bucketed dispatch M={M}")
+        C = tg.gemm_bias_act(to_dev(A), to_dev(B), to_dev(bias), act="relu")
+        torch.cuda.synchronize()
+        assert_close(out_f64(C), gemm_ref.gemm(A, B, bias, "relu"), dtype, f"bucketed M={M}")
+
+    try:
+        tg.set_shape_buckets(True)
+        tg.cache_clear()
+        s0 = tg.stats()
+        for M in (17, 20, 25, 32):
+            assert tg.dispatch_m(M) == 32
+            run(M)
+        s1 = tg.stats()
+        assert s1["tunes"] == s0["tunes"] + 1, "one tuning for the whole bucket"
+        assert s1["cache_hits"] == s0["cache_hits"] + 3
+        assert tg.cache_lookup(32, N, K, dtype) is not None and tg.cache_lookup(20, N, K, dtype) is None
+        # buckets off: every M is its own key
+        tg.set_shape_buckets(False)
+        tg.cache_clear()
+        s2 = tg.stats()
+        for M in (20, 25):
+            assert tg.dispatch_m(M) == M
+            run(M)
+        assert tg.stats()["tunes"] == s2["tunes"] + 2
+    finally:
+        tg.set_shape_buckets(True)
+        tg.cache_clear()

@@ -239,6 +239,21 @@ def test_model_mode_tuning_and_cache_roundtrip(tmp_path, monkeypatch):
     N.cache_clear()
 
 
+def test_dispatch_keys_follow_the_oracle_buckets():
+    try:
+        N.set_shape_buckets(True)
+        for M in range(0, 600):
+            assert N.dispatch_m(M) == S.bucket_m(M), M
+        N.set_shape_buckets(False)
+        for M in (1, 3, 17, 100, 257):
+            assert N.dispatch_m(M) == M
+    finally:
+        N.set_shape_buckets(True)
+    with pytest.raises(N.TileGemmError) as e:
+        N.dispatch_m(-1)
+    assert e.value.status == N.TG_E_INVAL
+
+
 def test_measured_tuning_needs_a_device(monkeypatch):
     monkeypatch.setenv("TILEGEMM_TUNE_MODE", "hybrid")
     N.cache_clear()

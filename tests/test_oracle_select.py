@@ -278,3 +278,27 @@ def test_choice_tie_break_is_first_in_canonical_order():
     best, bt = S.model_choice(4100, 3000, 1000, S.BF16)
     ties = [c for c in feas if S.model_time(4100, 3000, 1000, S.BF16, c) == bt]
     assert best == ties[0]
+
+
+def test_shape_buckets():
+    # a handful of keys for every batch size a decode step can have
+    keys = [S.bucket_m(M) for M in range(1, 257)]
+    assert sorted(set(keys)) == [16, 32, 48, 64, 128, 256]
+    assert all(k >= M for M, k in zip(range(1, 257), keys))           # tuned at the bucket's largest M
+    assert all(S.bucket_m(k) == k for k in set(keys))                  # a key is its own bucket
+    assert [S.bucket_m(M) for M in (1, 16, 17, 33, 48, 49, 64, 65, 128, 129, 256)] == \
+        [16, 16, 32, 48, 48, 64, 64, 128, 128, 256, 256]
+    assert [S.bucket_m(M) for M in (0, 257, 1000, 4100)] == [0, 257, 1000, 4100]   # exact keys
+
+
+@pytest.mark.parametrize("N,K,dt", [(28672, 8192, S.BF16), (1032, 1064, S.BF16_F32OUT), (1000, 8192, S.F32),
+                                    (33, 630, S.BF16)])
+def test_bucket_configuration_fits_every_m_of_the_bucket(N, K, dt):
+    # what is feasible at a bucket's key is feasible for every M the bucket serves
+    for key in (16, 32, 48, 64, 128, 256):
+        members = [M for M in range(1, 257) if S.bucket_m(M) == key]
+        feas = S.enumerate_feasible(key, N, K, dt)
+        assert feas
+        for c in feas:
+            for M in (members[0], members[len(members) // 2], members[-1]):
+                assert S.check(M, N, K, dt, c) == S.OK, (key, M, c)

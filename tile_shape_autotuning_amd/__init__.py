@@ -14,14 +14,14 @@ from ._native import (ACT, BF16, BF16_F32OUT, F32, Cfg, DeviceDesc, TileGemmErro
                       builtin_device_desc, cache_clear, cache_load, cache_lookup, cache_save, cache_size,
                       check_cfg, default_cfg, enumerate_feasible, gemm_autotune, get_device_desc, grid,
                       has_kernel, kernel_count, kernel_resources, model_choice, model_time_us, resources,
-                      set_device_override, space, stats)
+                      set_device_override, set_shape_buckets, dispatch_m, space, stats)
 
 __all__ = [
     "gemm_bias_act", "gemm_autotune", "Cfg", "DeviceDesc", "TileGemmError", "F32", "BF16", "BF16_F32OUT",
     "ACT", "enumerate_feasible", "space", "check_cfg", "model_time_us", "model_choice", "grid", "default_cfg",
     "resources", "builtin_device_desc", "set_device_override", "get_device_desc", "kernel_count",
     "has_kernel", "kernel_resources", "autotune_table", "cache_lookup", "cache_save", "cache_load",
-    "cache_clear", "cache_size", "stats", "dtype_code",
+    "cache_clear", "cache_size", "stats", "dtype_code", "set_shape_buckets", "dispatch_m",
 ]
 
 

@@ -26,7 +26,7 @@ EXPORTS = [
     "tg_default_cfg", "tg_resources", "tg_set_device_override", "tg_get_device_desc",
     "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources",
     "tg_autotune_table", "tg_cache_lookup", "tg_cache_save", "tg_cache_load", "tg_cache_clear",
-    "tg_cache_size", "tg_stats",
+    "tg_cache_size", "tg_stats", "tg_set_shape_buckets", "tg_dispatch_m",
 ]
 
 
@@ -116,6 +116,8 @@ def lib():
             "tg_cache_clear": ([], None),
             "tg_cache_size": ([], i32),
             "tg_stats": ([pi64, pi64, pi64], i32),
+            "tg_set_shape_buckets": ([i32], i32),
+            "tg_dispatch_m": ([i64, pi64], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -268,6 +270,18 @@ def cache_clear():
 
 def cache_size() -> int:
     return lib().tg_cache_size()
+
+
+def set_shape_buckets(on: bool):
+    """Key calls without a cfg on M's shape bucket (on) or on M itself (off)."""
+    check(lib().tg_set_shape_buckets(1 if on else 0))
+
+
+def dispatch_m(M: int) -> int:
+    """The M a call without a cfg is keyed and tuned on."""
+    k = ctypes.c_int64()
+    check(lib().tg_dispatch_m(int(M), ctypes.byref(k)))
+    return k.value
 
 
 def stats():

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -106,6 +107,16 @@ DeviceKey current_key()
         return di->key;
     return DeviceKey{"gfx950-nodevice", 256};
 }
+
+// ------------------------------------------------------------------ shape buckets
+// on unless TILEGEMM_SHAPE_BUCKETS=0; tg_set_shape_buckets switches it
+static std::atomic<int> g_buckets{[] {
+    const char* s = std::getenv("TILEGEMM_SHAPE_BUCKETS");
+    return (s && s[0] && std::strcmp(s, "0") == 0) ? 0 : 1;
+}()};
+
+// the M a dispatch without an explicit configuration is keyed (and tuned) on
+static int64_t dispatch_m(int64_t M) { return g_buckets.load() ? bucket_m(M) : M; }
 
 // ------------------------------------------------------------------ stream
 static thread_local hipStream_t t_stream = nullptr;
@@ -278,22 +289,47 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         c = *cfg;
     } else {
         from_selection = true;
+        // the cache entry of M's shape bucket: chosen (tuned) at the bucket's
+        // largest M, so one tuning serves the whole bucket
+        const int64_t Mk = dispatch_m(M);
         double us;
-        if (cache_find(M, N, K, dtype, &c, &us)) {
+        if (cache_find(Mk, N, K, dtype, &c, &us)) {
             count_cache_hit();
         } else {
             const char* dis = std::getenv("TILEGEMM_DISABLE_AUTOTUNE");
             if (dis && std::strcmp(dis, "0") != 0 && dis[0]) {
-                if (!model_choice(M, N, K, dtype, current_desc(), &c, nullptr))
+                if (!model_choice(Mk, N, K, dtype, current_desc(), &c, nullptr))
                     return set_error(TG_E_INFEASIBLE, "no feasible configuration");
             } else {
-                st = autotune(M, N, K, dtype, &c);
+                st = autotune(Mk, N, K, dtype, &c);
                 if (st != TG_OK)
                     return st;
             }
         }
+        // every rule that depends on M holds across a bucket (the skinny
+        // kind's row tile is M rounded up to 16, the same for the whole
+        // bucket); the check stays as a guard
+        if (Mk != M && check(M, N, K, dtype, c, current_desc()) != OK &&
+            !model_choice(M, N, K, dtype, current_desc(), &c, nullptr))
+            return set_error(TG_E_INFEASIBLE, "no feasible configuration");
     }
     return launch_cfg(M, N, K, A, B, bias, C, dtype, act, c, current_stream(), from_selection);
+}
+
+int tg_set_shape_buckets(int on)
+{
+    g_buckets.store(on ? 1 : 0);
+    return TG_OK;
+}
+
+int tg_dispatch_m(int64_t M, int64_t* key_m)
+{
+    if (!key_m)
+        return set_error(TG_E_INVAL, "key_m is NULL");
+    if (M < 0)
+        return set_error(TG_E_INVAL, "negative dimension");
+    *key_m = dispatch_m(M);
+    return TG_OK;
 }
 
 int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)

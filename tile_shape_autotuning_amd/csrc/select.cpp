@@ -481,4 +481,21 @@ tg_cfg default_cfg(int64_t N, int64_t K, int dtype)
     return tg_cfg{TG_KIND_TILED, 128, 128, 64, 2, 2, 2, 1};
 }
 
+// Run-time dispatch over shape buckets (page "Tile Selection: Cost Models
+// Against Measurement", "Hybrid strategies": a few tuned variants chosen at
+// launch from the actual extents; "Selection is per device, and devices
+// change": the batch-1 tile is not the batch-32 tile, so the buckets are
+// narrow where M is small).  Up to 64 rows, M rounded up to the 16-row MFMA
+// tile (the rows a kernel computes are the same across the bucket, and the
+// skinny kind's row tile is exactly that); then 128 and 256.  A bucket's
+// entry is tuned at its largest M.
+int64_t bucket_m(int64_t M)
+{
+    if (M <= 0 || M > kBucketMaxM)
+        return M;
+    if (M <= 64)
+        return cdiv(M, (int64_t)16) * 16;
+    return M <= 128 ? 128 : 256;
+}
+
 }  // namespace tg

@@ -47,4 +47,10 @@ std::vector<tg_cfg> enumerate_feasible(int64_t M, int64_t N, int64_t K, int dtyp
 bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t);
 tg_cfg default_cfg(int64_t N, int64_t K, int dtype);
 
+// Shape buckets of the run-time dispatch: row counts up to kBucketMaxM share
+// the entry of their bucket's largest M (16, 32, 48, 64, 128, 256); larger M
+// keep their own.
+constexpr int64_t kBucketMaxM = 256;
+int64_t bucket_m(int64_t M);
+
 }  // namespace tg
