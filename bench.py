@@ -17,6 +17,8 @@ wave-quantisation case); the other four workloads are reported under
                   [--cache-out FILE]         # with --report: save the exhaustive tuning
                   [--buckets]  # also: shape-bucket dispatch against per-M tuning
                                # on the decode weights (M = 1 .. 256)
+                  [--rmsnorm]  # also: the occupancy-tuned RMS normalisation
+                               # (16384 x 8192 bf16) against the HBM roofline
 
 The per-shape configurations come from the persisted tuning cache when it is
 present (the exhaustive measured autotune of every workload on MI355X, in the
@@ -292,6 +294,43 @@ def bucket_report(torch, steps):
             "max_bucketed_over_exact": max(ratios)}
 
 
+def rmsnorm_report(torch, steps, rows=16384, n=8192):
+    """The second workload: RMS normalisation of rows x n bf16 with
+    occupancy-only tuning.  Time per call at each occupancy and with the
+    tuned one (HIP events, back-to-back calls), against the HBM roofline of
+    reading x and writing y once."""
+    import tile_shape_autotuning_amd as tg
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn((rows, n), device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    w = torch.randn(n, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    nbytes = 2 * rows * n * 2 + n * 2
+
+    def timed(occ):
+        for _ in range(3):
+            tg.rmsnorm(x, w, 1e-6, occupancy=occ, out=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            tg.rmsnorm(x, w, 1e-6, occupancy=occ, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    per = {occ: round(timed(occ), 3) for occ in (1, 2, 4, 8)}
+    t0 = tg.rmsnorm_tunes()
+    tuned_us = timed(0)
+    occ, tuner_us = tg.rmsnorm_cache_lookup(rows, n)
+    gbs = nbytes / (tuned_us * 1e-6) / 1e9
+    log(f"rmsnorm {rows}x{n}: per occupancy {per}, tuned occupancy {occ}: {tuned_us:.2f} us, {gbs:.0f} GB/s")
+    return {"shape": f"{rows} x {n} bf16", "us_per_occupancy": per, "tuned_occupancy": occ,
+            "tuning_runs": tg.rmsnorm_tunes() - t0, "tuned_us": round(tuned_us, 3),
+            "tuner_measured_us": round(tuner_us, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK, 4), "bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +348,8 @@ def main():
     ap.add_argument("--cache-out", type=str, default="", help="with --report: save the exhaustive tuning here")
     ap.add_argument("--buckets", action="store_true",
                     help="also report shape-bucket dispatch against per-M tuning on the decode weights")
+    ap.add_argument("--rmsnorm", action="store_true",
+                    help="also report the occupancy-tuned RMS normalisation against the HBM roofline")
     ap.add_argument("--cfg", type=str, default="",
                     help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
@@ -396,6 +437,8 @@ def main():
         line["model_hit_rate"] = f"{hits}/{len(indices)}"
     if a.buckets:
         line["buckets"] = bucket_report(torch, 100)
+    if a.rmsnorm:
+        line["rmsnorm"] = rmsnorm_report(torch, 50)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(main_idx)

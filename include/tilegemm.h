@@ -227,6 +227,35 @@ int tg_cache_size(void);
 /* Counters: tuning runs, timed launches, cache hits served by gemm_bias_act. */
 int tg_stats(int64_t *n_tunes, int64_t *n_timed_launches, int64_t *n_cache_hits);
 
+/* ---------------------------------------------------------------- RMS normalisation (occupancy-only tuning) */
+/*
+ * A memory-bound second kernel whose only tuned parameter is occupancy
+ * (page "CuTile Autotuning", "Quick Reference -- Occupancy-Only Autotune":
+ * normalisation kernels tune the resident workgroups per compute unit only;
+ * grid = CUs x occupancy; tune once per shape, cache, launch directly).
+ *   y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w
+ * x, y: device pointers to rows x n bf16 (row-major), w: n bf16; all three
+ * 16-byte aligned; fp32 arithmetic, each row reduced in a fixed order (the
+ * result does not depend on the occupancy).  Constraints: n a multiple of 8,
+ * 8 <= n <= 32768, 0 <= rows < 2^31 (TG_E_UNSUPPORTED otherwise), eps finite
+ * and >= 0 (TG_E_INVAL).
+ * tg_rmsnorm: occupancy 1, 2, 4 or 8 launches min(rows, CUs x occupancy)
+ *   workgroups that stride over the rows; 0 takes the cached choice for
+ *   (device, rows, n), tuning first on a miss (blocking).  Asynchronous on the
+ *   stream set with tg_set_stream otherwise.  rows = 0: nothing to do.
+ * tg_rmsnorm_autotune: times occupancies 1, 2, 4, 8 on scratch rows of the
+ *   shape (interleaved rounds of about 1 ms of back-to-back launches, median)
+ *   and caches the fastest; a cached shape returns at once.  Blocking;
+ *   allocates and frees its scratch.  Outputs may be NULL.
+ * tg_rmsnorm_cache_lookup: *hit = 1 with the cached occupancy and its
+ *   measured microseconds, else *hit = 0.  In-memory cache, per device.
+ * tg_rmsnorm_tunes: number of tuning runs so far (this process).
+ */
+int tg_rmsnorm(int64_t rows, int64_t n, const void *x, const void *w, void *y, float eps, int occupancy);
+int tg_rmsnorm_autotune(int64_t rows, int64_t n, int *occupancy, double *us);
+int tg_rmsnorm_cache_lookup(int64_t rows, int64_t n, int *occupancy, double *us, int *hit);
+int tg_rmsnorm_tunes(int64_t *n_tunes);
+
 #ifdef __cplusplus
 }
 #endif

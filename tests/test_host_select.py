@@ -254,6 +254,16 @@ def test_dispatch_keys_follow_the_oracle_buckets():
     assert e.value.status == N.TG_E_INVAL
 
 
+def test_rmsnorm_argument_checks_without_a_device():
+    assert N.rmsnorm_ptr(4, 12, 0, 0, 0, 1e-6, 1) == N.TG_E_UNSUPPORTED      # n not a multiple of 8
+    assert N.rmsnorm_ptr(4, 32776, 0, 0, 0, 1e-6, 1) == N.TG_E_UNSUPPORTED   # n above 32768
+    assert N.rmsnorm_ptr(-1, 16, 0, 0, 0, 1e-6, 1) == N.TG_E_INVAL
+    assert N.rmsnorm_ptr(4, 16, 0, 0, 0, 1e-6, 5) == N.TG_E_INVAL            # occupancy not 0/1/2/4/8
+    assert N.rmsnorm_ptr(4, 16, 0, 0, 0, float("nan"), 1) == N.TG_E_INVAL
+    assert N.rmsnorm_ptr(0, 16, 0, 0, 0, 1e-6, 0) == N.TG_OK                  # nothing to do
+    assert N.rmsnorm_ptr(4, 16, 0, 0, 0, 1e-6, 1) == N.TG_E_INVAL            # NULL operands
+
+
 def test_measured_tuning_needs_a_device(monkeypatch):
     monkeypatch.setenv("TILEGEMM_TUNE_MODE", "hybrid")
     N.cache_clear()

@@ -14,7 +14,8 @@ from ._native import (ACT, BF16, BF16_F32OUT, F32, Cfg, DeviceDesc, TileGemmErro
                       builtin_device_desc, cache_clear, cache_load, cache_lookup, cache_save, cache_size,
                       check_cfg, default_cfg, enumerate_feasible, gemm_autotune, get_device_desc, grid,
                       has_kernel, kernel_count, kernel_resources, model_choice, model_time_us, resources,
-                      set_device_override, set_shape_buckets, dispatch_m, space, stats)
+                      set_device_override, set_shape_buckets, dispatch_m, space, stats, rmsnorm_autotune,
+                      rmsnorm_cache_lookup, rmsnorm_tunes)
 
 __all__ = [
     "gemm_bias_act", "gemm_autotune", "Cfg", "DeviceDesc", "TileGemmError", "F32", "BF16", "BF16_F32OUT",
@@ -22,6 +23,7 @@ __all__ = [
     "resources", "builtin_device_desc", "set_device_override", "get_device_desc", "kernel_count",
     "has_kernel", "kernel_resources", "autotune_table", "cache_lookup", "cache_save", "cache_load",
     "cache_clear", "cache_size", "stats", "dtype_code", "set_shape_buckets", "dispatch_m",
+    "rmsnorm", "rmsnorm_autotune", "rmsnorm_cache_lookup", "rmsnorm_tunes",
 ]
 
 
@@ -109,5 +111,32 @@ def gemm_bias_act(A, B, bias=None, act="none", out=None, out_dtype=None, cfg=Non
         st = _native.gemm_bias_act_ptr(M, N, K, A.data_ptr(), B.data_ptr(),
                                        bias.data_ptr() if bias is not None else 0, out.data_ptr(),
                                        code, act, cfg)
+    _native.check(st)
+    return out
+
+
+def rmsnorm(x, w, eps=1e-6, occupancy=0, out=None):
+    """y = x / sqrt(mean(x^2, row) + eps) * w on the GPU through libtilegemm.
+
+    x: [rows, n] bfloat16, w: [n] bfloat16 (contiguous, same device, n a
+    multiple of 8 up to 32768); occupancy: 1, 2, 4 or 8 workgroups per CU,
+    or 0 for the tuned choice (cached per shape).  Runs on the current stream
+    and returns y (bfloat16, like x).
+    """
+    import torch
+    if x.dim() != 2 or w.dim() != 1 or w.shape[0] != x.shape[1]:
+        raise ValueError(f"shape mismatch {tuple(x.shape)} / {tuple(w.shape)}")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bfloat16")
+    if not (x.is_cuda and w.is_cuda) or x.device != w.device or not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous tensors on the same GPU")
+    rows, n = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like x")
+    with torch.cuda.device(x.device):
+        _native.set_stream(torch.cuda.current_stream(x.device).cuda_stream)
+        st = _native.rmsnorm_ptr(rows, n, x.data_ptr(), w.data_ptr(), out.data_ptr(), eps, occupancy)
     _native.check(st)
     return out

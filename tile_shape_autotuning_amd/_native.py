@@ -27,6 +27,7 @@ EXPORTS = [
     "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources",
     "tg_autotune_table", "tg_cache_lookup", "tg_cache_save", "tg_cache_load", "tg_cache_clear",
     "tg_cache_size", "tg_stats", "tg_set_shape_buckets", "tg_dispatch_m",
+    "tg_rmsnorm", "tg_rmsnorm_autotune", "tg_rmsnorm_cache_lookup", "tg_rmsnorm_tunes",
 ]
 
 
@@ -118,6 +119,10 @@ def lib():
             "tg_stats": ([pi64, pi64, pi64], i32),
             "tg_set_shape_buckets": ([i32], i32),
             "tg_dispatch_m": ([i64, pi64], i32),
+            "tg_rmsnorm": ([i64, i64, vp, vp, vp, ctypes.c_float, i32], i32),
+            "tg_rmsnorm_autotune": ([i64, i64, pi, dp], i32),
+            "tg_rmsnorm_cache_lookup": ([i64, i64, pi, dp, pi], i32),
+            "tg_rmsnorm_tunes": ([pi64], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -281,6 +286,31 @@ def dispatch_m(M: int) -> int:
     """The M a call without a cfg is keyed and tuned on."""
     k = ctypes.c_int64()
     check(lib().tg_dispatch_m(int(M), ctypes.byref(k)))
+    return k.value
+
+
+def rmsnorm_ptr(rows: int, n: int, x: int, w: int, y: int, eps: float, occupancy: int) -> int:
+    """Raw C-ABI call on device pointers; returns the status."""
+    return lib().tg_rmsnorm(int(rows), int(n), x or None, w or None, y or None, float(eps), int(occupancy))
+
+
+def rmsnorm_autotune(rows: int, n: int):
+    """(occupancy, measured us) chosen for the shape; tunes on a cache miss."""
+    occ, us = ctypes.c_int(), ctypes.c_double()
+    check(lib().tg_rmsnorm_autotune(int(rows), int(n), ctypes.byref(occ), ctypes.byref(us)))
+    return occ.value, us.value
+
+
+def rmsnorm_cache_lookup(rows: int, n: int):
+    """(occupancy, measured us) if the shape is cached on the current device, else None."""
+    occ, us, hit = ctypes.c_int(), ctypes.c_double(), ctypes.c_int()
+    check(lib().tg_rmsnorm_cache_lookup(int(rows), int(n), ctypes.byref(occ), ctypes.byref(us), ctypes.byref(hit)))
+    return (occ.value, us.value) if hit.value else None
+
+
+def rmsnorm_tunes() -> int:
+    k = ctypes.c_int64()
+    check(lib().tg_rmsnorm_tunes(ctypes.byref(k)))
     return k.value
 
 

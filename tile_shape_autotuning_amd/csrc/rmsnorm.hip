@@ -1,0 +1,348 @@
+// RMS normalisation with occupancy-only autotuning (page "CuTile Autotuning",
+// "Quick Reference -- Occupancy-Only Autotune": memory-bound kernels such as
+// normalisations tune nothing but the number of resident workgroups per
+// compute unit; the grid is CUs x occupancy, the winner is cached per shape
+// and launched directly afterwards).
+//
+//     y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w      (bf16 in/out, fp32 math)
+//
+// One 256-thread workgroup normalises one row at a time and strides over the
+// rows (grid = min(rows, CUs x occupancy)).  A thread holds CPT 16-byte
+// chunks of the row in registers, so x is read once: HBM traffic is
+// 2 x rows x n x 2 bytes plus the weights.  The sum of squares is reduced in a
+// fixed order (chunks, then a butterfly over the wave, then the four waves in
+// order), so a row's result does not depend on the grid or on which
+// workgroup normalised it.  A workgroup loads the next row while it reduces
+// and stores the current one; occupancy sets how many rows are in flight
+// beyond that, which is what hides the HBM latency.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "kernels/common.hpp"
+#include "runtime.hpp"
+
+namespace tg {
+
+static constexpr int kNormThreads = 256;
+static constexpr int kNormMaxCpt = 16;              // n <= 256 x 8 x 16 = 32768
+
+__device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+template <int CPT>
+__global__ void __launch_bounds__(kNormThreads)
+rmsnorm_kernel(const u32x4_t* x, const u32x4_t* w, u32x4_t* y, int rows, int n, float eps)
+{
+    __shared__ float part[kNormThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nch = n / 8;                          // 16-byte chunks per row
+    u32x4_t wv[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int c = tid + k * kNormThreads;
+        wv[k] = c < nch ? w[c] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    const float inv_n = 1.0f / (float)n;
+    // the next row's loads are issued before this row is reduced and stored,
+    // so a workgroup keeps two rows in flight
+    auto load_row = [&](int64_t r, u32x4_t (&v)[CPT]) {
+        const u32x4_t* xr = x + (int64_t)r * nch;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int c = tid + k * kNormThreads;
+            v[k] = c < nch ? xr[c] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    u32x4_t xv[CPT], xn[CPT];
+    if (blockIdx.x < rows)
+        load_row(blockIdx.x, xv);
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        if (r + gridDim.x < rows)
+            load_row(r + gridDim.x, xn);
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = bf16_lo(xv[k][e]), b = bf16_hi(xv[k][e]);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            ss += __shfl_xor(ss, off);
+        if (lane == 0)
+            part[wave] = ss;
+        __syncthreads();
+        float total = part[0];
+#pragma unroll
+        for (int q = 1; q < kNormThreads / 64; ++q)
+            total += part[q];
+        __syncthreads();                            // part[] is rewritten by the next row
+        const float scale = 1.0f / sqrtf(total * inv_n + eps);
+        u32x4_t* yr = y + r * nch;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int c = tid + k * kNormThreads;
+            if (c < nch) {
+                u32x4_t o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_lo(xv[k][e]) * scale * bf16_lo(wv[k][e]);
+                    const float hi = bf16_hi(xv[k][e]) * scale * bf16_hi(wv[k][e]);
+                    o[e] = (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
+                }
+                yr[c] = o;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+            xv[k] = xn[k];
+    }
+}
+
+static int norm_cpt(int64_t n)
+{
+    const int64_t chunks = (n / 8 + kNormThreads - 1) / kNormThreads;
+    int cpt = 1;
+    while (cpt < chunks)
+        cpt *= 2;
+    return cpt;
+}
+
+static hipError_t launch_norm(int64_t rows, int64_t n, const void* x, const void* w, void* y, float eps, int occ,
+                              int n_cu, hipStream_t s)
+{
+    const int grid = (int)std::min<int64_t>(rows, (int64_t)n_cu * occ);
+    const auto* xp = static_cast<const u32x4_t*>(x);
+    const auto* wp = static_cast<const u32x4_t*>(w);
+    auto* yp = static_cast<u32x4_t*>(y);
+    const int r = (int)rows, nn = (int)n;
+    switch (norm_cpt(n)) {
+    case 1: hipLaunchKernelGGL(rmsnorm_kernel<1>, dim3(grid), dim3(kNormThreads), 0, s, xp, wp, yp, r, nn, eps); break;
+    case 2: hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(grid), dim3(kNormThreads), 0, s, xp, wp, yp, r, nn, eps); break;
+    case 4: hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(grid), dim3(kNormThreads), 0, s, xp, wp, yp, r, nn, eps); break;
+    case 8: hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3(grid), dim3(kNormThreads), 0, s, xp, wp, yp, r, nn, eps); break;
+    default: hipLaunchKernelGGL(rmsnorm_kernel<16>, dim3(grid), dim3(kNormThreads), 0, s, xp, wp, yp, r, nn, eps); break;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- tuning cache (in memory)
+struct NormEntry {
+    int occupancy;
+    double us;
+};
+using NormKey = std::tuple<int, int64_t, int64_t>;   // device ordinal, rows, n
+static std::mutex g_norm_mu;
+static std::map<NormKey, NormEntry> g_norm_cache;
+static int64_t g_norm_tunes = 0;
+
+static constexpr int kOccupancies[4] = {1, 2, 4, 8};
+
+static int norm_validate(int64_t rows, int64_t n)
+{
+    if (rows < 0 || n < 1)
+        return set_error(TG_E_INVAL, "rows must be >= 0 and n >= 1");
+    if (n % 8 != 0 || n > (int64_t)kNormThreads * 8 * kNormMaxCpt || rows > 0x7FFFFFFF)
+        return set_error(TG_E_UNSUPPORTED, "n must be a multiple of 8 and at most 32768, rows below 2^31");
+    return TG_OK;
+}
+
+static int device_cus(int* dev, int* n_cu)
+{
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess)
+        return set_hip_error(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, *dev);
+    if (e != hipSuccess)
+        return set_hip_error(e, "hipDeviceGetAttribute");
+    return TG_OK;
+}
+
+static int norm_tune(int64_t rows, int64_t n, int dev, int n_cu, NormEntry* out)
+{
+    // scratch rows of the problem's size; values do not change the timing of
+    // this kernel beyond their bytes
+    void *x = nullptr, *w = nullptr, *y = nullptr;
+    const size_t xb = (size_t)rows * (size_t)n * 2;
+    hipError_t e;
+    auto release = [&] {
+        if (x) (void)hipFree(x);
+        if (w) (void)hipFree(w);
+        if (y) (void)hipFree(y);
+    };
+    if ((e = hipMalloc(&x, xb)) != hipSuccess || (e = hipMalloc(&w, (size_t)n * 2)) != hipSuccess ||
+        (e = hipMalloc(&y, xb)) != hipSuccess) {
+        release();
+        return set_error(TG_E_NOMEM, std::string("rmsnorm tuning scratch: ") + hipGetErrorString(e));
+    }
+    hipStream_t s = current_stream();
+    if ((e = fill_uniform(x, rows * n, 1, 0x9e37u, s)) != hipSuccess ||
+        (e = fill_uniform(w, n, 1, 0x7f4au, s)) != hipSuccess) {
+        release();
+        return set_hip_error(e, "rmsnorm tuning scratch fill");
+    }
+    hipEvent_t e0, e1;
+    if ((e = hipEventCreate(&e0)) != hipSuccess || (e = hipEventCreate(&e1)) != hipSuccess) {
+        release();
+        return set_hip_error(e, "hipEventCreate");
+    }
+    // interleaved rounds of back-to-back launches, about 1 ms per sample; median
+    const int rounds = 7;
+    std::vector<double> samples[4];
+    int reps = 0;
+    for (int round = -1; round < rounds && e == hipSuccess; ++round) {
+        for (int i = 0; i < 4 && e == hipSuccess; ++i) {
+            const int occ = kOccupancies[i];
+            if (round < 0) {                          // warm-up, and size the samples on occupancy 1
+                for (int k = 0; k < 3 && e == hipSuccess; ++k)
+                    e = launch_norm(rows, n, x, w, y, 1e-6f, occ, n_cu, s);
+                if (i == 0 && e == hipSuccess) {
+                    (void)hipEventRecord(e0, s);
+                    e = launch_norm(rows, n, x, w, y, 1e-6f, occ, n_cu, s);
+                    (void)hipEventRecord(e1, s);
+                    (void)hipEventSynchronize(e1);
+                    float ms = 0.0f;
+                    (void)hipEventElapsedTime(&ms, e0, e1);
+                    reps = std::max(1, std::min(2000, (int)std::ceil(1000.0 / std::max(1.0, ms * 1e3))));
+                }
+                continue;
+            }
+            (void)hipEventRecord(e0, s);
+            for (int k = 0; k < reps && e == hipSuccess; ++k)
+                e = launch_norm(rows, n, x, w, y, 1e-6f, occ, n_cu, s);
+            (void)hipEventRecord(e1, s);
+            (void)hipEventSynchronize(e1);
+            float ms = 0.0f;
+            (void)hipEventElapsedTime(&ms, e0, e1);
+            samples[i].push_back(ms * 1e3 / reps);
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    const hipError_t sync = hipStreamSynchronize(s);
+    release();
+    if (e != hipSuccess)
+        return set_hip_error(e, "rmsnorm tuning launch");
+    if (sync != hipSuccess)
+        return set_hip_error(sync, "rmsnorm tuning");
+    NormEntry best{0, 0.0};
+    for (int i = 0; i < 4; ++i) {
+        std::vector<double> v = samples[i];
+        std::sort(v.begin(), v.end());
+        const double med = v[v.size() / 2];
+        if (best.occupancy == 0 || med < best.us)
+            best = NormEntry{kOccupancies[i], med};
+    }
+    *out = best;
+    std::lock_guard<std::mutex> lk(g_norm_mu);
+    g_norm_cache[NormKey{dev, rows, n}] = best;
+    ++g_norm_tunes;
+    return TG_OK;
+}
+
+}  // namespace tg
+
+using namespace tg;
+
+extern "C" {
+
+int tg_rmsnorm_autotune(int64_t rows, int64_t n, int* occupancy, double* us)
+{
+    int st = norm_validate(rows, n);
+    if (st != TG_OK)
+        return st;
+    if (rows == 0)
+        return set_error(TG_E_INVAL, "empty problem has nothing to tune");
+    if (!have_device())
+        return set_error(TG_E_UNSUPPORTED, "no HIP device");
+    int dev = 0, n_cu = 0;
+    if ((st = device_cus(&dev, &n_cu)) != TG_OK)
+        return st;
+    NormEntry ent{};
+    bool hit = false;
+    {
+        std::lock_guard<std::mutex> lk(g_norm_mu);
+        auto it = g_norm_cache.find(NormKey{dev, rows, n});
+        if (it != g_norm_cache.end()) {
+            ent = it->second;
+            hit = true;
+        }
+    }
+    if (!hit && (st = norm_tune(rows, n, dev, n_cu, &ent)) != TG_OK)
+        return st;
+    if (occupancy)
+        *occupancy = ent.occupancy;
+    if (us)
+        *us = ent.us;
+    return TG_OK;
+}
+
+int tg_rmsnorm(int64_t rows, int64_t n, const void* x, const void* w, void* y, float eps, int occupancy)
+{
+    int st = norm_validate(rows, n);
+    if (st != TG_OK)
+        return st;
+    if (occupancy != 0 && occupancy != 1 && occupancy != 2 && occupancy != 4 && occupancy != 8)
+        return set_error(TG_E_INVAL, "occupancy must be 0 (tuned), 1, 2, 4 or 8");
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return set_error(TG_E_INVAL, "eps must be finite and >= 0");
+    if (rows == 0)
+        return TG_OK;
+    if (!x || !w || !y)
+        return set_error(TG_E_INVAL, "NULL pointer");
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15u)
+        return set_error(TG_E_INVAL, "x, w and y must be 16-byte aligned");
+    if (!have_device())
+        return set_error(TG_E_UNSUPPORTED, "no HIP device");
+    int dev = 0, n_cu = 0;
+    if ((st = device_cus(&dev, &n_cu)) != TG_OK)
+        return st;
+    int occ = occupancy;
+    if (occ == 0 && (st = tg_rmsnorm_autotune(rows, n, &occ, nullptr)) != TG_OK)
+        return st;
+    const hipError_t e = launch_norm(rows, n, x, w, y, eps, occ, n_cu, current_stream());
+    if (e != hipSuccess)
+        return set_hip_error(e, "rmsnorm launch");
+    return TG_OK;
+}
+
+int tg_rmsnorm_cache_lookup(int64_t rows, int64_t n, int* occupancy, double* us, int* hit)
+{
+    if (!hit)
+        return set_error(TG_E_INVAL, "hit is NULL");
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        dev = 0;
+    std::lock_guard<std::mutex> lk(g_norm_mu);
+    auto it = g_norm_cache.find(NormKey{dev, rows, n});
+    *hit = it != g_norm_cache.end();
+    if (*hit) {
+        if (occupancy)
+            *occupancy = it->second.occupancy;
+        if (us)
+            *us = it->second.us;
+    }
+    return TG_OK;
+}
+
+int tg_rmsnorm_tunes(int64_t* n_tunes)
+{
+    if (!n_tunes)
+        return set_error(TG_E_INVAL, "n_tunes is NULL");
+    std::lock_guard<std::mutex> lk(g_norm_mu);
+    *n_tunes = g_norm_tunes;
+    return TG_OK;
+}
+
+}  // extern "C"
