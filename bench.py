@@ -118,7 +118,7 @@ def shape_summary(p, sec):
     if p.cfg is not None:
         cfg, meas = p.tg.Cfg.of(p.cfg), float("nan")
     else:
-        cfg, meas = p.tg.cache_lookup(w.M, w.N, w.K, w.dtype)
+        cfg, meas = p.tg.cache_lookup(p.tg.dispatch_m(w.M), w.N, w.K, w.dtype)   # the entry the call used
     return {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": wl.DTYPE_NAMES[w.dtype],
             "act": p.act, "us": round(sec * 1e6, 3), "TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 1),
             "bound": bound, "roofline_frac": round(frac, 4), "cfg": list(cfg.astuple()),
@@ -397,7 +397,7 @@ def main():
             p.step()
         torch.cuda.synchronize()
         steps = a.steps if i == main_idx else max(10, min(a.steps, int(0.3 / max(1e-6, p.tg.cache_lookup(
-            p.w.M, p.w.N, p.w.K, p.w.dtype)[1] * 1e-6))))
+            p.tg.dispatch_m(p.w.M), p.w.N, p.w.K, p.w.dtype)[1] * 1e-6))))
         sec, wall = time_steps(p, steps, torch)
         s = shape_summary(p, sec)
         s["steps"] = steps
