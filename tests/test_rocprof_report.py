@@ -135,3 +135,8 @@ def test_split_k_calls_count_both_launches(tmp_path):
     text, _ = R.counters_text("w", (0, 128, 64, 64, 2, 2, 3, 4), "gemm_tiled_dma_kernel", tr, [], fetch, write,
                               copy_bytes, 1.0e12, 0, ["cmd"], 131072, ("splitk_reduce", 250112))
     assert "per call (both launches):   35.000 us" in text
+
+
+def test_observed_clock_from_busy_cycles():
+    # 8 XCDs busy 2.0e6 cycles each over a 1 ms kernel: 2.0 GHz
+    assert R.observed_clock_ghz({"GRBM_GUI_ACTIVE": 8 * 2.0e6}, 1000.0) == pytest.approx(2.0)

@@ -130,6 +130,12 @@ def summary(trace_dir, pmc_dirs=(), fetch_dir=None, write_dir=None, copy_bytes=0
     return out
 
 
+def observed_clock_ghz(ctrs, avg_us, xcds=8):
+    """Shader clock while the kernel ran: GRBM_GUI_ACTIVE (summed over the
+    XCDs) per XCD, over the kernel's average duration."""
+    return ctrs["GRBM_GUI_ACTIVE"] / xcds / (avg_us * 1e-6) / 1e9
+
+
 def hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel="gemm"):
     """HBM bytes per dispatch of the kernel, from FETCH_SIZE and WRITE_SIZE (KiB),
     each scaled so that a plain copy of copy_bytes reads and writes exactly
@@ -201,6 +207,8 @@ def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_di
         lines.append(f"MFMA busy / (4 x CU busy):  {sm['mfma_util']:.3f}")
     if c.get("GRBM_GUI_ACTIVE") and c.get("SQ_BUSY_CU_CYCLES"):
         lines.append(f"busy CUs (CU-busy / GPU-busy cycles, 8 XCDs): {c['SQ_BUSY_CU_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / 8):.0f}")
+    if c.get("GRBM_GUI_ACTIVE"):
+        lines.append(f"observed clock (GPU-busy cycles per XCD / duration): {observed_clock_ghz(c, sm['avg_us']):.2f} GHz")
     if "lds_conflict_cycles_per_lds_inst" in sm:
         lines.append(f"LDS bank-conflict cycles per LDS instruction: {sm['lds_conflict_cycles_per_lds_inst']:.2f}")
     if "wait_any_frac" in sm:
