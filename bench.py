@@ -17,8 +17,10 @@ wave-quantisation case); the other four workloads are reported under
                   [--cache-out FILE]         # with --report: save the exhaustive tuning
                   [--buckets]  # also: shape-bucket dispatch against per-M tuning
                                # on the decode weights (M = 1 .. 256)
-                  [--rmsnorm]  # also: the occupancy-tuned RMS normalisation
-                               # (16384 x 8192 bf16) against the HBM roofline
+                  [--no-rmsnorm]  # skip the second workload: the occupancy-tuned
+                                  # RMS normalisation (16384 x 8192 bf16) against
+                                  # the HBM roofline, reported under "rmsnorm"
+                  [--rmsnorm]     # report it also with --only
 
 The per-shape configurations come from the persisted tuning cache when it is
 present (the exhaustive measured autotune of every workload on MI355X, in the
@@ -349,7 +351,8 @@ def main():
     ap.add_argument("--buckets", action="store_true",
                     help="also report shape-bucket dispatch against per-M tuning on the decode weights")
     ap.add_argument("--rmsnorm", action="store_true",
-                    help="also report the occupancy-tuned RMS normalisation against the HBM roofline")
+                    help="report the occupancy-tuned RMS normalisation also with --only")
+    ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMS normalisation report")
     ap.add_argument("--cfg", type=str, default="",
                     help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
@@ -437,7 +440,7 @@ def main():
         line["model_hit_rate"] = f"{hits}/{len(indices)}"
     if a.buckets:
         line["buckets"] = bucket_report(torch, 100)
-    if a.rmsnorm:
+    if (a.rmsnorm or not a.only) and not a.no_rmsnorm:
         line["rmsnorm"] = rmsnorm_report(torch, 50)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
