@@ -244,7 +244,7 @@ def test_per_cu_model_terms():
     base = S.Cfg(S.KIND_TILED, 64, 64, 32, 2, 2, 2, 1)
     deeper = S.Cfg(S.KIND_TILED, 64, 64, 32, 2, 2, 4, 1)
     assert S.model_time(1000, 1000, 8192, S.BF16, deeper, d) <= S.model_time(1000, 1000, 8192, S.BF16, base, d)
-    # split-K costs the reducer's reads and a round trip through memory
+    # split-K costs the slab writes and the second pass
     s1 = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
     s2 = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 2)
     t_no = S.model_time(8192, 8192, 8192, S.BF16, s1, d)

@@ -17,8 +17,9 @@
 // Languages", "Workshop" (HBM traffic divided by g, compute divided by wave
 // efficiency and tile efficiency, time = the larger).  The H100 replica mode
 // reproduces that page's model; the MI355X mode adds the CU/SIMD occupancy,
-// pipeline-fill and split-K workspace terms.  Every expression below is in
-// the same order as the selection rules the tests compare against.
+// pipeline-fill, output-store and split-K (slabs, second pass) terms.  Every
+// expression below is in the same order as the selection rules the tests
+// compare against.
 #include "select.hpp"
 
 #include <algorithm>
