@@ -426,7 +426,8 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
       * their L2-to-CU traffic (rows narrower than a cache line cost a line),
       * the memory latency divided by the pipeline depth (stages - 1
         transfers in flight; page "Tiling the hierarchy", double buffering),
-    and a lone wave on a SIMD issues everything in order (w1_eff).  Blocks run
+    and a lone wave on a SIMD issues its MFMAs and LDS reads in order
+    (w1_eff; the global-to-LDS transfers run without it).  Blocks run
     in rounds of n_cu x resident (wave quantisation; the partial last round
     spreads its blocks); each round starts with one latency.  The chip-wide
     HBM time of the traffic bounds it from below (with split-K that traffic
@@ -447,9 +448,10 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
 
     def step(res: int) -> float:
         busy = min(dev.simds, res * w)
-        t = max(res * f_step / (simd_peak * busy), res * lds_step / dev.lds_bw_cu,
-                res * l2_step / dev.cu_bw, lat / depth)
-        return t / dev.w1_eff if res * w <= dev.simds else t
+        issue = max(res * f_step / (simd_peak * busy), res * lds_step / dev.lds_bw_cu)
+        if res * w <= dev.simds:
+            issue = issue / dev.w1_eff
+        return max(issue, res * l2_step / dev.cu_bw, lat / depth)
 
     slots = dev.n_cu * bcu
     full = units // slots

@@ -372,8 +372,9 @@ static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, con
 // per K step.  One K step of the blocks resident on a CU takes the longest of
 // their MFMA work on the SIMDs their waves occupy, their LDS traffic, their
 // L2-to-CU traffic (rows narrower than a cache line cost a line) and the
-// memory latency over the pipeline depth; a lone wave on a SIMD issues all of
-// it in order (w1_eff).  Blocks run in rounds of n_cu x resident, the partial
+// memory latency over the pipeline depth; a lone wave on a SIMD issues its
+// MFMAs and LDS reads in order (w1_eff; the global-to-LDS transfers run
+// without it).  Blocks run in rounds of n_cu x resident, the partial
 // last round spread out, each round starting with one latency; the HBM time of
 // the traffic bounds it from below (with split-K that traffic includes
 // writing the partial-sum slabs). The output stores come after each block's
@@ -397,11 +398,12 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
 
     auto step = [&](int64_t res) {
         const int64_t busy = std::min<int64_t>(d.simds, res * w);
-        double t = (double)res * f_step / (simd_peak * (double)busy);
-        t = std::max(t, (double)res * lds_step / d.lds_bw_cu);
-        t = std::max(t, (double)res * l2_step / d.cu_bw);
-        t = std::max(t, lat / (double)depth);
-        return res * w <= d.simds ? t / d.w1_eff : t;
+        double issue = (double)res * f_step / (simd_peak * (double)busy);
+        issue = std::max(issue, (double)res * lds_step / d.lds_bw_cu);
+        if (res * w <= d.simds)
+            issue = issue / d.w1_eff;
+        double t = std::max(issue, (double)res * l2_step / d.cu_bw);
+        return std::max(t, lat / (double)depth);
     };
     const int64_t slots = (int64_t)d.n_cu * bcu;
     const int64_t full = units / slots;
