@@ -132,27 +132,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 DEFAULT_CACHE = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "mi355x.cache")
 
 
-def library_digest():
-    import hashlib
-    from tile_shape_autotuning_amd import _native
-    with open(_native.LIB_PATH, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
 def measured_traffic(workload, cfg):
-    """HBM bytes per launch recorded by the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs for this workload and configuration -- only if they were taken on
-    the library that is loaded now (else the kernel may have changed: None)."""
+    """HBM bytes per call recorded by the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs for this workload and configuration -- only if they were taken with
+    the kernel sources, launch path and compile flags of this tree (else the
+    kernel may have changed: None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    digest = library_digest()
+    from tile_shape_autotuning_amd.build_lib import kernel_source_digest
+    digest = kernel_source_digest()
     want = ",".join(str(x) for x in cfg)
     with open(TRAFFIC_FILE) as f:
         for line in f:
             if not line.startswith("traffic "):
                 continue
             kv = dict(t.split("=", 1) for t in line.split()[1:])
-            if kv.get("workload") == workload and kv.get("cfg") == want and kv.get("lib_sha256") == digest:
+            if kv.get("workload") == workload and kv.get("cfg") == want and kv.get("kernel_src_sha256") == digest:
                 return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
     return None
 
