@@ -91,6 +91,30 @@ def test_hbm_traffic_scaled_by_the_copy_calibration(tmp_path):
     assert t["bytes"] == pytest.approx(1000.0 * 1024 * 2.0 + 300.0 * 1024)
 
 
+def test_copy_calibration_ignores_smaller_copies_of_the_same_kernel(tmp_path):
+    # three calibration copies of 1 GiB plus the program's own 470 MB copy under
+    # the same kernel name: the scale comes from the calibration copies alone
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    copy_bytes = 1 << 30
+    half = copy_bytes / 1024 / 2
+    fetch_rows = [(COPY, 1, "FETCH_SIZE", half + 8), (COPY, 2, "FETCH_SIZE", half),
+                  (COPY, 3, "FETCH_SIZE", half), (COPY, 4, "FETCH_SIZE", 229406.0),
+                  (GEMM, 5, "FETCH_SIZE", 1000.0), (GEMM, 6, "FETCH_SIZE", 1002.0)]
+    # per-instance rows of one dispatch add up
+    write_rows = [(COPY, 1, "WRITE_SIZE", copy_bytes / 2048), (COPY, 1, "WRITE_SIZE", copy_bytes / 2048),
+                  (COPY, 4, "WRITE_SIZE", 450000.0), (GEMM, 5, "WRITE_SIZE", 300.0)]
+    _pmc_db(fetch, fetch_rows)
+    _pmc_db(write, write_rows)
+    t = R.hbm_traffic(fetch, write, copy_bytes, kernel="gemm")
+    assert t["FETCH_SIZE"]["scale"] == pytest.approx(2.0)
+    assert t["FETCH_SIZE"]["kib_raw"] == pytest.approx(1001.0)
+    assert t["WRITE_SIZE"]["scale"] == pytest.approx(1.0)
+    # a mean over every copy dispatch would have given a scale of about 2.3
+    per = R.dispatch_counters(fetch)
+    assert sorted(per[COPY]["FETCH_SIZE"])[0] == 229406.0
+    assert R.copy_calibration(per, "FETCH_SIZE") == pytest.approx(half)
+
+
 def test_missing_results_raise(tmp_path):
     with pytest.raises(FileNotFoundError):
         R.kernel_times(str(tmp_path / "nothing"))

@@ -64,15 +64,35 @@ def kernel_times(trace_dir, grid=None):
     return {k: (n, s / n) for k, (n, s) in acc.items()}
 
 
-def counters(pmc_dir):
-    """{kernel name: {counter: mean value per dispatch}}."""
+def dispatch_counters(pmc_dir):
+    """{kernel name: {counter: [value of each dispatch]}} (a counter's
+    per-instance values summed within a dispatch)."""
     acc = collections.defaultdict(lambda: collections.defaultdict(dict))
     for db in _dbs(pmc_dir):
         c = sqlite3.connect(db)
         q = "select kernel_name, dispatch_id, counter_name, value from counters_collection"
         for name, disp, ctr, val in c.execute(q):
             acc[name][ctr][(db, disp)] = acc[name][ctr].get((db, disp), 0.0) + float(val)
-    return {k: {ctr: sum(v.values()) / len(v) for ctr, v in d.items()} for k, d in acc.items()}
+    return {k: {ctr: list(v.values()) for ctr, v in d.items()} for k, d in acc.items()}
+
+
+def counters(pmc_dir):
+    """{kernel name: {counter: mean value per dispatch}}."""
+    return {k: {ctr: sum(v) / len(v) for ctr, v in d.items()}
+            for k, d in dispatch_counters(pmc_dir).items()}
+
+
+def copy_calibration(per_dispatch, counter):
+    """The counter's reading for the calibration copy: the median over the
+    largest copy dispatches (those within 10 % of the largest).  The program
+    may run smaller copies of its own under the same kernel name (a weight
+    replica, say); a mean over every dispatch of that name would mix them in."""
+    vals = [v for n, d in per_dispatch.items() if "copy" in n.lower() or "elementwise" in n.lower()
+            for v in d.get(counter, [])]
+    if not vals or max(vals) <= 0:
+        return 0.0
+    top = sorted(v for v in vals if v >= 0.9 * max(vals))
+    return top[len(top) // 2]
 
 
 def _pick(d, sub):
@@ -142,12 +162,12 @@ def hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel="gemm"):
     copy_bytes."""
     res = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        cs = counters(d)
+        per = dispatch_counters(d)
+        cs = {n: {c: sum(v) / len(v) for c, v in dd.items()} for n, dd in per.items()}
         k = next((n for n in cs if kernel in n), None)
-        copy = [n for n in cs if "copy" in n.lower() or "elementwise" in n.lower()]
-        if k is None or not copy:
+        copy_kib = copy_calibration(per, name)
+        if k is None or copy_kib <= 0:
             raise KeyError(f"{name}: kernel or copy calibration missing")
-        copy_kib = max(cs[n].get(name, 0.0) for n in copy)
         scale = (copy_bytes / 1024.0) / copy_kib if copy_kib > 0 else float("nan")
         res[name] = {"kib_raw": cs[k].get(name, 0.0), "copy_kib_raw": copy_kib, "scale": scale,
                      "bytes": cs[k].get(name, 0.0) * 1024.0 * scale}
