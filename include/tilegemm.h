@@ -209,6 +209,15 @@ int tg_has_kernel(int dtype, const tg_cfg *cfg);
  * TG_E_INFEASIBLE if no kernel serves cfg.  The autotuner skips kernels that
  * spill (set TILEGEMM_ALLOW_SPILLS=1 to keep them). */
 int tg_kernel_resources(int dtype, const tg_cfg *cfg, int *out5);
+/* Whether a call of M rows with cfg reads B with the non-temporal cache
+ * policy (*out = 1) or the default one (*out = 0).  B is streamed that way
+ * when every element of it is read by exactly one workgroup: the skinny kind
+ * always, and bf16 tiled kinds of at most 64 rows when M fits in one tile row
+ * (page "Tiling the hierarchy", failure regimes: matrix-vector-like products
+ * move the weights once and reuse none of them).  Host-only: no GPU work.
+ * TG_E_INFEASIBLE if no kernel serves cfg, TG_E_INVAL for NULL pointers or
+ * M < 0. */
+int tg_streams_b(int64_t M, int dtype, const tg_cfg *cfg, int *out);
 
 /* ---------------------------------------------------------------- tuning cache */
 /* Table of the last tuning run for this key (GPU): every measured candidate

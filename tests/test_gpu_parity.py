@@ -129,6 +129,26 @@ def test_skinny_kernels_integer_exact(M):
             _exact_check(C, ref, dtype, f"skinny M={M} {c.astuple()}")
 
 
+@pytest.mark.parametrize("M", [1, 16, 40, 64])
+def test_streaming_b_tiles_integer_exact(M):
+    """Launches with one row of tiles read B with the non-temporal policy
+    (their own instantiations): every such feasible configuration, split-K
+    included, must still be exact.  N and K ragged against every tile."""
+    N, K = 1000, 1064
+    for dtype in (wl.BF16, wl.BF16_F32OUT):
+        A, B, bias = _int_inputs(M, N, K, dtype, 6)
+        ref = gemm_ref.gemm(A, B, bias, "relu")
+        A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+        feas = [c for c in tg.enumerate_feasible(M, N, K, dtype)
+                if c.kind == S.KIND_TILED and tg.has_kernel(dtype, c) and tg.streams_b(M, dtype, c)]
+        assert len(feas) > 50
+        for c in feas:
+            mark(f"streaming B M={M} dt{dtype} {c.astuple()}")
+            C = _run(A_d, B_d, b_d, "relu", dtype, c)
+            torch.cuda.synchronize()
+            _exact_check(C, ref, dtype, f"streaming B M={M} {c.astuple()}")
+
+
 @pytest.mark.parametrize("act", ACT_NAMES)
 def test_activations_random_inputs(act):
     M, N, K = 333, 200, 512

@@ -279,3 +279,25 @@ def _has_gpu():
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+def test_b_streaming_rule():
+    """B is read with the non-temporal policy exactly when every element of it
+    is read by one workgroup: always for the skinny kind, and for bf16 tiled
+    tiles of at most 64 rows when M fits in one tile row."""
+    seen = {True: 0, False: 0}
+    for dtype in (S.BF16, S.BF16_F32OUT, S.F32):
+        for c in tg.space(dtype):
+            if not tg.has_kernel(dtype, c):
+                continue
+            for M in (1, 16, 17, 40, 64, 65, 200):
+                got = tg.streams_b(M, dtype, c)
+                if c.kind == S.KIND_SKINNY:
+                    want = True
+                else:
+                    want = dtype != S.F32 and c.kind == S.KIND_TILED and c.bm <= 64 and M <= c.bm
+                assert got == want, (M, dtype, c.astuple())
+                seen[got] += 1
+    assert seen[True] > 100 and seen[False] > 100
+    with pytest.raises(tg.TileGemmError):
+        tg.streams_b(-1, S.BF16, tg.space(S.BF16)[0])

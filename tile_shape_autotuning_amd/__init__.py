@@ -13,7 +13,7 @@ from . import _native
 from ._native import (ACT, BF16, BF16_F32OUT, F32, Cfg, DeviceDesc, TileGemmError, autotune_table,
                       builtin_device_desc, cache_clear, cache_load, cache_lookup, cache_save, cache_size,
                       check_cfg, default_cfg, enumerate_feasible, gemm_autotune, get_device_desc, grid,
-                      has_kernel, kernel_count, kernel_resources, model_choice, model_time_us, resources,
+                      has_kernel, kernel_count, kernel_resources, streams_b, model_choice, model_time_us, resources,
                       set_device_override, set_shape_buckets, dispatch_m, space, stats, rmsnorm_autotune,
                       rmsnorm_cache_lookup, rmsnorm_tunes)
 
@@ -21,7 +21,7 @@ __all__ = [
     "gemm_bias_act", "gemm_autotune", "Cfg", "DeviceDesc", "TileGemmError", "F32", "BF16", "BF16_F32OUT",
     "ACT", "enumerate_feasible", "space", "check_cfg", "model_time_us", "model_choice", "grid", "default_cfg",
     "resources", "builtin_device_desc", "set_device_override", "get_device_desc", "kernel_count",
-    "has_kernel", "kernel_resources", "autotune_table", "cache_lookup", "cache_save", "cache_load",
+    "has_kernel", "kernel_resources", "streams_b", "autotune_table", "cache_lookup", "cache_save", "cache_load",
     "cache_clear", "cache_size", "stats", "dtype_code", "set_shape_buckets", "dispatch_m",
     "rmsnorm", "rmsnorm_autotune", "rmsnorm_cache_lookup", "rmsnorm_tunes",
 ]

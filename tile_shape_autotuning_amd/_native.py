@@ -24,7 +24,7 @@ EXPORTS = [
     "tg_last_error", "tg_version", "tg_set_stream", "gemm_bias_act", "gemm_autotune",
     "tg_enumerate", "tg_space", "tg_check_cfg", "tg_model_time", "tg_model_choice", "tg_grid",
     "tg_default_cfg", "tg_resources", "tg_set_device_override", "tg_get_device_desc",
-    "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources",
+    "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources", "tg_streams_b",
     "tg_autotune_table", "tg_cache_lookup", "tg_cache_save", "tg_cache_load", "tg_cache_clear",
     "tg_cache_size", "tg_stats", "tg_set_shape_buckets", "tg_dispatch_m",
     "tg_rmsnorm", "tg_rmsnorm_autotune", "tg_rmsnorm_cache_lookup", "tg_rmsnorm_tunes",
@@ -110,6 +110,7 @@ def lib():
             "tg_kernel_count": ([], i32),
             "tg_has_kernel": ([i32, pc], i32),
             "tg_kernel_resources": ([i32, pc, pi], i32),
+            "tg_streams_b": ([i64, i32, pc, pi], i32),
             "tg_autotune_table": ([i64, i64, i64, i32, ctypes.POINTER(TuneRow), i32, pi], i32),
             "tg_cache_lookup": ([i64, i64, i64, i32, pc, dp, pi], i32),
             "tg_cache_save": ([ctypes.c_char_p], i32),
@@ -242,6 +243,13 @@ def kernel_resources(dtype, cfg):
     r = (ctypes.c_int * 5)()
     check(lib().tg_kernel_resources(int(dtype), ctypes.byref(Cfg.of(cfg)), r))
     return tuple(r)
+
+
+def streams_b(M, dtype, cfg) -> bool:
+    """Whether a call of M rows with cfg reads B with the non-temporal policy."""
+    r = ctypes.c_int()
+    check(lib().tg_streams_b(int(M), int(dtype), ctypes.byref(Cfg.of(cfg)), ctypes.byref(r)))
+    return bool(r.value)
 
 
 # ---------------------------------------------------------------- cache

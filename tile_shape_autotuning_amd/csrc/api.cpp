@@ -182,6 +182,15 @@ int validate_problem(int64_t M, int64_t N, int64_t K, int dtype)
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A launch with a single row of tiles reads every element of B in exactly one
+// workgroup: B is then streamed with the non-temporal policy, where such an
+// instantiation exists (page "Tiling the hierarchy", failure regimes: a
+// matrix-vector-like product moves the weights once and reuses none of them).
+static LaunchFn launch_fn(const KernelEntry& ke, const GemmParams& p)
+{
+    return (p.tiles_m == 1 && ke.launch_stream_b) ? ke.launch_stream_b : ke.launch;
+}
+
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, void* C,
                int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked)
 {
@@ -242,7 +251,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
             return st;
         p.slab = splitk_slab(M, N);
     }
-    hipError_t e = ke->launch(p, (int)blocks, stream);
+    hipError_t e = launch_fn(*ke, p)(p, (int)blocks, stream);
     if (e != hipSuccess)
         return set_hip_error(e, "kernel launch");
     if (c.split_k > 1) {
@@ -484,6 +493,21 @@ int tg_has_kernel(int dtype, const tg_cfg* cfg)
     if (!cfg)
         return 0;
     return find_kernel(dtype, *cfg) ? 1 : 0;
+}
+
+int tg_streams_b(int64_t M, int dtype, const tg_cfg* cfg, int* out)
+{
+    if (!cfg || !out)
+        return set_error(TG_E_INVAL, "NULL argument");
+    if (M < 0)
+        return set_error(TG_E_INVAL, "negative dimension");
+    const KernelEntry* k = find_kernel(dtype, *cfg);
+    if (!k)
+        return set_error(TG_E_INFEASIBLE, "no compiled kernel for this configuration");
+    GemmParams p{};
+    p.tiles_m = cfg->kind == TG_KIND_SKINNY ? 1 : (int)((M + cfg->bm - 1) / cfg->bm);
+    *out = (cfg->kind == TG_KIND_SKINNY || launch_fn(*k, p) == k->launch_stream_b) ? 1 : 0;
+    return TG_OK;
 }
 
 int tg_kernel_resources(int dtype, const tg_cfg* cfg, int* out5)

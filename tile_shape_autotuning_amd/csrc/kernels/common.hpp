@@ -56,6 +56,14 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int voff)
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
 
+// The same load with the non-temporal cache policy (cache-policy operand 2 =
+// nt on this chip family): for data the grid reads exactly once, which then
+// does not displace lines that other workgroups re-read.
+__device__ __forceinline__ u32x4_t load16_stream(__amdgpu_buffer_rsrc_t r, int voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2);
+}
+
 __device__ __forceinline__ unsigned short load2(__amdgpu_buffer_rsrc_t r, int voff)
 {
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);

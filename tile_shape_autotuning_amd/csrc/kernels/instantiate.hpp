@@ -7,11 +7,11 @@
 
 namespace tg {
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ST>
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB>
 hipError_t launch_tiled_dma(const GemmParams& p, int blocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tiled_dma_kernel<BM, BN, BK, WGM, WGN, ST>), dim3(blocks), dim3(64 * WGM * WGN), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_tiled_dma_kernel<BM, BN, BK, WGM, WGN, ST, NTB>), dim3(blocks), dim3(64 * WGM * WGN),
+                       0, stream, p);
     return hipGetLastError();
 }
 

@@ -21,7 +21,14 @@ struct KernelEntry {
     LaunchFn launch;
     int threads;
     KernelResources res;
+    // the same kernel reading B with the non-temporal policy, for launches
+    // with a single row of tiles (B read exactly once); null if not built
+    LaunchFn launch_stream_b;
 };
+
+// Tile rows up to this height get a B-streaming instantiation (a single row
+// of tiles means M <= BM: the decode regime).
+constexpr int kStreamBMaxBM = 64;
 
 // all entries, sorted by (in_bf16, cfg)
 const KernelEntry* registry_begin();
