@@ -121,7 +121,9 @@ def test_missing_results_raise(tmp_path):
 
 
 def test_kernel_names_match_the_template_instances():
-    assert R.kernel_name((0, 64, 128, 64, 2, 4, 2, 4)) == "gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2>"
+    assert R.kernel_name((0, 64, 128, 64, 2, 4, 2, 4)) == "gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2, false>"
+    assert R.kernel_name((0, 32, 256, 32, 1, 2, 4, 2), stream_b=True) == \
+        "gemm_tiled_dma_kernel<32, 256, 32, 1, 2, 4, true>"
     assert R.kernel_name((1, 32, 128, 32, 4, 1, 2, 8)) == "gemm_skinny_kernel<2, 4, 2>"
 
 

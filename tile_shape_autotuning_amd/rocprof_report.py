@@ -191,11 +191,13 @@ def kernel_table(trace_dir, top=12):
     return "\n".join(out)
 
 
-def kernel_name(cfg, in_bf16=True):
-    """The template name rocprofv3 prints for a configuration's kernel."""
+def kernel_name(cfg, in_bf16=True, stream_b=False):
+    """The template name rocprofv3 prints for a configuration's kernel
+    (stream_b: the instantiation that reads B with the non-temporal policy,
+    which launches with a single row of tiles use)."""
     kind, bm, bn, bk, wgm, wgn, st, _ = cfg
     if kind == 0 and in_bf16:
-        return f"gemm_tiled_dma_kernel<{bm}, {bn}, {bk}, {wgm}, {wgn}, {st}>"
+        return f"gemm_tiled_dma_kernel<{bm}, {bn}, {bk}, {wgm}, {wgn}, {st}, {'true' if stream_b else 'false'}>"
     if kind == 1:
         return f"gemm_skinny_kernel<{bm // 16}, {wgm}, {st}>"
     return f"gemm_tiled_kernel<{'true' if in_bf16 else 'false'}, {bm}, {bn}, {bk}, {wgm}, {wgn}, {st}"
