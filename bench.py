@@ -198,13 +198,14 @@ def report(indices, torch, dump_dir=None, cache_out=None):
         t0 = time.perf_counter()
         tg.gemm_autotune(w.M, w.N, w.K, w.dtype)
         tune_s = time.perf_counter() - t0
-        rows = [(c.astuple(), pred, meas) for c, pred, meas in tg.autotune_table(w.M, w.N, w.K, w.dtype)
-                if meas > 0]
+        table = tg.autotune_table(w.M, w.N, w.K, w.dtype)
+        rows = [(c.astuple(), pred, meas) for c, pred, meas, _ in table if meas > 0]
+        confirmed = {c.astuple(): conf for c, _, _, conf in table if conf > 0}
         if dump_dir:
             os.makedirs(dump_dir, exist_ok=True)
             with open(os.path.join(dump_dir, f"table_{w.name}.json"), "w") as f:
                 json.dump({"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype,
-                           "rows": [[list(c), pred, meas] for c, pred, meas in rows]}, f)
+                           "rows": [[list(c), pred, meas, confirmed.get(c, -1.0)] for c, pred, meas in rows]}, f)
         best = min(rows, key=lambda r: r[2])
         worst = max(rows, key=lambda r: r[2])
         fixed = [r for r in rows if r[0] == tuple(tg.default_cfg(w.M, w.N, w.K, w.dtype).astuple())]
@@ -216,9 +217,14 @@ def report(indices, torch, dump_dir=None, cache_out=None):
         pr = np.argsort(np.argsort([r[1] for r in rows]))
         mr = np.argsort(np.argsort([r[2] for r in rows]))
         rho = float(np.corrcoef(pr, mr)[0, 1]) if len(rows) > 2 else float("nan")
+        chosen = tg.cache_lookup(w.M, w.N, w.K, w.dtype)[0].astuple()
         out[w.name] = {
             "measured": len(rows), "tune_s": round(tune_s, 2),
             "best": {"cfg": list(best[0]), "us": round(best[2], 3)},
+            # the tuner's choice: the fastest of the best few (and the default)
+            # re-timed with long samples
+            "chosen": {"cfg": list(chosen), "us": round(confirmed.get(chosen, -1.0), 3),
+                       "confirmed": {",".join(str(x) for x in c): round(v, 3) for c, v in confirmed.items()}},
             "worst": {"cfg": list(worst[0]), "us": round(worst[2], 3)},
             "worst_over_best": round(worst[2] / best[2], 3),
             "fixed_over_best": round(fixed[0][2] / best[2], 3) if fixed else None,

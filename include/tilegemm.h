@@ -91,11 +91,17 @@ typedef struct {
  * formula and ignores lds_bw_cu .. hbm_eff. */
 } tg_device_desc;
 
-/* One row of an autotuning table. */
+/* One row of an autotuning table.  Every candidate is first measured with
+ * short samples (TILEGEMM_TUNE_SAMPLE_US, default 2 ms of back-to-back
+ * launches); the best few of those (TILEGEMM_TUNE_CONFIRM, default 4; 0 turns
+ * the stage off) and the fixed default are then measured again with long
+ * samples (TILEGEMM_TUNE_CONFIRM_US, default 10 ms), where clocks have settled
+ * as in sustained use, and the tuner's choice is the fastest of those. */
 typedef struct {
     tg_cfg cfg;
     double predicted_us;   /* cost-model time */
-    double measured_us;    /* median measured time per launch, or -1 if not measured */
+    double measured_us;    /* median of the short samples per launch, or -1 if not measured */
+    double confirmed_us;   /* median of the long samples, or -1 if not in the confirmation stage */
 } tg_tune_row;
 
 /* ---------------------------------------------------------------- errors */

@@ -110,8 +110,8 @@ MI355X = Device(mode=0, n_cu=256, simds=4, lds_cu=163840, lds_block=163840,
                 max_threads=1024, waves_max=8, blocks_max=32, vgpr_max=512,
                 acc_max=256, peak_bf16=2516.6e12, peak_f32=157.3e12, bw=8.0e12,
                 a_ref=16384.0, c_fill=2.0, t0=4.0e-6, unaligned_eff=0.25,
-                lat_mem=2.0e-6, cu_bw=45.0e9, r0=24, lds_bw_cu=153.6e9, lat_step=1.5e-6,
-                lat_l2=0.2e-6, l2_bytes=32.0e6, w1_eff=0.75, skinny_eff=0.75, hbm_eff=0.9125)
+                lat_mem=2.0e-6, cu_bw=75.0e9, r0=24, lds_bw_cu=307.2e9, lat_step=0.8e-6,
+                lat_l2=0.5e-6, l2_bytes=32.0e6, w1_eff=0.55, skinny_eff=0.75, hbm_eff=0.9125)
 
 # The page's H100 model: 132 SMs, 228 KB shared memory, 989 TFLOP/s bf16,
 # 3.35 TB/s; one tile per SM at a time; no register model; no pipeline-fill

@@ -200,7 +200,7 @@ def test_model_mode_tuning_and_cache_roundtrip(tmp_path, monkeypatch):
         chosen[(M, Nn, K, dt)] = _t(c)
         assert _t(N.cache_lookup(M, Nn, K, dt)[0]) == _t(c)
         rows = N.autotune_table(M, Nn, K, dt)
-        assert len(rows) == 1 and rows[0][2] == -1.0
+        assert len(rows) == 1 and rows[0][2] == -1.0 and rows[0][3] == -1.0
     assert N.stats()["tunes"] == s0["tunes"] + 3
     # a second call is a cache hit: no new tuning run
     N.gemm_autotune(4100, 3000, 1000, S.BF16)

@@ -67,7 +67,8 @@ class DeviceDesc(ctypes.Structure):
 
 
 class TuneRow(ctypes.Structure):
-    _fields_ = [("cfg", Cfg), ("predicted_us", ctypes.c_double), ("measured_us", ctypes.c_double)]
+    _fields_ = [("cfg", Cfg), ("predicted_us", ctypes.c_double), ("measured_us", ctypes.c_double),
+                ("confirmed_us", ctypes.c_double)]
 
 
 class TileGemmError(RuntimeError):
@@ -254,11 +255,14 @@ def streams_b(M, dtype, cfg) -> bool:
 
 # ---------------------------------------------------------------- cache
 def autotune_table(M, N, K, dtype):
+    """Rows of the last tuning run for the key: (cfg, model us, median of the
+    short samples, median of the long confirmation samples); -1 where not
+    measured or not confirmed."""
     n = ctypes.c_int()
     check(lib().tg_autotune_table(M, N, K, int(dtype), None, 0, ctypes.byref(n)))
     buf = (TuneRow * max(1, n.value))()
     check(lib().tg_autotune_table(M, N, K, int(dtype), buf, n.value, ctypes.byref(n)))
-    return [(buf[i].cfg, buf[i].predicted_us, buf[i].measured_us) for i in range(n.value)]
+    return [(buf[i].cfg, buf[i].predicted_us, buf[i].measured_us, buf[i].confirmed_us) for i in range(n.value)]
 
 
 def cache_lookup(M, N, K, dtype):

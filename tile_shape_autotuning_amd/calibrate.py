@@ -29,12 +29,12 @@ import sys
 from . import _native as N
 
 GRID = {
-    "lds_bw_cu": [153.6e9, 230.0e9, 307.2e9],
-    "cu_bw": [45.0e9, 60.0e9, 90.0e9],
-    "lat_step": [1.0e-6, 1.5e-6, 2.0e-6],
-    "lat_l2": [0.2e-6, 0.3e-6, 0.5e-6],
-    "w1_eff": [0.6, 0.75, 0.9],
-    "t0": [3.0e-6, 4.0e-6],
+    "lds_bw_cu": [192.0e9, 230.0e9, 307.2e9],
+    "cu_bw": [60.0e9, 75.0e9, 90.0e9, 120.0e9],
+    "lat_step": [0.6e-6, 0.8e-6, 1.0e-6],
+    "lat_l2": [0.4e-6, 0.5e-6, 0.75e-6],
+    "w1_eff": [0.5, 0.55, 0.6, 0.75],
+    "t0": [4.0e-6],
 }
 
 
@@ -52,7 +52,8 @@ def _rank_stats(tab, desc, topk):
     M, Nn, K, dt = tab["M"], tab["N"], tab["K"], tab["dtype"]
     N.set_device_override(desc)
     pred, meas = [], []
-    for cfg, _, m in tab["rows"]:
+    for row in tab["rows"]:
+        cfg, m = row[0], row[2]
         try:
             pred.append(N.model_time_us(M, Nn, K, dt, cfg))
             meas.append(m)

@@ -12,6 +12,13 @@
 // Page "CuTile Autotuning" (rules): the fixed default configuration is always
 // among the measured candidates, so tuning never picks something slower than
 // the default it replaces; at most 30 candidates are measured in hybrid mode.
+//
+// Short samples rank every candidate; the best few and the default are then
+// timed again with samples five times longer, and the choice is made among
+// those.  Configurations that burn matrix-core power they do not need run
+// fast in short bursts and lose their lead once the clock settles (on the
+// 16 x 28672 x 8192 decode, a 64-row tile that led the 2 ms ranking by 0.3 %
+// ran 5 % behind a 32-row one over 20 ms).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -131,8 +138,18 @@ struct Timed {
     double predicted_us;
     int reps = 1;
     bool ok = true;
-    std::vector<double> samples;   // us per launch
+    std::vector<double> samples;   // us per launch, short samples
+    std::vector<double> confirm;   // us per launch, long samples (confirmation stage)
+    double med = -1.0, med_confirm = -1.0;
 };
+
+double median_of(std::vector<double> v)
+{
+    if (v.empty())
+        return -1.0;
+    std::sort(v.begin(), v.end());
+    return v[v.size() / 2];
+}
 
 }  // namespace
 
@@ -170,7 +187,7 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
         entry.cfg = feas[ranked[0].second];
         entry.predicted_us = ranked[0].first * 1e6;
         entry.measured_us = -1.0;
-        entry.table.push_back(tg_tune_row{entry.cfg, entry.predicted_us, -1.0});
+        entry.table.push_back(tg_tune_row{entry.cfg, entry.predicted_us, -1.0, -1.0});
     } else {
         if (!have_device())
             return set_error(TG_E_UNSUPPORTED, "measured tuning needs a HIP device (TILEGEMM_TUNE_MODE=model does not)");
@@ -286,51 +303,91 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
             t.reps = (int)std::max(1.0, std::min(2000.0, std::ceil(sample_us / us)));
         }
         int64_t timed = 0;
-        for (int r = 0; r < rounds; ++r) {
-            const size_t n = cands.size();
-            for (size_t j = 0; j < n; ++j) {
-                Timed& t = cands[(j + (size_t)r) % n];   // rotate the order every round
-                if (!t.ok)
-                    continue;
-                hipEventRecord(e0, st);
-                t.ok = run(t, t.reps);
-                hipEventRecord(e1, st);
-                e = hipEventSynchronize(e1);
-                if (e != hipSuccess) {
-                    hipEventDestroy(e0);
-                    hipEventDestroy(e1);
-                    return set_hip_error(e, "timing");
+        // one stage: `rounds` interleaved samples of every candidate in `set`
+        // (the order rotates every round), each sample `scale` times the
+        // sized repetition count
+        auto measure = [&](const std::vector<size_t>& set, int scale, bool conf) -> int {
+            for (int r = 0; r < rounds; ++r) {
+                const size_t n = set.size();
+                for (size_t j = 0; j < n; ++j) {
+                    Timed& t = cands[set[(j + (size_t)r) % n]];
+                    if (!t.ok)
+                        continue;
+                    const int reps = (int)std::min<int64_t>((int64_t)t.reps * scale, 20000);
+                    hipEventRecord(e0, st);
+                    t.ok = run(t, reps);
+                    hipEventRecord(e1, st);
+                    e = hipEventSynchronize(e1);
+                    if (e != hipSuccess)
+                        return set_hip_error(e, "timing");
+                    float ms = 0.f;
+                    hipEventElapsedTime(&ms, e0, e1);
+                    (conf ? t.confirm : t.samples).push_back((double)ms * 1e3 / reps);
+                    timed += reps;
                 }
-                float ms = 0.f;
-                hipEventElapsedTime(&ms, e0, e1);
-                t.samples.push_back((double)ms * 1e3 / t.reps);
-                timed += t.reps;
+                if (progress)
+                    std::fprintf(stderr, "[tilegemm]   %s round %d/%d done\n", conf ? "confirmation" : "ranking",
+                                 r + 1, rounds);
             }
-            if (progress)
-                std::fprintf(stderr, "[tilegemm]   round %d/%d done\n", r + 1, rounds);
+            return TG_OK;
+        };
+        std::vector<size_t> all(cands.size());
+        for (size_t i = 0; i < all.size(); ++i)
+            all[i] = i;
+        int rc = measure(all, 1, false);
+        if (rc == TG_OK) {
+            for (Timed& t : cands)
+                t.med = (t.ok && !t.samples.empty()) ? median_of(t.samples) : -1.0;
+            // confirmation stage: the best few by the short samples, plus the default
+            const int n_conf = std::max(0, std::min(env_int("TILEGEMM_TUNE_CONFIRM", 4), 30));
+            const int conf_us = std::max(100, env_int("TILEGEMM_TUNE_CONFIRM_US", 10000));
+            std::vector<size_t> order;
+            for (size_t i = 0; i < cands.size(); ++i)
+                if (cands[i].med > 0)
+                    order.push_back(i);
+            std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+                return cands[a].med < cands[b].med;
+            });
+            std::vector<size_t> conf(order.begin(), order.begin() + std::min<size_t>(order.size(), n_conf));
+            if (!conf.empty())
+                for (size_t i = 0; i < cands.size(); ++i)
+                    if (cfg_equal(cands[i].cfg, def) && cands[i].med > 0 &&
+                        std::find(conf.begin(), conf.end(), i) == conf.end())
+                        conf.push_back(i);
+            if (!conf.empty()) {
+                const int scale = std::max(1, (int)std::lround((double)conf_us / sample_us));
+                rc = measure(conf, scale, true);
+                for (size_t i : conf)
+                    cands[i].med_confirm = (cands[i].ok && !cands[i].confirm.empty()) ? median_of(cands[i].confirm)
+                                                                                       : -1.0;
+            }
         }
         hipEventDestroy(e0);
         hipEventDestroy(e1);
+        if (rc != TG_OK)
+            return rc;
+        // the choice: fastest confirmed candidate, or fastest by the short
+        // samples when the confirmation stage is off (ties: canonical order)
+        bool any_conf = false;
+        for (const Timed& t : cands)
+            any_conf = any_conf || t.med_confirm > 0;
         int best = -1;
         double best_us = 0.0;
         for (size_t i = 0; i < cands.size(); ++i) {
             Timed& t = cands[i];
-            double med = -1.0;
-            if (t.ok && !t.samples.empty()) {
-                std::vector<double> v = t.samples;
-                std::sort(v.begin(), v.end());
-                med = v[v.size() / 2];
-                if (best < 0 || med < best_us || (med == best_us && cfg_less(t.cfg, cands[best].cfg))) {
-                    best = (int)i;
-                    best_us = med;
-                }
+            const double v = any_conf ? t.med_confirm : t.med;
+            if (v > 0 && (best < 0 || v < best_us || (v == best_us && cfg_less(t.cfg, cands[best].cfg)))) {
+                best = (int)i;
+                best_us = v;
             }
-            entry.table.push_back(tg_tune_row{t.cfg, t.predicted_us, med});
+            entry.table.push_back(tg_tune_row{t.cfg, t.predicted_us, t.med, t.med_confirm});
             if (log)
                 std::fprintf(stderr,
-                             "[tilegemm] %lldx%lldx%lld dt%d kind%d %dx%dx%d w%dx%d st%d sk%d: model %.2f us, measured %.2f us\n",
+                             "[tilegemm] %lldx%lldx%lld dt%d kind%d %dx%dx%d w%dx%d st%d sk%d: model %.2f us, measured %.2f us"
+                             "%s%.2f\n",
                              (long long)M, (long long)N, (long long)K, dtype, t.cfg.kind, t.cfg.bm, t.cfg.bn, t.cfg.bk,
-                             t.cfg.wgm, t.cfg.wgn, t.cfg.stages, t.cfg.split_k, t.predicted_us, med);
+                             t.cfg.wgm, t.cfg.wgn, t.cfg.stages, t.cfg.split_k, t.predicted_us, t.med,
+                             t.med_confirm > 0 ? ", confirmed " : "", t.med_confirm > 0 ? t.med_confirm : 0.0);
         }
         if (best < 0)
             return set_error(TG_E_HIP, "every candidate failed to launch: " + std::string(tg_last_error()));
@@ -457,7 +514,7 @@ int tg_cache_load(const char* path, int* n_loaded, int* n_skipped)
             ++skipped;
             continue;
         }
-        e.table.push_back(tg_tune_row{e.cfg, e.predicted_us, e.measured_us});
+        e.table.push_back(tg_tune_row{e.cfg, e.predicted_us, e.measured_us, -1.0});
         parsed.emplace_back(k, e);
     }
     std::lock_guard<std::mutex> lk(g_cache_mu);
