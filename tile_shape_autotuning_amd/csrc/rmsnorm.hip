@@ -199,7 +199,8 @@ static int norm_tune(int64_t rows, int64_t n, int dev, int n_cu, NormEntry* out)
         release();
         return set_hip_error(e, "hipEventCreate");
     }
-    // interleaved rounds of back-to-back launches, about 1 ms per sample; median
+    // interleaved rounds of back-to-back launches, about 10 ms per sample (long
+    // enough for clocks to settle as in sustained use); median
     const int rounds = 7;
     std::vector<double> samples[4];
     int reps = 0;
@@ -216,7 +217,7 @@ static int norm_tune(int64_t rows, int64_t n, int dev, int n_cu, NormEntry* out)
                     (void)hipEventSynchronize(e1);
                     float ms = 0.0f;
                     (void)hipEventElapsedTime(&ms, e0, e1);
-                    reps = std::max(1, std::min(2000, (int)std::ceil(1000.0 / std::max(1.0, ms * 1e3))));
+                    reps = std::max(1, std::min(2000, (int)std::ceil(10000.0 / std::max(1.0, ms * 1e3))));
                 }
                 continue;
             }
