@@ -93,9 +93,10 @@ typedef struct {
 
 /* One row of an autotuning table.  Every candidate is first measured with
  * short samples (TILEGEMM_TUNE_SAMPLE_US, default 2 ms of back-to-back
- * launches); the best few of those (TILEGEMM_TUNE_CONFIRM, default 4; 0 turns
+ * launches); the best few of those (TILEGEMM_TUNE_CONFIRM, default 8; 0 turns
  * the stage off) and the fixed default are then measured again with long
- * samples (TILEGEMM_TUNE_CONFIRM_US, default 10 ms), where clocks have settled
+ * samples (TILEGEMM_TUNE_CONFIRM_US, default 10 ms), each preceded by as long
+ * again of untimed launches of the same candidate so that clocks have settled
  * as in sustained use, and the tuner's choice is the fastest of those. */
 typedef struct {
     tg_cfg cfg;

@@ -13,12 +13,15 @@
 // among the measured candidates, so tuning never picks something slower than
 // the default it replaces; at most 30 candidates are measured in hybrid mode.
 //
-// Short samples rank every candidate; the best few and the default are then
-// timed again with samples five times longer, and the choice is made among
+// Short samples rank every candidate; the best eight and the default are then
+// timed again with samples five times longer, each after as long again of
+// untimed launches of the same candidate, and the choice is made among
 // those.  Configurations that burn matrix-core power they do not need run
-// fast in short bursts and lose their lead once the clock settles (on the
-// 16 x 28672 x 8192 decode, a 64-row tile that led the 2 ms ranking by 0.3 %
-// ran 5 % behind a 32-row one over 20 ms).
+// fast in short bursts and lose their lead once the clock settles to their
+// own power draw (on the 16 x 28672 x 8192 decode, a 64-row, 8-wave tile that
+// led the 2 ms ranking by 0.3 % runs 5 % behind a 32-row, 2-wave one
+// sustained; with all-zero operands, which draw little matrix-core power,
+// the two tie).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -314,6 +317,13 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
                     if (!t.ok)
                         continue;
                     const int reps = (int)std::min<int64_t>((int64_t)t.reps * scale, 20000);
+                    // a long sample starts after as long again of untimed launches of
+                    // the same candidate: the clock then reflects this candidate's
+                    // own power draw, not that of the one timed before it
+                    if (conf && !run(t, reps)) {
+                        t.ok = false;
+                        continue;
+                    }
                     hipEventRecord(e0, st);
                     t.ok = run(t, reps);
                     hipEventRecord(e1, st);
@@ -339,7 +349,7 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
             for (Timed& t : cands)
                 t.med = (t.ok && !t.samples.empty()) ? median_of(t.samples) : -1.0;
             // confirmation stage: the best few by the short samples, plus the default
-            const int n_conf = std::max(0, std::min(env_int("TILEGEMM_TUNE_CONFIRM", 4), 30));
+            const int n_conf = std::max(0, std::min(env_int("TILEGEMM_TUNE_CONFIRM", 8), 30));
             const int conf_us = std::max(100, env_int("TILEGEMM_TUNE_CONFIRM_US", 10000));
             std::vector<size_t> order;
             for (size_t i = 0; i < cands.size(); ++i)
