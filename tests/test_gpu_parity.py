@@ -290,6 +290,30 @@ def test_workload5_ragged():
     _workload_parity(5, [None] + feas[::9])
 
 
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_persisted_tuning_launch_path(index):
+    """The launch the benchmark times: the persisted tuning cache loaded into
+    the library, then a call without a configuration (key lookup, cached
+    entry).  Full output against the oracle, sampled entries for 8192^3."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "tile_shape_autotuning_amd", "tuned", "mi355x.cache")
+    w = wl.WORKLOADS[index]
+    tg.cache_clear()
+    try:
+        loaded, _ = tg.cache_load(path)
+        assert loaded >= 5
+        hit = tg.cache_lookup(tg.dispatch_m(w.M), w.N, w.K, w.dtype)
+        assert hit is not None, "the persisted cache has an entry for this workload"
+        s0 = tg.stats()
+        _workload_parity(index, [None], sample=3000 if index == 3 else None)
+        s1 = tg.stats()
+        assert s1["tunes"] == s0["tunes"] and s1["cache_hits"] == s0["cache_hits"] + 1
+        assert tg.cache_lookup(tg.dispatch_m(w.M), w.N, w.K, w.dtype)[0] == hit[0]
+    finally:
+        tg.cache_clear()
+
+
 def test_max_sizes():
     # K at its limit (2^21) with a skinny M; N at its limit; a tall M
     for (M, N, K, dtype) in [(16, 64, 1 << 21, wl.BF16_F32OUT), (8, 1 << 21, 64, wl.BF16),
