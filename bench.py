@@ -95,6 +95,29 @@ class Prepared:
         self.i += 1
 
 
+def warm_up(step, min_steps, torch, min_seconds=0.1):
+    """Untimed steps until the GPU has run for at least min_seconds (and at
+    least min_steps steps); returns how many were run.  After the host-side
+    input generation the GPU has idled for seconds and its clocks ramp up
+    over tens of milliseconds: timed right away, a 200-step run of the
+    16-row decode read 80 us per step that reads 74 us after 30 ms of warm-up
+    (the 1000 x 1000 x 8192 headline: 34.2 vs 32.3 us)."""
+    t0 = time.perf_counter()
+    n = max(1, min_steps)
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    while elapsed < min_seconds:
+        more = max(1, int(n * (min_seconds - elapsed) / max(elapsed, 1e-6)) + 1)
+        for _ in range(more):
+            step()
+        torch.cuda.synchronize()
+        n += more
+        elapsed = time.perf_counter() - t0
+    return n
+
+
 def time_steps(p, steps, torch):
     """Average seconds per step over `steps`, timed with HIP events on the launch stream."""
     stream = torch.cuda.current_stream()
@@ -310,9 +333,7 @@ def rmsnorm_report(torch, steps, rows=16384, n=8192):
     nbytes = 2 * rows * n * 2 + n * 2
 
     def timed(occ):
-        for _ in range(3):
-            tg.rmsnorm(x, w, 1e-6, occupancy=occ, out=y)
-        torch.cuda.synchronize()
+        warm_up(lambda: tg.rmsnorm(x, w, 1e-6, occupancy=occ, out=y), 3, torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
@@ -338,7 +359,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed steps before the timed ones (default: enough for 100 ms of GPU time)")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--only", action="store_true")
     ap.add_argument("--report", action="store_true")
@@ -387,6 +409,7 @@ def main():
     indices = [main_idx] if a.only else [main_idx] + [i for i in sorted(wl.WORKLOADS) if i != main_idx]
     shapes = {}
     main_res = None
+    main_warmup = 0
     for i in indices:
         # decode: stream distinct weights every call (copies together exceed the 256 MiB
         # last-level cache twice over, as the library's tuner times it)
@@ -397,9 +420,18 @@ def main():
         p = Prepared(i, torch, rotate=rotate)
         if i == main_idx and a.cfg:
             p.cfg = tuple(int(x) for x in a.cfg.split(","))
-        for _ in range(max(1, a.warmup)):               # first call tunes and caches
-            p.step()
-        torch.cuda.synchronize()
+        # the first call tunes (without a persisted entry) and caches; the
+        # main workload runs exactly --warmup untimed steps when given, every
+        # workload otherwise warms up for at least 100 ms of GPU time
+        if i == main_idx and a.warmup >= 0:
+            for _ in range(max(1, a.warmup)):
+                p.step()
+            torch.cuda.synchronize()
+            warm = max(1, a.warmup)
+        else:
+            warm = warm_up(p.step, 10, torch)
+        if i == main_idx:
+            main_warmup = warm
         steps = a.steps if i == main_idx else max(10, min(a.steps, int(0.3 / max(1e-6, p.tg.cache_lookup(
             p.tg.dispatch_m(p.w.M), p.w.N, p.w.K, p.w.dtype)[1] * 1e-6))))
         sec, wall = time_steps(p, steps, torch)
@@ -422,7 +454,7 @@ def main():
         "metric": "autotuned GEMM TFLOP/s (or GB/s) per shape and % of MI355X roofline",
         "value": round(w.flops * steps / (sec * steps) / 1e12, 3) if bound == "mfma" else round(achieved, 1),
         "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
-        "n_gpus": 1, "steps": steps, "warmup": a.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": main_warmup,
         "ms_per_step": round(sec * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": prec, "data": "synthetic",
