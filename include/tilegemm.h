@@ -134,10 +134,11 @@ int tg_set_stream(void *hip_stream);
  * (cfg fails the filter: nothing is launched), TG_E_HIP, TG_E_NOMEM.
  * Split-K configurations run two kernels on the stream: the GEMM writes one
  * fp32 slab of partial sums per split (split_k x M x N floats) to a
- * library-owned workspace per device, then a second kernel adds the slabs in
- * split order and applies bias, activation and conversion.  Launches on one
- * device that use split-K must not run concurrently on different streams
- * (they share the workspace).
+ * library-owned workspace, then a second kernel adds the slabs in split order
+ * and applies bias, activation and conversion.  There is one workspace per
+ * (device, stream), grown on demand (growth waits for that stream), so calls
+ * on different streams may run concurrently; calls on one stream are ordered
+ * by it.
  */
 int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   const float *bias, void *C, int dtype, int act, const tg_cfg *cfg);

@@ -216,6 +216,32 @@ def test_split_k_deterministic_and_exact():
         assert_close(out_f64(C1), ref, dtype, f"split {s}")
 
 
+def test_split_k_on_two_streams_concurrently():
+    """Each stream has its own split-K workspace: split-K calls queued on two
+    streams at once (different problems, different split counts) both stay
+    exact."""
+    M, N, K, dtype = 96, 1000, 2048, wl.BF16_F32OUT
+    probs = []
+    for seed, cfg in ((11, (0, 64, 128, 64, 2, 2, 2, 8)), (12, (0, 32, 256, 32, 1, 2, 4, 4))):
+        A, B, bias = _int_inputs(M, N, K, dtype, seed)
+        probs.append((to_dev(A), to_dev(B), to_dev(bias), gemm_ref.gemm(A, B, bias, "relu"), cfg))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in probs]
+    # first calls grow each stream's workspace
+    for (A_d, B_d, b_d, _, cfg), st, C in zip(probs, streams, outs):
+        with torch.cuda.stream(st):
+            tg.gemm_bias_act(A_d, B_d, b_d, act="relu", out=C, cfg=cfg)
+    torch.cuda.synchronize()
+    mark("split-K on two streams")
+    for rep in range(20):
+        for (A_d, B_d, b_d, _, cfg), st, C in zip(probs, streams, outs):
+            with torch.cuda.stream(st):
+                tg.gemm_bias_act(A_d, B_d, b_d, act="relu", out=C, cfg=cfg)
+    torch.cuda.synchronize()
+    for (_, _, _, ref, cfg), C in zip(probs, outs):
+        _exact_check(C, ref, dtype, f"two streams {cfg}")
+
+
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])
 def test_split_k_second_pass_edges(dtype):
     # an unaligned shape (N = 33) runs the element-load kind, which takes any C: the second pass

@@ -122,49 +122,6 @@ static int64_t dispatch_m(int64_t M) { return g_buckets.load() ? bucket_m(M) : M
 static thread_local hipStream_t t_stream = nullptr;
 hipStream_t current_stream() { return t_stream; }
 
-// ------------------------------------------------------------------ workspace
-struct Workspace {
-    float* ws = nullptr;
-    size_t ws_bytes = 0;
-};
-static std::mutex g_ws_mu;
-static std::vector<Workspace> g_ws;
-
-size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& c)
-{
-    if (c.split_k <= 1)
-        return 0;
-    return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
-}
-
-int ensure_workspace(size_t ws_bytes, float** ws)
-{
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return set_hip_error(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    if ((int)g_ws.size() <= dev)
-        g_ws.resize(dev + 1);
-    Workspace& w = g_ws[dev];
-    if (w.ws_bytes < ws_bytes) {
-        // the old buffer may still be in use by queued kernels
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess)
-            return set_hip_error(e, "hipDeviceSynchronize (workspace growth)");
-        if (w.ws)
-            (void)hipFree(w.ws);
-        w.ws = nullptr;
-        w.ws_bytes = 0;
-        e = hipMalloc(&w.ws, ws_bytes);
-        if (e != hipSuccess)
-            return set_error(TG_E_NOMEM, std::string("split-K workspace: ") + hipGetErrorString(e));
-        w.ws_bytes = ws_bytes;
-    }
-    *ws = w.ws;
-    return TG_OK;
-}
-
 // ------------------------------------------------------------------ launch
 static constexpr int64_t kMaxKN = int64_t(1) << 21;
 static constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
@@ -246,7 +203,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     if (blocks > 0x7FFFFFFF)
         return set_error(TG_E_UNSUPPORTED, "too many workgroups");
     if (c.split_k > 1) {
-        const int st = ensure_workspace(workspace_bytes_for(M, N, c), &p.ws);
+        const int st = ensure_workspace(workspace_bytes_for(M, N, c), stream, &p.ws);
         if (st != TG_OK)
             return st;
         p.slab = splitk_slab(M, N);

@@ -33,8 +33,8 @@ hipStream_t current_stream();
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias,
                void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked);
 
-// Split-K workspace: grows to at least `ws_bytes`.
-int ensure_workspace(size_t ws_bytes, float** ws);
+// Split-K workspace of the current device and `stream`: grows to at least `ws_bytes`.
+int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws);
 size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& cfg);
 
 // Split-K second pass (splitk_reduce.hip): C = act(sum of the split slabs +

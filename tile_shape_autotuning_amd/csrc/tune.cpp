@@ -263,7 +263,7 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
             wsb = std::max(wsb, workspace_bytes_for(M, N, t.cfg));
         if (wsb > 0) {
             float* w;
-            const int r = ensure_workspace(wsb, &w);
+            const int r = ensure_workspace(wsb, st, &w);
             if (r != TG_OK)
                 return r;
         }
