@@ -120,7 +120,8 @@ int tg_set_stream(void *hip_stream);
  * C = act(A . B + bias) on the device current for this thread, on the stream
  * set with tg_set_stream.  Asynchronous: returns once the kernel is queued,
  * except that cfg == NULL with a shape not yet in the tuning cache first runs
- * gemm_autotune (blocking), or takes the cost model's choice when the
+ * gemm_autotune (blocking; it times the candidates on copies of this call's
+ * A, B and bias), or takes the cost model's choice when the
  * environment variable TILEGEMM_DISABLE_AUTOTUNE=1 is set.  With cfg == NULL
  * the cache is keyed on M's shape bucket (tg_dispatch_m): one tuning serves
  * every M of the bucket.
@@ -167,8 +168,11 @@ int tg_dispatch_m(int64_t M, int64_t *key_m);
  * Measurement", "Measurement, and what it must control" and "Hybrid
  * strategies"): the feasibility filter, then the cost model ranks the
  * survivors, then the best top_k plus the fixed default configuration are
- * timed on scratch inputs of the workload's distribution, interleaved over
- * several rounds, and the smallest median wins.  A cache hit returns at once
+ * timed on scratch inputs (uniform values in [-1, 1); a gemm_bias_act call
+ * tuned on first use times copies of its own operands instead), interleaved
+ * over several rounds; the best few by those medians and the default are
+ * re-timed with long samples (see tg_tune_row) and the fastest of those
+ * wins.  A cache hit returns at once
  * without measuring.  Blocking.  Mode and top_k come from
  * TILEGEMM_TUNE_MODE = hybrid (default) | model | exhaustive and
  * TILEGEMM_TUNE_TOPK (default 16, at most 30).  Each sample is about

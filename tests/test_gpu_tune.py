@@ -154,3 +154,28 @@ def test_shape_buckets_one_tuning_per_bucket(monkeypatch):
     finally:
         tg.set_shape_buckets(True)
         tg.cache_clear()
+
+
+def test_first_use_tuning_times_the_callers_operands(monkeypatch, capfd):
+    """A call without a configuration that misses the cache tunes on copies of
+    its own operands (the values set the matrix cores' power draw and so the
+    clock); explicit tuning, without operands, on synthetic uniform values."""
+    monkeypatch.setenv("TILEGEMM_TUNE_MODE", "hybrid")
+    monkeypatch.setenv("TILEGEMM_TUNE_TOPK", "4")
+    monkeypatch.setenv("TILEGEMM_LOG", "1")
+    tg.cache_clear()
+    M, N, K, dtype = 40, 1024, 512, wl.BF16          # M's shape bucket is 48: 8 rows are synthetic
+    A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("int", 2), wl.Dist("int", 2), wl.Dist("int", 4), 21)
+    mark("first-use tuning 40x1024x512")
+    C = tg.gemm_bias_act(to_dev(A), to_dev(B), to_dev(bias), act="relu")
+    torch.cuda.synchronize()
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    want = wl.f32_to_bf16_bits(ref.astype(np.float32))
+    from gpu_util import out_bits
+    assert np.array_equal(out_bits(C), want)
+    err = capfd.readouterr().err
+    assert "tuning 48x1024x512 dt1 on the caller's operands" in err
+    mark("explicit tuning 48x2048x512")
+    tg.gemm_autotune(48, 2048, 512, dtype)
+    assert "on uniform synthetic operands" in capfd.readouterr().err
+    tg.cache_clear()

@@ -267,7 +267,8 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                 if (!model_choice(Mk, N, K, dtype, current_desc(), &c, nullptr))
                     return set_error(TG_E_INFEASIBLE, "no feasible configuration");
             } else {
-                st = autotune(Mk, N, K, dtype, &c);
+                const TuneData own{A, B, bias, M};
+                st = autotune(Mk, N, K, dtype, &c, &own);
                 if (st != TG_OK)
                     return st;
             }

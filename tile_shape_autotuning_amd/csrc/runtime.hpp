@@ -46,8 +46,16 @@ hipError_t splitk_reduce(const float* ws, int split, int64_t M, int64_t N, const
 // Argument validation shared by the entry points.
 int validate_problem(int64_t M, int64_t N, int64_t K, int dtype);
 
-// tuner
-int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out);
+// tuner.  `data` (optional): the caller's operands of the call being tuned
+// (rows of A available: data->rows <= M); the timed runs then use their values
+// instead of synthetic ones.
+struct TuneData {
+    const void* A;
+    const void* B;
+    const float* bias;
+    int64_t rows;
+};
+int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const TuneData* data = nullptr);
 bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us);
 void count_cache_hit();
 

@@ -156,7 +156,7 @@ double median_of(std::vector<double> v)
 
 }  // namespace
 
-int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
+int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const TuneData* data)
 {
     const CacheKey key = make_key(M, N, K, dtype);
     {
@@ -251,12 +251,36 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
         for (int i = 0; i < nbc; ++i)
             if ((e = hipMalloc(&s.B[i], nb * eb)) != hipSuccess)
                 return set_error(TG_E_NOMEM, std::string("tuning scratch: ") + hipGetErrorString(e));
-        if ((e = fill_uniform(s.A, (int64_t)na, dtype != TG_F32, 0x1234u, st)) != hipSuccess ||
-            (e = fill_uniform(s.bias, N, 0, 0x9abcu, st)) != hipSuccess)
+        // The matrix cores' power draw, and with it the clock a configuration
+        // sustains, depends on the operand values (on the decode weights an
+        // 8-wave tile runs 78 us on the workload's values and 74.5 us on
+        // zeros).  A call tuned on first use therefore times its candidates on
+        // copies of its own operands; explicit tuning, which has none, on
+        // uniform values in [-1, 1).
+        const bool own = data && data->A && data->B && K > 0;
+        const int64_t own_rows = own ? std::min<int64_t>(data->rows, M) : 0;
+        if (own_rows > 0 &&
+            (e = hipMemcpyAsync(s.A, data->A, (size_t)(own_rows * K) * eb, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+            return set_hip_error(e, "tuning scratch copy");
+        if (own_rows < M &&
+            (e = fill_uniform(static_cast<char*>(s.A) + (size_t)(own_rows * K) * eb, (M - own_rows) * K,
+                              dtype != TG_F32, 0x1234u, st)) != hipSuccess)
             return set_hip_error(e, "tuning scratch fill");
-        for (int i = 0; i < nbc; ++i)
-            if ((e = fill_uniform(s.B[i], (int64_t)nb, dtype != TG_F32, 0x5678u + (uint32_t)i, st)) != hipSuccess)
+        if (own && data->bias)
+            e = hipMemcpyAsync(s.bias, data->bias, (size_t)N * sizeof(float), hipMemcpyDeviceToDevice, st);
+        else
+            e = fill_uniform(s.bias, N, 0, 0x9abcu, st);
+        if (e != hipSuccess)
+            return set_hip_error(e, "tuning scratch fill");
+        for (int i = 0; i < nbc; ++i) {
+            e = own ? hipMemcpyAsync(s.B[i], data->B, nb * eb, hipMemcpyDeviceToDevice, st)
+                    : fill_uniform(s.B[i], (int64_t)nb, dtype != TG_F32, 0x5678u + (uint32_t)i, st);
+            if (e != hipSuccess)
                 return set_hip_error(e, "tuning scratch fill");
+        }
+        if (log)
+            std::fprintf(stderr, "[tilegemm] tuning %lldx%lldx%lld dt%d on %s operands\n", (long long)M, (long long)N,
+                         (long long)K, dtype, own ? "the caller's" : "uniform synthetic");
         // workspace for the largest split-K candidate, allocated before timing
         size_t wsb = 0;
         for (const Timed& t : cands)
