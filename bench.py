@@ -151,6 +151,28 @@ def shape_summary(p, sec):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+# the report of the exhaustive measured tuning behind the persisted cache
+DEFAULT_REPORT = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "mi355x_report.json")
+
+
+def persisted_report(shapes):
+    """Best/worst, best/fixed-128x128 and model-versus-measured figures of the
+    exhaustive tuning that produced the persisted cache, per workload, each
+    marked with whether the configuration timed here is the one that tuning
+    chose."""
+    with open(DEFAULT_REPORT) as f:
+        rep = json.load(f)
+    out = {"source": rep["source"], "model_hit_rate": rep["model_hit_rate"], "workloads": {}}
+    for name, r in rep["report"].items():
+        timed = shapes.get(name, {}).get("cfg")
+        out["workloads"][name] = {
+            "candidates_measured": r["measured"], "best_us": r["best"]["us"], "worst_us": r["worst"]["us"],
+            "worst_over_best": r["worst_over_best"], "fixed_128x128_over_best": r["fixed_over_best"],
+            "chosen": r["chosen"]["cfg"], "chosen_confirmed_us": r["chosen"]["us"],
+            "model_choice": r["model_choice"], "model_choice_over_best": r["model_choice_over_best"],
+            "model_hit": r["model_hit"], "rank_corr": r["rank_corr"],
+            "timed_here_is_chosen": timed == r["chosen"]["cfg"] if timed is not None else None}
+    return out
 # per-shape tuning results measured on MI355X (the library's cache file format)
 DEFAULT_CACHE = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "mi355x.cache")
 
@@ -371,6 +393,8 @@ def main():
                     help="tune from scratch instead of loading the persisted tuning cache")
     ap.add_argument("--cache", type=str, default=DEFAULT_CACHE, help="tuning cache file to load")
     ap.add_argument("--cache-out", type=str, default="", help="with --report: save the exhaustive tuning here")
+    ap.add_argument("--report-out", type=str, default="",
+                    help="with --report: save the report (ratios, confirmed choices, model hits) here as JSON")
     ap.add_argument("--buckets", action="store_true",
                     help="also report shape-bucket dispatch against per-M tuning on the decode weights")
     ap.add_argument("--rmsnorm", action="store_true",
@@ -471,6 +495,12 @@ def main():
         rep, hits = report([i for i in indices], torch, a.dump, a.cache_out or None)
         line["report"] = rep
         line["model_hit_rate"] = f"{hits}/{len(indices)}"
+        if a.report_out:
+            with open(a.report_out, "w") as f:
+                json.dump({"source": "bench.py --report on MI355X (exhaustive measured autotune of each workload)",
+                           "model_hit_rate": line["model_hit_rate"], "report": rep}, f, indent=1)
+    elif tuning.startswith("cache") and os.path.exists(DEFAULT_REPORT):
+        line["tuning_report"] = persisted_report(shapes)
     if a.buckets:
         line["buckets"] = bucket_report(torch, 100)
     if (a.rmsnorm or not a.only) and not a.no_rmsnorm:

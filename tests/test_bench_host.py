@@ -63,3 +63,21 @@ def test_recorded_traffic_is_used_only_for_matching_sources(monkeypatch):
     assert bench.measured_traffic(kv["workload"], cfg[:-1] + [cfg[-1] + 1]) is None
     monkeypatch.setattr(build_lib, "kernel_source_digest", lambda: "0" * 64)
     assert bench.measured_traffic(kv["workload"], cfg) is None
+
+
+def test_persisted_report_matches_persisted_cache():
+    """The tuning report shipped beside the persisted cache describes the runs
+    that chose the cache's entries."""
+    import json
+    from tile_shape_autotuning_amd import workloads as wl
+    with open(bench.DEFAULT_REPORT) as f:
+        rep = json.load(f)
+    with open(bench.DEFAULT_CACHE) as f:
+        entries = [line.split() for line in f if line.startswith("gfx950")]
+    cfg_of = {(int(e[3]), int(e[4]), int(e[5]), int(e[6])): [int(x) for x in e[7:15]] for e in entries}
+    for w in wl.WORKLOADS.values():
+        r = rep["report"][w.name]
+        assert r["chosen"]["cfg"] == cfg_of[(w.M, w.N, w.K, w.dtype)], w.name
+        assert r["worst_over_best"] >= 1.0 and r["fixed_over_best"] >= 1.0
+    out = bench.persisted_report({})
+    assert set(out["workloads"]) == {w.name for w in wl.WORKLOADS.values()}
