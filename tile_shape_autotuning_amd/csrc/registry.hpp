@@ -26,9 +26,6 @@ struct KernelEntry {
     LaunchFn launch_stream_b;
 };
 
-// Tile rows up to this height get a B-streaming instantiation (a single row
-// of tiles means M <= BM: the decode regime).
-constexpr int kStreamBMaxBM = 64;
 
 // all entries, sorted by (in_bf16, cfg)
 const KernelEntry* registry_begin();
