@@ -176,7 +176,7 @@ def space(dtype: int, dev: Device = MI355X):
         tiles_m, tiles_n, bks = (32, 64, 128), (32, 64, 128), (8, 16, 32)
     else:
         # 16-row tiles for the bf16 kernel: a 16-row decode wastes no MFMA rows
-        tiles_m, tiles_n, bks = (16, 32, 64, 128, 256), (32, 64, 128, 256), (32, 64)
+        tiles_m, tiles_n, bks = (16, 32, 64, 128, 256), (32, 64, 128, 256), (32, 64, 128)
     # fp32 kernel: 1 or 2 LDS buffers; bf16 kernel: 2 to 8 stages in flight
     # (page "Tiling the hierarchy", double buffering: a latency-bound tile wants
     # a deeper pipeline; the LDS rule keeps the deep ones to small tiles)

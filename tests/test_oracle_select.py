@@ -137,7 +137,11 @@ def test_lds_examples():
     assert S.check(8192, 8192, 8192, S.BF16, two, d) == S.OK
     big = S.Cfg(S.KIND_TILED, 256, 256, 128, 2, 2, 2, 1)
     assert S.lds_bytes(big, S.BF16) == 256 * 1024 > d.lds_block
-    assert S.check(8192, 8192, 8192, S.BF16, big, d) == S.R_SPACE   # bf16 BK is 32 or 64
+    assert S.check(8192, 8192, 8192, S.BF16, big, d) == S.R_LDS     # 2 x 128 KiB stages
+    one = S.Cfg(S.KIND_TILED, 128, 128, 128, 2, 4, 2, 1)              # 2 x 64 KiB stages fit
+    assert S.lds_bytes(one, S.BF16) == 2 * 64 * 1024 and S.check(8192, 8192, 8192, S.BF16, one, d) == S.OK
+    odd = S.Cfg(S.KIND_TILED, 128, 128, 96, 2, 4, 2, 1)
+    assert S.check(8192, 8192, 8192, S.BF16, odd, d) == S.R_SPACE     # bf16 BK is 32, 64 or 128
     # the largest bf16 tiles at one stage fit; fp32 128x128x32 two stages fit
     assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 2, 1), d) == S.OK
     assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 3, 1), d) == S.R_LDS

@@ -34,7 +34,8 @@
 //     loads are issued as inline assembly so that the compiler does not add
 //     its own full drain before the LDS reads);
 //   * A sits in LDS as whole rows [BM][2 BK bytes], K-contiguous (a transfer
-//     carries 8 or 16 complete rows, so BK = 64 requests whole 128-byte lines),
+//     carries 16, 8 or 4 complete rows, so BK >= 64 requests whole 128-byte
+//     lines),
 //     and is read with ds_read_b128 (8 k values of one row per lane = the A
 //     operand of v_mfma_f32_16x16x32_bf16);
 //   * B stays N-contiguous in 64-column blocks [BN/64][BK][128 B] whose rows
@@ -66,7 +67,7 @@ struct TiledDma {
     static constexpr int KK = BK / 32;                  // 32-wide k slices per step
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int ROWB = BK * 2;                 // bytes of one A row in LDS (all KK slices)
-    static constexpr int RPA = 1024 / ROWB;             // A rows per transfer (16 or 8)
+    static constexpr int RPA = 1024 / ROWB;             // A rows per transfer (16, 8 or 4)
     static constexpr int LPR = ROWB / 16;               // lanes per A row
     static constexpr int QW = BN < 64 ? BN : 64;        // columns per B block
     static constexpr int U = QW / 16;                   // 16-column units per B row
@@ -100,17 +101,20 @@ struct TiledDma {
 };
 
 // A: rows of 2 BK bytes (all k of the stage, 4 KK chunks of 8 k); chunk c of
-// row r sits at c ^ swz_a<KK>(r).  Uses row bits 1..3 only: 16 consecutive
-// rows reading one logical chunk land in 16 distinct 16-byte slots of a
-// 256-byte window (no bank conflicts).  With BK = 64 a row is a whole
-// 128-byte line, so every A transfer requests whole lines (half-line requests
-// halve what the L2 delivers per request).
+// row r sits at c ^ swz_a<KK>(r).  16 consecutive rows reading one logical
+// chunk land in 16 distinct 16-byte slots of a 256-byte window (no bank
+// conflicts): with 64- and 128-byte rows (BK = 32, 64) two or four rows share
+// a window and the swizzle uses row bits 1..3; a 256-byte row (BK = 128) is a
+// window of its own and the swizzle is the row within its 16-row group.  With
+// BK >= 64 a row is one or two whole 128-byte lines, so every A transfer
+// requests whole lines (half-line requests halve what the L2 delivers per
+// request).
 template <int KK>
 __device__ __forceinline__ int swz_a(int r)
 {
-    static_assert(KK == 1 || KK == 2, "BK is 32 or 64");
+    static_assert(KK == 1 || KK == 2 || KK == 4, "BK is 32, 64 or 128");
     r &= 15;   // a function of the row within its 16-row group (what a fragment read sees)
-    return KK == 1 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r >> 1) & 7);
+    return KK == 1 ? (((r >> 1) ^ (r >> 3)) & 3) : KK == 2 ? ((r >> 1) & 7) : r;
 }
 
 // B: 32-byte unit u (16 columns) of block row p sits at u ^ swz_b(p).

@@ -140,7 +140,7 @@ static std::vector<tg_cfg> build_space(int dtype, int mode)
     } else {
         ms = {16, 32, 64, 128, 256};   // 16-row tiles: a 16-row decode wastes no MFMA rows
         ns = {32, 64, 128, 256};
-        bks = {32, 64};
+        bks = {32, 64, 128};
         sts = {2, 3, 4, 6, 8};      // direct-to-LDS kernel: stages in flight
     }
     for (int bm : ms)
