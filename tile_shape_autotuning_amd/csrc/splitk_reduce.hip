@@ -9,7 +9,11 @@
 // The pass is elementwise over the flattened M x N array: each thread owns
 // four consecutive elements (one 16-byte load per slab), so every access is
 // coalesced whatever the GEMM's tile shape was.  It reads S x M x N x 4 bytes
-// and writes M x N elements: HBM-bound.
+// and writes M x N elements: HBM-bound.  A thread issues the loads of all its
+// slabs before the first add (with the split count a template argument the
+// loads do not wait on one another; adding as each arrives would pay the
+// memory latency S times), then adds them in split order, so the sum is the
+// same as the one-at-a-time loop's.  Slabs are read once: non-temporal loads.
 #include <hip/hip_runtime.h>
 
 #include "kernels/common.hpp"
@@ -19,25 +23,40 @@ namespace tg {
 
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
+// S > 0: the split count, known at compile time; S == 0: `split` at run time.
+template <int S>
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* ws, int split, int64_t slab, int64_t mn, int n, const float* bias, void* C,
                      int out_bf16, int act, int vec_out)
 {
+    const int nsplit = S > 0 ? S : split;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
     for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < mn; i += stride) {
         const int cnt = mn - i < 4 ? (int)(mn - i) : 4;
         float v[4];
         if (cnt == 4) {
-            f32x4_t s = *reinterpret_cast<const f32x4_t*>(ws + i);
-            for (int k = 1; k < split; ++k)
-                s += *reinterpret_cast<const f32x4_t*>(ws + k * slab + i);
+            f32x4_t s;
+            if constexpr (S > 0) {
+                f32x4_t part[S];
+#pragma unroll
+                for (int k = 0; k < S; ++k)
+                    part[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ws + k * slab + i));
+                s = part[0];
+#pragma unroll
+                for (int k = 1; k < S; ++k)
+                    s += part[k];
+            } else {
+                s = *reinterpret_cast<const f32x4_t*>(ws + i);
+                for (int k = 1; k < nsplit; ++k)
+                    s += *reinterpret_cast<const f32x4_t*>(ws + k * slab + i);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 v[e] = s[e];
         } else {
             for (int e = 0; e < cnt; ++e) {
                 float s = ws[i + e];
-                for (int k = 1; k < split; ++k)
+                for (int k = 1; k < nsplit; ++k)
                     s += ws[k * slab + i + e];
                 v[e] = s;
             }
@@ -88,8 +107,18 @@ hipError_t splitk_reduce(const float* ws, int split, int64_t M, int64_t N, const
     // four outputs per store where C's alignment allows it (the element-load
     // kind accepts any C)
     const int vec_out = ((uintptr_t)C & (out_bf16 ? 7u : 15u)) == 0;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, ws, split, splitk_slab(M, N), mn,
-                       (int)N, bias, C, out_bf16, act, vec_out);
+    const int64_t slab = splitk_slab(M, N);
+#define TG_REDUCE(S)                                                                                          \
+    hipLaunchKernelGGL(splitk_reduce_kernel<S>, dim3(blocks), dim3(256), 0, stream, ws, split, slab, mn, (int)N, \
+                       bias, C, out_bf16, act, vec_out)
+    switch (split) {
+    case 2: TG_REDUCE(2); break;
+    case 4: TG_REDUCE(4); break;
+    case 8: TG_REDUCE(8); break;
+    case 16: TG_REDUCE(16); break;
+    default: TG_REDUCE(0); break;
+    }
+#undef TG_REDUCE
     return hipGetLastError();
 }
 
