@@ -31,7 +31,7 @@ SIMDS_PER_CU = 4
 MFMA_FLOPS_PER_MOP = 512        # SQ_INSTS_VALU_MFMA_MOPS_* counts 512-flop units
 
 
-def commands(bench_args, outdir="gpurun_out/prof"):
+def commands(bench_args, outdir="rocprof_out"):
     """The rocprofv3 invocations that produce the summaries (one pass each)."""
     b = " ".join(["python3", "bench.py"] + list(bench_args))
     return [
