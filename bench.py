@@ -2,10 +2,24 @@
 """Benchmark of the autotuned fused GEMM on one MI355X.
 
 A step is one call of gemm_bias_act (cached autotuned configuration: key
-lookup, launch geometry, one kernel) on inputs already resident in HBM.  The
-headline line times the 1000 x 1000 x 8192 bf16 workload (fp32 output, the
-wave-quantisation case); the other four workloads are reported under
-"shapes" with their own throughput and roofline fraction.
+lookup, launch geometry, the GEMM kernel, plus the second pass when the
+configuration splits K) on inputs already resident in HBM.  The headline line
+times the largest workload, the 8192^3 bf16 multiply with bias and GELU
+(compute-bound); the other four workloads are reported under "shapes" with
+their own throughput and roofline fraction.
+
+Every workload is also timed, in the same run, with the fixed 128 x 128
+default configuration and with the cost model's first choice: the ratios
+fixed/tuned and model/tuned and the model's hit rate in the line are measured
+here (page "Tile Selection: Cost Models Against Measurement", "Measurement,
+and what it must control").  Worst/best needs every configuration measured;
+that figure comes from the exhaustive tuning behind the persisted cache and
+is labelled so ("tuning_report"), or from --report, which re-measures it.
+
+All inputs are generated and copied to the GPU before anything is timed, and
+the headline workload is timed last, right after the others, on a GPU whose
+clocks are those of sustained use: exactly --warmup untimed steps of it, then
+exactly --steps timed ones.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
                   [--report]   # also measure every feasible configuration
@@ -25,8 +39,8 @@ wave-quantisation case); the other four workloads are reported under
 The per-shape configurations come from the persisted tuning cache when it is
 present (the exhaustive measured autotune of every workload on MI355X, in the
 library's own cache format); --fresh runs the library's hybrid tuner instead.
-The JSON "config.tuning" says which.  Prints one JSON line.  Needs the built library; the oracle is used only for
-the CPU-baseline leg.
+The JSON "config.tuning" says which.  Prints one JSON line.  Needs the built
+library; the oracle is used only for the CPU-baseline leg.
 """
 from __future__ import annotations
 
@@ -69,30 +83,37 @@ def bound_of(w):
 
 
 class Prepared:
+    """One workload's inputs on the GPU and its output buffer."""
+
     def __init__(self, index, torch, rotate=1):
         import tile_shape_autotuning_amd as tg
         self.w = w = wl.WORKLOADS[index]
         self.index = index
         A, B, bias = wl.workload_inputs(index)
+        self.host = (A, B, bias)
         self.A, self.B, self.bias = _dev(A, torch), _dev(B, torch), _dev(bias, torch)
         self.Bs = [self.B] + [self.B.clone() for _ in range(rotate - 1)]
         self.act = ["none", "relu", "gelu"][w.act]
         self.out_dtype = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
         self.C = torch.empty((w.M, w.N), dtype=self.out_dtype, device="cuda")
         self.tg = tg
-        self.i = 0
-        self.calls = None
-        self.cfg = None          # None: autotuned; else a forced configuration
 
-    def step(self):
-        if self.calls is None:
-            # first call tunes and caches; then bind the C-ABI call once per weight copy
-            self.tg.gemm_bias_act(self.A, self.B, self.bias, act=self.act, out=self.C, cfg=self.cfg)
-            self.calls = [self.tg.BoundGemm(self.A, B, self.bias, act=self.act, out=self.C, cfg=self.cfg)
-                          for B in self.Bs]
-            return
-        self.calls[self.i % len(self.calls)]()
-        self.i += 1
+    def bind(self, cfg=None):
+        """A step: one C-ABI call, rotating through the weight copies; cfg None
+        takes the cached (tuned) configuration, tuning on a miss."""
+        calls = [self.tg.BoundGemm(self.A, B, self.bias, act=self.act, out=self.C, cfg=cfg) for B in self.Bs]
+        state = [0]
+
+        def step():
+            calls[state[0] % len(calls)]()
+            state[0] += 1
+        return step
+
+    def tuned(self):
+        """(cfg, tuner's measured us) of the cache entry a call without cfg uses."""
+        w = self.w
+        return self.tg.cache_lookup(self.tg.dispatch_m(w.M), w.N, w.K, w.dtype, act=self.act,
+                                    bias=self.bias is not None)
 
 
 def warm_up(step, min_steps, torch, min_seconds=0.1):
@@ -101,7 +122,7 @@ def warm_up(step, min_steps, torch, min_seconds=0.1):
     input generation the GPU has idled for seconds and its clocks ramp up
     over tens of milliseconds: timed right away, a 200-step run of the
     16-row decode read 80 us per step that reads 74 us after 30 ms of warm-up
-    (the 1000 x 1000 x 8192 headline: 34.2 vs 32.3 us)."""
+    (the 1000 x 1000 x 8192 case: 34.2 vs 32.3 us)."""
     t0 = time.perf_counter()
     n = max(1, min_steps)
     for _ in range(n):
@@ -118,8 +139,10 @@ def warm_up(step, min_steps, torch, min_seconds=0.1):
     return n
 
 
-def time_steps(p, steps, torch):
-    """Average seconds per step over `steps`, timed with HIP events on the launch stream."""
+def time_steps(step, steps, torch):
+    """Average seconds per step over `steps`, timed with HIP events on the
+    launch stream (torch's current stream, which the binding hands to the
+    library), and the host wall time of the region."""
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -127,23 +150,49 @@ def time_steps(p, steps, torch):
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        p.step()
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) * 1e-3 / steps, wall
 
 
-def shape_summary(p, sec):
+def secondary_steps(p, sec_hint, steps):
+    """Steps for a measurement off the headline: about 0.2 s of GPU time
+    (between 10 and 5000 steps), whatever the headline's step count."""
+    return max(10, min(5000, int(0.2 / max(1e-6, sec_hint))))
+
+
+def compare_configs(p, torch, steps, tuned_sec):
+    """The fixed 128 x 128 default and the cost model's first choice, each
+    timed here after its own warm-up, against the tuned configuration."""
+    w, tg = p.w, p.tg
+    tuned_cfg = tuple(p.tuned()[0].astuple())
+    out = {}
+    for name, cfg in (("fixed_128x128", tg.default_cfg(w.M, w.N, w.K, w.dtype)),
+                      ("model_choice", tg.model_choice(w.M, w.N, w.K, w.dtype)[0])):
+        cfg = tuple(cfg.astuple())
+        if cfg == tuned_cfg:
+            sec = tuned_sec
+        else:
+            step = p.bind(cfg)
+            warm_up(step, 3, torch)
+            sec, _ = time_steps(step, secondary_steps(p, tuned_sec, steps), torch)
+        out[name] = {"cfg": list(cfg), "us": round(sec * 1e6, 3), "over_tuned": round(sec / tuned_sec, 4),
+                     "is_tuned": cfg == tuned_cfg}
+    return out
+
+
+def shape_summary(p, sec, forced_cfg=None):
     w = p.w
     bound, prec = bound_of(w)
     tflops = w.flops / sec / 1e12
     gbs = w.compulsory_bytes / sec / 1e9
     frac = gbs / HBM_PEAK if bound == "hbm" else tflops / PEAK[prec]
-    if p.cfg is not None:
-        cfg, meas = p.tg.Cfg.of(p.cfg), float("nan")
+    if forced_cfg is not None:
+        cfg, meas = p.tg.Cfg.of(forced_cfg), float("nan")
     else:
-        cfg, meas = p.tg.cache_lookup(p.tg.dispatch_m(w.M), w.N, w.K, w.dtype)   # the entry the call used
+        cfg, meas = p.tuned()   # the entry the call used
     return {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": wl.DTYPE_NAMES[w.dtype],
             "act": p.act, "us": round(sec * 1e6, 3), "TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 1),
             "bound": bound, "roofline_frac": round(frac, 4), "cfg": list(cfg.astuple()),
@@ -162,7 +211,8 @@ def persisted_report(shapes):
     chose."""
     with open(DEFAULT_REPORT) as f:
         rep = json.load(f)
-    out = {"source": rep["source"], "model_hit_rate": rep["model_hit_rate"], "workloads": {}}
+    out = {"source": rep["source"], "measured_in_this_run": False, "model_hit_rate": rep["model_hit_rate"],
+           "workloads": {}}
     for name, r in rep["report"].items():
         timed = shapes.get(name, {}).get("cfg")
         out["workloads"][name] = {
@@ -197,21 +247,30 @@ def measured_traffic(workload, cfg):
     return None
 
 
-def cpu_baseline(index, target_s=12.0):
-    """The oracle on a bounded row sample of the workload (host cores)."""
+def cpu_baseline(index, host=None, target_s=12.0):
+    """The oracle, as it stands, on a bounded row sample of the workload on
+    the host's cores: the sample grows until one pass takes about a second
+    (so fixed per-call costs do not set the rate), then is scaled to about
+    target_s seconds; a workload that is done within that is repeated."""
     from oracle import gemm_ref
     w = wl.WORKLOADS[index]
-    A, B, bias = wl.workload_inputs(index)
+    A, B, bias = host if host is not None else wl.workload_inputs(index)
     act = ["none", "relu", "gelu"][w.act]
-    rows = 4
-    t0 = time.perf_counter()
-    gemm_ref.gemm(A[:rows], B, bias, act)
-    dt = time.perf_counter() - t0
+    rows, dt = 8, 0.0
+    while True:
+        rows = min(rows, w.M)
+        t0 = time.perf_counter()
+        gemm_ref.gemm(A[:rows], B, bias, act)
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or rows == w.M:
+            break
+        rows *= 4
     rows2 = int(max(rows, min(w.M, rows * target_s / max(dt, 1e-3))))
     reps = 1
-    t0 = time.perf_counter()
-    gemm_ref.gemm(A[:rows2], B, bias, act)
-    dt = time.perf_counter() - t0
+    if rows2 != rows:
+        t0 = time.perf_counter()
+        gemm_ref.gemm(A[:rows2], B, bias, act)
+        dt = time.perf_counter() - t0
     if rows2 == w.M and dt < target_s:          # the whole workload is quick: repeat it
         reps = max(1, int(target_s / max(dt, 1e-3)))
         t0 = time.perf_counter()
@@ -241,9 +300,10 @@ def report(indices, torch, dump_dir=None, cache_out=None):
         # split-K cannot help a problem with thousands of tiles; keep its sweep short
         os.environ["TILEGEMM_TUNE_MAX_SPLIT"] = "1" if w.flops > 1e12 else "64"
         t0 = time.perf_counter()
-        tg.gemm_autotune(w.M, w.N, w.K, w.dtype)
+        act, has_bias = ["none", "relu", "gelu"][w.act], w.bias_dist is not None
+        tg.gemm_autotune(w.M, w.N, w.K, w.dtype, act=act, bias=has_bias)
         tune_s = time.perf_counter() - t0
-        table = tg.autotune_table(w.M, w.N, w.K, w.dtype)
+        table = tg.autotune_table(w.M, w.N, w.K, w.dtype, act=act, bias=has_bias)
         rows = [(c.astuple(), pred, meas) for c, pred, meas, _ in table if meas > 0]
         confirmed = {c.astuple(): conf for c, _, _, conf in table if conf > 0}
         if dump_dir:
@@ -262,7 +322,7 @@ def report(indices, torch, dump_dir=None, cache_out=None):
         pr = np.argsort(np.argsort([r[1] for r in rows]))
         mr = np.argsort(np.argsort([r[2] for r in rows]))
         rho = float(np.corrcoef(pr, mr)[0, 1]) if len(rows) > 2 else float("nan")
-        chosen = tg.cache_lookup(w.M, w.N, w.K, w.dtype)[0].astuple()
+        chosen = tg.cache_lookup(w.M, w.N, w.K, w.dtype, act=act, bias=has_bias)[0].astuple()
         out[w.name] = {
             "measured": len(rows), "tune_s": round(tune_s, 2),
             "best": {"cfg": list(best[0]), "us": round(best[2], 3)},
@@ -323,7 +383,7 @@ def bucket_report(torch, steps):
                 e1.record()
                 torch.cuda.synchronize()
                 key = tg.dispatch_m(M)
-                cfg = tg.cache_lookup(key, N, K, wl.BF16)[0].astuple()
+                cfg = tg.cache_lookup(key, N, K, wl.BF16, act="none", bias=True)[0].astuple()
                 rows[M][mode + "_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 3)
                 rows[M][mode + "_cfg"] = list(cfg)
                 if mode == "bucketed":
@@ -381,10 +441,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=-1,
-                    help="untimed steps before the timed ones (default: enough for 100 ms of GPU time)")
-    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed steps of the headline workload right before its timed ones")
+    ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--only", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the fixed default and the model's choice (profiling runs)")
     ap.add_argument("--report", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0)
@@ -430,10 +492,11 @@ def main():
         log(f"tuning: {tuning}")
 
     main_idx = a.workload
-    indices = [main_idx] if a.only else [main_idx] + [i for i in sorted(wl.WORKLOADS) if i != main_idx]
-    shapes = {}
-    main_res = None
-    main_warmup = 0
+    # the headline goes last: it is timed on a GPU that the others kept busy
+    indices = [main_idx] if a.only else [i for i in sorted(wl.WORKLOADS) if i != main_idx] + [main_idx]
+    forced = tuple(int(x) for x in a.cfg.split(",")) if a.cfg else None
+    # every input is generated and resident before anything is timed
+    prepared = {}
     for i in indices:
         # decode: stream distinct weights every call (copies together exceed the 256 MiB
         # last-level cache twice over, as the library's tuner times it)
@@ -441,33 +504,47 @@ def main():
         b_bytes = wi.K * wi.N * (4 if wi.dtype == wl.F32 else 2)
         rotate = min(8, max(2, -(-(512 << 20) // b_bytes))) if wi.M <= 64 else 1
         log(f"workload {i}: preparing")
-        p = Prepared(i, torch, rotate=rotate)
-        if i == main_idx and a.cfg:
-            p.cfg = tuple(int(x) for x in a.cfg.split(","))
-        # the first call tunes (without a persisted entry) and caches; the
-        # main workload runs exactly --warmup untimed steps when given, every
-        # workload otherwise warms up for at least 100 ms of GPU time
-        if i == main_idx and a.warmup >= 0:
-            for _ in range(max(1, a.warmup)):
-                p.step()
-            torch.cuda.synchronize()
-            warm = max(1, a.warmup)
-        else:
-            warm = warm_up(p.step, 10, torch)
-        if i == main_idx:
-            main_warmup = warm
-        steps = a.steps if i == main_idx else max(10, min(a.steps, int(0.3 / max(1e-6, p.tg.cache_lookup(
-            p.tg.dispatch_m(p.w.M), p.w.N, p.w.K, p.w.dtype)[1] * 1e-6))))
-        sec, wall = time_steps(p, steps, torch)
-        s = shape_summary(p, sec)
-        s["steps"] = steps
+        prepared[i] = Prepared(i, torch, rotate=rotate)
+    torch.cuda.synchronize()
+
+    shapes = {}
+    main_res = None
+    hits, compared = 0, 0
+    for i in indices:
+        p = prepared[i]
+        is_main = i == main_idx
+        cfg = forced if (is_main and forced) else None
+        step = p.bind(cfg)     # the first call tunes (without a persisted entry) and caches
+        tuned_us = p.tuned()[1] if cfg is None else float("nan")
+        if not is_main:
+            warm_up(step, 10, torch)
+            steps = secondary_steps(p, (tuned_us if tuned_us > 0 else 100.0) * 1e-6, a.steps)
+            sec, wall = time_steps(step, steps, torch)
+            s = shape_summary(p, sec, cfg)
+            s["steps"] = steps
+        if not a.no_compare and cfg is None:
+            hint = sec if not is_main else max(tuned_us, 1.0) * 1e-6
+            cmp_ = compare_configs(p, torch, a.steps, hint)
+        if is_main:
+            # exactly --warmup untimed steps, then exactly --steps timed ones
+            for _ in range(a.warmup):
+                step()
+            sec, wall = time_steps(step, a.steps, torch)
+            s = shape_summary(p, sec, cfg)
+            s["steps"] = a.steps
+            main_res = (p, sec, wall, a.steps)
+        if not a.no_compare and cfg is None:
+            # re-express the ratios against this run's tuned time
+            for v in cmp_.values():
+                if v["is_tuned"]:
+                    v["us"] = round(sec * 1e6, 3)
+                v["over_tuned"] = round(v["us"] * 1e-6 / sec, 4)
+            s["fixed_128x128"] = cmp_["fixed_128x128"]
+            s["model_choice"] = cmp_["model_choice"]
+            hits += cmp_["model_choice"]["is_tuned"]
+            compared += 1
         shapes[p.w.name] = s
         log(f"workload {i}: {s}")
-        if i == main_idx:
-            main_res = (p, sec, wall, steps)
-        else:
-            del p
-            torch.cuda.empty_cache()
 
     p, sec, wall, steps = main_res
     w = p.w
@@ -476,21 +553,31 @@ def main():
     peak = PEAK[prec] if bound == "mfma" else HBM_PEAK
     line = {
         "metric": "autotuned GEMM TFLOP/s (or GB/s) per shape and % of MI355X roofline",
-        "value": round(w.flops * steps / (sec * steps) / 1e12, 3) if bound == "mfma" else round(achieved, 1),
+        "value": round(achieved, 3) if bound == "mfma" else round(achieved, 1),
         "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
-        "n_gpus": 1, "steps": steps, "warmup": main_warmup,
+        "n_gpus": 1, "steps": steps, "warmup": a.warmup,
         "ms_per_step": round(sec * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": prec, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
-                   "dtype": wl.DTYPE_NAMES[w.dtype], "act": p.act,
-                   "cfg": shapes[w.name]["cfg"], "tuning": tuning, "parallelism": "single-gpu"},
+                   "dtype": wl.DTYPE_NAMES[w.dtype], "act": p.act, "bias": p.bias is not None,
+                   "cfg": shapes[w.name]["cfg"], "tuning": tuning, "parallelism": "single-gpu",
+                   "order": "headline timed last, after " + (", ".join(wl.WORKLOADS[i].name for i in indices[:-1])
+                                                            or "nothing")},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, shapes[w.name]["cfg"])},
         "shapes": shapes,
     }
+    if compared:
+        line["measured_here"] = {
+            "model_hit_rate": f"{hits}/{compared}",
+            "fixed_128x128_over_tuned": {k: v["fixed_128x128"]["over_tuned"] for k, v in shapes.items()
+                                         if "fixed_128x128" in v},
+            "model_choice_over_tuned": {k: v["model_choice"]["over_tuned"] for k, v in shapes.items()
+                                        if "model_choice" in v},
+            "note": "hit = the cost model's first choice is the configuration the measured tuning chose"}
     if a.report:
         rep, hits = report([i for i in indices], torch, a.dump, a.cache_out or None)
         line["report"] = rep
@@ -507,7 +594,7 @@ def main():
         line["rmsnorm"] = rmsnorm_report(torch, 50)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(main_idx)
+        line["cpu_baseline"] = cpu_baseline(main_idx, p.host)
     print(json.dumps(line), flush=True)
 
 

@@ -24,7 +24,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 1
+#define TG_VERSION 2
 
 typedef enum {
     TG_OK = 0,
@@ -61,8 +61,9 @@ typedef enum {
  * tile, reduction step, per-thread tile; page "Compilers and Kernel
  * Languages": pipeline depth and split-K are further choices).
  *   tiled / unaligned: bm x bn block tile, bk reduction step, wgm x wgn waves
- *       (64 lanes each) per workgroup, stages = LDS buffers (1 or 2),
- *       split_k = workgroups sharing one tile's K range.
+ *       (64 lanes each) per workgroup, stages = pipeline depth (bf16 tiled:
+ *       2, 3, 4, 6 or 8 K steps in flight global -> LDS; fp32 and unaligned:
+ *       1 or 2 LDS buffers), split_k = workgroups sharing one tile's K range.
  *   skinny: bm = 16 * ceil(M / 16), bn = 128 columns per workgroup, bk = 32,
  *       wgm = waves per workgroup (each takes interleaved 32-row chunks of
  *       K), wgn = 1, stages = chunks per pipelined step, split_k as above.
@@ -169,7 +170,9 @@ int tg_dispatch_m(int64_t M, int64_t *key_m);
  * strategies"): the feasibility filter, then the cost model ranks the
  * survivors, then the best top_k plus the fixed default configuration are
  * timed on scratch inputs (uniform values in [-1, 1); a gemm_bias_act call
- * tuned on first use times copies of its own operands instead), interleaved
+ * tuned on first use times copies of its own operands instead), running the
+ * epilogue of the call being tuned (the measured runs must be the runs that
+ * are served: same page, "Measurement, and what it must control"), interleaved
  * over several rounds; the best few by those medians and the default are
  * re-timed with long samples (see tg_tune_row) and the fastest of those
  * wins.  A cache hit returns at once
@@ -182,32 +185,73 @@ int tg_dispatch_m(int64_t M, int64_t *key_m);
  * A, C, bias and one to eight copies of B, freed before returning.
  */
 int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out);
+/*
+ * The tuning cache is keyed by (device, M, N, K, dtype, act, bias present):
+ * gemm_autotune tunes and caches the call without activation and bias;
+ * gemm_autotune_ep the call with activation act (tg_act) and, if has_bias is
+ * nonzero, a bias vector -- the entry a gemm_bias_act call of that epilogue
+ * without cfg uses.  Errors as gemm_autotune, plus TG_E_INVAL for an unknown
+ * act.
+ */
+int gemm_autotune_ep(int64_t M, int64_t N, int64_t K, int dtype, int act, int has_bias, tg_cfg *out);
 
-/* ---------------------------------------------------------------- selection queries (host only) */
-/* Feasible configurations in canonical order; writes at most cap, reports the total. */
+/* ---------------------------------------------------------------- selection queries (host only)
+ * None of these touches the GPU; all use the device description in force
+ * (tg_set_device_override, else the current device's, else MI355X). */
+/* Candidate enumeration (page "Tile Selection: Cost Models Against
+ * Measurement", "The structure of the search space": the cross product of
+ * block tile, reduction step and per-wave tile, cut down by resource limits
+ * checkable before anything runs): the feasible configurations for the shape
+ * in canonical order; writes at most cap into out (may be NULL when cap is
+ * 0), reports the total in *n_feasible.  TG_E_INVAL for a bad dtype, negative
+ * sizes or a NULL out with cap > 0. */
 int tg_enumerate(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, int cap, int *n_feasible);
-/* The whole candidate space before filtering, canonical order. */
+/* The whole candidate space before filtering (same section), canonical order;
+ * buffer convention as tg_enumerate. */
 int tg_space(int dtype, tg_cfg *out, int cap, int *n_total);
-/* Feasibility of one configuration: *reason = 0 if feasible, else the first failing rule:
+/* Feasibility filter for one configuration (same section: LDS for both panels,
+ * accumulator registers, the register file, whole MFMA tiles, occupancy):
+ * *reason = 0 if feasible, else the first failing rule:
  * 1 dtype, 2 alignment, 3 shape, 4 waves, 5 divisibility, 6 LDS, 7 accumulators,
  * 8 VGPR estimate, 9 occupancy, 10 split-K, 11 not in the space, 12 more transfers in flight per
- * wave than the memory counter tracks (63; bf16 tiled kind, ST x transfers per wave and stage). */
+ * wave than the memory counter tracks (63; bf16 tiled kind, ST x transfers per wave and stage),
+ * 13 the compiled kernel spills registers (page "Autotuning & cost models", the search space:
+ * the register cliff).  TG_E_INVAL for NULL pointers. */
 int tg_check_cfg(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, int *reason);
-/* Cost-model time of a feasible configuration, in microseconds. */
+/* Cost-model time of a feasible configuration, in microseconds (page "Tile
+ * Selection: Cost Models Against Measurement", "Analytical models and where
+ * they break"; page "Compilers and Kernel Languages", "Workshop": the larger
+ * of compute time at the wave and tile efficiencies and memory time).
+ * TG_E_INFEASIBLE if cfg fails the filter for the shape. */
 int tg_model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, double *us);
-/* First feasible configuration with the smallest model time. */
+/* The model's choice (same passages; ties keep the first in canonical order):
+ * the feasible configuration with the smallest model time and that time (us
+ * may be NULL).  TG_E_INFEASIBLE if nothing is feasible. */
 int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, double *us);
-/* Output tiles ceil(M/bm) * ceil(N/bn) and launched workgroups (tiles * split_k). */
+/* Launch geometry (page "Tile Selection: Cost Models Against Measurement",
+ * "The structure of the search space": ceil(M/bm) * ceil(N/bn) blocks): output
+ * tiles and launched workgroups (tiles * split_k).  TG_E_INVAL for NULL
+ * pointers, non-positive tile sizes or split, negative M or N. */
 int tg_grid(int64_t M, int64_t N, int64_t K, const tg_cfg *cfg, int64_t *tiles, int64_t *blocks);
-/* The configuration autotuning is always compared against for this shape. */
+/* The fixed configuration autotuning is always compared against (page "CuTile
+ * Autotuning", key rules: the default is among the measured candidates):
+ * 128 x 128 tiles where the shape allows vector loads. */
 int tg_default_cfg(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out);
-/* Resource estimates the filter uses: LDS bytes, VGPRs per lane, workgroups per CU. */
+/* The filter's pre-build estimates (page "Tile Selection: Cost Models Against
+ * Measurement", "The structure of the search space": shared memory for both
+ * panels, registers per thread): LDS bytes, VGPR+AGPR per lane, workgroups per
+ * CU.  They decide which kernels are compiled; once a kernel exists the cost
+ * model counts resident workgroups from what the compiler allotted
+ * (tg_kernel_resources) instead.  Outputs may be NULL. */
 int tg_resources(int dtype, const tg_cfg *cfg, int *lds_bytes, int *vgprs, int *blocks_per_cu);
-/* Use desc for every selection rule (NULL = the real device / MI355X defaults). */
+/* Use desc for every selection rule (NULL = the real device / MI355X defaults);
+ * mode 1 replays the H100 model of page "Compilers and Kernel Languages",
+ * "Workshop".  TG_E_INVAL for an implausible description. */
 int tg_set_device_override(const tg_device_desc *desc);
 /* The description in force (override, else the current device's, else MI355X defaults). */
 int tg_get_device_desc(tg_device_desc *out);
-/* Built-in descriptions: which = 0 MI355X, 1 H100 replica. */
+/* Built-in descriptions: which = 0 MI355X, 1 H100 replica (page "Compilers and
+ * Kernel Languages", "Workshop": 132 SMs, 989 TFLOP/s, 3.35 TB/s). */
 int tg_builtin_device_desc(int which, tg_device_desc *out);
 
 /* ---------------------------------------------------------------- kernel registry (host only) */
@@ -218,8 +262,9 @@ int tg_has_kernel(int dtype, const tg_cfg *cfg);
 /* What the compiler allotted to the kernel serving cfg (from its resource
  * report at build time): out[0..4] = VGPRs, AGPRs, scratch bytes per lane
  * (register spills), LDS bytes, waves per SIMD; -1 where unknown.
- * TG_E_INFEASIBLE if no kernel serves cfg.  The autotuner skips kernels that
- * spill (set TILEGEMM_ALLOW_SPILLS=1 to keep them). */
+ * TG_E_INFEASIBLE if no kernel serves cfg.  A kernel that spills fails the
+ * filter (rule 13); the cost model counts resident workgroups from these
+ * registers and LDS bytes. */
 int tg_kernel_resources(int dtype, const tg_cfg *cfg, int *out5);
 /* Whether a call of M rows with cfg reads B with the non-temporal cache
  * policy (*out = 1) or the default one (*out = 0).  B is streamed that way
@@ -231,16 +276,26 @@ int tg_kernel_resources(int dtype, const tg_cfg *cfg, int *out5);
  * M < 0. */
 int tg_streams_b(int64_t M, int dtype, const tg_cfg *cfg, int *out);
 
-/* ---------------------------------------------------------------- tuning cache */
-/* Table of the last tuning run for this key (GPU): every measured candidate
- * plus the model's time; rows in measurement order. */
-int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, tg_tune_row *rows, int cap, int *n);
-/* Cached entry for the key on the current device: *hit = 1 and *out filled, or *hit = 0. */
-int tg_cache_lookup(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, double *measured_us, int *hit);
+/* ---------------------------------------------------------------- tuning cache
+ * Page "Tile Selection: Cost Models Against Measurement", "Measurement, and
+ * what it must control": the results are cached keyed by device, shape, dtype
+ * and library version, and may be stored in a file.  Keys here are
+ * (device, M, N, K, dtype, act, has_bias != 0). */
+/* Table of the last tuning run for this key: every measured candidate with the
+ * model's time, the short-sample median and the confirmation median; rows in
+ * measurement order; writes at most cap, reports the count in *n (0 if the
+ * key has no table). */
+int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, int act, int has_bias, tg_tune_row *rows,
+                      int cap, int *n);
+/* Cached entry for the key on the current device: *hit = 1 and *out filled
+ * (and *measured_us, if not NULL), or *hit = 0. */
+int tg_cache_lookup(int64_t M, int64_t N, int64_t K, int dtype, int act, int has_bias, tg_cfg *out,
+                    double *measured_us, int *hit);
 /* Persist / restore the cache as text, one line per key (arch, CU count,
- * library version, M, N, K, dtype -> cfg, measured and predicted us).
- * Loading skips lines for another library version; a malformed file is
- * TG_E_CACHE and leaves the cache unchanged. */
+ * library version, M, N, K, dtype, act, bias -> cfg, measured and predicted
+ * us).  Loading skips lines for another library version and configurations
+ * this build cannot run; a malformed file is TG_E_CACHE and leaves the cache
+ * unchanged. */
 int tg_cache_save(const char *path);
 int tg_cache_load(const char *path, int *n_loaded, int *n_skipped);
 void tg_cache_clear(void);

@@ -39,7 +39,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
 from __future__ import annotations
 
 import itertools
+import json
 import math
+import os
 from dataclasses import dataclass
 
 F32, BF16, BF16_F32OUT = 0, 1, 2
@@ -59,6 +61,7 @@ R_OCC = 9
 R_SPLIT = 10
 R_SPACE = 11
 R_INFLIGHT = 12
+R_SPILL = 13
 
 
 @dataclass(frozen=True)
@@ -245,6 +248,53 @@ def blocks_per_cu(c: Cfg, dtype: int, dev: Device) -> int:
     return b
 
 
+# What the compiler allotted to each compiled kernel (a fixed input, see
+# oracle/refresh_allocation.py): (in_bf16, kind, bm, bn, bk, wgm, wgn, stages)
+# -> (vgpr, agpr, lds, scratch, reported waves per SIMD).
+_ALLOC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kernel_allocation.json")
+_ALLOC = None
+
+
+def allocation_table():
+    global _ALLOC
+    if _ALLOC is None:
+        with open(_ALLOC_FILE) as f:
+            t = json.load(f)
+        _ALLOC = {tuple(r[:8]): tuple(r[8:]) for r in t["kernels"]}
+    return _ALLOC
+
+
+def compiled_alloc(dtype: int, c: Cfg):
+    """(vgpr, agpr, lds, scratch) of the kernel serving c, or None."""
+    r = allocation_table().get((0 if dtype == F32 else 1, c.kind, c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages))
+    return None if r is None else r[:4]
+
+
+def waves_per_simd_alloc(vgpr: int, agpr: int, dev: Device) -> int:
+    """Waves of one kernel a SIMD holds: the unified register file has
+    vgpr_max registers per lane, and a wave takes its architectural VGPRs
+    rounded up to 4 plus its AGPRs, rounded up to 8 (page "Tile Selection:
+    Cost Models Against Measurement", "Analytical models and where they
+    break": occupancy follows from registers and shared memory together)."""
+    regs = cdiv(cdiv(vgpr, 4) * 4 + agpr, 8) * 8
+    return min(dev.waves_max, dev.vgpr_max // regs) if regs > 0 else dev.waves_max
+
+
+def resident_blocks(c: Cfg, dtype: int, dev: Device) -> int:
+    """Workgroups one CU holds at once, as the cost model counts them: from
+    the compiled kernel's registers and LDS under the MI355X rules, else the
+    filter's estimate."""
+    a = compiled_alloc(dtype, c) if dev.mode == 0 else None
+    if a is None:
+        return blocks_per_cu(c, dtype, dev)
+    vgpr, agpr, lds, _ = a
+    w = c.wgm * c.wgn
+    b = min(dev.blocks_max, (dev.simds * waves_per_simd_alloc(vgpr, agpr, dev)) // w)
+    if lds > 0:
+        b = min(b, dev.lds_cu // lds)
+    return b
+
+
 def transfers_per_wave(c: Cfg, dtype: int) -> int:
     """16-byte-per-lane (1 KiB) transfers a wave issues per stage in the bf16
     tiled kernel: the A and B panels of one stage spread over the waves."""
@@ -305,6 +355,13 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
     r = check_static(dtype, c, dev)
     if r != OK:
         return r
+    # past the register cliff (page "Autotuning & cost models", the search
+    # space): a configuration whose compiled kernel spills is no candidate
+    a = compiled_alloc(dtype, c) if dev.mode == 0 else None
+    if a is not None and a[3] > 0:
+        return R_SPILL
+    if resident_blocks(c, dtype, dev) < 1:
+        return R_OCC
     if c.split_k > 1:
         if K == 0 or cdiv(K, k_per_split(c, K)) != c.split_k:
             return R_SPLIT
@@ -349,7 +406,7 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
     compulsory = float(eb * (M * K + K * N) + ec * M * N)
     tiles, units = grid(M, N, c)
     w = c.wgm * c.wgn
-    bcu = blocks_per_cu(c, dtype, dev)
+    bcu = resident_blocks(c, dtype, dev)
 
     if c.kind == KIND_SKINNY:
         flops_pad = 2.0 * c.bm * N * K

@@ -87,7 +87,7 @@ int main(int argc, char** argv)
 
     TG_OK_(tg_set_stream(NULL));
     tg_cfg cfg;
-    TG_OK_(gemm_autotune(M, N, K, TG_BF16_F32OUT, &cfg));
+    TG_OK_(gemm_autotune_ep(M, N, K, TG_BF16_F32OUT, TG_ACT_RELU, 1, &cfg));
     printf("tuned cfg: kind %d bm %d bn %d bk %d waves %dx%d stages %d split %d\n", cfg.kind, cfg.bm, cfg.bn, cfg.bk,
            cfg.wgm, cfg.wgn, cfg.stages, cfg.split_k);
     /* without a configuration: the cached choice */

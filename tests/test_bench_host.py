@@ -74,10 +74,12 @@ def test_persisted_report_matches_persisted_cache():
         rep = json.load(f)
     with open(bench.DEFAULT_CACHE) as f:
         entries = [line.split() for line in f if line.startswith("gfx950")]
-    cfg_of = {(int(e[3]), int(e[4]), int(e[5]), int(e[6])): [int(x) for x in e[7:15]] for e in entries}
+    # arch, CUs, version, M, N, K, dtype, act, bias, cfg (8 fields), measured us, predicted us
+    cfg_of = {tuple(int(x) for x in e[3:9]): [int(x) for x in e[9:17]] for e in entries}
     for w in wl.WORKLOADS.values():
         r = rep["report"][w.name]
-        assert r["chosen"]["cfg"] == cfg_of[(w.M, w.N, w.K, w.dtype)], w.name
+        key = (w.M, w.N, w.K, w.dtype, w.act, int(w.bias_dist is not None))
+        assert r["chosen"]["cfg"] == cfg_of[key], w.name
         assert r["worst_over_best"] >= 1.0 and r["fixed_over_best"] >= 1.0
     out = bench.persisted_report({})
     assert set(out["workloads"]) == {w.name for w in wl.WORKLOADS.values()}

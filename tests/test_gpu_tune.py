@@ -32,11 +32,12 @@ def test_autotune_measures_default_and_picks_argmin(monkeypatch):
     M, N, K, dtype = 4100, 3000, 1000, wl.BF16
     tg.cache_clear()
     s0 = tg.stats()
+    ep = dict(act="relu", bias=True)       # the epilogue of the call served below
     mark("autotune 4100x3000x1000 bf16")
-    c = tg.gemm_autotune(M, N, K, dtype)
+    c = tg.gemm_autotune(M, N, K, dtype, **ep)
     s1 = tg.stats()
     assert s1["tunes"] == s0["tunes"] + 1 and s1["timed_launches"] > s0["timed_launches"]
-    table = tg.autotune_table(M, N, K, dtype)
+    table = tg.autotune_table(M, N, K, dtype, **ep)
     measured = [(row[0].astuple(), row[2]) for row in table if row[2] > 0]
     confirmed = {row[0].astuple(): row[3] for row in table if row[3] > 0}
     assert len(measured) >= 2
@@ -49,13 +50,13 @@ def test_autotune_measures_default_and_picks_argmin(monkeypatch):
     best = min(confirmed.items(), key=lambda kv: kv[1])
     assert c.astuple() == best[0]
     assert best[1] <= confirmed[default]
-    assert tg.cache_lookup(M, N, K, dtype)[1] == best[1]
+    assert tg.cache_lookup(M, N, K, dtype, **ep)[1] == best[1]
     # every measured candidate is feasible and has a kernel that does not spill
     for cfg, _ in measured:
         assert tg.check_cfg(M, N, K, dtype, cfg) == 0
         assert tg.kernel_resources(dtype, cfg)[2] == 0
     # second request: cache hit, no new tuning
-    assert tg.gemm_autotune(M, N, K, dtype).astuple() == c.astuple()
+    assert tg.gemm_autotune(M, N, K, dtype, **ep).astuple() == c.astuple()
     assert tg.stats()["tunes"] == s1["tunes"]
     # gemm_bias_act without a cfg serves the cached choice and counts a hit
     A, B, bias = wl.workload_inputs(5)
@@ -142,7 +143,10 @@ def test_shape_buckets_one_tuning_per_bucket(monkeypatch):
         s1 = tg.stats()
         assert s1["tunes"] == s0["tunes"] + 1, "one tuning for the whole bucket"
         assert s1["cache_hits"] == s0["cache_hits"] + 3
-        assert tg.cache_lookup(32, N, K, dtype) is not None and tg.cache_lookup(20, N, K, dtype) is None
+        ep = dict(act="relu", bias=True)
+        assert tg.cache_lookup(32, N, K, dtype, **ep) is not None and tg.cache_lookup(20, N, K, dtype, **ep) is None
+        # the key holds the epilogue the calls ran: the plain call has no entry yet
+        assert tg.cache_lookup(32, N, K, dtype) is None
         # buckets off: every M is its own key
         tg.set_shape_buckets(False)
         tg.cache_clear()

@@ -69,7 +69,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert N.lib().tg_version() == 1
+    assert N.lib().tg_version() == 2
 
 
 @pytest.mark.parametrize("dtype", [S.F32, S.BF16, S.BF16_F32OUT])
@@ -205,25 +205,35 @@ def test_model_mode_tuning_and_cache_roundtrip(tmp_path, monkeypatch):
     # a second call is a cache hit: no new tuning run
     N.gemm_autotune(4100, 3000, 1000, S.BF16)
     assert N.stats()["tunes"] == s0["tunes"] + 3
-    # a different dtype is a different key
+    with pytest.raises(N.TileGemmError):
+        N.gemm_autotune(64, 64, 64, S.BF16, act=7)
+    # a different dtype is a different key, and so is a different epilogue
     assert N.cache_lookup(4100, 3000, 1000, S.BF16_F32OUT) is None
+    assert N.cache_lookup(4100, 3000, 1000, S.BF16, act="relu", bias=True) is None
+    c_ep = N.gemm_autotune(4100, 3000, 1000, S.BF16, act="gelu", bias=True)
+    assert N.stats()["tunes"] == s0["tunes"] + 4
+    assert _t(N.cache_lookup(4100, 3000, 1000, S.BF16, act="gelu", bias=True)[0]) == _t(c_ep)
+    assert N.cache_lookup(4100, 3000, 1000, S.BF16, act="gelu", bias=False) is None
+    chosen_ep = {(4100, 3000, 1000, S.BF16, "gelu", True): _t(c_ep)}
     path = str(tmp_path / "cache.txt")
     N.cache_save(path)
     N.cache_clear()
     assert N.cache_size() == 0
-    assert N.cache_load(path) == (3, 0)
+    assert N.cache_load(path) == (4, 0)
     for (M, Nn, K, dt), c in chosen.items():
         assert _t(N.cache_lookup(M, Nn, K, dt)[0]) == c
+    for (M, Nn, K, dt, act, b), c in chosen_ep.items():
+        assert _t(N.cache_lookup(M, Nn, K, dt, act=act, bias=b)[0]) == c
     # lines of another library version are skipped; stale configurations too
     lines = open(path).read().splitlines()
     other = lines[1].split()
     other[2] = "999"
     stale = lines[1].split()
-    stale[8:16] = ["0", "256", "256", "32", "1", "1", "1", "1"]
+    stale[9:17] = ["0", "256", "256", "32", "1", "1", "1", "1"]
     with open(path, "w") as f:
         f.write("\n".join([lines[0], " ".join(other), " ".join(stale)] + lines[2:]) + "\n")
     N.cache_clear()
-    assert N.cache_load(path) == (2, 2)
+    assert N.cache_load(path) == (3, 2)
     # a malformed file is rejected and leaves the cache as it was
     before = N.cache_size()
     bad = tmp_path / "bad.txt"
@@ -301,3 +311,24 @@ def test_b_streaming_rule():
     assert seen[True] > 100 and seen[False] > 100
     with pytest.raises(tg.TileGemmError):
         tg.streams_b(-1, S.BF16, tg.space(S.BF16)[0])
+
+
+def test_allocation_table_matches_the_built_kernels():
+    # the oracle's fixed input (oracle/kernel_allocation.json) must describe the
+    # kernels this library was built with; refresh it with
+    # `python -m oracle.refresh_allocation` after a kernel change
+    table = S.allocation_table()
+    assert N.kernel_count() == len(table)
+    for key, (vgpr, agpr, lds, scratch, occ) in table.items():
+        in_bf16, cfg = key[0], key[1:] + (1,)
+        dt = S.BF16 if in_bf16 else S.F32
+        assert N.kernel_resources(dt, cfg) == (vgpr, agpr, scratch, lds, occ), key
+
+
+def test_spill_rule_through_the_abi():
+    for key, v in S.allocation_table().items():
+        if v[3] > 0:
+            c = key[1:] + (1,)
+            dt = S.BF16 if key[0] else S.F32
+            M = c[1] if c[0] == S.KIND_SKINNY else 1024
+            assert N.check_cfg(M, 1024, 1024, dt, c) == S.R_SPILL

@@ -306,3 +306,141 @@ def test_bucket_configuration_fits_every_m_of_the_bucket(N, K, dt):
         for c in feas:
             for M in (members[0], members[len(members) // 2], members[-1]):
                 assert S.check(M, N, K, dt, c) == S.OK, (key, M, c)
+
+
+# ---------------------------------------------------------------- register file and occupancy
+# The oracle counts resident workgroups from the compiler's allocation
+# (oracle/kernel_allocation.json, a fixed input).  Its register-file rule is
+# pinned against the compiler's own occupancy figure for every compiled
+# kernel; the compiler also bounds the waves by LDS, rounding the waves a CU's
+# worth of workgroups gives each SIMD up.
+
+def _compiler_occupancy(vgpr, agpr, lds, w, dev=S.MI355X):
+    occ = S.waves_per_simd_alloc(vgpr, agpr, dev)
+    if lds > 0:
+        occ = min(occ, S.cdiv((dev.lds_cu // lds) * w, dev.simds))
+    return occ
+
+
+def test_register_file_rule_reproduces_the_compilers_occupancy():
+    table = S.allocation_table()
+    assert len(table) > 1000
+    for key, (vgpr, agpr, lds, scratch, occ) in table.items():
+        kind, wgm, wgn = key[1], key[5], key[6]
+        w = wgm * (1 if kind == S.KIND_SKINNY else wgn)
+        assert _compiler_occupancy(vgpr, agpr, lds, w) == occ, (key, vgpr, agpr, lds, occ)
+
+
+def test_register_file_rule_closed_forms():
+    d = S.MI355X
+    # 512 registers per lane: a wave of 128 registers leaves room for four
+    assert S.waves_per_simd_alloc(64, 64, d) == 4
+    # VGPRs round up to 4, the sum to 8: 61 + 3 -> 64 + 3 -> 72 -> 7 waves
+    assert S.waves_per_simd_alloc(61, 3, d) == 7
+    assert S.waves_per_simd_alloc(256, 256, d) == 1
+    # at most 8 waves per SIMD however few registers
+    assert S.waves_per_simd_alloc(8, 0, d) == 8
+    # a planted mistake (AGPRs not counted) fails the pin above
+    bad = 0
+    for key, (vgpr, agpr, lds, scratch, occ) in S.allocation_table().items():
+        w = key[5] * (1 if key[1] == S.KIND_SKINNY else key[6])
+        o = S.waves_per_simd_alloc(vgpr, 0, d)
+        if lds > 0:
+            o = min(o, S.cdiv((d.lds_cu // lds) * w, d.simds))
+        bad += o != occ
+    assert bad > 100
+
+
+def test_bf16_accumulators_are_exactly_the_agprs():
+    # the bf16 tiled kernel keeps its BM x BN / (64 W) fp32 accumulators in AGPRs
+    n = 0
+    for key, (vgpr, agpr, lds, scratch, occ) in S.allocation_table().items():
+        in_bf16, kind = key[0], key[1]
+        if in_bf16 == 1 and kind == S.KIND_TILED:
+            c = S.Cfg(*key[1:], 1)
+            assert agpr == S.acc_regs(c), key
+            assert lds == S.lds_bytes(c, S.BF16), key
+            n += 1
+    assert n > 500
+
+
+def test_resident_blocks_from_the_allocation():
+    d = S.MI355X
+    # 256 x 256 x 64 tile, 2 x 4 waves: 128 AGPRs of accumulators per lane,
+    # 128 KiB of LDS -- one workgroup per CU whatever the registers allow
+    c = S.Cfg(S.KIND_TILED, 256, 256, 64, 2, 4, 2, 1)
+    vgpr, agpr, lds, scratch = S.compiled_alloc(S.BF16, c)
+    assert lds == 2 * (256 * 64 + 64 * 256) * 2 and scratch == 0
+    assert S.resident_blocks(c, S.BF16, d) == 1
+    # a configuration without a compiled kernel falls back to the estimate
+    assert S.compiled_alloc(S.BF16, S.Cfg(S.KIND_TILED, 256, 256, 128, 2, 4, 2, 1)) is None
+    # the H100 replica never looks at the allocation
+    assert S.resident_blocks(c, S.BF16, S.H100_REPLICA) == S.blocks_per_cu(c, S.BF16, S.H100_REPLICA)
+    # wherever the two counts differ, the model prices the compiler's
+    diff = 0
+    for key in S.allocation_table():
+        c = S.Cfg(*key[1:], 1)
+        dt = S.BF16 if key[0] else S.F32
+        if S.check_static(dt, c) == S.OK and S.resident_blocks(c, dt, d) != S.blocks_per_cu(c, dt, d):
+            diff += 1
+    assert diff > 0
+
+
+def test_spilling_kernels_are_rejected():
+    spilling = [k for k, v in S.allocation_table().items() if v[3] > 0]
+    assert spilling
+    for key in spilling:
+        c = S.Cfg(*key[1:], 1)
+        dt = S.BF16 if key[0] else S.F32
+        M = c.bm if c.kind == S.KIND_SKINNY else 1024
+        Nn, K = 1024, 1024
+        assert S.check(M, Nn, K, dt, c) == S.R_SPILL, key
+    # the estimate is only the pre-build filter: it lets through every kernel
+    # that was compiled, and those that spill are caught by the rule above
+    for key in S.allocation_table():
+        c = S.Cfg(*key[1:], 1)
+        dt = S.BF16 if key[0] else S.F32
+        assert S.check_static(dt, c) == S.OK
+
+
+# ---------------------------------------------------------------- skinny branch of the model
+def _neutral_skinny(**kw):
+    # no latency limit on the stream (a vanishing latency), no per-CU limit,
+    # no efficiency factors, no launch overhead
+    base = dict(lat_mem=1e-30, cu_bw=1e30, skinny_eff=1.0, hbm_eff=1.0, t0=0.0)
+    base.update(kw)
+    return dataclasses.replace(S.MI355X, **base)
+
+
+def test_skinny_model_closed_forms():
+    M, Nn, K = 16, 28672, 8192
+    comp = 2 * (M * K + K * Nn) + 2 * M * Nn
+    c = S.Cfg(S.KIND_SKINNY, 16, 128, 32, 4, 1, 2, 1)
+    d = _neutral_skinny()
+    # memory-bound: the compulsory bytes at the HBM rate, nothing else
+    assert S.model_time(M, Nn, K, S.BF16, c, d) == pytest.approx(comp / d.bw, rel=1e-12)
+    # the achievable fraction divides the stream time
+    d2 = _neutral_skinny(skinny_eff=0.5)
+    assert S.model_time(M, Nn, K, S.BF16, c, d2) == pytest.approx(2 * comp / d.bw, rel=1e-12)
+    # too few loads in flight: bytes in flight = resident waves x 64 lanes x
+    # stages x 8 x 16 bytes; with a latency that makes them half of bw x latency,
+    # the stream runs at half the rate
+    tiles = S.cdiv(Nn, 128)
+    w = c.wgm
+    resident = min(tiles * w, d.n_cu * S.resident_blocks(c, S.BF16, d) * w)
+    inflight = resident * 64.0 * c.stages * 8 * 16
+    d3 = _neutral_skinny(lat_mem=2 * inflight / d.bw)
+    assert S.model_time(M, Nn, K, S.BF16, c, d3) == pytest.approx(2 * comp / d.bw, rel=1e-12)
+    # per-CU limit: 224 active workgroups each at a quarter of the share the
+    # HBM rate would give them
+    d4 = _neutral_skinny(cu_bw=d.bw / (4 * min(tiles, d.n_cu)))
+    assert S.model_time(M, Nn, K, S.BF16, c, d4) == pytest.approx(4 * comp / d.bw, rel=1e-12)
+    # compute-bound: padded rows count (17 rows run as 32)
+    d5 = _neutral_skinny(peak_bf16=1e9)
+    c32 = S.Cfg(S.KIND_SKINNY, 32, 128, 32, 4, 1, 2, 1)
+    assert S.model_time(17, Nn, K, S.BF16, c32, d5) == pytest.approx(2.0 * 32 * Nn * K / 1e9, rel=1e-12)
+    # split-K adds the fp32 slabs to the stream and the second pass after it
+    cs = S.Cfg(S.KIND_SKINNY, 16, 128, 32, 4, 1, 2, 2)
+    slabs = 4.0 * 2 * M * Nn
+    want = (comp + slabs) / d.bw + (slabs + 2 * M * Nn) / d.bw
+    assert S.model_time(M, Nn, K, S.BF16, cs, d) == pytest.approx(want, rel=1e-12)

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_E_INVAL", -2: "TG_E_INFEASIBLE", -3: "TG_E_U
 
 # every symbol include/tilegemm.h declares
 EXPORTS = [
-    "tg_last_error", "tg_version", "tg_set_stream", "gemm_bias_act", "gemm_autotune",
+    "tg_last_error", "tg_version", "tg_set_stream", "gemm_bias_act", "gemm_autotune", "gemm_autotune_ep",
     "tg_enumerate", "tg_space", "tg_check_cfg", "tg_model_time", "tg_model_choice", "tg_grid",
     "tg_default_cfg", "tg_resources", "tg_set_device_override", "tg_get_device_desc",
     "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources", "tg_streams_b",
@@ -97,6 +97,7 @@ def lib():
             "tg_set_stream": ([vp], i32),
             "gemm_bias_act": ([i64, i64, i64, vp, vp, vp, vp, i32, i32, pc], i32),
             "gemm_autotune": ([i64, i64, i64, i32, pc], i32),
+            "gemm_autotune_ep": ([i64, i64, i64, i32, i32, i32, pc], i32),
             "tg_enumerate": ([i64, i64, i64, i32, pc, i32, pi], i32),
             "tg_space": ([i32, pc, i32, pi], i32),
             "tg_check_cfg": ([i64, i64, i64, i32, pc, pi], i32),
@@ -112,8 +113,8 @@ def lib():
             "tg_has_kernel": ([i32, pc], i32),
             "tg_kernel_resources": ([i32, pc, pi], i32),
             "tg_streams_b": ([i64, i32, pc, pi], i32),
-            "tg_autotune_table": ([i64, i64, i64, i32, ctypes.POINTER(TuneRow), i32, pi], i32),
-            "tg_cache_lookup": ([i64, i64, i64, i32, pc, dp, pi], i32),
+            "tg_autotune_table": ([i64, i64, i64, i32, i32, i32, ctypes.POINTER(TuneRow), i32, pi], i32),
+            "tg_cache_lookup": ([i64, i64, i64, i32, i32, i32, pc, dp, pi], i32),
             "tg_cache_save": ([ctypes.c_char_p], i32),
             "tg_cache_load": ([ctypes.c_char_p, pi, pi], i32),
             "tg_cache_clear": ([], None),
@@ -155,9 +156,19 @@ def gemm_bias_act_ptr(M, N, K, A, B, bias, C, dtype, act, cfg=None) -> int:
     return lib().gemm_bias_act(M, N, K, A or None, B or None, bias or None, C or None, int(dtype), a, c)
 
 
-def gemm_autotune(M, N, K, dtype) -> Cfg:
+def _act(act) -> int:
+    return ACT[act] if isinstance(act, str) else int(act)
+
+
+def gemm_autotune(M, N, K, dtype, act="none", bias=False) -> Cfg:
+    """Tune (or look up) the call of this shape with activation `act` and,
+    if `bias`, a bias vector: gemm_autotune for the plain call, else
+    gemm_autotune_ep."""
     out = Cfg()
-    check(lib().gemm_autotune(M, N, K, int(dtype), ctypes.byref(out)))
+    if _act(act) == 0 and not bias:
+        check(lib().gemm_autotune(M, N, K, int(dtype), ctypes.byref(out)))
+    else:
+        check(lib().gemm_autotune_ep(M, N, K, int(dtype), _act(act), 1 if bias else 0, ctypes.byref(out)))
     return out
 
 
@@ -254,20 +265,22 @@ def streams_b(M, dtype, cfg) -> bool:
 
 
 # ---------------------------------------------------------------- cache
-def autotune_table(M, N, K, dtype):
+def autotune_table(M, N, K, dtype, act="none", bias=False):
     """Rows of the last tuning run for the key: (cfg, model us, median of the
     short samples, median of the long confirmation samples); -1 where not
     measured or not confirmed."""
     n = ctypes.c_int()
-    check(lib().tg_autotune_table(M, N, K, int(dtype), None, 0, ctypes.byref(n)))
+    a, b = _act(act), 1 if bias else 0
+    check(lib().tg_autotune_table(M, N, K, int(dtype), a, b, None, 0, ctypes.byref(n)))
     buf = (TuneRow * max(1, n.value))()
-    check(lib().tg_autotune_table(M, N, K, int(dtype), buf, n.value, ctypes.byref(n)))
+    check(lib().tg_autotune_table(M, N, K, int(dtype), a, b, buf, n.value, ctypes.byref(n)))
     return [(buf[i].cfg, buf[i].predicted_us, buf[i].measured_us, buf[i].confirmed_us) for i in range(n.value)]
 
 
-def cache_lookup(M, N, K, dtype):
+def cache_lookup(M, N, K, dtype, act="none", bias=False):
     out, us, hit = Cfg(), ctypes.c_double(), ctypes.c_int()
-    check(lib().tg_cache_lookup(M, N, K, int(dtype), ctypes.byref(out), ctypes.byref(us), ctypes.byref(hit)))
+    check(lib().tg_cache_lookup(M, N, K, int(dtype), _act(act), 1 if bias else 0, ctypes.byref(out),
+                                ctypes.byref(us), ctypes.byref(hit)))
     return (out, us.value) if hit.value else None
 
 

@@ -202,8 +202,10 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     grid(M, N, c, &tiles, &blocks);
     if (blocks > 0x7FFFFFFF)
         return set_error(TG_E_UNSUPPORTED, "too many workgroups");
+    // held until both kernels of a split-K call are queued (see ensure_workspace)
+    std::unique_lock<std::mutex> ws_hold;
     if (c.split_k > 1) {
-        const int st = ensure_workspace(workspace_bytes_for(M, N, c), stream, &p.ws);
+        const int st = ensure_workspace(workspace_bytes_for(M, N, c), stream, &p.ws, &ws_hold);
         if (st != TG_OK)
             return st;
         p.slab = splitk_slab(M, N);
@@ -259,7 +261,7 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
         // largest M, so one tuning serves the whole bucket
         const int64_t Mk = dispatch_m(M);
         double us;
-        if (cache_find(Mk, N, K, dtype, &c, &us)) {
+        if (cache_find(Mk, N, K, dtype, act, bias != nullptr, &c, &us)) {
             count_cache_hit();
         } else {
             const char* dis = std::getenv("TILEGEMM_DISABLE_AUTOTUNE");
@@ -268,7 +270,7 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
                     return set_error(TG_E_INFEASIBLE, "no feasible configuration");
             } else {
                 const TuneData own{A, B, bias, M};
-                st = autotune(Mk, N, K, dtype, &c, &own);
+                st = autotune(Mk, N, K, dtype, act, bias != nullptr, &c, &own);
                 if (st != TG_OK)
                     return st;
             }
@@ -299,16 +301,23 @@ int tg_dispatch_m(int64_t M, int64_t* key_m)
     return TG_OK;
 }
 
-int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
+int gemm_autotune_ep(int64_t M, int64_t N, int64_t K, int dtype, int act, int has_bias, tg_cfg* out)
 {
     if (!out)
         return set_error(TG_E_INVAL, "out is NULL");
     const int st = validate_problem(M, N, K, dtype);
     if (st != TG_OK)
         return st;
+    if (act < TG_ACT_NONE || act > TG_ACT_GELU)
+        return set_error(TG_E_INVAL, "unknown activation " + std::to_string(act));
     if (M == 0 || N == 0)
         return set_error(TG_E_INVAL, "empty problem has nothing to tune");
-    return autotune(M, N, K, dtype, out);
+    return autotune(M, N, K, dtype, act, has_bias != 0, out);
+}
+
+int gemm_autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out)
+{
+    return gemm_autotune_ep(M, N, K, dtype, TG_ACT_NONE, 0, out);
 }
 
 int tg_enumerate(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, int cap, int* n_feasible)

@@ -115,8 +115,12 @@ __device__ __forceinline__ int swz(int r)
 // error function of Abramowitz & Stegun, Handbook of Mathematical Functions,
 // formula 7.1.26: erfc(x) ~= (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^(-x^2),
 // t = 1 / (1 + p x), x >= 0, absolute error <= 1.5e-7.  1 + erf(z) is taken as
-// 2 - erfc(|z|) for z >= 0 and erfc(|z|) for z < 0, so the negative tail keeps
-// its relative precision.  One reciprocal, one exponential and five FMAs: the
+// 2 - erfc(|z|) for z >= 0 and erfc(|z|) for z < 0, so the GELU error is at
+// most 0.5 |v| 1.5e-7 plus fp32 rounding.  The bound is absolute only: far in
+// the negative tail, where erfc itself falls below 1e-7, the approximation's
+// relative error grows without a useful bound (both values there are far
+// below anything a bf16 output or the tolerance resolves).  One reciprocal,
+// one exponential and five FMAs: the
 // library erff costs several times that, and the epilogue of a 256 x 256 tile
 // evaluates it 65,536 times.
 __device__ __forceinline__ float gelu_erf(float v)

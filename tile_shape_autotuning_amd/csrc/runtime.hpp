@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "../../include/tilegemm.h"
@@ -33,8 +34,10 @@ hipStream_t current_stream();
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias,
                void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked);
 
-// Split-K workspace of the current device and `stream`: grows to at least `ws_bytes`.
-int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws);
+// Split-K workspace of the current device and `stream`: grows to at least
+// `ws_bytes`.  With `hold`, the workspace's lock is handed to the caller, who
+// keeps it until every kernel that uses the buffer is queued.
+int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws, std::unique_lock<std::mutex>* hold = nullptr);
 size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& cfg);
 
 // Split-K second pass (splitk_reduce.hip): C = act(sum of the split slabs +
@@ -55,8 +58,11 @@ struct TuneData {
     const float* bias;
     int64_t rows;
 };
-int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const TuneData* data = nullptr);
-bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us);
+// Candidates are timed running the call's epilogue (act, bias or not), and
+// the result is cached under that epilogue.
+int autotune(int64_t M, int64_t N, int64_t K, int dtype, int act, bool has_bias, tg_cfg* out,
+             const TuneData* data = nullptr);
+bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, int act, bool bias, tg_cfg* out, double* measured_us);
 void count_cache_hit();
 
 // fill kernels for tuning scratch (defined in tune_kernels.hip)

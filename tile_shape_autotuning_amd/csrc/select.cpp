@@ -240,6 +240,24 @@ int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d)
     return b;
 }
 
+int64_t waves_per_simd_alloc(int64_t vgpr, int64_t agpr, const tg_device_desc& d)
+{
+    const int64_t regs = cdiv(cdiv(vgpr, 4) * 4 + agpr, 8) * 8;
+    return regs > 0 ? std::min<int64_t>(d.waves_max, d.vgpr_max / regs) : d.waves_max;
+}
+
+int64_t resident_blocks(const tg_cfg& c, int dtype, const tg_device_desc& d)
+{
+    Alloc a;
+    if (d.mode != 0 || !compiled_alloc(dtype, c, &a) || a.vgpr < 0 || a.agpr < 0 || a.lds < 0)
+        return blocks_per_cu(c, dtype, d);
+    const int64_t w = (int64_t)c.wgm * c.wgn;
+    int64_t b = std::min<int64_t>(d.blocks_max, (d.simds * waves_per_simd_alloc(a.vgpr, a.agpr, d)) / w);
+    if (a.lds > 0)
+        b = std::min<int64_t>(b, d.lds_cu / a.lds);
+    return b;
+}
+
 int64_t transfers_per_wave(const tg_cfg& c, int dtype)
 {
     const int64_t inst = ((int64_t)c.bm + c.bn) * c.bk * in_bytes(dtype) / 1024;
@@ -299,6 +317,14 @@ int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_
     const int st = check_static(dtype, c, d);
     if (st != OK)
         return st;
+    // the register cliff (page "Autotuning & cost models", the search space:
+    // a tile past the register file spills and falls off a cliff): a
+    // configuration whose compiled kernel spills is not a candidate
+    Alloc a;
+    if (d.mode == 0 && compiled_alloc(dtype, c, &a) && a.scratch > 0)
+        return R_SPILL;
+    if (resident_blocks(c, dtype, d) < 1)
+        return R_OCC;
     if (c.split_k > 1) {
         if (K == 0 || cdiv(K, k_per_split(c, K)) != c.split_k)
             return R_SPLIT;
@@ -433,7 +459,7 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     int64_t tiles, units;
     grid(M, N, c, &tiles, &units);
     const int64_t w = (int64_t)c.wgm * c.wgn;
-    const int64_t bcu = blocks_per_cu(c, dtype, d);
+    const int64_t bcu = resident_blocks(c, dtype, d);
 
     if (c.kind == TG_KIND_SKINNY) {
         const double flops_pad = 2.0 * (double)c.bm * (double)N * (double)K;

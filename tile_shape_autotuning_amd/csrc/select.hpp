@@ -12,7 +12,7 @@ namespace tg {
 
 enum Reason {
     OK = 0, R_DTYPE = 1, R_ALIGN = 2, R_SHAPE = 3, R_WAVES = 4, R_DIV = 5, R_LDS = 6,
-    R_ACC = 7, R_VGPR = 8, R_OCC = 9, R_SPLIT = 10, R_SPACE = 11, R_INFLIGHT = 12
+    R_ACC = 7, R_VGPR = 8, R_OCC = 9, R_SPLIT = 10, R_SPACE = 11, R_INFLIGHT = 12, R_SPILL = 13
 };
 
 tg_device_desc mi355x_desc();
@@ -35,6 +35,24 @@ int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d);
 int64_t waves_per_simd(const tg_cfg& c, int dtype, const tg_device_desc& d);
 int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d);
 int64_t transfers_per_wave(const tg_cfg& c, int dtype);
+
+// What the compiler allotted to the kernel that serves a configuration (its
+// resource remarks at build time).  compiled_alloc is defined by the kernel
+// registry of the library (false when no kernel serves c) and returns false
+// in programs built without one (the instantiation-set generator, which runs
+// before any kernel exists).
+struct Alloc {
+    int vgpr, agpr, lds, scratch;
+};
+bool compiled_alloc(int dtype, const tg_cfg& c, Alloc* out);
+// Waves of one kernel a SIMD holds with that allocation: the register file
+// has vgpr_max registers per lane; a wave's share is its architectural VGPRs
+// rounded up to 4, plus its AGPRs, rounded up to 8.
+int64_t waves_per_simd_alloc(int64_t vgpr, int64_t agpr, const tg_device_desc& d);
+// Workgroups resident on one CU, as the cost model counts them: from the
+// compiled kernel's registers and LDS where it exists (MI355X rules), else
+// the filter's estimate (blocks_per_cu).
+int64_t resident_blocks(const tg_cfg& c, int dtype, const tg_device_desc& d);
 int64_t k_per_split(const tg_cfg& c, int64_t K);
 
 // shape-independent rules only (waves, divisibility, LDS, registers, occupancy)

@@ -42,14 +42,19 @@
 
 namespace tg {
 
+// A call is keyed by what it runs: the device, the shape and dtype, and the
+// epilogue (activation, bias or not), since the candidates are timed with it.
 struct CacheKey {
     std::string arch;
     int n_cu;
     int64_t M, N, K;
     int dtype;
+    int act;
+    int bias;
     bool operator<(const CacheKey& o) const
     {
-        return std::tie(arch, n_cu, M, N, K, dtype) < std::tie(o.arch, o.n_cu, o.M, o.N, o.K, o.dtype);
+        return std::tie(arch, n_cu, M, N, K, dtype, act, bias) <
+               std::tie(o.arch, o.n_cu, o.M, o.N, o.K, o.dtype, o.act, o.bias);
     }
 };
 
@@ -64,15 +69,15 @@ static std::mutex g_cache_mu;
 static std::map<CacheKey, CacheEntry> g_cache;
 static int64_t g_n_tunes = 0, g_n_timed = 0, g_n_hits = 0;
 
-static CacheKey make_key(int64_t M, int64_t N, int64_t K, int dtype)
+static CacheKey make_key(int64_t M, int64_t N, int64_t K, int dtype, int act, bool bias)
 {
     const DeviceKey dk = current_key();
-    return CacheKey{dk.arch, dk.n_cu, M, N, K, dtype};
+    return CacheKey{dk.arch, dk.n_cu, M, N, K, dtype, act, bias ? 1 : 0};
 }
 
-bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us)
+bool cache_find(int64_t M, int64_t N, int64_t K, int dtype, int act, bool bias, tg_cfg* out, double* measured_us)
 {
-    const CacheKey k = make_key(M, N, K, dtype);
+    const CacheKey k = make_key(M, N, K, dtype, act, bias);
     std::lock_guard<std::mutex> lk(g_cache_mu);
     auto it = g_cache.find(k);
     if (it == g_cache.end())
@@ -156,9 +161,9 @@ double median_of(std::vector<double> v)
 
 }  // namespace
 
-int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const TuneData* data)
+int autotune(int64_t M, int64_t N, int64_t K, int dtype, int act, bool has_bias, tg_cfg* out, const TuneData* data)
 {
-    const CacheKey key = make_key(M, N, K, dtype);
+    const CacheKey key = make_key(M, N, K, dtype, act, has_bias);
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         auto it = g_cache.find(key);
@@ -194,14 +199,10 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const Tune
     } else {
         if (!have_device())
             return set_error(TG_E_UNSUPPORTED, "measured tuning needs a HIP device (TILEGEMM_TUNE_MODE=model does not)");
-        // only candidates with a compiled kernel can be measured; kernels the
-        // compiler had to spill sit past the register cliff and are skipped
-        const bool allow_spills = env_int("TILEGEMM_ALLOW_SPILLS", 0) != 0;
+        // only candidates with a compiled kernel can be measured (kernels the
+        // compiler had to spill are already out: the filter's spill rule)
         const int max_split = env_int("TILEGEMM_TUNE_MAX_SPLIT", 1 << 30);
-        auto runnable = [&](const tg_cfg& c) {
-            const KernelEntry* k = find_kernel(dtype, c);
-            return k != nullptr && (allow_spills || k->res.scratch <= 0) && c.split_k <= max_split;
-        };
+        auto runnable = [&](const tg_cfg& c) { return find_kernel(dtype, c) != nullptr && c.split_k <= max_split; };
         std::vector<Timed> cands;
         const size_t take = mode == "exhaustive" ? ranked.size() : (size_t)topk;
         std::vector<char> picked(ranked.size(), 0);
@@ -298,7 +299,9 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const Tune
         auto run = [&](Timed& t, int reps) -> bool {
             for (int r = 0; r < reps; ++r) {
                 const void* b = s.B[launches++ % s.B.size()];
-                if (launch_cfg(M, N, K, s.A, b, s.bias, s.C, dtype, TG_ACT_NONE, t.cfg, st, false) != TG_OK)
+                // the call being tuned: its activation, its bias or none
+                if (launch_cfg(M, N, K, s.A, b, has_bias ? s.bias : nullptr, s.C, dtype, act, t.cfg, st, false) !=
+                    TG_OK)
                     return false;
             }
             return true;
@@ -445,15 +448,16 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, const Tune
 
 using namespace tg;
 
-static const char* kHeader = "# tilegemm tuning cache v1";
+static const char* kHeader = "# tilegemm tuning cache v2";
 
 extern "C" {
 
-int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, tg_tune_row* rows, int cap, int* n)
+int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, int act, int has_bias, tg_tune_row* rows, int cap,
+                      int* n)
 {
     if (cap < 0 || (cap > 0 && !rows))
         return set_error(TG_E_INVAL, "bad output buffer");
-    const CacheKey k = make_key(M, N, K, dtype);
+    const CacheKey k = make_key(M, N, K, dtype, act, has_bias != 0);
     std::lock_guard<std::mutex> lk(g_cache_mu);
     auto it = g_cache.find(k);
     if (it == g_cache.end()) {
@@ -470,11 +474,12 @@ int tg_autotune_table(int64_t M, int64_t N, int64_t K, int dtype, tg_tune_row* r
     return TG_OK;
 }
 
-int tg_cache_lookup(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* measured_us, int* hit)
+int tg_cache_lookup(int64_t M, int64_t N, int64_t K, int dtype, int act, int has_bias, tg_cfg* out,
+                    double* measured_us, int* hit)
 {
     if (!out || !hit)
         return set_error(TG_E_INVAL, "NULL argument");
-    *hit = cache_find(M, N, K, dtype, out, measured_us) ? 1 : 0;
+    *hit = cache_find(M, N, K, dtype, act, has_bias != 0, out, measured_us) ? 1 : 0;
     return TG_OK;
 }
 
@@ -490,9 +495,9 @@ int tg_cache_save(const char* path)
         for (const auto& kv : g_cache) {
             const CacheKey& k = kv.first;
             const CacheEntry& e = kv.second;
-            std::snprintf(buf, sizeof buf, "%s %d %d %lld %lld %lld %d %d %d %d %d %d %d %d %d %.17g %.17g\n",
+            std::snprintf(buf, sizeof buf, "%s %d %d %lld %lld %lld %d %d %d %d %d %d %d %d %d %d %d %.17g %.17g\n",
                           k.arch.c_str(), k.n_cu, TG_VERSION, (long long)k.M, (long long)k.N, (long long)k.K,
-                          k.dtype, e.cfg.kind, e.cfg.bm, e.cfg.bn, e.cfg.bk, e.cfg.wgm, e.cfg.wgn, e.cfg.stages,
+                          k.dtype, k.act, k.bias, e.cfg.kind, e.cfg.bm, e.cfg.bn, e.cfg.bk, e.cfg.wgm, e.cfg.wgn, e.cfg.stages,
                           e.cfg.split_k, e.measured_us, e.predicted_us);
             os << buf;
         }
@@ -528,7 +533,7 @@ int tg_cache_load(const char* path, int* n_loaded, int* n_skipped)
         CacheEntry e{};
         int ver;
         long long M, N, K;
-        if (!(is >> k.arch >> k.n_cu >> ver >> M >> N >> K >> k.dtype >> e.cfg.kind >> e.cfg.bm >> e.cfg.bn >>
+        if (!(is >> k.arch >> k.n_cu >> ver >> M >> N >> K >> k.dtype >> k.act >> k.bias >> e.cfg.kind >> e.cfg.bm >> e.cfg.bn >>
               e.cfg.bk >> e.cfg.wgm >> e.cfg.wgn >> e.cfg.stages >> e.cfg.split_k >> e.measured_us >>
               e.predicted_us))
             return set_error(TG_E_CACHE, "malformed cache line " + std::to_string(lineno));
@@ -538,7 +543,8 @@ int tg_cache_load(const char* path, int* n_loaded, int* n_skipped)
         k.M = M;
         k.N = N;
         k.K = K;
-        if (ver != TG_VERSION || validate_problem(M, N, K, k.dtype) != TG_OK) {
+        if (ver != TG_VERSION || validate_problem(M, N, K, k.dtype) != TG_OK || k.act < TG_ACT_NONE ||
+            k.act > TG_ACT_GELU || (k.bias != 0 && k.bias != 1)) {
             ++skipped;   // another library version, or not a valid problem
             continue;
         }

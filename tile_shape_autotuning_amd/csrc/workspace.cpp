@@ -15,11 +15,16 @@ namespace tg {
 // One split-K workspace per (device, stream): the slabs a GEMM writes are read
 // by the second pass queued behind it on the same stream, so calls on
 // different streams never touch each other's slabs and may run concurrently.
+// Host threads that share a stream (every thread's default is the null
+// stream) take the workspace's lock from the size check until both kernels
+// of their call are queued: the GEMM and the second pass of one call are
+// then adjacent on the stream, and the buffer is never replaced between them.
 struct Workspace {
+    std::mutex mu;
     float* ws = nullptr;
     size_t ws_bytes = 0;
 };
-static std::mutex g_ws_mu;
+static std::mutex g_ws_mu;   // guards the map itself
 static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& c)
@@ -29,14 +34,19 @@ size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& c)
     return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
 }
 
-int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws)
+int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws, std::unique_lock<std::mutex>* hold)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return set_hip_error(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    Workspace& w = g_ws[{dev, stream}];
+    Workspace* wp;
+    {
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        wp = &g_ws[{dev, stream}];   // map nodes never move
+    }
+    Workspace& w = *wp;
+    std::unique_lock<std::mutex> lk(w.mu);
     if (w.ws_bytes < ws_bytes) {
         // the old buffer may still be in use by kernels queued on this stream
         e = hipStreamSynchronize(stream);
@@ -52,6 +62,8 @@ int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws)
         w.ws_bytes = ws_bytes;
     }
     *ws = w.ws;
+    if (hold)
+        *hold = std::move(lk);
     return TG_OK;
 }
 
