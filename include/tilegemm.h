@@ -18,6 +18,7 @@
 #ifndef TILEGEMM_H
 #define TILEGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -144,6 +145,26 @@ int tg_set_stream(void *hip_stream);
  */
 int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   const float *bias, void *C, int dtype, int act, const tg_cfg *cfg);
+
+/*
+ * gemm_bias_act for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, layouts, stream and results as gemm_bias_act (the same
+ * kernels run), but the call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine, and it never tunes -- with cfg == NULL it takes
+ * the cache entry of M's shape bucket, else the cost model's choice.
+ * Split-K partial sums go to one fixed device array of
+ * tg_noalloc_scratch_bytes() bytes (32 MiB) that each GPU the library runs on
+ * holds until the process ends; a call whose slabs need more
+ * (split_k x M x N floats, each slab rounded up to 64) is refused with
+ * TG_E_INVAL before anything is queued.  Every call on one GPU shares that
+ * GPU's array: calls on one stream are ordered by it, but calls that overlap
+ * on one GPU through different streams race on the array and may return
+ * wrong results.  Other errors as gemm_bias_act.
+ */
+int gemm_bias_act_noalloc(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                          const float *bias, void *C, int dtype, int act, const tg_cfg *cfg);
+size_t tg_noalloc_scratch_bytes(void);
 
 /*
  * Run-time dispatch over shape buckets (page "Tile Selection: Cost Models

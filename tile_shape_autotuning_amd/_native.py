@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_E_INVAL", -2: "TG_E_INFEASIBLE", -3: "TG_E_U
 # every symbol include/tilegemm.h declares
 EXPORTS = [
     "tg_last_error", "tg_version", "tg_set_stream", "gemm_bias_act", "gemm_autotune", "gemm_autotune_ep",
+    "gemm_bias_act_noalloc", "tg_noalloc_scratch_bytes",
     "tg_enumerate", "tg_space", "tg_check_cfg", "tg_model_time", "tg_model_choice", "tg_grid",
     "tg_default_cfg", "tg_resources", "tg_set_device_override", "tg_get_device_desc",
     "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources", "tg_streams_b",
@@ -97,6 +98,8 @@ def lib():
             "tg_set_stream": ([vp], i32),
             "gemm_bias_act": ([i64, i64, i64, vp, vp, vp, vp, i32, i32, pc], i32),
             "gemm_autotune": ([i64, i64, i64, i32, pc], i32),
+            "gemm_bias_act_noalloc": ([i64, i64, i64, vp, vp, vp, vp, i32, i32, pc], i32),
+            "tg_noalloc_scratch_bytes": ([], ctypes.c_size_t),
             "gemm_autotune_ep": ([i64, i64, i64, i32, i32, i32, pc], i32),
             "tg_enumerate": ([i64, i64, i64, i32, pc, i32, pi], i32),
             "tg_space": ([i32, pc, i32, pi], i32),
@@ -154,6 +157,18 @@ def gemm_bias_act_ptr(M, N, K, A, B, bias, C, dtype, act, cfg=None) -> int:
     c = None if cfg is None else ctypes.byref(Cfg.of(cfg))
     a = ACT[act] if isinstance(act, str) else int(act)
     return lib().gemm_bias_act(M, N, K, A or None, B or None, bias or None, C or None, int(dtype), a, c)
+
+
+def gemm_bias_act_noalloc_ptr(M, N, K, A, B, bias, C, dtype, act, cfg=None) -> int:
+    """Raw C-ABI call of the entry point that allocates nothing (device
+    addresses as ints); returns the status."""
+    c = None if cfg is None else ctypes.byref(Cfg.of(cfg))
+    a = ACT[act] if isinstance(act, str) else int(act)
+    return lib().gemm_bias_act_noalloc(M, N, K, A or None, B or None, bias or None, C or None, int(dtype), a, c)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().tg_noalloc_scratch_bytes())
 
 
 def _act(act) -> int:

@@ -149,7 +149,8 @@ static LaunchFn launch_fn(const KernelEntry& ke, const GemmParams& p)
 }
 
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, void* C,
-               int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked)
+               int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked,
+               const ExternalWorkspace* ext)
 {
     const tg_device_desc d = current_desc();
     tg_cfg c = cfg;
@@ -205,9 +206,18 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     // held until both kernels of a split-K call are queued (see ensure_workspace)
     std::unique_lock<std::mutex> ws_hold;
     if (c.split_k > 1) {
-        const int st = ensure_workspace(workspace_bytes_for(M, N, c), stream, &p.ws, &ws_hold);
-        if (st != TG_OK)
-            return st;
+        const size_t need = workspace_bytes_for(M, N, c);
+        if (ext) {
+            if (need > ext->bytes)
+                return set_error(TG_E_INVAL, "split-K partial sums need " + std::to_string(need) +
+                                                 " bytes, more than the " + std::to_string(ext->bytes) +
+                                                 " bytes of the caller-independent scratch");
+            p.ws = ext->ws;
+        } else {
+            const int st = ensure_workspace(need, stream, &p.ws, &ws_hold);
+            if (st != TG_OK)
+                return st;
+        }
         p.slab = splitk_slab(M, N);
     }
     hipError_t e = launch_fn(*ke, p)(p, (int)blocks, stream);
@@ -218,6 +228,54 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
         if (e != hipSuccess)
             return set_hip_error(e, "split-K reduction launch");
     }
+    return TG_OK;
+}
+
+int validate_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, int dtype, int act)
+{
+    const int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    if (act < TG_ACT_NONE || act > TG_ACT_GELU)
+        return set_error(TG_E_INVAL, "unknown activation " + std::to_string(act));
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (!C || (K > 0 && (!A || !B)))
+        return set_error(TG_E_INVAL, "NULL pointer for a non-empty operand");
+    if (!have_device())
+        return set_error(TG_E_UNSUPPORTED, "no HIP device");
+    return TG_OK;
+}
+
+int select_for_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, int dtype,
+                    int act, bool allow_tuning, tg_cfg* out)
+{
+    // the cache entry of M's shape bucket: chosen (tuned) at the bucket's
+    // largest M, so one tuning serves the whole bucket
+    const int64_t Mk = dispatch_m(M);
+    tg_cfg c;
+    double us;
+    if (cache_find(Mk, N, K, dtype, act, bias != nullptr, &c, &us)) {
+        count_cache_hit();
+    } else {
+        const char* dis = std::getenv("TILEGEMM_DISABLE_AUTOTUNE");
+        if (!allow_tuning || (dis && std::strcmp(dis, "0") != 0 && dis[0])) {
+            if (!model_choice(Mk, N, K, dtype, current_desc(), &c, nullptr))
+                return set_error(TG_E_INFEASIBLE, "no feasible configuration");
+        } else {
+            const TuneData own{A, B, bias, M};
+            const int st = autotune(Mk, N, K, dtype, act, bias != nullptr, &c, &own);
+            if (st != TG_OK)
+                return st;
+        }
+    }
+    // every rule that depends on M holds across a bucket (the skinny kind's
+    // row tile is M rounded up to 16, the same for the whole bucket); the
+    // check stays as a guard
+    if (Mk != M && check(M, N, K, dtype, c, current_desc()) != OK &&
+        !model_choice(M, N, K, dtype, current_desc(), &c, nullptr))
+        return set_error(TG_E_INFEASIBLE, "no feasible configuration");
+    *out = c;
     return TG_OK;
 }
 
@@ -240,49 +298,18 @@ int tg_set_stream(void* hip_stream)
 int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, void* C,
                   int dtype, int act, const tg_cfg* cfg)
 {
-    int st = validate_problem(M, N, K, dtype);
-    if (st != TG_OK)
+    const int st = validate_call(M, N, K, A, B, C, dtype, act);
+    if (st != TG_OK || M == 0 || N == 0)
         return st;
-    if (act < TG_ACT_NONE || act > TG_ACT_GELU)
-        return set_error(TG_E_INVAL, "unknown activation " + std::to_string(act));
-    if (M == 0 || N == 0)
-        return TG_OK;
-    if (!C || (K > 0 && (!A || !B)))
-        return set_error(TG_E_INVAL, "NULL pointer for a non-empty operand");
-    if (!have_device())
-        return set_error(TG_E_UNSUPPORTED, "no HIP device");
     tg_cfg c;
-    bool from_selection = false;
     if (cfg) {
         c = *cfg;
     } else {
-        from_selection = true;
-        // the cache entry of M's shape bucket: chosen (tuned) at the bucket's
-        // largest M, so one tuning serves the whole bucket
-        const int64_t Mk = dispatch_m(M);
-        double us;
-        if (cache_find(Mk, N, K, dtype, act, bias != nullptr, &c, &us)) {
-            count_cache_hit();
-        } else {
-            const char* dis = std::getenv("TILEGEMM_DISABLE_AUTOTUNE");
-            if (dis && std::strcmp(dis, "0") != 0 && dis[0]) {
-                if (!model_choice(Mk, N, K, dtype, current_desc(), &c, nullptr))
-                    return set_error(TG_E_INFEASIBLE, "no feasible configuration");
-            } else {
-                const TuneData own{A, B, bias, M};
-                st = autotune(Mk, N, K, dtype, act, bias != nullptr, &c, &own);
-                if (st != TG_OK)
-                    return st;
-            }
-        }
-        // every rule that depends on M holds across a bucket (the skinny
-        // kind's row tile is M rounded up to 16, the same for the whole
-        // bucket); the check stays as a guard
-        if (Mk != M && check(M, N, K, dtype, c, current_desc()) != OK &&
-            !model_choice(M, N, K, dtype, current_desc(), &c, nullptr))
-            return set_error(TG_E_INFEASIBLE, "no feasible configuration");
+        const int r = select_for_call(M, N, K, A, B, bias, dtype, act, true, &c);
+        if (r != TG_OK)
+            return r;
     }
-    return launch_cfg(M, N, K, A, B, bias, C, dtype, act, c, current_stream(), from_selection);
+    return launch_cfg(M, N, K, A, B, bias, C, dtype, act, c, current_stream(), cfg == nullptr);
 }
 
 int tg_set_shape_buckets(int on)

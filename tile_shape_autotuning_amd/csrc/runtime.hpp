@@ -28,11 +28,28 @@ bool have_device();
 
 hipStream_t current_stream();
 
+// Split-K partial sums in memory the caller provides instead of the
+// library-owned workspace: `bytes` of device memory at `ws`, 256-byte aligned.
+struct ExternalWorkspace {
+    float* ws;
+    size_t bytes;
+};
+
 // Validates arguments and launches one configuration (no selection).
-// `allow_misaligned_unaligned_kind` lets an aligned shape with misaligned
-// pointers run the element-load kernel.
+// `pointers_checked` = false: the configuration came from selection, which did
+// not see the pointers; misaligned pointers then run the element-load kernel.
+// `ext`: split-K slabs go there (nothing is allocated; a call needing more
+// than ext->bytes is refused), else into the (device, stream) workspace.
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias,
-               void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked);
+               void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked,
+               const ExternalWorkspace* ext = nullptr);
+
+// The configuration a call without cfg uses: the cache entry of M's shape
+// bucket; on a miss, tuning (allow_tuning, unless TILEGEMM_DISABLE_AUTOTUNE
+// is set) or else the cost model's choice.
+int select_for_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, int dtype,
+                    int act, bool allow_tuning, tg_cfg* out);
+int validate_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B, void* C, int dtype, int act);
 
 // Split-K workspace of the current device and `stream`: grows to at least
 // `ws_bytes`.  With `hold`, the workspace's lock is handed to the caller, who
