@@ -223,6 +223,22 @@ def persisted_report(shapes):
             "model_hit": r["model_hit"], "rank_corr": r["rank_corr"],
             "timed_here_is_chosen": timed == r["chosen"]["cfg"] if timed is not None else None}
     return out
+CALIBRATION_REPORT = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "calibration_report.json")
+
+
+def calibration_summary():
+    """The cost model's calibration, scored on shapes the fit did not see
+    (offline: tile_shape_autotuning_amd.calibrate on the committed tables)."""
+    with open(CALIBRATION_REPORT) as f:
+        r = json.load(f)
+    keep = ("tables", "model_hits", "best_in_topk", "geomean_choice_over_best", "mean_rank_corr", "msle")
+    return {"measured_in_this_run": False, "source": r.get("source", ""),
+            "train": r["split"]["train"], "held_out": r["split"]["held_out"],
+            "constants_fitted": r["constants_fitted"],
+            **{k: {x: r[k][x] for x in keep} for k in ("held_out_before", "held_out_after",
+                                                       "train_before", "train_after")}}
+
+
 # per-shape tuning results measured on MI355X (the library's cache file format)
 DEFAULT_CACHE = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "mi355x.cache")
 
@@ -588,6 +604,8 @@ def main():
                            "model_hit_rate": line["model_hit_rate"], "report": rep}, f, indent=1)
     elif tuning.startswith("cache") and os.path.exists(DEFAULT_REPORT):
         line["tuning_report"] = persisted_report(shapes)
+    if os.path.exists(CALIBRATION_REPORT):
+        line["calibration"] = calibration_summary()
     if a.buckets:
         line["buckets"] = bucket_report(torch, 100)
     if (a.rmsnorm or not a.only) and not a.no_rmsnorm:

@@ -245,6 +245,11 @@ int tg_check_cfg(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, 
  * of compute time at the wave and tile efficiencies and memory time).
  * TG_E_INFEASIBLE if cfg fails the filter for the shape. */
 int tg_model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg, double *us);
+/* The cost-model times of n configurations at once (same passages), in
+ * microseconds; -1 for a configuration that fails the filter for the shape.
+ * For fitting the model's constants to measured tables.  TG_E_INVAL for
+ * n < 0 or NULL buffers with n > 0. */
+int tg_model_times(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfgs, int n, double *us);
 /* The model's choice (same passages; ties keep the first in canonical order):
  * the feasible configuration with the smallest model time and that time (us
  * may be NULL).  TG_E_INFEASIBLE if nothing is feasible. */

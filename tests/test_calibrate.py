@@ -1,0 +1,99 @@
+"""The cost-model calibration (tile_shape_autotuning_amd/calibrate.py), on the
+CPU: tables synthesised from the library's own model under known constants
+must be fitted back to exactly those constants, with a perfect score on the
+training and on the held-out tables; the train / held-out split is the fixed
+one the report states."""
+import math
+import os
+
+import pytest
+
+from oracle import select_ref as S
+
+tg = pytest.importorskip("tile_shape_autotuning_amd")
+from tile_shape_autotuning_amd import _native as N  # noqa: E402
+from tile_shape_autotuning_amd import calibrate as C  # noqa: E402
+
+SHAPES = [("bf16_workload_a", 1000, 1000, 8192, S.BF16), ("c01_bf16_64x4096x4096", 64, 4096, 4096, S.BF16),
+          ("c02_bf16_2048x2048x1024", 2048, 2048, 1024, S.BF16), ("c03_f32_256x384x256", 256, 384, 256, S.F32),
+          ("c04_bf16_16x8192x2048", 16, 8192, 2048, S.BF16)]
+GRID = {"lds_bw_cu": [160.0e9, 230.0e9], "lat_step": [0.8e-6, 1.25e-6], "w1_eff": [0.4, 0.55]}
+TRUTH = {"lds_bw_cu": 230.0e9, "lat_step": 1.25e-6, "w1_eff": 0.4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(N.LIB_PATH):
+        pytest.skip("libtilegemm.so not built")
+    yield
+    N.set_device_override(None)
+
+
+def _tables(truth):
+    base = N.builtin_device_desc(0)
+    d = N.DeviceDesc.from_buffer_copy(base)
+    for k, v in truth.items():
+        setattr(d, k, v)
+    tabs = []
+    for name, M, Nn, K, dt in SHAPES:
+        cfgs = [c.astuple() for c in S.enumerate_feasible(M, Nn, K, dt)][::3]
+        N.set_device_override(d)
+        meas = N.model_times_us(M, Nn, K, dt, cfgs)
+        N.set_device_override(base)
+        pred = N.model_times_us(M, Nn, K, dt, cfgs)
+        tabs.append({"workload": name, "M": M, "N": Nn, "K": K, "dtype": dt,
+                     "rows": [[list(c), p, m] for c, p, m in zip(cfgs, pred, meas)]})
+    N.set_device_override(None)
+    return tabs
+
+
+def test_split_is_fixed_by_name():
+    assert C.held_out("c01_bf16_1x4096x4096") and C.held_out("c23_x")
+    assert not C.held_out("c02_bf16_8x14336x4096") and not C.held_out("bf16_decode_m16")
+    train, test = C.split(_tables(TRUTH))
+    assert [t["workload"] for t in test] == ["c01_bf16_64x4096x4096", "c03_f32_256x384x256"]
+    assert len(train) == 3
+
+
+def test_fit_recovers_known_constants_and_scores_held_out_tables():
+    rep = C.calibrate(_tables(TRUTH), topk=16, grid=GRID)
+    assert rep["constants_fitted"] == TRUTH
+    for part in ("train_after", "held_out_after"):
+        r = rep[part]
+        assert r["model_hits"] == r["tables"] and r["best_in_topk"] == r["tables"]
+        assert r["msle"] == 0.0 and r["geomean_choice_over_best"] == 1.0
+        assert all(math.isclose(v["rank_corr"], 1.0) for v in r["per_table"].values())
+    # before the fit the model (other constants) is off the synthetic truth
+    assert rep["held_out_before"]["msle"] > 0.0
+
+
+def test_fit_sees_only_the_training_tables():
+    # corrupt the held-out tables: the fitted constants must not move
+    tabs = _tables(TRUTH)
+    for t in tabs:
+        if C.held_out(t["workload"]):
+            for r in t["rows"]:
+                r[2] = 1.0
+    rep = C.calibrate(tabs, topk=16, grid=GRID)
+    assert rep["constants_fitted"] == TRUTH
+
+
+def test_committed_report_matches_the_committed_tables_and_built_in_constants():
+    """The held-out figures the report states are what the committed tables give
+    under the library's built-in MI355X constants, which are the fitted ones."""
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    tuned = os.path.join(root, "tile_shape_autotuning_amd", "tuned")
+    with open(os.path.join(tuned, "calibration_report.json")) as f:
+        rep = json.load(f)
+    base = N.builtin_device_desc(0)
+    for k, v in rep["constants_fitted"].items():
+        assert getattr(base, k) == v, k
+    tabs = C.load_tables(os.path.join(tuned, "tables"))
+    train, test = C.split(tabs)
+    assert [t["workload"] for t in test] == rep["split"]["held_out"]
+    got = C.evaluate(test, base, rep["topk"])
+    N.set_device_override(None)
+    for k in ("model_hits", "best_in_topk", "geomean_choice_over_best", "mean_rank_corr", "msle"):
+        assert got[k] == rep["held_out_after"][k], k
+    assert rep["held_out_after"]["model_hits"] > rep["held_out_before"]["model_hits"]

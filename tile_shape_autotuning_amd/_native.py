@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_E_INVAL", -2: "TG_E_INFEASIBLE", -3: "TG_E_U
 EXPORTS = [
     "tg_last_error", "tg_version", "tg_set_stream", "gemm_bias_act", "gemm_autotune", "gemm_autotune_ep",
     "gemm_bias_act_noalloc", "tg_noalloc_scratch_bytes",
-    "tg_enumerate", "tg_space", "tg_check_cfg", "tg_model_time", "tg_model_choice", "tg_grid",
+    "tg_enumerate", "tg_space", "tg_check_cfg", "tg_model_time", "tg_model_times", "tg_model_choice", "tg_grid",
     "tg_default_cfg", "tg_resources", "tg_set_device_override", "tg_get_device_desc",
     "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources", "tg_streams_b",
     "tg_autotune_table", "tg_cache_lookup", "tg_cache_save", "tg_cache_load", "tg_cache_clear",
@@ -106,6 +106,7 @@ def lib():
             "tg_check_cfg": ([i64, i64, i64, i32, pc, pi], i32),
             "tg_model_time": ([i64, i64, i64, i32, pc, dp], i32),
             "tg_model_choice": ([i64, i64, i64, i32, pc, dp], i32),
+            "tg_model_times": ([i64, i64, i64, i32, pc, i32, dp], i32),
             "tg_grid": ([i64, i64, i64, pc, pi64, pi64], i32),
             "tg_default_cfg": ([i64, i64, i64, i32, pc], i32),
             "tg_resources": ([i32, pc, pi, pi, pi], i32),
@@ -214,6 +215,15 @@ def model_time_us(M, N, K, dtype, cfg) -> float:
     us = ctypes.c_double()
     check(lib().tg_model_time(M, N, K, int(dtype), ctypes.byref(Cfg.of(cfg)), ctypes.byref(us)))
     return us.value
+
+
+def model_times_us(M, N, K, dtype, cfgs):
+    """Model times (us) of many configurations in one call; -1 where infeasible."""
+    n = len(cfgs)
+    buf = (Cfg * max(1, n))(*[Cfg.of(c) for c in cfgs])
+    out = (ctypes.c_double * max(1, n))()
+    check(lib().tg_model_times(M, N, K, int(dtype), buf, n, out))
+    return [out[i] for i in range(n)]
 
 
 def model_choice(M, N, K, dtype):

@@ -398,6 +398,19 @@ int tg_model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg* cfg,
     return TG_OK;
 }
 
+int tg_model_times(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg* cfgs, int n, double* us)
+{
+    if (n < 0 || (n > 0 && (!cfgs || !us)))
+        return set_error(TG_E_INVAL, "bad buffers");
+    const int st = validate_problem(M, N, K, dtype);
+    if (st != TG_OK)
+        return st;
+    const tg_device_desc d = current_desc();
+    for (int i = 0; i < n; ++i)
+        us[i] = check(M, N, K, dtype, cfgs[i], d) == OK ? model_time(M, N, K, dtype, cfgs[i], d) * 1e6 : -1.0;
+    return TG_OK;
+}
+
 int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, double* us)
 {
     if (!out)

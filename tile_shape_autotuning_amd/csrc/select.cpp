@@ -50,12 +50,12 @@ tg_device_desc mi355x_desc()
     d.t0 = 4.0e-6;
     d.unaligned_eff = 0.25;
     d.lat_mem = 2.0e-6;
-    d.cu_bw = 75.0e9;
-    d.lds_bw_cu = 307.2e9;
-    d.lat_step = 0.8e-6;
-    d.lat_l2 = 0.5e-6;
+    d.cu_bw = 60.0e9;
+    d.lds_bw_cu = 192.0e9;
+    d.lat_step = 1.0e-6;
+    d.lat_l2 = 0.4e-6;
     d.l2_bytes = 32.0e6;
-    d.w1_eff = 0.55;
+    d.w1_eff = 0.5;
     d.skinny_eff = 0.75;
     d.hbm_eff = 0.9125;
     return d;

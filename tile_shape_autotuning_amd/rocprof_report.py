@@ -227,11 +227,13 @@ def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_di
         lines.append(f"algorithmic GB/s:           {sm['GB/s']:.1f}   (compulsory {algo_bytes:.4g} B per {per})")
     if "mfma_util" in sm:
         lines.append(f"MFMA busy / (4 x CU busy):  {sm['mfma_util']:.3f}")
-    if c.get("GRBM_GUI_ACTIVE") and c.get("SQ_BUSY_CU_CYCLES"):
-        lines.append(f"busy CUs (CU-busy / GPU-busy cycles, 8 XCDs): {c['SQ_BUSY_CU_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / 8):.0f}")
     if c.get("GRBM_GUI_ACTIVE") and sm["avg_us"] >= 200.0:
-        # the busy-cycle counter also spans a few microseconds around each
-        # dispatch: only long kernels give a usable clock
+        # the GPU-busy counter also spans several microseconds around each
+        # dispatch (a 27 us kernel read as 80,000 cycles per XCD, 3 GHz): both
+        # figures that divide by it are printed for long kernels only
+        if c.get("SQ_BUSY_CU_CYCLES"):
+            lines.append(f"busy CUs (CU-busy / GPU-busy cycles, 8 XCDs): "
+                         f"{c['SQ_BUSY_CU_CYCLES'] / (c['GRBM_GUI_ACTIVE'] / 8):.0f}")
         lines.append(f"clock (GPU-busy cycles per XCD / duration): {observed_clock_ghz(c, sm['avg_us']):.2f} GHz")
     if "lds_conflict_cycles_per_lds_inst" in sm:
         lines.append(f"LDS bank-conflict cycles per LDS instruction: {sm['lds_conflict_cycles_per_lds_inst']:.2f}")
