@@ -418,6 +418,50 @@ def bucket_report(torch, steps):
             "max_bucketed_over_exact": max(ratios)}
 
 
+STREAMK_SHAPE = (4352, 4352, 8192)
+
+
+def streamk_study(torch):
+    """The stream-K kind where it pays: a bf16 problem of 17 x 17 tiles of
+    256 x 256 (one full round of 256 and a tail of 33) with a long K.  Times
+    the same tile data-parallel (two rounds) and with the stream-K tail, and
+    the hybrid tuner's own choice for the shape (which sees both kinds)."""
+    import tile_shape_autotuning_amd as tg
+    M, N, K = STREAMK_SHAPE
+    sk_ = 1.0 / np.sqrt(K)
+    A, B, _ = wl.make_inputs(M, N, K, wl.BF16, wl.Dist("normal", sk_), wl.Dist("normal", sk_), None, 6)
+    A_d, B_d = _dev(A, torch), _dev(B, torch)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    out = {"shape": f"{M} x {N} x {K} bf16", "tiles_256x256": 17 * 17}
+
+    def timed(cfg):
+        call = tg.BoundGemm(A_d, B_d, None, act="none", out=C, cfg=cfg)
+        warm_up(call, 3, torch)
+        sec, _ = time_steps(call, max(10, int(0.2 / max(1e-6, _one(call)))), torch)
+        return sec
+
+    def _one(call):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    dp_cfg, sk_cfg = (0, 256, 256, 64, 2, 4, 2, 1), (3, 256, 256, 64, 2, 4, 2, 1)
+    t_dp, t_sk = timed(dp_cfg), timed(sk_cfg)
+    out.update({"data_parallel": {"cfg": list(dp_cfg), "us": round(t_dp * 1e6, 2)},
+                "stream_k": {"cfg": list(sk_cfg), "us": round(t_sk * 1e6, 2)},
+                "data_parallel_over_stream_k": round(t_dp / t_sk, 3)})
+    tuned = tuple(tg.gemm_autotune(M, N, K, wl.BF16).astuple())
+    out["tuner_choice"] = {"cfg": list(tuned), "us": round(timed(tuned) * 1e6, 2), "kind_is_stream_k": tuned[0] == 3}
+    model = tuple(tg.model_choice(M, N, K, wl.BF16)[0].astuple())
+    out["model_choice"] = list(model)
+    out["TFLOP/s_best"] = round(2.0 * M * N * K / min(t_dp, t_sk) / 1e12, 1)
+    log(f"stream-K study: {out}")
+    return out
+
+
 def rmsnorm_report(torch, steps, rows=16384, n=8192):
     """The second workload: RMS normalisation of rows x n bf16 with
     occupancy-only tuning.  Time per call at each occupancy and with the
@@ -478,6 +522,9 @@ def main():
     ap.add_argument("--rmsnorm", action="store_true",
                     help="report the occupancy-tuned RMS normalisation also with --only")
     ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMS normalisation report")
+    ap.add_argument("--streamk", action="store_true", help="report the stream-K study also with --only")
+    ap.add_argument("--no-streamk", action="store_true",
+                    help="skip the stream-K study (4352 x 4352 x 8192: data-parallel against stream-K tail)")
     ap.add_argument("--cfg", type=str, default="",
                     help="force a configuration for the main workload: kind,bm,bn,bk,wgm,wgn,stages,split_k")
     a = ap.parse_args()
@@ -610,6 +657,8 @@ def main():
         line["buckets"] = bucket_report(torch, 100)
     if (a.rmsnorm or not a.only) and not a.no_rmsnorm:
         line["rmsnorm"] = rmsnorm_report(torch, 50)
+    if (a.streamk or not a.only) and not a.no_streamk:
+        line["streamk_study"] = streamk_study(torch)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(main_idx, p.host)

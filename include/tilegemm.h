@@ -53,8 +53,13 @@ typedef enum {
 typedef enum {
     TG_KIND_TILED = 0,     /* block-tiled MFMA kernel, 16-byte vector loads */
     TG_KIND_SKINNY = 1,    /* M <= 64 weight-streaming kernel (bf16 only) */
-    TG_KIND_UNALIGNED = 2  /* block-tiled kernel with element loads, for K or N
+    TG_KIND_UNALIGNED = 2, /* block-tiled kernel with element loads, for K or N
                               not a multiple of the 16-byte vector */
+    TG_KIND_STREAMK = 3    /* bf16 block-tiled kernel: full rounds of tiles one
+                              workgroup each, the last partial round's K steps
+                              spread evenly over a full round of workgroups
+                              (stream-K), pieces of split tiles added in K order
+                              by a second pass; split_k = 1 */
 } tg_kind;
 
 /*
@@ -256,8 +261,11 @@ int tg_model_times(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg
 int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, double *us);
 /* Launch geometry (page "Tile Selection: Cost Models Against Measurement",
  * "The structure of the search space": ceil(M/bm) * ceil(N/bn) blocks): output
- * tiles and launched workgroups (tiles * split_k).  TG_E_INVAL for NULL
- * pointers, non-positive tile sizes or split, negative M or N. */
+ * tiles and launched workgroups (tiles * split_k; for the stream-K kind the
+ * data-parallel tiles plus min(CUs x resident workgroups, tail tiles x K
+ * steps) workgroups for the tail, on the device description in force).
+ * TG_E_INVAL for NULL pointers, non-positive tile sizes, K step or split, and
+ * negative M, N or K. */
 int tg_grid(int64_t M, int64_t N, int64_t K, const tg_cfg *cfg, int64_t *tiles, int64_t *blocks);
 /* The fixed configuration autotuning is always compared against (page "CuTile
  * Autotuning", key rules: the default is among the measured candidates):

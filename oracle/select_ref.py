@@ -45,7 +45,7 @@ import os
 from dataclasses import dataclass
 
 F32, BF16, BF16_F32OUT = 0, 1, 2
-KIND_TILED, KIND_SKINNY, KIND_UNALIGNED = 0, 1, 2
+KIND_TILED, KIND_SKINNY, KIND_UNALIGNED, KIND_STREAMK = 0, 1, 2, 3
 
 # reasons a candidate is rejected (first failing rule)
 OK = 0
@@ -200,7 +200,16 @@ def space(dtype: int, dev: Device = MI355X):
     ubk = 16 if dtype == F32 else 32
     for (bm, bn, wm, wn), s in itertools.product(UNALIGNED_TILES, SPLITS):
         out.append(Cfg(KIND_UNALIGNED, bm, bn, ubk, wm, wn, 2, s))
+    if dtype != F32:
+        # stream-K kind: large tiles, whose last partial round is worth spreading
+        for bm, bn, (wm, wn), st in itertools.product((128, 256), (128, 256), ((2, 2), (2, 4), (4, 2)), (2, 3, 4)):
+            out.append(Cfg(KIND_STREAMK, bm, bn, 64, wm, wn, st, 1))
     return out
+
+
+def dma_kind(c: Cfg, dtype: int) -> bool:
+    """The bf16 kernels that move panels straight into LDS (tiled, stream-K)."""
+    return c.kind in (KIND_TILED, KIND_STREAMK) and dtype != F32
 
 
 # ---------------------------------------------------------------- resources
@@ -227,8 +236,8 @@ def vgpr_estimate(c: Cfg, dtype: int, dev: Device) -> int:
     threads = 64 * c.wgm * c.wgn
     eb = in_bytes(dtype)
     frag = 4 * ((c.bm // c.wgm) // 16 + (c.bn // c.wgn) // 16)
-    if c.kind == KIND_TILED and dtype != F32:
-        # the bf16 tiled kernel loads panels straight into LDS: no staging registers
+    if dma_kind(c, dtype):
+        # the bf16 tiled kernels load panels straight into LDS: no staging registers
         return acc_regs(c) + frag + dev.r0
     chunks_a = c.bm * c.bk * eb // 16
     stage = 4 * cdiv(chunks_a, threads)
@@ -328,7 +337,7 @@ def check_static(dtype: int, c: Cfg, dev: Device = MI355X) -> int:
         return R_LDS
     # the bf16 tiled kernel keeps ST stages of transfers in flight after its
     # prologue; a wave's memory counter tracks at most 63 (MI355X only)
-    if (dev.mode == 0 and c.kind == KIND_TILED and dtype != F32
+    if (dev.mode == 0 and dma_kind(c, dtype)
             and c.stages * transfers_per_wave(c, dtype) > 63):
         return R_INFLIGHT
     if acc_regs(c) > dev.acc_max:
@@ -348,8 +357,11 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
         return R_SHAPE
     if c not in _space_set(dtype, dev):
         return R_SPACE
-    if c.kind == KIND_SKINNY and dtype == F32:
+    if c.kind in (KIND_SKINNY, KIND_STREAMK) and dtype == F32:
         return R_DTYPE
+    # a stream-K workgroup spreads K steps: K = 0 has none to spread
+    if c.kind == KIND_STREAMK and K == 0:
+        return R_SHAPE
     aligned = shape_aligned(N, K, dtype)
     if dev.mode == 0:
         if c.kind == KIND_UNALIGNED and aligned:
@@ -389,12 +401,51 @@ def enumerate_feasible(M: int, N: int, K: int, dtype: int, dev: Device = MI355X)
 
 
 # ---------------------------------------------------------------- geometry
-def grid(M: int, N: int, c: Cfg):
+def grid(M: int, N: int, c: Cfg, dev: Device = MI355X, K: int | None = None):
     """(tiles, launched blocks).  Tiles = ceil(M/BM) * ceil(N/BN) (page
     "Tile Selection: Cost Models Against Measurement", search-space section);
-    split-K launches that many blocks per tile."""
+    split-K launches that many blocks per tile; the stream-K kind launches
+    one per data-parallel tile plus a round of workgroups for the tail."""
     tiles = cdiv(M, c.bm) * cdiv(N, c.bn)
+    if c.kind == KIND_STREAMK:
+        assert K is not None, "the stream-K kind's workgroup count depends on K"
+        return tiles, streamk_plan(M, N, K, c, dev)["blocks"]
     return tiles, tiles * c.split_k
+
+
+def sk_owner(x: int, I: int, G: int) -> int:
+    """Workgroup holding iteration x when I iterations are cut into G
+    contiguous ranges [g I / G, (g + 1) I / G): the largest g with
+    floor(g I / G) <= x."""
+    return ((x + 1) * G - 1) // I
+
+
+def streamk_plan(M: int, N: int, K: int, c: Cfg, dev: Device = MI355X) -> dict:
+    """The stream-K partition (page "Compilers and Kernel Languages", "A
+    different tile for every shape": the order and the assignment of tiles to
+    compute units is a choice of its own).  A round is G = CUs x resident
+    workgroups; the tiles beyond the last full round (tail = tiles mod G)
+    have their K steps spread evenly over min(G, their K steps) workgroups;
+    the others run one
+    workgroup each.  smax: most pieces a tail tile is cut into; pieces: the
+    pieces of every tile cut into two or more."""
+    tiles = cdiv(M, c.bm) * cdiv(N, c.bn)
+    G = dev.n_cu * max(1, resident_blocks(c, BF16, dev))
+    tail = tiles % G
+    ks = cdiv(K, c.bk)
+    # never more stream-K workgroups than tail iterations: each then has at
+    # least one, and a tile's pieces come from consecutive workgroups
+    wgs = min(G, tail * ks)
+    smax = pieces = 0
+    if tail > 0 and ks > 0:
+        I = tail * ks
+        for j in range(tail):
+            n = sk_owner((j + 1) * ks - 1, I, wgs) - sk_owner(j * ks, I, wgs) + 1
+            smax = max(smax, n)
+            if n >= 2:
+                pieces += n
+    return {"tiles": tiles, "G": G, "dp": tiles - tail, "tail": tail, "ks": ks, "wgs": wgs, "smax": smax,
+            "pieces": pieces, "blocks": tiles - tail + (wgs if tail > 0 else 0)}
 
 
 # ---------------------------------------------------------------- cost model
@@ -410,7 +461,7 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
     peak = dev.peak_f32 if dtype == F32 else dev.peak_bf16
     flops = 2.0 * M * N * K
     compulsory = float(eb * (M * K + K * N) + ec * M * N)
-    tiles, units = grid(M, N, c)
+    tiles, units = grid(M, N, c, dev, K)
     w = c.wgm * c.wgn
     bcu = resident_blocks(c, dtype, dev)
 
@@ -502,11 +553,11 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
     simd_peak = peak / (dev.n_cu * dev.simds)
     f_step = 2.0 * c.bm * c.bn * c.bk
     lds_step = float(c.bk * eb * (w * (wm + wn) + c.bm + c.bn))
-    qw = min(c.bn, 64) if (c.kind == KIND_TILED and dtype != F32) else c.bn
+    qw = min(c.bn, 64) if dma_kind(c, dtype) else c.bn
     l2_step = float(c.bm * _line(c.bk * eb) + c.bk * (c.bn // qw) * _line(qw * eb))
     if c.kind == KIND_UNALIGNED:
         l2_step = l2_step / dev.unaligned_eff
-    depth = max(1, c.stages - 1) if (c.kind == KIND_TILED and dtype != F32) else 1
+    depth = max(1, c.stages - 1) if dma_kind(c, dtype) else 1
     lat = dev.lat_step if compulsory > dev.l2_bytes else dev.lat_l2
 
     def step(res: int) -> float:
@@ -517,6 +568,24 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
         return max(issue, res * l2_step / dev.cu_bw, lat / depth)
 
     slots = dev.n_cu * bcu
+    if c.kind == KIND_STREAMK:
+        # full rounds of whole tiles, then the tail's K steps spread over a
+        # round of workgroups; pieces of split tiles stored as fp32 and read
+        # back once by the second pass
+        sp = streamk_plan(M, N, K, c, dev)
+        dp_rounds = sp["dp"] // slots
+        sk_steps = cdiv(sp["tail"] * sp["ks"], sp["wgs"]) if sp["tail"] > 0 else 0
+        t_cu = (dp_rounds * ktiles + sk_steps) * step(bcu)
+        t_cu = t_cu + (dp_rounds + (1 if sp["tail"] > 0 else 0)) * lat
+        pieces = 4.0 * c.bm * c.bn * sp["pieces"]
+        raw = float(tiles) * eb * K * (c.bm + c.bn)
+        g = math.sqrt(min(tiles, slots))
+        t_hbm = (max(compulsory, raw / g) + pieces) / (dev.bw * dev.hbm_eff)
+        t_cu = t_cu + (float(ec) * M * N + pieces) / (dev.bw * dev.hbm_eff)
+        fix = 0.0
+        if sp["pieces"] > 0:
+            fix = (pieces + float(ec) * c.bm * c.bn * sp["tail"]) / (dev.bw * dev.hbm_eff) + dev.t0
+        return max(t_cu, t_hbm) + fix + dev.t0
     full = units // slots
     rem = units - full * slots
     t_cu = full * ktiles * step(bcu)

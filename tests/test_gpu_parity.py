@@ -291,6 +291,51 @@ def test_split_k_two_host_threads_on_the_null_stream():
             _exact_check(C, probs[name][6], dtype, f"thread {t} call {i} ({name})")
 
 
+def _streamk_cfgs(M, N, K, dtype):
+    return [c.astuple() for c in tg.enumerate_feasible(M, N, K, dtype) if c.kind == 3 and tg.has_kernel(dtype, c)]
+
+
+@pytest.mark.parametrize("M,N,K,dtype,act", [
+    (1024, 1040, 2048, wl.BF16_F32OUT, "none"),   # every tile in the tail, each cut among many workgroups
+    (4352, 4224, 136, wl.BF16, "relu"),           # a full round of whole tiles plus a tail; K mod 64 = 8
+    (200, 264, 64, wl.BF16, "relu"),              # one K step: every piece is a whole tile
+])
+def test_streamk_integer_exact(M, N, K, dtype, act):
+    """Data-parallel tiles plus the stream-K tail: every stream-K configuration,
+    integer-valued inputs, output equal to the exact result (fp32) or to its
+    round-to-nearest-even bf16; the pieces of split tiles are added in K order
+    by the second pass."""
+    A, B, bias = _int_inputs(M, N, K, dtype, 31)
+    ref = gemm_ref.gemm(A, B, bias, act)
+    cfgs = _streamk_cfgs(M, N, K, dtype)
+    assert len(cfgs) >= 12
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    for cfg in cfgs:
+        mark(f"stream-K {M}x{N}x{K} dt{dtype} {cfg}")
+        C = _run(A_d, B_d, b_d, act, dtype, cfg)
+        torch.cuda.synchronize()
+        _exact_check(C, ref, dtype, f"stream-K {cfg}")
+    # the workgroup count is the plan's: full-round tiles plus the tail's workgroups
+    c = cfgs[0]
+    plan = S.streamk_plan(M, N, K, S.Cfg(*c))
+    assert tg.grid(M, N, K, c) == (plan["tiles"], plan["blocks"])
+
+
+def test_streamk_gelu_random_inputs_and_repeatable():
+    M, N, K, dtype = 1024, 1040, 2048, wl.BF16
+    A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("normal", 0.5), wl.Dist("normal", 0.5),
+                                wl.Dist("normal", 0.5), 33)
+    ref = gemm_ref.gemm(A, B, bias, "gelu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    for cfg in [(3, 256, 256, 64, 2, 4, 2, 1), (3, 128, 128, 64, 2, 2, 3, 1)]:
+        mark(f"stream-K gelu {cfg}")
+        C1 = _run(A_d, B_d, b_d, "gelu", dtype, cfg)
+        C2 = _run(A_d, B_d, b_d, "gelu", dtype, cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(C1, C2), "the same call gives the same bits"
+        assert_close(out_f64(C1), ref, dtype, f"stream-K gelu {cfg}")
+
+
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])
 def test_split_k_second_pass_edges(dtype):
     # an unaligned shape (N = 33) runs the element-load kind, which takes any C: the second pass

@@ -104,7 +104,7 @@ def test_model_times_bitwise_and_choice(M, Nn, K, dtype):
 @pytest.mark.parametrize("M,Nn,K,dtype", SHAPES)
 def test_grid_default_and_resources_identical(M, Nn, K, dtype):
     for c in S.enumerate_feasible(M, Nn, K, dtype)[::7]:
-        assert N.grid(M, Nn, K, c.astuple()) == S.grid(M, Nn, c)
+        assert N.grid(M, Nn, K, c.astuple()) == S.grid(M, Nn, c, K=K)
         lds, v, b = N.resources(dtype, c.astuple())
         assert lds == S.lds_bytes(c, dtype)
         assert v == S.vgpr_estimate(c, dtype, S.MI355X)

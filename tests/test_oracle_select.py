@@ -444,3 +444,74 @@ def test_skinny_model_closed_forms():
     slabs = 4.0 * 2 * M * Nn
     want = (comp + slabs) / d.bw + (slabs + 2 * M * Nn) / d.bw
     assert S.model_time(M, Nn, K, S.BF16, cs, d) == pytest.approx(want, rel=1e-12)
+
+
+# ---------------------------------------------------------------- stream-K partition
+def _simulate_streamk(tail, ks, G):
+    """Brute force: cut the tail's iterations into min(G, I) contiguous ranges
+    the plain way, list every workgroup's pieces (tile, first K step, end)."""
+    I = tail * ks
+    G = min(G, I)
+    bounds = [g * I // G for g in range(G + 1)]
+    pieces = {}
+    for g in range(G):
+        it = bounds[g]
+        while it < bounds[g + 1]:
+            j, kb = divmod(it, ks)
+            ke = min(ks, kb + bounds[g + 1] - it)
+            pieces.setdefault(j, []).append((g, kb, ke))
+            it += ke - kb
+    return pieces
+
+
+@pytest.mark.parametrize("tail,ks,G", [(33, 128, 256), (16, 128, 256), (204, 16, 256), (1, 5, 8), (7, 3, 8),
+                                       (255, 1, 256), (81, 256, 256), (3, 1, 8)])
+def test_streamk_partition_against_brute_force(tail, ks, G):
+    pieces = _simulate_streamk(tail, ks, G)
+    I = tail * ks
+    wgs = min(G, I)
+    smax = 0
+    total = 0
+    for j in range(tail):
+        ps = pieces[j]
+        # the pieces of a tile cover its K steps once, in order, from consecutive workgroups
+        assert ps[0][1] == 0 and ps[-1][2] == ks
+        assert all(a[2] == b[1] for a, b in zip(ps, ps[1:]))
+        assert [p[0] for p in ps] == list(range(ps[0][0], ps[0][0] + len(ps)))
+        # the owner formula names the workgroup of a tile's first and last step
+        assert S.sk_owner(j * ks, I, wgs) == ps[0][0] and S.sk_owner((j + 1) * ks - 1, I, wgs) == ps[-1][0]
+        smax = max(smax, len(ps))
+        total += len(ps) if len(ps) >= 2 else 0
+    # no workgroup holds more than two pieces, nor more than ceil(I / G) steps
+    per_g = {}
+    for j, ps in pieces.items():
+        for g, kb, ke in ps:
+            per_g.setdefault(g, []).append(ke - kb)
+    assert len(per_g) == wgs
+    assert all(len(v) <= 2 and 1 <= sum(v) <= S.cdiv(I, wgs) for v in per_g.values())
+    # the plan's counts agree (a configuration with G = CUs x resident blocks)
+    dev = dataclasses.replace(S.MI355X, n_cu=G)
+    c = S.Cfg(S.KIND_STREAMK, 256, 256, 64, 2, 4, 2, 1)
+    assert S.resident_blocks(c, S.BF16, dev) == 1
+    M, Nn = 256 * (G + tail), 256
+    plan = S.streamk_plan(M, Nn, 64 * ks, c, dev)
+    assert (plan["G"], plan["dp"], plan["tail"], plan["ks"]) == (G, G, tail, ks)
+    assert plan["wgs"] == wgs and plan["smax"] == smax and plan["pieces"] == total
+    assert plan["blocks"] == G + wgs and S.grid(M, Nn, c, dev, 64 * ks) == (G + tail, G + wgs)
+
+
+def test_streamk_model_closed_form():
+    # compute only (no LDS, L2, latency, store or fixup costs): a full round
+    # plus the tail's K steps spread over a round, against two rounds
+    d = dataclasses.replace(S.MI355X, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0, bw=1e30, t0=0.0)
+    sk = S.Cfg(S.KIND_STREAMK, 256, 256, 64, 2, 4, 2, 1)
+    dp = S.Cfg(S.KIND_TILED, 256, 256, 64, 2, 4, 2, 1)
+    M, Nn, K = 256 * 17, 256 * 17, 8192            # 289 tiles: one round of 256 and a tail of 33
+    step = 2.0 * 256 * 256 * 64 / (d.peak_bf16 / (d.n_cu * d.simds) * d.simds)
+    assert S.model_time(M, Nn, K, S.BF16, dp, d) == pytest.approx(2 * 128 * step, rel=1e-12)
+    assert S.model_time(M, Nn, K, S.BF16, sk, d) == pytest.approx((128 + S.cdiv(33 * 128, 256)) * step, rel=1e-12)
+    # no tail: the stream-K kind is plain data-parallel and costs the same
+    assert S.model_time(4096, 4096, K, S.BF16, sk, d) == S.model_time(4096, 4096, K, S.BF16, dp, d)
+    # K = 0 has nothing to spread; fp32 has no stream-K kernel
+    assert S.check(4096, 4096, 0, S.BF16, sk) == S.R_SHAPE
+    assert S.check(4096, 4096, 64, S.F32, sk) != S.OK

@@ -200,13 +200,23 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     }();
     p.group_m = group_m;
     int64_t tiles, blocks;
-    grid(M, N, c, &tiles, &blocks);
+    grid(M, N, K, c, &tiles, &blocks, &d);
     if (blocks > 0x7FFFFFFF)
         return set_error(TG_E_UNSUPPORTED, "too many workgroups");
+    bool fixup = false;
+    if (c.kind == TG_KIND_STREAMK) {
+        const SkPlan sp = streamk_plan(M, N, K, c, d);
+        p.sk_dp = (int)sp.dp;
+        p.sk_g = (int)sp.wgs;
+        p.sk_tail = (int)sp.tail;
+        p.sk_ks = (int)sp.ks;
+        p.sk_smax = (int)std::max<int64_t>(1, sp.smax);
+        fixup = sp.smax >= 2;
+    }
     // held until both kernels of a split-K call are queued (see ensure_workspace)
     std::unique_lock<std::mutex> ws_hold;
-    if (c.split_k > 1) {
-        const size_t need = workspace_bytes_for(M, N, c);
+    if (c.split_k > 1 || fixup) {
+        const size_t need = workspace_bytes_for(M, N, K, c);
         if (ext) {
             if (need > ext->bytes)
                 return set_error(TG_E_INVAL, "split-K partial sums need " + std::to_string(need) +
@@ -227,6 +237,11 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
         e = splitk_reduce(p.ws, c.split_k, M, N, bias, C, p.out_bf16, act, stream);
         if (e != hipSuccess)
             return set_hip_error(e, "split-K reduction launch");
+    }
+    if (fixup) {
+        e = streamk_fixup(p, c.bm, c.bn, stream);
+        if (e != hipSuccess)
+            return set_hip_error(e, "stream-K second pass launch");
     }
     return TG_OK;
 }
@@ -428,10 +443,11 @@ int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg* out, dou
 
 int tg_grid(int64_t M, int64_t N, int64_t K, const tg_cfg* cfg, int64_t* tiles, int64_t* blocks)
 {
-    (void)K;
-    if (!cfg || !tiles || !blocks || cfg->bm <= 0 || cfg->bn <= 0 || cfg->split_k <= 0 || M < 0 || N < 0)
+    if (!cfg || !tiles || !blocks || cfg->bm <= 0 || cfg->bn <= 0 || cfg->bk <= 0 || cfg->split_k <= 0 || M < 0 ||
+        N < 0 || K < 0)
         return set_error(TG_E_INVAL, "bad argument");
-    grid(M, N, *cfg, tiles, blocks);
+    const tg_device_desc d = current_desc();
+    grid(M, N, K, *cfg, tiles, blocks, &d);
     return TG_OK;
 }
 

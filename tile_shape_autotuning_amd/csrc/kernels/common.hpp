@@ -36,6 +36,12 @@ struct GemmParams {
     int out_bf16;         // 1: C is bf16, 0: C is fp32
     int act;              // 0 none, 1 ReLU, 2 GELU (erf form)
     int group_m;          // tile rows per scheduling group (>= 1)
+    // stream-K kind: the first sk_dp tiles (in scheduling order) run one
+    // workgroup each; the remaining sk_tail tiles' sk_ks K steps each are
+    // spread evenly over sk_g further workgroups, whose pieces of a tile go to
+    // slots of bm x bn floats (tile j, piece s at slot j * sk_smax + s) that a
+    // second pass adds in piece order
+    int sk_dp, sk_g, sk_tail, sk_ks, sk_smax;
 };
 
 // Buffer-resource word 3 for gfx9-family raw buffers (32-bit dwords, no swizzle).
@@ -154,18 +160,21 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float v)
 // C); a second kernel adds the slabs in split order and applies the rest.
 // Kernel boundaries order the two passes, so no flags or cache control are
 // needed between them.
+// Output (row, col) of the problem goes to dst[(row - row0) * ld + col - col0].
 struct OutSpec {
     void* dst;
     const float* bias;
     int act;
     int bf16;
+    int row0, col0;
+    int64_t ld;
 };
 
 __device__ __forceinline__ OutSpec out_spec(const GemmParams& p, int split)
 {
     if (p.split > 1)
-        return OutSpec{p.ws + (int64_t)split * p.slab, nullptr, 0, 0};
-    return OutSpec{p.C, p.bias, p.act, p.out_bf16};
+        return OutSpec{p.ws + (int64_t)split * p.slab, nullptr, 0, 0, 0, 0, (int64_t)p.N};
+    return OutSpec{p.C, p.bias, p.act, p.out_bf16, 0, 0, (int64_t)p.N};
 }
 
 // Wait until every vector memory access this wave issued has completed.
@@ -177,6 +186,19 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 // rows and B columns then share that XCD's L2).  Logical ids enumerate tiles
 // split-major, and tiles in groups of group_m tile rows, column-major inside a
 // group.
+// Tile number (scheduling order) -> tile coordinates: groups of group_m tile
+// rows, column-major inside a group.
+__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int group_m, int& tm, int& tn)
+{
+    const int per_group = group_m * tiles_n;
+    const int g = tile / per_group;
+    const int first_m = g * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int in_g = tile - g * per_group;
+    tm = first_m + in_g % gsize;
+    tn = in_g / gsize;
+}
+
 __device__ __forceinline__ void map_block(int bid, int total, int tiles_m, int tiles_n, int group_m,
                                           int& tile, int& tm, int& tn, int& split)
 {
@@ -186,13 +208,14 @@ __device__ __forceinline__ void map_block(int bid, int total, int tiles_m, int t
     const int tiles = tiles_m * tiles_n;
     tile = logical % tiles;
     split = logical / tiles;
-    const int per_group = group_m * tiles_n;
-    const int g = tile / per_group;
-    const int first_m = g * group_m;
-    const int gsize = min(tiles_m - first_m, group_m);
-    const int in_g = tile - g * per_group;
-    tm = first_m + in_g % gsize;
-    tn = in_g / gsize;
+    tile_coords(tile, tiles_m, tiles_n, group_m, tm, tn);
 }
+
+// Stream-K partition of the sk_tail tiles' iterations (K steps) over sk_g
+// workgroups: workgroup g takes iterations [g I / G, (g + 1) I / G),
+// I = sk_tail * sk_ks.  The workgroup holding iteration x is the largest g
+// with g I / G <= x, i.e. ((x + 1) G - 1) / I.
+__device__ __forceinline__ int64_t sk_start(int64_t g, int64_t I, int64_t G) { return g * I / G; }
+__device__ __forceinline__ int64_t sk_owner(int64_t x, int64_t I, int64_t G) { return ((x + 1) * G - 1) / I; }
 
 }  // namespace tg

@@ -208,23 +208,22 @@ __device__ __forceinline__ u32x2_t lds_read_tr(unsigned addr)
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-// NTB: B is streamed -- the launch has a single row of tiles, so every
-// element of B is read by exactly one workgroup (the decode regime: a
-// matrix-vector-like product reads the weights once and reuses nothing, page
-// "Tiling the hierarchy", failure regimes) -- and its transfers carry the
-// non-temporal policy.  Measured on the 16 x 28672 x 8192 decode it lifts the
-// weight stream by 3-5 %; where tiles of other rows re-read B through L2 the
-// same policy costs 6-19 %, so it is never used there.
+// One output tile (tm, tn) over the K range [kbeg, kend): the transfers, the
+// pipelined MFMA loop and the epilogue into `out`.  `lds` is the workgroup's
+// ST * STAGE_BYTES of LDS.  Every lane of the workgroup calls it.
 template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-gemm_tiled_dma_kernel(GemmParams p)
+__device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int tm, int tn, int kbeg, int kend,
+                                         const OutSpec& out)
 {
     using Cf = TiledDma<BM, BN, BK, WGM, WGN, ST>;
     constexpr int T = Cf::T, FM = Cf::FM, FN = Cf::FN, W = Cf::W, KK = Cf::KK;
     constexpr int RB = Cf::RB, U = Cf::U, QW = Cf::QW;
-    __shared__ u32x4_t lds[ST * Cf::STAGE_BYTES / 16];
 
-    const int tid = threadIdx.x;
+    // an opaque copy of the thread index: where the tile body is used more
+    // than once in a kernel, nothing derived from it is shared between the
+    // uses (and held in registers from one to the next)
+    int tid = threadIdx.x;
+    __asm__ __volatile__("" : "+v"(tid));
     const int lane = tid & 63;
     // uniform per wave (scalar registers); a constant for one-wave blocks, so
     // that the transfer schedule below is resolved at compile time
@@ -232,12 +231,8 @@ gemm_tiled_dma_kernel(GemmParams p)
     const int l16 = lane & 15, g = lane >> 4;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    int tile, tm, tn, split;
-    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tile, tm, tn, split);
     const int M = p.M, N = p.N, K = p.K;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kbeg = split * p.kps;
-    const int kend = min(K, kbeg + p.kps);
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     const char* Ab = static_cast<const char*>(p.A);
     const char* Bb = static_cast<const char*>(p.B);
@@ -471,7 +466,6 @@ gemm_tiled_dma_kernel(GemmParams p)
     const int wme = wave_e / WGN, wne = wave_e % WGN;
     const int row_w = m0 + wme * Cf::WM;          // first output row of the wave tile
     const int col_w = n0 + wne * Cf::WN;          // first output column
-    const OutSpec out = out_spec(p, split);
 
     if constexpr (Cf::EPI_LDS) {
         // Each wave turns its accumulators, one 16-row slab at a time, into
@@ -511,7 +505,7 @@ gemm_tiled_dma_kernel(GemmParams p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         o[e] = apply_act(o[e] + bias8[e], out.act);
-                    const int64_t idx = (int64_t)row * N + col0;
+                    const int64_t idx = (int64_t)(row - out.row0) * out.ld + (col0 - out.col0);
                     if (out.bf16) {
                         u32x4_t w;
 #pragma unroll
@@ -539,7 +533,7 @@ gemm_tiled_dma_kernel(GemmParams p)
                     const int row = row_w + i * 16 + ge * 4 + r;
                     if (cv && row < M) {
                         const float v = apply_act(acc[i][j][r] + bj, out.act);
-                        const int64_t idx = (int64_t)row * N + col;
+                        const int64_t idx = (int64_t)(row - out.row0) * out.ld + (col - out.col0);
                         if (out.bf16)
                             static_cast<unsigned short*>(out.dst)[idx] = f32_to_bf16_rne(v);
                         else
@@ -548,6 +542,90 @@ gemm_tiled_dma_kernel(GemmParams p)
                 }
             }
         }
+    }
+}
+
+// NTB: B is streamed -- the launch has a single row of tiles, so every
+// element of B is read by exactly one workgroup (the decode regime: a
+// matrix-vector-like product reads the weights once and reuses nothing, page
+// "Tiling the hierarchy", failure regimes) -- and its transfers carry the
+// non-temporal policy.  Measured on the 16 x 28672 x 8192 decode it lifts the
+// weight stream by 3-5 %; where tiles of other rows re-read B through L2 the
+// same policy costs 6-19 %, so it is never used there.
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+gemm_tiled_dma_kernel(GemmParams p)
+{
+    __shared__ u32x4_t lds[ST * TiledDma<BM, BN, BK, WGM, WGN, ST>::STAGE_BYTES / 16];
+    int tile, tm, tn, split;
+    map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tile, tm, tn, split);
+    const int kbeg = split * p.kps;
+    const int kend = min(p.K, kbeg + p.kps);
+    dma_tile<BM, BN, BK, WGM, WGN, ST, NTB>(p, lds, tm, tn, kbeg, kend, out_spec(p, split));
+}
+
+// Data-parallel tiles plus a stream-K tail (page "Compilers and Kernel
+// Languages", "A different tile for every shape": the order and the way tiles
+// are handed to compute units is a choice of its own).  Blocks below sk_dp
+// each run one whole tile, the first sk_dp tiles of the scheduling order
+// (full rounds of the machine).  The sk_g blocks after them split the
+// remaining sk_tail tiles' K steps evenly: each takes a contiguous range of
+// (tile, K step) iterations, which covers the end of one tile, possibly whole
+// tiles, and the start of another.  A piece that is a whole tile goes through
+// the epilogue into C; any other piece writes its raw fp32 sums to its slot,
+// and streamk_fixup adds a tile's pieces in K order afterwards (no flags, no
+// atomics: the kernel boundary orders the two passes, and the sums do not
+// depend on timing).
+// One piece: iterations [it, it + n) of tile j (scheduling order), n <= ks.
+template <int BM, int BN, int BK, int WGM, int WGN, int ST>
+__device__ __forceinline__ void streamk_piece(const GemmParams& p, u32x4_t* lds, int64_t it, int64_t end, int64_t g)
+{
+    const int64_t G = p.sk_g, ks = p.sk_ks, dp = p.sk_dp;
+    const int64_t I = (int64_t)p.sk_tail * ks;
+    const int64_t j = it / ks;
+    const int64_t kb = it - j * ks;
+    const int64_t ke = min(ks, kb + (end - it));
+    int tm, tn;
+    tile_coords((int)j, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    OutSpec out = out_spec(p, 0);
+    if (kb != 0 || ke != ks) {
+        // a piece of a tail tile: raw sums to its slot
+        const int64_t jt = j - dp;
+        const int64_t piece = g - sk_owner(jt * ks, I, G);
+        out = OutSpec{p.ws + (jt * p.sk_smax + piece) * (int64_t)(BM * BN), nullptr, 0, 0, tm * BM, tn * BN,
+                      (int64_t)BN};
+    }
+    const int kend = ke * BK < (int64_t)p.K ? (int)(ke * BK) : p.K;
+    dma_tile<BM, BN, BK, WGM, WGN, ST, false>(p, lds, tm, tn, (int)(kb * BK), kend, out);
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int ST>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+gemm_streamk_kernel(GemmParams p)
+{
+    __shared__ u32x4_t lds[ST * TiledDma<BM, BN, BK, WGM, WGN, ST>::STAGE_BYTES / 16];
+    const int bid = blockIdx.x;
+    if (bid < p.sk_dp) {
+        int tile, tm, tn, split;
+        map_block(bid, p.sk_dp, p.tiles_m, p.tiles_n, p.group_m, tile, tm, tn, split);
+        dma_tile<BM, BN, BK, WGM, WGN, ST, false>(p, lds, tm, tn, 0, p.K, out_spec(p, 0));
+        return;
+    }
+    // iterations (tile, K step) in scheduling order; this block's share of the
+    // tail is fewer than one tile's K steps (the tail has fewer tiles than a
+    // round has blocks), so it touches at most two tiles
+    const int64_t G = p.sk_g, ks = p.sk_ks, dp = p.sk_dp;
+    const int64_t I = (int64_t)p.sk_tail * ks;
+    const int64_t g = bid - dp;
+    const int64_t it = dp * ks + sk_start(g, I, G);
+    const int64_t end = dp * ks + sk_start(g + 1, I, G);
+    if (it >= end)
+        return;
+    streamk_piece<BM, BN, BK, WGM, WGN, ST>(p, lds, it, end, g);
+    const int64_t next = (it / ks + 1) * ks;             // first iteration of the next tile
+    if (next < end) {
+        __syncthreads();   // the next piece's transfers overwrite the LDS this one's epilogue used
+        streamk_piece<BM, BN, BK, WGM, WGN, ST>(p, lds, next, end, g);
     }
 }
 

@@ -77,9 +77,9 @@ int gemm_bias_act_noalloc(int64_t M, int64_t N, int64_t K, const void* A, const 
         if (st != TG_OK)
             return st;
     }
-    if (workspace_bytes_for(M, N, c) > kScratchBytes)
+    if (workspace_bytes_for(M, N, K, c) > kScratchBytes)
         return set_error(TG_E_INVAL, "split-K partial sums of this call need " +
-                                         std::to_string(workspace_bytes_for(M, N, c)) + " bytes; the no-allocation "
+                                         std::to_string(workspace_bytes_for(M, N, K, c)) + " bytes; the no-allocation "
                                          "entry point has " + std::to_string(kScratchBytes));
     float* ws = nullptr;
     int dev = 0;

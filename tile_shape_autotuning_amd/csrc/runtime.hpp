@@ -55,13 +55,17 @@ int validate_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 // `ws_bytes`.  With `hold`, the workspace's lock is handed to the caller, who
 // keeps it until every kernel that uses the buffer is queued.
 int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws, std::unique_lock<std::mutex>* hold = nullptr);
-size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& cfg);
+size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, const tg_cfg& cfg);
 
 // Split-K second pass (splitk_reduce.hip): C = act(sum of the split slabs +
 // bias), slabs `splitk_slab(M, N)` floats apart.
 int64_t splitk_slab(int64_t M, int64_t N);
 hipError_t splitk_reduce(const float* ws, int split, int64_t M, int64_t N, const float* bias, void* C,
                          int out_bf16, int act, hipStream_t stream);
+
+// Stream-K second pass (splitk_reduce.hip): adds the pieces of every tail
+// tile split among workgroups, then bias, activation, conversion into C.
+hipError_t streamk_fixup(const GemmParams& p, int bm, int bn, hipStream_t stream);
 
 // Argument validation shared by the entry points.
 int validate_problem(int64_t M, int64_t N, int64_t K, int dtype);

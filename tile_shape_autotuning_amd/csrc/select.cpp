@@ -116,6 +116,12 @@ bool shape_aligned(int64_t N, int64_t K, int dtype)
     return K % vec == 0 && N % vec == 0;
 }
 
+// the bf16 kernels that move panels straight into LDS (tiled and stream-K)
+static bool dma_kind(const tg_cfg& c, int dtype)
+{
+    return (c.kind == TG_KIND_TILED || c.kind == TG_KIND_STREAMK) && dtype != TG_F32;
+}
+
 // ------------------------------------------------------------------ space
 static const int kWaveGrids[6][2] = {{1, 1}, {1, 2}, {2, 1}, {2, 2}, {2, 4}, {4, 2}};
 static const int kSplits[5] = {1, 2, 4, 8, 16};
@@ -163,6 +169,15 @@ static std::vector<tg_cfg> build_space(int dtype, int mode)
     for (const auto& t : kUnaligned)
         for (int s : kSplits)
             out.push_back(tg_cfg{TG_KIND_UNALIGNED, t[0], t[1], ubk, t[2], t[3], 2, s});
+    if (dtype != TG_F32) {
+        // stream-K: the large tiles whose last partial round is worth spreading
+        const int ts[2] = {128, 256}, wg[3][2] = {{2, 2}, {2, 4}, {4, 2}}, sts[3] = {2, 3, 4};
+        for (int bm : ts)
+            for (int bn : ts)
+                for (const auto& w : wg)
+                    for (int st : sts)
+                        out.push_back(tg_cfg{TG_KIND_STREAMK, bm, bn, 64, w[0], w[1], st, 1});
+    }
     return out;
 }
 
@@ -212,7 +227,7 @@ int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d)
     const int64_t threads = 64 * (int64_t)c.wgm * c.wgn;
     const int64_t eb = in_bytes(dtype);
     const int64_t frag = 4 * ((c.bm / c.wgm) / 16 + (c.bn / c.wgn) / 16);
-    if (c.kind == TG_KIND_TILED && dtype != TG_F32)
+    if (dma_kind(c, dtype))
         return acc_regs(c) + frag + d.r0;   // panels go global -> LDS directly: no staging registers
     const int64_t chunks_a = (int64_t)c.bm * c.bk * eb / 16;
     int64_t stage = 4 * cdiv(chunks_a, threads);
@@ -284,7 +299,7 @@ int check_static(int dtype, const tg_cfg& c, const tg_device_desc& d)
         return R_LDS;
     // the direct-to-LDS kernel keeps ST stages of transfers in flight after its
     // prologue; a wave's memory counter tracks at most 63 (MI355X only)
-    if (d.mode == 0 && c.kind == TG_KIND_TILED && dtype != TG_F32 && c.stages * transfers_per_wave(c, dtype) > 63)
+    if (d.mode == 0 && dma_kind(c, dtype) && c.stages * transfers_per_wave(c, dtype) > 63)
         return R_INFLIGHT;
     if (acc_regs(c) > d.acc_max)
         return R_ACC;
@@ -303,8 +318,11 @@ int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_
         return R_SHAPE;
     if (!in_space(dtype, d, c))
         return R_SPACE;
-    if (c.kind == TG_KIND_SKINNY && dtype == TG_F32)
+    if ((c.kind == TG_KIND_SKINNY || c.kind == TG_KIND_STREAMK) && dtype == TG_F32)
         return R_DTYPE;
+    // a stream-K workgroup spreads K steps: K = 0 has none to spread
+    if (c.kind == TG_KIND_STREAMK && K == 0)
+        return R_SHAPE;
     const bool aligned = shape_aligned(N, K, dtype);
     if (d.mode == 0) {
         if (c.kind == TG_KIND_UNALIGNED && aligned)
@@ -342,11 +360,41 @@ std::vector<tg_cfg> enumerate_feasible(int64_t M, int64_t N, int64_t K, int dtyp
 }
 
 // ------------------------------------------------------------------ geometry
-void grid(int64_t M, int64_t N, const tg_cfg& c, int64_t* tiles, int64_t* blocks)
+void grid(int64_t M, int64_t N, int64_t K, const tg_cfg& c, int64_t* tiles, int64_t* blocks, const tg_device_desc* d)
 {
     const int64_t t = cdiv(M, c.bm) * cdiv(N, c.bn);
     *tiles = t;
+    if (c.kind == TG_KIND_STREAMK) {
+        *blocks = streamk_plan(M, N, K, c, d ? *d : mi355x_desc()).blocks;
+        return;
+    }
     *blocks = t * c.split_k;
+}
+
+int64_t sk_owner_host(int64_t x, int64_t I, int64_t G) { return ((x + 1) * G - 1) / I; }
+
+SkPlan streamk_plan(int64_t M, int64_t N, int64_t K, const tg_cfg& c, const tg_device_desc& d)
+{
+    SkPlan p{};
+    p.tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    p.G = (int64_t)d.n_cu * std::max<int64_t>(1, resident_blocks(c, TG_BF16, d));
+    p.tail = p.tiles % p.G;
+    p.dp = p.tiles - p.tail;
+    p.ks = cdiv(K, c.bk);
+    // never more stream-K workgroups than tail iterations: every one then has
+    // at least one, and the pieces of a tile come from consecutive workgroups
+    p.wgs = std::min(p.G, p.tail * p.ks);
+    p.blocks = p.dp + (p.tail > 0 ? p.wgs : 0);
+    if (p.tail > 0 && p.ks > 0) {
+        const int64_t I = p.tail * p.ks;
+        for (int64_t j = 0; j < p.tail; ++j) {
+            const int64_t n = sk_owner_host((j + 1) * p.ks - 1, I, p.wgs) - sk_owner_host(j * p.ks, I, p.wgs) + 1;
+            p.smax = std::max(p.smax, n);
+            if (n >= 2)
+                p.pieces += n;
+        }
+    }
+    return p;
 }
 
 // ------------------------------------------------------------------ cost model
@@ -415,11 +463,11 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
     const double simd_peak = peak / (double)((int64_t)d.n_cu * d.simds);
     const double f_step = 2.0 * (double)c.bm * (double)c.bn * (double)c.bk;
     const double lds_step = (double)(c.bk * eb * (w * (wm + wn) + c.bm + c.bn));
-    const int64_t qw = (c.kind == TG_KIND_TILED && dtype != TG_F32) ? std::min<int64_t>(c.bn, 64) : c.bn;
+    const int64_t qw = dma_kind(c, dtype) ? std::min<int64_t>(c.bn, 64) : c.bn;
     double l2_step = (double)(c.bm * line_bytes(c.bk * eb) + c.bk * (c.bn / qw) * line_bytes(qw * eb));
     if (c.kind == TG_KIND_UNALIGNED)
         l2_step = l2_step / d.unaligned_eff;
-    const int64_t depth = (c.kind == TG_KIND_TILED && dtype != TG_F32) ? std::max<int64_t>(1, c.stages - 1) : 1;
+    const int64_t depth = dma_kind(c, dtype) ? std::max<int64_t>(1, c.stages - 1) : 1;
     const double lat = compulsory > d.l2_bytes ? d.lat_step : d.lat_l2;
 
     auto step = [&](int64_t res) {
@@ -432,6 +480,25 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
         return std::max(t, lat / (double)depth);
     };
     const int64_t slots = (int64_t)d.n_cu * bcu;
+    if (c.kind == TG_KIND_STREAMK) {
+        // full rounds of whole tiles, then the tail's K steps spread evenly
+        // over a round of workgroups; the pieces of split tiles are stored as
+        // fp32 and read back once by the second pass
+        const SkPlan sp = streamk_plan(M, N, K, c, d);
+        const int64_t dp_rounds = sp.dp / slots;
+        const int64_t sk_steps = sp.tail > 0 ? cdiv(sp.tail * sp.ks, sp.wgs) : 0;
+        double t_cu = (double)(dp_rounds * ktiles + sk_steps) * step(bcu);
+        t_cu = t_cu + (double)(dp_rounds + (sp.tail > 0 ? 1 : 0)) * lat;
+        const double pieces = 4.0 * (double)c.bm * (double)c.bn * (double)sp.pieces;
+        const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
+        const double g = std::sqrt((double)std::min<int64_t>(tiles, slots));
+        const double t_hbm = (std::max(compulsory, raw / g) + pieces) / (d.bw * d.hbm_eff);
+        t_cu = t_cu + ((double)ec * (double)M * (double)N + pieces) / (d.bw * d.hbm_eff);
+        double fix = 0.0;
+        if (sp.pieces > 0)
+            fix = (pieces + (double)ec * (double)c.bm * (double)c.bn * (double)sp.tail) / (d.bw * d.hbm_eff) + d.t0;
+        return std::max(t_cu, t_hbm) + fix + d.t0;
+    }
     const int64_t full = units / slots;
     const int64_t rem = units - full * slots;
     double t_cu = (double)(full * ktiles) * step(bcu);
@@ -457,7 +524,7 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     const double flops = 2.0 * (double)M * (double)N * (double)K;
     const double compulsory = (double)(eb * (M * K + K * N) + ec * M * N);
     int64_t tiles, units;
-    grid(M, N, c, &tiles, &units);
+    grid(M, N, K, c, &tiles, &units, &d);
     const int64_t w = (int64_t)c.wgm * c.wgn;
     const int64_t bcu = resident_blocks(c, dtype, d);
 

@@ -59,7 +59,24 @@ int64_t k_per_split(const tg_cfg& c, int64_t K);
 int check_static(int dtype, const tg_cfg& c, const tg_device_desc& d);
 int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d);
 
-void grid(int64_t M, int64_t N, const tg_cfg& c, int64_t* tiles, int64_t* blocks);
+// Launch geometry: output tiles and launched workgroups.  The stream-K kind's
+// workgroup count depends on the device (d; NULL = MI355X defaults) and on K.
+void grid(int64_t M, int64_t N, int64_t K, const tg_cfg& c, int64_t* tiles, int64_t* blocks,
+          const tg_device_desc* d = nullptr);
+
+// The stream-K kind's partition (see TG_KIND_STREAMK): G = CUs x resident
+// workgroups; the first dp = tiles - tail tiles (tail = tiles mod G) run one
+// workgroup each; the tail tiles' ks K steps each are spread over
+// wgs = min(G, I) more workgroups, workgroup g taking iterations
+// [g I / wgs, (g + 1) I / wgs) of I = tail * ks.  smax: most pieces any tail
+// tile is split into; pieces: slots written (pieces of the tiles split in two
+// or more).
+struct SkPlan {
+    int64_t tiles, G, dp, tail, ks, wgs, smax, pieces, blocks;
+};
+SkPlan streamk_plan(int64_t M, int64_t N, int64_t K, const tg_cfg& c, const tg_device_desc& d);
+// the workgroup that holds iteration x of I over G workgroups
+int64_t sk_owner_host(int64_t x, int64_t I, int64_t G);
 double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d);
 std::vector<tg_cfg> enumerate_feasible(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d);
 bool model_choice(int64_t M, int64_t N, int64_t K, int dtype, const tg_device_desc& d, tg_cfg* out, double* t);

@@ -90,6 +90,61 @@ splitk_reduce_kernel(const float* ws, int split, int64_t slab, int64_t mn, int n
     }
 }
 
+// Second pass of the stream-K kind: every tail tile whose K steps were split
+// among two or more workgroups has its pieces, raw fp32 sums in bm x bn slots
+// (tile j, piece s at slot j * smax + s), added in piece order -- which is K
+// order -- then bias, activation and conversion, and the result stored in C.
+// Tiles taken whole by one workgroup were finished by the GEMM kernel and are
+// skipped.  One block row of the grid per tail tile; each thread owns four
+// consecutive columns of a tile row (N is a multiple of 8 for this kind, so
+// the four are inside or outside C together).
+__global__ void __launch_bounds__(256)
+streamk_fixup_kernel(const float* ws, int bm, int bn, int M, int N, int tiles_m, int tiles_n, int group_m, int dp,
+                     int tail, int ks, int G, int smax, const float* bias, void* C, int out_bf16, int act)
+{
+    const int64_t j = blockIdx.y;
+    const int64_t I = (int64_t)tail * ks;
+    const int64_t first = sk_owner(j * ks, I, G);
+    const int nseg = (int)(sk_owner((j + 1) * ks - 1, I, G) - first + 1);
+    if (nseg < 2)
+        return;
+    int tm, tn;
+    tile_coords(dp + (int)j, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t area = (int64_t)bm * bn;
+    const float* base = ws + j * smax * area;
+    for (int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; e < area;
+         e += (int64_t)gridDim.x * blockDim.x * 4) {
+        const int r = (int)(e / bn), c = (int)(e % bn);
+        const int row = tm * bm + r, col = tn * bn + c;
+        if (row >= M || col >= N)
+            continue;
+        f32x4_t s = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(base + e));
+        for (int k = 1; k < nseg; ++k)
+            s += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(base + k * area + e));
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] = apply_act(s[q] + (bias ? bias[col + q] : 0.0f), act);
+        const int64_t idx = (int64_t)row * N + col;
+        if (out_bf16) {
+            const u32x2_t w = {(unsigned)f32_to_bf16_rne(v[0]) | ((unsigned)f32_to_bf16_rne(v[1]) << 16),
+                               (unsigned)f32_to_bf16_rne(v[2]) | ((unsigned)f32_to_bf16_rne(v[3]) << 16)};
+            *reinterpret_cast<u32x2_t*>(static_cast<unsigned short*>(C) + idx) = w;
+        } else {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(C) + idx) = f32x4_t{v[0], v[1], v[2], v[3]};
+        }
+    }
+}
+
+hipError_t streamk_fixup(const GemmParams& p, int bm, int bn, hipStream_t stream)
+{
+    const int per_tile = (int)(((int64_t)bm * bn / 4 + 255) / 256);
+    hipLaunchKernelGGL(streamk_fixup_kernel, dim3(per_tile, p.sk_tail), dim3(256), 0, stream, p.ws, bm, bn, p.M, p.N,
+                       p.tiles_m, p.tiles_n, p.group_m, p.sk_dp, p.sk_tail, p.sk_ks, p.sk_g, p.sk_smax, p.bias, p.C,
+                       p.out_bf16, p.act);
+    return hipGetLastError();
+}
+
 int64_t splitk_slab(int64_t M, int64_t N)
 {
     // each slab starts 256-byte aligned, so 16-byte loads stay aligned

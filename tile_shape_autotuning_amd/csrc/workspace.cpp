@@ -8,6 +8,7 @@
 #include <utility>
 
 #include "runtime.hpp"
+#include "select.hpp"
 
 namespace tg {
 
@@ -27,8 +28,15 @@ struct Workspace {
 static std::mutex g_ws_mu;   // guards the map itself
 static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-size_t workspace_bytes_for(int64_t M, int64_t N, const tg_cfg& c)
+size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, const tg_cfg& c)
 {
+    if (c.kind == TG_KIND_STREAMK) {
+        // one bm x bn slot per piece: tail tiles x most pieces per tile
+        const SkPlan sp = streamk_plan(M, N, K, c, current_desc());
+        if (sp.smax < 2)
+            return 0;
+        return (size_t)sp.tail * (size_t)sp.smax * (size_t)c.bm * (size_t)c.bn * sizeof(float);
+    }
     if (c.split_k <= 1)
         return 0;
     return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
