@@ -59,7 +59,8 @@ typedef enum {
                               workgroup each, the last partial round's K steps
                               spread evenly over a full round of workgroups
                               (stream-K), pieces of split tiles added in K order
-                              by a second pass; split_k = 1 */
+                              by a second pass; split_k = 1; feasible only
+                              when the tiles do not fill whole rounds */
 } tg_kind;
 
 /*

@@ -380,6 +380,9 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
         return R_SPILL
     if resident_blocks(c, dtype, dev) < 1:
         return R_OCC
+    # without a partial last round the stream-K kind is the data-parallel one
+    if c.kind == KIND_STREAMK and streamk_plan(M, N, K, c, dev)["tail"] == 0:
+        return R_SHAPE
     if c.split_k > 1:
         if K == 0 or cdiv(K, k_per_split(c, K)) != c.split_k:
             return R_SPLIT

@@ -510,8 +510,8 @@ def test_streamk_model_closed_form():
     step = 2.0 * 256 * 256 * 64 / (d.peak_bf16 / (d.n_cu * d.simds) * d.simds)
     assert S.model_time(M, Nn, K, S.BF16, dp, d) == pytest.approx(2 * 128 * step, rel=1e-12)
     assert S.model_time(M, Nn, K, S.BF16, sk, d) == pytest.approx((128 + S.cdiv(33 * 128, 256)) * step, rel=1e-12)
-    # no tail: the stream-K kind is plain data-parallel and costs the same
-    assert S.model_time(4096, 4096, K, S.BF16, sk, d) == S.model_time(4096, 4096, K, S.BF16, dp, d)
+    # no tail: the stream-K kind would be the data-parallel one, so it is not a candidate
+    assert S.check(4096, 4096, K, S.BF16, sk) == S.R_SHAPE
     # K = 0 has nothing to spread; fp32 has no stream-K kernel
     assert S.check(4096, 4096, 0, S.BF16, sk) == S.R_SHAPE
     assert S.check(4096, 4096, 64, S.F32, sk) != S.OK

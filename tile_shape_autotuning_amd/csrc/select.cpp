@@ -343,6 +343,9 @@ int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_
         return R_SPILL;
     if (resident_blocks(c, dtype, d) < 1)
         return R_OCC;
+    // without a partial last round the stream-K kind is the data-parallel one
+    if (c.kind == TG_KIND_STREAMK && streamk_plan(M, N, K, c, d).tail == 0)
+        return R_SHAPE;
     if (c.split_k > 1) {
         if (K == 0 || cdiv(K, k_per_split(c, K)) != c.split_k)
             return R_SPLIT;
