@@ -166,3 +166,36 @@ def test_split_k_calls_count_both_launches(tmp_path):
 def test_observed_clock_from_busy_cycles():
     # 8 XCDs busy 2.0e6 cycles each over a 1 ms kernel: 2.0 GHz
     assert R.observed_clock_ghz({"GRBM_GUI_ACTIVE": 8 * 2.0e6}, 1000.0) == pytest.approx(2.0)
+
+
+def test_short_kernels_print_no_busy_cu_or_clock_figure(tmp_path):
+    """GRBM_GUI_ACTIVE spans microseconds around each dispatch: the busy-CU
+    count and the clock that divide by it are left out below 200 us."""
+    from tile_shape_autotuning_amd import rocprof_report as R
+
+    def fake_summary(*a, **k):
+        return {"calls": 10, "avg_us": us, "call_us": us, "counters": {"GRBM_GUI_ACTIVE": 8.0e5,
+                                                                     "SQ_BUSY_CU_CYCLES": 1.0e7}}
+    import pytest as _pt
+    mp = _pt.MonkeyPatch()
+    mp.setattr(R, "summary", fake_summary)
+    try:
+        us = 27.0
+        text, _ = R.counters_text("w", (0, 1, 1, 1, 1, 1, 1, 1), "k", "t", [], None, None, 0, None, None, [])
+        assert "busy CUs" not in text and "clock" not in text
+        us = 800.0
+        text, _ = R.counters_text("w", (0, 1, 1, 1, 1, 1, 1, 1), "k", "t", [], None, None, 0, None, None, [])
+        assert "busy CUs" in text and "clock" in text
+    finally:
+        mp.undo()
+
+
+def test_workload_launch_picks_the_dispatches_of_a_workload():
+    from tile_shape_autotuning_amd import rocprof_report as R
+    # 8192^3 at 256 x 256 with 8 waves: 1024 workgroups of 512 lanes, no second pass
+    assert R.workload_launch(3, (0, 256, 256, 64, 2, 4, 2, 1)) == (
+        "gemm_tiled_dma_kernel<256, 256, 64, 2, 4, 2, false>", 1024 * 512, None)
+    # the decode with split 2 streams B (one tile row) and adds a second pass over 16 x 28672 outputs
+    name, grid, second = R.workload_launch(4, (0, 64, 256, 32, 2, 4, 4, 2))
+    assert name.endswith("true>") and grid == 112 * 2 * 512
+    assert second == ("splitk_reduce_kernel<2>", 448 * 256)

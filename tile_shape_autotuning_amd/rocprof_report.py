@@ -256,9 +256,58 @@ def counters_text(workload, cfg, kname, trace_dir, pmc_dirs, fetch_dir, write_di
     return "\n".join(lines) + "\n", sm
 
 
+def workload_launch(index, cfg):
+    """Kernel name, work-items of its dispatch, and the second pass (name,
+    work-items) or None, for a workload run with cfg -- the figures that pick
+    its dispatches out of a trace of several workloads."""
+    from . import workloads as wl
+    w = wl.WORKLOADS[index]
+    kind, bm, bn, bk, wgm, wgn, st, split = cfg
+    in_bf16 = w.dtype != wl.F32
+    tiles = -(-w.M // bm) * -(-w.N // bn)
+    stream_b = kind == 0 and in_bf16 and bm <= 64 and w.M <= bm
+    if kind == 1:
+        threads = 64 * wgm
+        tiles = -(-w.N // 128)
+    else:
+        threads = 64 * wgm * wgn
+    name = kernel_name(cfg, in_bf16, stream_b)
+    second = None
+    if split > 1:
+        blocks = min(-(-w.M * w.N // 1024), 65536)
+        second = (f"splitk_reduce_kernel<{split}>", blocks * 256)
+    return name, tiles * split * threads, second
+
+
+def render(index, cfg, trace, pmc_dirs, fetch, write, commands_used, out_path=None):
+    """Text summary of one workload's kernel: average duration of its
+    dispatches in `trace` (picked by kernel name and work-items, so a trace of
+    several workloads serves), counters from the pmc passes, HBM traffic from
+    the FETCH_SIZE / WRITE_SIZE passes (each run with a 1 GiB copy for the
+    scale); `commands_used` are the commands printed at the top."""
+    from . import workloads as wl
+    w = wl.WORKLOADS[index]
+    name, grid, second = workload_launch(index, cfg)
+    text, sm = counters_text(w.name, cfg, name, trace, pmc_dirs, fetch, write, 1 << 30, w.flops,
+                             w.compulsory_bytes, commands_used, grid=grid, second=second)
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(text)
+    return text, sm
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("render")
+    r.add_argument("--workload", type=int, required=True)
+    r.add_argument("--cfg", required=True, help="kind,bm,bn,bk,wgm,wgn,stages,split_k")
+    r.add_argument("--trace", required=True)
+    r.add_argument("--pmc", action="append", default=[])
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--command", action="append", default=[], help="a command that made the data (repeatable)")
+    r.add_argument("--out", default="")
     c = sub.add_parser("commands")
     c.add_argument("bench_args", nargs=argparse.REMAINDER)
     s = sub.add_parser("summary")
@@ -271,6 +320,11 @@ def main(argv=None):
     s.add_argument("--flops", type=float)
     s.add_argument("--bytes", type=float)
     a = ap.parse_args(argv)
+    if a.cmd == "render":
+        cfg = tuple(int(x) for x in a.cfg.split(","))
+        text, _ = render(a.workload, cfg, a.trace, a.pmc, a.fetch, a.write, a.command, a.out or None)
+        print(text)
+        return 0
     if a.cmd == "commands":
         print("\n".join(commands(a.bench_args)))
     else:
