@@ -649,22 +649,38 @@ def default_cfg(N: int, K: int, dtype: int) -> Cfg:
 
 
 # ---------------------------------------------------------------- page counts
-def page1_candidates(smem_bytes: int = 48 * 1024, max_threads: int = 1024):
-    """The float32 tile enumeration described on "Tile Selection: Cost Models
-    Against Measurement" (search-space section): BM, BN in {32..256}, KS in
-    {8..64}, per-thread TM, TN in {2, 4, 8}; keep a tuple when both panels fit
-    in shared memory, the thread count is between 32 and the block limit and
-    a whole number of 32-wide warps, and TM*TN accumulators stay within 128."""
-    keep = []
-    for bm, bn, ks, tm, tn in itertools.product((32, 64, 128, 256), (32, 64, 128, 256),
-                                                (8, 16, 32, 64), (2, 4, 8), (2, 4, 8)):
-        smem = 4 * ks * (bm + bn)
-        threads = (bm // tm) * (bn // tn)
-        ok = (smem <= smem_bytes and 32 <= threads <= max_threads
-              and threads % 32 == 0 and tm * tn <= 128)
-        if ok:
-            keep.append((bm, bn, ks, tm, tn))
-    return keep
+def page1_space_count(smem_bytes: int = 48 * 1024, max_threads: int = 1024):
+    """Size of the float32 search space that "Tile Selection: Cost Models
+    Against Measurement" (search-space section) describes -- block tile BM, BN
+    in {32, 64, 128, 256}, reduction step KS in {8, 16, 32, 64}, per-thread tile
+    TM, TN in {2, 4, 8} -- counted from its three constraints rather than by
+    listing it:
+      * shared memory: both fp32 panels, 4 KS (BM + BN) bytes, fit in
+        smem_bytes, so a block tile admits every KS up to
+        smem_bytes / (4 (BM + BN));
+      * threads: (BM / TM)(BN / TN) is a whole number of 32-wide warps, at
+        least one and at most max_threads;
+      * registers: TM TN accumulators per thread, at most 128.
+    The KS bound depends on the block tile alone and the other two on the
+    per-thread tile, so the count is a sum over block tiles of (admissible
+    KS values) x (admissible per-thread tiles).  Returns (tuples, distinct
+    (BM, BN, KS) triples, largest KS (BM + BN) admitted)."""
+    tiles, steps, per_thread = (32, 64, 128, 256), (8, 16, 32, 64), (2, 4, 8)
+    n_tuples = n_triples = 0
+    widest = 0
+    for bm in tiles:
+        for bn in tiles:
+            ks_cap = smem_bytes // (4 * (bm + bn))
+            n_ks = sum(1 for ks in steps if ks <= ks_cap)
+            n_thr = sum(1 for tm in per_thread for tn in per_thread
+                        if tm * tn <= 128 and (bm // tm) * (bn // tn) % 32 == 0
+                        and 32 <= (bm // tm) * (bn // tn) <= max_threads)
+            n_tuples += n_ks * n_thr
+            if n_thr:
+                n_triples += n_ks
+                if n_ks:
+                    widest = max(widest, max(ks for ks in steps if ks <= ks_cap) * (bm + bn))
+    return n_tuples, n_triples, widest
 
 
 def loop_nest_traffic(n: int, t: int) -> int:

@@ -6,8 +6,8 @@
 * Counting invariants: blocks = ceil(M/BM) * ceil(N/BN) (page "Tile Selection:
   Cost Models Against Measurement", search-space section, checked by brute
   force), the shared-memory cap of 12,288 float32 elements at 48 KB (same
-  section), the enumeration size "a few hundred to a few thousand" (same
-  section), and loop-nest traffic 2 N^3 / T (page "Tiling the hierarchy",
+  section), the size of the space that section describes (hundreds to
+  thousands of points; 398 here), and loop-nest traffic 2 N^3 / T (page "Tiling the hierarchy",
   derivation, checked by simulating the loop nest).
 * Invariants of the MI355X model whose constants the pages do not give
   ("parity unpinned" against the pages): wave efficiency is 1 exactly when
@@ -99,20 +99,28 @@ def test_block_count_formula_vs_brute_force(M, N, bm, bn):
     assert S.grid(M, N, c4)[1] == 4 * S.block_count_brute(M, N, bm, bn)
 
 
-def test_page1_enumeration_size_and_caps():
-    cands = S.page1_candidates()
-    # "a few hundred to a few thousand configurations depending on the bounds"
-    assert 200 <= len(cands) <= 5000
-    assert len(cands) == 398
-    assert len({c[:3] for c in cands}) == 55
+def test_page1_space_size_and_caps():
+    n, triples, widest = S.page1_space_count()
+    # the section puts such spaces at hundreds to thousands of points
+    assert 200 <= n <= 5000
+    assert (n, triples) == (398, 55)
     # 48 KB of float32 panels caps BM*KS + KS*BN at 12,288 elements
-    assert max(ks * (bm + bn) for bm, bn, ks, _, _ in cands) == 12288
-    for bm, bn, ks, tm, tn in cands:
-        threads = (bm // tm) * (bn // tn)
-        assert 32 <= threads <= 1024 and threads % 32 == 0 and tm * tn <= 128
+    assert widest == 12288
+    # the count against brute force over the whole cross product (a planted
+    # mistake in either constraint would move it)
+    brute = 0
+    for bm in (32, 64, 128, 256):
+        for bn in (32, 64, 128, 256):
+            for ks in (8, 16, 32, 64):
+                for tm in (2, 4, 8):
+                    for tn in (2, 4, 8):
+                        thr = (bm // tm) * (bn // tn)
+                        brute += 4 * ks * (bm + bn) <= 48 * 1024 and thr % 32 == 0 and 32 <= thr <= 1024 \
+                            and tm * tn <= 128
+    assert brute == n
     # a larger shared memory admits strictly more tuples; a smaller thread cap fewer
-    assert len(S.page1_candidates(smem_bytes=96 * 1024)) > len(cands)
-    assert len(S.page1_candidates(max_threads=256)) < len(cands)
+    assert S.page1_space_count(smem_bytes=96 * 1024)[0] > n
+    assert S.page1_space_count(max_threads=256)[0] < n
 
 
 @pytest.mark.parametrize("n,t", [(8, 8), (16, 4), (32, 8), (64, 8), (64, 16), (48, 12)])

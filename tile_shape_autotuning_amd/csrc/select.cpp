@@ -3,9 +3,10 @@
 // Candidate space and feasibility filter: page "Tile Selection: Cost Models
 // Against Measurement", "The structure of the search space" -- the block
 // tile, reduction step and per-thread (here per-wave) tile are the free
-// parameters; limits that are "checkable before any code is generated" bound
-// the space: both panels must fit in on-chip memory, the accumulators must
-// fit in registers, and the tile must leave the device filled.  On MI355X
+// parameters; resource limits that can be checked without generating or
+// running any code bound the space: both panels must fit in on-chip memory,
+// the accumulators must fit in registers, and the tile must leave the device
+// filled.  On MI355X
 // these become: LDS per workgroup and per CU (160 KiB), 256 accumulator and
 // 512 unified VGPR+AGPR registers per lane, 8 wave slots per SIMD, whole
 // 16x16 MFMA tiles per wave, K step a multiple of the MFMA K.
