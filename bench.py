@@ -418,6 +418,29 @@ def bucket_report(torch, steps):
             "max_bucketed_over_exact": max(ratios)}
 
 
+def tile_order_study(p, torch, groups=(1, 2, 4, 8, 16, 32)):
+    """The headline workload's tuned call with each scheduling order (tile
+    rows per group; the order changes which tiles share an XCD's L2 at a
+    time, not what they compute)."""
+    tg = p.tg
+    out = {}
+    try:
+        for g in groups:
+            tg.set_tile_order(g)
+            step = p.bind(None)
+            warm_up(step, 3, torch)
+            sec, _ = time_steps(step, secondary_steps(p, 1e-3, 0), torch)
+            out[str(g)] = round(sec * 1e6, 2)
+    finally:
+        tg.set_tile_order(0)
+    best = min(out, key=out.get)
+    res = {"workload": p.w.name, "us_per_group_rows": out, "default": tg.tile_order(), "best": int(best),
+           "default_over_best": round(out[str(tg.tile_order())] / out[best], 4) if str(tg.tile_order()) in out
+           else None}
+    log(f"tile order study: {res}")
+    return res
+
+
 STREAMK_SHAPE = (4352, 4352, 8192)
 
 
@@ -523,6 +546,7 @@ def main():
                     help="report the occupancy-tuned RMS normalisation also with --only")
     ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMS normalisation report")
     ap.add_argument("--streamk", action="store_true", help="report the stream-K study also with --only")
+    ap.add_argument("--no-order", action="store_true", help="skip the tile-order study of the headline workload")
     ap.add_argument("--no-streamk", action="store_true",
                     help="skip the stream-K study (4352 x 4352 x 8192: data-parallel against stream-K tail)")
     ap.add_argument("--cfg", type=str, default="",
@@ -659,6 +683,8 @@ def main():
         line["rmsnorm"] = rmsnorm_report(torch, 50)
     if (a.streamk or not a.only) and not a.no_streamk:
         line["streamk_study"] = streamk_study(torch)
+    if not a.only and not a.no_order and forced is None:
+        line["tile_order_study"] = tile_order_study(p, torch)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(main_idx, p.host)

@@ -173,6 +173,21 @@ int gemm_bias_act_noalloc(int64_t M, int64_t N, int64_t K, const void *A, const 
 size_t tg_noalloc_scratch_bytes(void);
 
 /*
+ * Tile scheduling order (page "Compilers and Kernel Languages", "A different
+ * tile for every shape": the order in which tiles are scheduled is one of the
+ * choices the analytical model leaves out).  Workgroups are renumbered so
+ * that each of the 8 XCDs owns a contiguous range of tiles, enumerated in
+ * groups of group_m tile rows, column-major inside a group (tiles that share
+ * A rows and B columns then share an L2).  The order never changes results,
+ * only which operands an L2 holds at a time.  tg_set_tile_order: group_m
+ * tile rows per group, 1 .. 4096, or 0 for the default (8, or the
+ * environment variable TILEGEMM_GROUP_M); process-wide; TG_E_INVAL outside
+ * that range.  tg_tile_order: the value in force.
+ */
+int tg_set_tile_order(int group_m);
+int tg_tile_order(void);
+
+/*
  * Run-time dispatch over shape buckets (page "Tile Selection: Cost Models
  * Against Measurement", "Hybrid strategies": a few tuned variants selected at
  * launch from the actual extents, so that a varying batch does not make every

@@ -291,6 +291,30 @@ def test_split_k_two_host_threads_on_the_null_stream():
             _exact_check(C, probs[name][6], dtype, f"thread {t} call {i} ({name})")
 
 
+@pytest.mark.parametrize("M,N,K,cfg", [
+    (2048, 2056, 520, (0, 128, 128, 64, 2, 2, 2, 1)),     # many tiles, ragged N and K
+    (1000, 1000, 2048, (0, 128, 128, 128, 2, 4, 2, 4)),   # split-K
+    (4352, 4224, 136, (3, 256, 256, 64, 2, 4, 2, 1)),     # a full round plus a stream-K tail
+])
+def test_tile_order_changes_no_result(M, N, K, cfg):
+    """The scheduling order (tile rows per group) decides which workgroup
+    computes which tile, never what a tile computes: every order gives the
+    exact result."""
+    dtype = wl.BF16_F32OUT
+    A, B, bias = _int_inputs(M, N, K, dtype, 41)
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    try:
+        for g in (1, 3, 8, 64):
+            tg.set_tile_order(g)
+            mark(f"tile order {g}: {M}x{N}x{K} {cfg}")
+            C = _run(A_d, B_d, b_d, "relu", dtype, cfg)
+            torch.cuda.synchronize()
+            _exact_check(C, ref, dtype, f"tile order {g} {cfg}")
+    finally:
+        tg.set_tile_order(0)
+
+
 def _streamk_cfgs(M, N, K, dtype):
     return [c.astuple() for c in tg.enumerate_feasible(M, N, K, dtype) if c.kind == 3 and tg.has_kernel(dtype, c)]
 

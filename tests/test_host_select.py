@@ -249,6 +249,21 @@ def test_model_mode_tuning_and_cache_roundtrip(tmp_path, monkeypatch):
     N.cache_clear()
 
 
+def test_tile_order_setting():
+    try:
+        assert N.tile_order() == 8
+        N.set_tile_order(3)
+        assert N.tile_order() == 3
+        with pytest.raises(N.TileGemmError):
+            N.set_tile_order(-1)
+        with pytest.raises(N.TileGemmError):
+            N.set_tile_order(5000)
+        assert N.tile_order() == 3
+    finally:
+        N.set_tile_order(0)
+    assert N.tile_order() == 8
+
+
 def test_dispatch_keys_follow_the_oracle_buckets():
     try:
         N.set_shape_buckets(True)

@@ -15,6 +15,7 @@ from ._native import (ACT, BF16, BF16_F32OUT, F32, Cfg, DeviceDesc, TileGemmErro
                       check_cfg, default_cfg, enumerate_feasible, gemm_autotune, get_device_desc, grid,
                       has_kernel, kernel_count, kernel_resources, streams_b, model_choice, model_time_us, resources,
                       set_device_override, set_shape_buckets, dispatch_m, space, stats, rmsnorm_autotune,
+                      set_tile_order, tile_order,
                       rmsnorm_cache_lookup, rmsnorm_tunes)
 
 __all__ = [
@@ -22,7 +23,8 @@ __all__ = [
     "ACT", "enumerate_feasible", "space", "check_cfg", "model_time_us", "model_choice", "grid", "default_cfg",
     "resources", "builtin_device_desc", "set_device_override", "get_device_desc", "kernel_count",
     "has_kernel", "kernel_resources", "streams_b", "autotune_table", "cache_lookup", "cache_save", "cache_load",
-    "cache_clear", "cache_size", "stats", "dtype_code", "set_shape_buckets", "dispatch_m",
+    "cache_clear", "cache_size", "stats", "dtype_code", "set_shape_buckets", "dispatch_m", "set_tile_order",
+    "tile_order",
     "rmsnorm", "rmsnorm_autotune", "rmsnorm_cache_lookup", "rmsnorm_tunes",
 ]
 

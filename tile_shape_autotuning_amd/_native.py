@@ -27,7 +27,7 @@ EXPORTS = [
     "tg_default_cfg", "tg_resources", "tg_set_device_override", "tg_get_device_desc",
     "tg_builtin_device_desc", "tg_kernel_count", "tg_has_kernel", "tg_kernel_resources", "tg_streams_b",
     "tg_autotune_table", "tg_cache_lookup", "tg_cache_save", "tg_cache_load", "tg_cache_clear",
-    "tg_cache_size", "tg_stats", "tg_set_shape_buckets", "tg_dispatch_m",
+    "tg_cache_size", "tg_stats", "tg_set_shape_buckets", "tg_dispatch_m", "tg_set_tile_order", "tg_tile_order",
     "tg_rmsnorm", "tg_rmsnorm_autotune", "tg_rmsnorm_cache_lookup", "tg_rmsnorm_tunes",
 ]
 
@@ -125,6 +125,8 @@ def lib():
             "tg_cache_size": ([], i32),
             "tg_stats": ([pi64, pi64, pi64], i32),
             "tg_set_shape_buckets": ([i32], i32),
+            "tg_set_tile_order": ([i32], i32),
+            "tg_tile_order": ([], i32),
             "tg_dispatch_m": ([i64, pi64], i32),
             "tg_rmsnorm": ([i64, i64, vp, vp, vp, ctypes.c_float, i32], i32),
             "tg_rmsnorm_autotune": ([i64, i64, pi, dp], i32),
@@ -325,6 +327,15 @@ def cache_clear():
 
 def cache_size() -> int:
     return lib().tg_cache_size()
+
+
+def set_tile_order(group_m: int):
+    """Tile rows per scheduling group (0: the default)."""
+    check(lib().tg_set_tile_order(int(group_m)))
+
+
+def tile_order() -> int:
+    return lib().tg_tile_order()
 
 
 def set_shape_buckets(on: bool):

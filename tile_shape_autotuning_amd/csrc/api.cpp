@@ -118,6 +118,21 @@ static std::atomic<int> g_buckets{[] {
 // the M a dispatch without an explicit configuration is keyed (and tuned) on
 static int64_t dispatch_m(int64_t M) { return g_buckets.load() ? bucket_m(M) : M; }
 
+// ------------------------------------------------------------------ tile order
+// Tile rows per scheduling group (page "Compilers and Kernel Languages", "A
+// different tile for every shape": the order in which tiles are scheduled is
+// a choice of its own).  The order changes which tiles share an XCD's L2 at a
+// time, never what a tile computes.  Default 8 (TILEGEMM_GROUP_M overrides);
+// tg_set_tile_order changes it process-wide.
+static int default_tile_order()
+{
+    const char* s = std::getenv("TILEGEMM_GROUP_M");
+    const int v = s ? std::atoi(s) : 0;
+    return v > 0 ? v : 8;
+}
+static std::atomic<int> g_group_m{default_tile_order()};
+static int tile_order() { return g_group_m.load(); }
+
 // ------------------------------------------------------------------ stream
 static thread_local hipStream_t t_stream = nullptr;
 hipStream_t current_stream() { return t_stream; }
@@ -193,12 +208,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     }
     p.out_bf16 = dtype == TG_BF16 ? 1 : 0;
     p.act = act;
-    static const int group_m = [] {
-        const char* s = std::getenv("TILEGEMM_GROUP_M");
-        const int v = s ? std::atoi(s) : 0;
-        return v > 0 ? v : 8;
-    }();
-    p.group_m = group_m;
+    p.group_m = tile_order();
     int64_t tiles, blocks;
     grid(M, N, K, c, &tiles, &blocks, &d);
     if (blocks > 0x7FFFFFFF)
@@ -326,6 +336,16 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
     }
     return launch_cfg(M, N, K, A, B, bias, C, dtype, act, c, current_stream(), cfg == nullptr);
 }
+
+int tg_set_tile_order(int group_m)
+{
+    if (group_m < 0 || group_m > 4096)
+        return set_error(TG_E_INVAL, "tile rows per scheduling group must be 0 (default) .. 4096");
+    g_group_m.store(group_m == 0 ? default_tile_order() : group_m);
+    return TG_OK;
+}
+
+int tg_tile_order(void) { return tile_order(); }
 
 int tg_set_shape_buckets(int on)
 {
