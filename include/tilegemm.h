@@ -25,7 +25,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 2
+#define TG_VERSION 3
 
 typedef enum {
     TG_OK = 0,
@@ -55,12 +55,20 @@ typedef enum {
     TG_KIND_SKINNY = 1,    /* M <= 64 weight-streaming kernel (bf16 only) */
     TG_KIND_UNALIGNED = 2, /* block-tiled kernel with element loads, for K or N
                               not a multiple of the 16-byte vector */
-    TG_KIND_STREAMK = 3    /* bf16 block-tiled kernel: full rounds of tiles one
+    TG_KIND_STREAMK = 3,   /* bf16 block-tiled kernel: full rounds of tiles one
                               workgroup each, the last partial round's K steps
                               spread evenly over a full round of workgroups
                               (stream-K), pieces of split tiles added in K order
                               by a second pass; split_k = 1; feasible only
                               when the tiles do not fill whole rounds */
+    TG_KIND_SLICEDK = 4    /* block-tiled kernel whose workgroup holds split_k
+                              groups of wgm x wgn waves, each multiplying its
+                              own share of every stage's K slices; the groups'
+                              sums meet in LDS before the epilogue (K split
+                              inside one workgroup: one launch, no partial-sum
+                              slabs; page "Compilers and Kernel Languages", "A
+                              different tile for every shape": how the K
+                              reduction is shared out is a choice of its own) */
 } tg_kind;
 
 /*
@@ -68,9 +76,11 @@ typedef enum {
  * tile, reduction step, per-thread tile; page "Compilers and Kernel
  * Languages": pipeline depth and split-K are further choices).
  *   tiled / unaligned: bm x bn block tile, bk reduction step, wgm x wgn waves
- *       (64 lanes each) per workgroup, stages = pipeline depth (bf16 tiled:
- *       2, 3, 4, 6 or 8 K steps in flight global -> LDS; fp32 and unaligned:
- *       1 or 2 LDS buffers), split_k = workgroups sharing one tile's K range.
+ *       (64 lanes each) per workgroup, stages = pipeline depth (tiled: 2, 3,
+ *       4, 6 or 8 K steps in flight global -> LDS; unaligned: 2 LDS
+ *       buffers), split_k = workgroups sharing one tile's K range.
+ *   sliced-K: as tiled, with split_k = the K groups inside one workgroup
+ *       (2 or 4; the workgroup has wgm x wgn x split_k waves).
  *   skinny: bm = 16 * ceil(M / 16), bn = 128 columns per workgroup, bk = 32,
  *       wgm = waves per workgroup (each takes interleaved 32-row chunks of
  *       K), wgn = 1, stages = chunks per pipelined step, split_k as above.
@@ -93,10 +103,12 @@ typedef struct {
            l2_bytes,
            w1_eff,      /* issue efficiency of a lone wave on a SIMD */
            skinny_eff,  /* achievable fraction of the decode kernel's streaming model */
-           hbm_eff;     /* achievable fraction of the HBM peak */
+           hbm_eff,     /* achievable fraction of the HBM peak */
+           sliced_eff;  /* issue efficiency of the sliced-K kind (its K groups meet a
+                           barrier after every short run of MFMAs) */
 /* The MI355X mode prices a K step per CU (MFMA, LDS, L2-to-CU, latency /
  * depth) over rounds of resident blocks; the replica mode is the page's
- * formula and ignores lds_bw_cu .. hbm_eff. */
+ * formula and ignores lds_bw_cu .. sliced_eff. */
 } tg_device_desc;
 
 /* One row of an autotuning table.  Every candidate is first measured with

@@ -21,7 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 REPO = os.path.dirname(HERE)
 SRC = os.path.join(REPO, "tile_shape_autotuning_amd", "_lib", "kernel_resources.json")
 OUT = os.path.join(HERE, "kernel_allocation.json")
-FIELDS = ("in_bf16", "kind", "bm", "bn", "bk", "wgm", "wgn", "stages", "vgpr", "agpr", "lds", "scratch", "occupancy")
+FIELDS = ("in_bf16", "kind", "bm", "bn", "bk", "wgm", "wgn", "stages", "k_groups", "vgpr", "agpr", "lds", "scratch",
+          "occupancy")
 
 
 def main():

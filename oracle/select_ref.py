@@ -45,7 +45,7 @@ import os
 from dataclasses import dataclass
 
 F32, BF16, BF16_F32OUT = 0, 1, 2
-KIND_TILED, KIND_SKINNY, KIND_UNALIGNED, KIND_STREAMK = 0, 1, 2, 3
+KIND_TILED, KIND_SKINNY, KIND_UNALIGNED, KIND_STREAMK, KIND_SLICEDK = 0, 1, 2, 3, 4
 
 # reasons a candidate is rejected (first failing rule)
 OK = 0
@@ -96,31 +96,34 @@ class Device:
     w1_eff: float = 1.0
     skinny_eff: float = 1.0
     hbm_eff: float = 1.0
+    sliced_eff: float = 1.0
 
 
 # MI355X (gfx950): 256 CUs x 4 SIMDs, 160 KiB LDS per CU, 512 unified
 # VGPR+AGPR per lane, 8 wave slots per SIMD; dense bf16 MFMA 2516.6 TFLOP/s,
 # fp32 MFMA 157.3 TFLOP/s, HBM3E 8 TB/s.  The rest are calibration constants
 # (page "Tile Selection: Cost Models Against Measurement", "Hybrid
-# strategies"): the LDS and L2-to-CU bandwidths, the two latencies and the
-# lone-wave efficiency were fitted on the measured exhaustive tables of the
-# five workloads and eleven further shapes and scored on twelve shapes the
-# fit did not see (grid search on the number of training tables whose
-# measured best is the model's first choice, then in its top 16, then the
-# mean squared log error; held-out first-choice hits 3 -> 5 of 12, best in
-# the top 16 5 -> 8, measured time of the first choice over the best, geometric
-# mean, 1.24 -> 1.07).  They are: effective LDS and
+# strategies"): the LDS and L2-to-CU bandwidths, the two latencies, the
+# lone-wave efficiency and the sliced-K kind's efficiency were fitted on the
+# measured exhaustive tables of the five workloads and eleven further shapes
+# and scored on twelve shapes the fit did not see (grid search on the number
+# of training tables whose measured best is outside the model's top 16, then
+# the geometric mean of the measured time of the model's first choice over
+# the best, then the mean squared log error; held out: first choice over the
+# best 1.166 -> 1.091, first choice = best 4 and best in the top 16 6 of 12
+# before and after).  They are: effective LDS and
 # L2-to-CU bandwidth per CU, memory latency a K step waits for (from HBM /
 # from L2), the footprint below which the L2 serves a problem, the issue
-# efficiency of a lone wave on a SIMD, the decode kernel's and HBM's
-# achievable fractions (7.3 TB/s measured for streaming reads), launch
-# overhead; r0 is the register base of the VGPR estimate.
+# efficiency of a lone wave on a SIMD and of the sliced-K kind, the decode
+# kernel's and HBM's achievable fractions (7.3 TB/s measured for streaming
+# reads), launch overhead; r0 is the register base of the VGPR estimate.
 MI355X = Device(mode=0, n_cu=256, simds=4, lds_cu=163840, lds_block=163840,
                 max_threads=1024, waves_max=8, blocks_max=32, vgpr_max=512,
                 acc_max=256, peak_bf16=2516.6e12, peak_f32=157.3e12, bw=8.0e12,
                 a_ref=16384.0, c_fill=2.0, t0=4.0e-6, unaligned_eff=0.25,
-                lat_mem=2.0e-6, cu_bw=60.0e9, r0=24, lds_bw_cu=192.0e9, lat_step=1.0e-6,
-                lat_l2=0.4e-6, l2_bytes=32.0e6, w1_eff=0.5, skinny_eff=0.75, hbm_eff=0.9125)
+                lat_mem=2.0e-6, cu_bw=50.0e9, r0=24, lds_bw_cu=192.0e9, lat_step=1.0e-6,
+                lat_l2=0.3e-6, l2_bytes=32.0e6, w1_eff=0.35, skinny_eff=0.75, hbm_eff=0.9125,
+                sliced_eff=1.0)
 
 # The page's H100 model: 132 SMs, 228 KB shared memory, 989 TFLOP/s bf16,
 # 3.35 TB/s; one tile per SM at a time; no register model; no pipeline-fill
@@ -181,15 +184,16 @@ def space(dtype: int, dev: Device = MI355X):
             for bn in (32, 64, 128, 256):
                 out.append(Cfg(KIND_TILED, bm, bn, 64, 1, 1, 1, 1))
         return out
+    # 16-row tiles: a 16-row decode wastes no MFMA rows.  The reduction step
+    # spans 64, 128 or 256 bytes of an A row (fp32 16/32/64, bf16 32/64/128 k).
     if dtype == F32:
-        tiles_m, tiles_n, bks = (32, 64, 128), (32, 64, 128), (8, 16, 32)
+        tiles_m, tiles_n, bks = (16, 32, 64, 128), (32, 64, 128), (16, 32, 64)
     else:
-        # 16-row tiles for the bf16 kernel: a 16-row decode wastes no MFMA rows
         tiles_m, tiles_n, bks = (16, 32, 64, 128, 256), (32, 64, 128, 256), (32, 64, 128)
-    # fp32 kernel: 1 or 2 LDS buffers; bf16 kernel: 2 to 8 stages in flight
-    # (page "Tiling the hierarchy", double buffering: a latency-bound tile wants
-    # a deeper pipeline; the LDS rule keeps the deep ones to small tiles)
-    stages = (1, 2) if dtype == F32 else (2, 3, 4, 6, 8)
+    # 2 to 8 stages in flight (page "Tiling the hierarchy", double buffering: a
+    # latency-bound tile wants a deeper pipeline; the LDS rule keeps the deep
+    # ones to small tiles)
+    stages = (2, 3, 4, 6, 8)
     for bm, bn, bk, (wm, wn), st, s in itertools.product(
             tiles_m, tiles_n, bks, WAVE_GRIDS, stages, SPLITS):
         out.append(Cfg(KIND_TILED, bm, bn, bk, wm, wn, st, s))
@@ -204,12 +208,35 @@ def space(dtype: int, dev: Device = MI355X):
         # stream-K kind: large tiles, whose last partial round is worth spreading
         for bm, bn, (wm, wn), st in itertools.product((128, 256), (128, 256), ((2, 2), (2, 4), (4, 2)), (2, 3, 4)):
             out.append(Cfg(KIND_STREAMK, bm, bn, 64, wm, wn, st, 1))
+    # sliced-K kind: small tiles whose K loop is a chain of short steps; the
+    # split_k field is the number of K groups inside one workgroup (2 or 4)
+    bns = (32, 64) if dtype == F32 else (64, 128)
+    bks = (32, 64) if dtype == F32 else (64, 128)
+    for bm, bn, bk, (wm, wn), st, g in itertools.product((16, 32, 64), bns, bks, ((1, 1), (1, 2), (2, 2)),
+                                                       (2, 3, 4), (2, 4)):
+        out.append(Cfg(KIND_SLICEDK, bm, bn, bk, wm, wn, st, g))
     return out
 
 
 def dma_kind(c: Cfg, dtype: int) -> bool:
-    """The bf16 kernels that move panels straight into LDS (tiled, stream-K)."""
-    return c.kind in (KIND_TILED, KIND_STREAMK) and dtype != F32
+    """The kernels that move panels straight into LDS: the tiled and sliced-K
+    kinds (fp32 and bf16) and stream-K (bf16 only)."""
+    return c.kind in (KIND_TILED, KIND_SLICEDK) or (c.kind == KIND_STREAMK and dtype != F32)
+
+
+def cta_splits(c: Cfg) -> int:
+    """Workgroups that share one tile's K range: split_k, except for the
+    sliced-K kind, whose K groups live inside one workgroup."""
+    return 1 if c.kind == KIND_SLICEDK else c.split_k
+
+
+def k_groups(c: Cfg) -> int:
+    """K groups of waves inside one workgroup (sliced-K: split_k; else 1)."""
+    return c.split_k if c.kind == KIND_SLICEDK else 1
+
+
+def waves_per_block(c: Cfg) -> int:
+    return c.wgm * c.wgn * k_groups(c)
 
 
 # ---------------------------------------------------------------- resources
@@ -217,7 +244,8 @@ def lds_bytes(c: Cfg, dtype: int) -> int:
     eb = in_bytes(dtype)
     if c.kind == KIND_SKINNY:
         return c.wgm * c.bm * 128 * 4 if c.wgm > 1 else 0
-    pad_b = 4 if dtype == F32 else 0
+    # the register-staged fp32 kernel pads B rows by 4 floats
+    pad_b = 4 if dtype == F32 and not dma_kind(c, dtype) else 0
     return c.stages * (c.bm * c.bk + c.bk * (c.bn + pad_b)) * eb
 
 
@@ -237,7 +265,7 @@ def vgpr_estimate(c: Cfg, dtype: int, dev: Device) -> int:
     eb = in_bytes(dtype)
     frag = 4 * ((c.bm // c.wgm) // 16 + (c.bn // c.wgn) // 16)
     if dma_kind(c, dtype):
-        # the bf16 tiled kernels load panels straight into LDS: no staging registers
+        # panels go straight into LDS: no staging registers
         return acc_regs(c) + frag + dev.r0
     chunks_a = c.bm * c.bk * eb // 16
     stage = 4 * cdiv(chunks_a, threads)
@@ -255,7 +283,7 @@ def waves_per_simd(c: Cfg, dtype: int, dev: Device) -> int:
 
 
 def blocks_per_cu(c: Cfg, dtype: int, dev: Device) -> int:
-    w = c.wgm * c.wgn
+    w = waves_per_block(c)
     b = min(dev.blocks_max, (dev.simds * waves_per_simd(c, dtype, dev)) // w)
     lds = lds_bytes(c, dtype)
     if lds > 0:
@@ -264,8 +292,9 @@ def blocks_per_cu(c: Cfg, dtype: int, dev: Device) -> int:
 
 
 # What the compiler allotted to each compiled kernel (a fixed input, see
-# oracle/refresh_allocation.py): (in_bf16, kind, bm, bn, bk, wgm, wgn, stages)
-# -> (vgpr, agpr, lds, scratch, reported waves per SIMD).
+# oracle/refresh_allocation.py): (in_bf16, kind, bm, bn, bk, wgm, wgn, stages,
+# k_groups) -> (vgpr, agpr, lds, scratch, reported waves per SIMD); k_groups is
+# the sliced-K kind's compiled K-group count, 0 for every other kind.
 _ALLOC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kernel_allocation.json")
 _ALLOC = None
 
@@ -275,13 +304,14 @@ def allocation_table():
     if _ALLOC is None:
         with open(_ALLOC_FILE) as f:
             t = json.load(f)
-        _ALLOC = {tuple(r[:8]): tuple(r[8:]) for r in t["kernels"]}
+        _ALLOC = {tuple(r[:9]): tuple(r[9:]) for r in t["kernels"]}
     return _ALLOC
 
 
 def compiled_alloc(dtype: int, c: Cfg):
     """(vgpr, agpr, lds, scratch) of the kernel serving c, or None."""
-    r = allocation_table().get((0 if dtype == F32 else 1, c.kind, c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages))
+    kg = c.split_k if c.kind == KIND_SLICEDK else 0
+    r = allocation_table().get((0 if dtype == F32 else 1, c.kind, c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, kg))
     return None if r is None else r[:4]
 
 
@@ -303,7 +333,7 @@ def resident_blocks(c: Cfg, dtype: int, dev: Device) -> int:
     if a is None:
         return blocks_per_cu(c, dtype, dev)
     vgpr, agpr, lds, _ = a
-    w = c.wgm * c.wgn
+    w = waves_per_block(c)
     b = min(dev.blocks_max, (dev.simds * waves_per_simd_alloc(vgpr, agpr, dev)) // w)
     if lds > 0:
         b = min(b, dev.lds_cu // lds)
@@ -314,26 +344,29 @@ def transfers_per_wave(c: Cfg, dtype: int) -> int:
     """16-byte-per-lane (1 KiB) transfers a wave issues per stage in the bf16
     tiled kernel: the A and B panels of one stage spread over the waves."""
     inst = (c.bm + c.bn) * c.bk * in_bytes(dtype) // 1024
-    return cdiv(inst, c.wgm * c.wgn)
+    return cdiv(inst, waves_per_block(c))
 
 
 def k_per_split(c: Cfg, K: int) -> int:
     unit = 32 if c.kind == KIND_SKINNY else c.bk
-    return cdiv(cdiv(K, c.split_k), unit) * unit
+    return cdiv(cdiv(K, cta_splits(c)), unit) * unit
 
 
 def check_static(dtype: int, c: Cfg, dev: Device = MI355X) -> int:
     """The rules that do not depend on the shape: threads, whole MFMA tiles
     per wave, LDS, accumulator and VGPR budgets, at least one resident
     workgroup per CU."""
-    w = c.wgm * c.wgn
-    if 64 * w > dev.max_threads:
+    if 64 * waves_per_block(c) > dev.max_threads:
         return R_WAVES
     if c.kind != KIND_SKINNY:
-        kstep = 16 if dtype == F32 else 32
+        # every K group takes whole MFMA slices (16 fp32 or 32 bf16 k) of a stage
+        kstep = (16 if dtype == F32 else 32) * k_groups(c)
         if c.bm % (16 * c.wgm) or c.bn % (16 * c.wgn) or c.bk % kstep:
             return R_DIV
     if lds_bytes(c, dtype) > dev.lds_block:
+        return R_LDS
+    # the K groups' bm x bn fp32 sums (all but one group's) meet in the stage buffers
+    if k_groups(c) > 1 and (k_groups(c) - 1) * c.bm * c.bn * 4 > lds_bytes(c, dtype):
         return R_LDS
     # the bf16 tiled kernel keeps ST stages of transfers in flight after its
     # prologue; a wave's memory counter tracks at most 63 (MI355X only)
@@ -383,7 +416,7 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
     # without a partial last round the stream-K kind is the data-parallel one
     if c.kind == KIND_STREAMK and streamk_plan(M, N, K, c, dev)["tail"] == 0:
         return R_SHAPE
-    if c.split_k > 1:
+    if cta_splits(c) > 1:
         if K == 0 or cdiv(K, k_per_split(c, K)) != c.split_k:
             return R_SPLIT
     return OK
@@ -413,7 +446,7 @@ def grid(M: int, N: int, c: Cfg, dev: Device = MI355X, K: int | None = None):
     if c.kind == KIND_STREAMK:
         assert K is not None, "the stream-K kind's workgroup count depends on K"
         return tiles, streamk_plan(M, N, K, c, dev)["blocks"]
-    return tiles, tiles * c.split_k
+    return tiles, tiles * cta_splits(c)
 
 
 def sk_owner(x: int, I: int, G: int) -> int:
@@ -465,7 +498,7 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
     flops = 2.0 * M * N * K
     compulsory = float(eb * (M * K + K * N) + ec * M * N)
     tiles, units = grid(M, N, c, dev, K)
-    w = c.wgm * c.wgn
+    w = waves_per_block(c)
     bcu = resident_blocks(c, dtype, dev)
 
     if c.kind == KIND_SKINNY:
@@ -495,13 +528,13 @@ def _splitk_slabs(M: int, N: int, c: Cfg) -> float:
     M x N slab per split (my reading of split-K, page "Compilers and Kernel
     Languages", "A different tile for a different shape": the partial sums
     of the K ranges have to meet before the non-linear epilogue)."""
-    return 4.0 * c.split_k * M * N if c.split_k > 1 else 0.0
+    return 4.0 * c.split_k * M * N if cta_splits(c) > 1 else 0.0
 
 
 def _splitk_pass(M: int, N: int, ec: int, c: Cfg, dev: Device) -> float:
     """The second split-K pass: one more launch that reads every slab once
     and writes C, at the HBM rate."""
-    if c.split_k <= 1:
+    if cta_splits(c) <= 1:
         return 0.0
     return (_splitk_slabs(M, N, c) + float(ec) * M * N) / (dev.bw * dev.hbm_eff) + dev.t0
 
@@ -527,7 +560,7 @@ def _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, unit
     t_c = flops / (peak * eff)
     raw = float(tiles) * eb * K * (c.bm + c.bn)
     g = math.sqrt(min(units, dev.n_cu * bcu))
-    ws = 8.0 * tiles * c.bm * c.bn * c.split_k if c.split_k > 1 else 0.0
+    ws = 8.0 * tiles * c.bm * c.bn * c.split_k if cta_splits(c) > 1 else 0.0
     t_m = (max(compulsory, raw / g) + ws) / dev.bw
     return max(t_c, t_m) + dev.t0
 
@@ -555,7 +588,9 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
     wm, wn = c.bm // c.wgm, c.bn // c.wgn
     simd_peak = peak / (dev.n_cu * dev.simds)
     f_step = 2.0 * c.bm * c.bn * c.bk
-    lds_step = float(c.bk * eb * (w * (wm + wn) + c.bm + c.bn))
+    # fragment reads of one K group's wgm x wgn waves (each group reads only
+    # its own slices) plus the transfers' writes
+    lds_step = float(c.bk * eb * (c.wgm * c.wgn * (wm + wn) + c.bm + c.bn))
     qw = min(c.bn, 64) if dma_kind(c, dtype) else c.bn
     l2_step = float(c.bm * _line(c.bk * eb) + c.bk * (c.bn // qw) * _line(qw * eb))
     if c.kind == KIND_UNALIGNED:
@@ -568,6 +603,9 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
         issue = max(res * f_step / (simd_peak * busy), res * lds_step / dev.lds_bw_cu)
         if res * w <= dev.simds:
             issue = issue / dev.w1_eff
+        if c.kind == KIND_SLICEDK:
+            # each K group meets the stage barrier after a short run of MFMAs
+            issue = issue / dev.sliced_eff
         return max(issue, res * l2_step / dev.cu_bw, lat / depth)
 
     slots = dev.n_cu * bcu
@@ -596,12 +634,16 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
         t_cu = t_cu + ktiles * step(cdiv(rem, dev.n_cu))
     rounds = full + (1 if rem > 0 else 0)
     t_cu = t_cu + rounds * lat
+    # sliced-K: after the K loop groups 1 .. g-1 of a tile write their sums to
+    # LDS and group 0 reads them back
+    red = 8.0 * (k_groups(c) - 1) * c.bm * c.bn / dev.lds_bw_cu if k_groups(c) > 1 else 0.0
+    t_cu = t_cu + (full * bcu + (cdiv(rem, dev.n_cu) if rem > 0 else 0)) * red
     raw = float(tiles) * eb * K * (c.bm + c.bn)
     g = math.sqrt(min(units, slots))
     t_hbm = (max(compulsory, raw / g) + _splitk_slabs(M, N, c)) / (dev.bw * dev.hbm_eff)
     # every block stores its outputs (C, or its split-K slab) after its K
     # loop: those stores do not overlap the loop
-    stores = _splitk_slabs(M, N, c) if c.split_k > 1 else float(ec) * M * N
+    stores = _splitk_slabs(M, N, c) if cta_splits(c) > 1 else float(ec) * M * N
     t_cu = t_cu + stores / (dev.bw * dev.hbm_eff)
     return max(t_cu, t_hbm) + _splitk_pass(M, N, ec, c, dev) + dev.t0
 

@@ -169,11 +169,10 @@ def test_gelu_epilogue_accuracy_over_its_range():
     M, N = 48, 4096
     bias = np.linspace(-12.0, 12.0, N).astype(np.float32)
     # K = 60 is not a multiple of 8: the element-load kind; M = 48 also admits the decode kernel
-    cases = [(wl.BF16_F32OUT, 64, (0, 32, 128, 64, 1, 2, 2, 1)), (wl.F32, 64, (0, 32, 32, 32, 2, 2, 1, 1)),
+    cases = [(wl.BF16_F32OUT, 64, (0, 32, 128, 64, 1, 2, 2, 1)), (wl.F32, 64, (0, 32, 32, 32, 2, 2, 2, 1)),
              (wl.BF16_F32OUT, 60, None), (wl.BF16_F32OUT, 64, (1, 48, 128, 32, 2, 1, 2, 1))]
     for dtype, K, cfg in cases:
-        if cfg is not None and not tg.has_kernel(dtype, cfg):
-            continue
+        assert cfg is None or tg.has_kernel(dtype, cfg), cfg
         A = np.zeros((M, K), np.float32 if dtype == wl.F32 else np.uint16)
         B = np.zeros((K, N), A.dtype)
         ref = gemm_ref.gemm(A, B, bias, "gelu")
@@ -358,6 +357,49 @@ def test_streamk_gelu_random_inputs_and_repeatable():
         torch.cuda.synchronize()
         assert torch.equal(C1, C2), "the same call gives the same bits"
         assert_close(out_f64(C1), ref, dtype, f"stream-K gelu {cfg}")
+
+
+@pytest.mark.parametrize("M,N,K,dtype,act", [
+    (100, 200, 1000, wl.F32, "relu"),          # ragged M, N; K not a multiple of any stage
+    (256, 256, 256, wl.F32, "none"),           # the fp32 256^3 shape
+    (130, 264, 1032, wl.BF16, "relu"),         # ragged M; K mod 128 = 8
+    (64, 512, 4096, wl.BF16_F32OUT, "none"),   # long K: many stages per K group
+    (17, 96, 40, wl.BF16, "none"),             # one partial stage
+])
+def test_sliced_k_integer_exact(M, N, K, dtype, act):
+    """The sliced-K kind (K groups inside one workgroup, their sums added in
+    LDS): every configuration, integer-valued inputs, output equal to the
+    exact result (fp32) or to its round-to-nearest-even bf16, one launch."""
+    A, B, bias = _int_inputs(M, N, K, dtype, 41)
+    ref = gemm_ref.gemm(A, B, bias, act)
+    cfgs = [c.astuple() for c in tg.enumerate_feasible(M, N, K, dtype) if c.kind == 4 and tg.has_kernel(dtype, c)]
+    assert len(cfgs) >= 40
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    for cfg in cfgs:
+        mark(f"sliced-K {M}x{N}x{K} dt{dtype} {cfg}")
+        C = _run(A_d, B_d, b_d, act, dtype, cfg)
+        torch.cuda.synchronize()
+        _exact_check(C, ref, dtype, f"sliced-K {cfg}")
+    c = cfgs[0]
+    tiles = S.cdiv(M, c[1]) * S.cdiv(N, c[2])
+    assert tg.grid(M, N, K, c) == (tiles, tiles)
+
+
+def test_sliced_k_gelu_random_inputs_and_repeatable():
+    for dtype, cfg in [(wl.F32, (4, 16, 32, 64, 1, 1, 2, 4)), (wl.BF16, (4, 32, 128, 128, 1, 2, 3, 4)),
+                       (wl.BF16_F32OUT, (4, 64, 64, 64, 2, 2, 2, 2))]:
+        M, N, K = 300, 640, 2048
+        A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("normal", 0.5), wl.Dist("normal", 0.5),
+                                    wl.Dist("normal", 0.5), 43)
+        ref = gemm_ref.gemm(A, B, bias, "gelu")
+        assert tg.has_kernel(dtype, cfg), cfg
+        A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+        mark(f"sliced-K gelu dt{dtype} {cfg}")
+        C1 = _run(A_d, B_d, b_d, "gelu", dtype, cfg)
+        C2 = _run(A_d, B_d, b_d, "gelu", dtype, cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(C1, C2), "the same call gives the same bits"
+        assert_close(out_f64(C1), ref, dtype, f"sliced-K gelu {cfg}")
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])

@@ -69,7 +69,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert N.lib().tg_version() == 2
+    assert N.lib().tg_version() == 3
 
 
 @pytest.mark.parametrize("dtype", [S.F32, S.BF16, S.BF16_F32OUT])
@@ -118,7 +118,7 @@ def test_builtin_descriptions_match_oracle_constants():
         for f in ("mode", "n_cu", "simds", "lds_cu", "lds_block", "max_threads", "waves_max", "blocks_max",
                   "vgpr_max", "acc_max", "r0", "peak_bf16", "peak_f32", "bw", "a_ref", "c_fill", "t0",
                   "unaligned_eff", "lat_mem", "cu_bw", "lds_bw_cu", "lat_step", "lat_l2", "l2_bytes", "w1_eff",
-                  "skinny_eff", "hbm_eff"):
+                  "skinny_eff", "hbm_eff", "sliced_eff"):
             assert getattr(d, f) == getattr(ref, f), f
 
 
@@ -151,10 +151,12 @@ def test_every_instantiable_configuration_has_a_kernel():
     n = 0
     for dtype in (S.F32, S.BF16):
         for c in S.space(dtype):
-            if c.split_k == 1 and S.check_static(dtype, c) == S.OK:
+            # split_k is a run-time value except for the sliced-K kind
+            compiled = c.split_k == 1 or c.kind == S.KIND_SLICEDK
+            if compiled and S.check_static(dtype, c) == S.OK:
                 assert N.has_kernel(dtype, c.astuple()), c
                 n += 1
-            elif c.split_k == 1:
+            elif compiled:
                 assert not N.has_kernel(dtype, c.astuple()), c
     assert N.kernel_count() == n
     # bf16->fp32 output uses the bf16 kernels
@@ -328,6 +330,12 @@ def test_b_streaming_rule():
         tg.streams_b(-1, S.BF16, tg.space(S.BF16)[0])
 
 
+def _cfg_of(key):
+    """The configuration an allocation-table key names (split_k = 1, or the
+    compiled K groups of a sliced-K kernel)."""
+    return key[1:8] + (key[8] if key[1] == S.KIND_SLICEDK else 1,)
+
+
 def test_allocation_table_matches_the_built_kernels():
     # the oracle's fixed input (oracle/kernel_allocation.json) must describe the
     # kernels this library was built with; refresh it with
@@ -335,7 +343,7 @@ def test_allocation_table_matches_the_built_kernels():
     table = S.allocation_table()
     assert N.kernel_count() == len(table)
     for key, (vgpr, agpr, lds, scratch, occ) in table.items():
-        in_bf16, cfg = key[0], key[1:] + (1,)
+        in_bf16, cfg = key[0], _cfg_of(key)
         dt = S.BF16 if in_bf16 else S.F32
         assert N.kernel_resources(dt, cfg) == (vgpr, agpr, scratch, lds, occ), key
 
@@ -343,7 +351,7 @@ def test_allocation_table_matches_the_built_kernels():
 def test_spill_rule_through_the_abi():
     for key, v in S.allocation_table().items():
         if v[3] > 0:
-            c = key[1:] + (1,)
+            c = _cfg_of(key)
             dt = S.BF16 if key[0] else S.F32
             M = c[1] if c[0] == S.KIND_SKINNY else 1024
             assert N.check_cfg(M, 1024, 1024, dt, c) == S.R_SPILL

@@ -150,21 +150,25 @@ def test_lds_examples():
     assert S.lds_bytes(one, S.BF16) == 2 * 64 * 1024 and S.check(8192, 8192, 8192, S.BF16, one, d) == S.OK
     odd = S.Cfg(S.KIND_TILED, 128, 128, 96, 2, 4, 2, 1)
     assert S.check(8192, 8192, 8192, S.BF16, odd, d) == S.R_SPACE     # bf16 BK is 32, 64 or 128
-    # the largest bf16 tiles at one stage fit; fp32 128x128x32 two stages fit
+    # the largest bf16 tiles at two stages fit; fp32 128x128x32 two stages fit
     assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 2, 1), d) == S.OK
     assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 3, 1), d) == S.R_LDS
     assert S.check(8192, 8192, 8192, S.BF16, S.Cfg(0, 256, 256, 64, 2, 4, 1, 1), d) == S.R_SPACE
-    assert S.lds_bytes(S.Cfg(0, 128, 128, 32, 2, 2, 2, 1), S.F32) == 2 * (128 * 32 + 32 * 132) * 4
-    # all 18 fp32 sweep triples fit LDS at one stage
-    for bm in (32, 64, 128):
+    # fp32 tiles travel straight into LDS unpadded; the register-staged
+    # kernel of the unaligned kind pads each B row by 4 floats
+    assert S.lds_bytes(S.Cfg(0, 128, 128, 32, 2, 2, 2, 1), S.F32) == 2 * (128 * 32 + 32 * 128) * 4
+    assert S.lds_bytes(S.Cfg(S.KIND_UNALIGNED, 128, 128, 16, 2, 2, 2, 1), S.F32) == 2 * (128 * 16 + 16 * 132) * 4
+    # all 36 fp32 tile triples fit LDS at two stages
+    for bm in (16, 32, 64, 128):
         for bn in (32, 64, 128):
-            for bk in (16, 32):
-                assert S.lds_bytes(S.Cfg(0, bm, bn, bk, 1, 1, 1, 1), S.F32) <= d.lds_block
+            for bk in (16, 32, 64):
+                assert S.lds_bytes(S.Cfg(0, bm, bn, bk, 1, 1, 2, 1), S.F32) <= d.lds_block
 
 
 def test_rejections_have_reasons():
     d = S.MI355X
-    assert S.check(256, 256, 256, S.F32, S.Cfg(0, 64, 64, 8, 1, 1, 1, 1), d) == S.R_DIV
+    assert S.check(256, 256, 256, S.F32, S.Cfg(0, 16, 64, 16, 2, 1, 2, 1), d) == S.R_DIV      # 16 rows, 2 waves
+    assert S.check(256, 256, 256, S.F32, S.Cfg(0, 64, 64, 8, 1, 1, 2, 1), d) == S.R_SPACE     # fp32 BK is 16, 32, 64
     assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 1, 4, 1, 1), d) == S.R_SPACE
     assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 32, 32, 32, 2, 4, 2, 1), d) == S.R_DIV
     assert S.check(256, 256, 256, S.BF16, S.Cfg(0, 256, 128, 32, 1, 1, 2, 1), d) == S.R_ACC
@@ -330,12 +334,24 @@ def _compiler_occupancy(vgpr, agpr, lds, w, dev=S.MI355X):
     return occ
 
 
+def _cfg_of(key):
+    """The configuration an allocation-table key names (split_k = 1, or the
+    compiled K groups of a sliced-K kernel)."""
+    return key[1:8] + (key[8] if key[1] == S.KIND_SLICEDK else 1,)
+
+
+def _waves(key):
+    """Waves per workgroup of an allocation-table key: wgm for the skinny
+    kind, wgm x wgn x the compiled K groups for sliced-K, wgm x wgn else."""
+    kind, wgm, wgn, kg = key[1], key[5], key[6], key[8]
+    return wgm * (1 if kind == S.KIND_SKINNY else wgn) * (kg if kind == S.KIND_SLICEDK else 1)
+
+
 def test_register_file_rule_reproduces_the_compilers_occupancy():
     table = S.allocation_table()
     assert len(table) > 1000
     for key, (vgpr, agpr, lds, scratch, occ) in table.items():
-        kind, wgm, wgn = key[1], key[5], key[6]
-        w = wgm * (1 if kind == S.KIND_SKINNY else wgn)
+        w = _waves(key)
         assert _compiler_occupancy(vgpr, agpr, lds, w) == occ, (key, vgpr, agpr, lds, occ)
 
 
@@ -351,12 +367,12 @@ def test_register_file_rule_closed_forms():
     # a planted mistake (AGPRs not counted) fails the pin above
     bad = 0
     for key, (vgpr, agpr, lds, scratch, occ) in S.allocation_table().items():
-        w = key[5] * (1 if key[1] == S.KIND_SKINNY else key[6])
+        w = _waves(key)
         o = S.waves_per_simd_alloc(vgpr, 0, d)
         if lds > 0:
             o = min(o, S.cdiv((d.lds_cu // lds) * w, d.simds))
         bad += o != occ
-    assert bad > 100
+    assert bad > 50
 
 
 def test_bf16_accumulators_are_exactly_the_agprs():
@@ -365,7 +381,7 @@ def test_bf16_accumulators_are_exactly_the_agprs():
     for key, (vgpr, agpr, lds, scratch, occ) in S.allocation_table().items():
         in_bf16, kind = key[0], key[1]
         if in_bf16 == 1 and kind == S.KIND_TILED:
-            c = S.Cfg(*key[1:], 1)
+            c = S.Cfg(*key[1:8], 1)
             assert agpr == S.acc_regs(c), key
             assert lds == S.lds_bytes(c, S.BF16), key
             n += 1
@@ -387,7 +403,7 @@ def test_resident_blocks_from_the_allocation():
     # wherever the two counts differ, the model prices the compiler's
     diff = 0
     for key in S.allocation_table():
-        c = S.Cfg(*key[1:], 1)
+        c = S.Cfg(*_cfg_of(key))
         dt = S.BF16 if key[0] else S.F32
         if S.check_static(dt, c) == S.OK and S.resident_blocks(c, dt, d) != S.blocks_per_cu(c, dt, d):
             diff += 1
@@ -398,7 +414,7 @@ def test_spilling_kernels_are_rejected():
     spilling = [k for k, v in S.allocation_table().items() if v[3] > 0]
     assert spilling
     for key in spilling:
-        c = S.Cfg(*key[1:], 1)
+        c = S.Cfg(*_cfg_of(key))
         dt = S.BF16 if key[0] else S.F32
         M = c.bm if c.kind == S.KIND_SKINNY else 1024
         Nn, K = 1024, 1024
@@ -406,7 +422,7 @@ def test_spilling_kernels_are_rejected():
     # the estimate is only the pre-build filter: it lets through every kernel
     # that was compiled, and those that spill are caught by the rule above
     for key in S.allocation_table():
-        c = S.Cfg(*key[1:], 1)
+        c = S.Cfg(*_cfg_of(key))
         dt = S.BF16 if key[0] else S.F32
         assert S.check_static(dt, c) == S.OK
 
@@ -523,3 +539,59 @@ def test_streamk_model_closed_form():
     # K = 0 has nothing to spread; fp32 has no stream-K kernel
     assert S.check(4096, 4096, 0, S.BF16, sk) == S.R_SHAPE
     assert S.check(4096, 4096, 64, S.F32, sk) != S.OK
+
+
+def test_sliced_k_rules_closed_forms():
+    d = S.MI355X
+    SK = S.KIND_SLICEDK
+    # the workgroup holds wgm x wgn x split_k waves; each K group takes whole
+    # MFMA slices (bf16 32 k, fp32 16 k) of every stage
+    c = S.Cfg(SK, 32, 64, 128, 1, 2, 2, 4)
+    assert S.waves_per_block(c) == 8 and S.k_groups(c) == 4 and S.cta_splits(c) == 1
+    assert S.check(256, 256, 1024, S.BF16, c, d) == S.OK
+    assert S.check(256, 256, 1024, S.BF16, S.Cfg(SK, 32, 64, 64, 1, 2, 2, 4), d) == S.R_DIV     # 64 k: two slices
+    assert S.check(256, 256, 1024, S.F32, S.Cfg(SK, 32, 32, 32, 1, 1, 2, 4), d) == S.R_DIV      # 32 k: two slices
+    assert S.check(256, 256, 1024, S.F32, S.Cfg(SK, 32, 32, 64, 1, 1, 2, 4), d) == S.OK
+    # the other groups' fp32 sums (3 x 64 x 64 x 4 = 48 KiB) must fit in the
+    # stage buffers (2 x (64 x 32 + 32 x 64) x 4 = 32 KiB)
+    big = S.Cfg(SK, 64, 64, 32, 1, 1, 2, 2)
+    assert S.lds_bytes(big, S.F32) == 32 * 1024 and (2 - 1) * 64 * 64 * 4 <= 32 * 1024
+    assert S.check(256, 256, 1024, S.F32, big, d) == S.OK
+    assert S.check_static(S.F32, S.Cfg(SK, 64, 64, 64, 1, 1, 2, 4)) == S.OK          # 64 KiB >= 48 KiB
+    # 64 x 256 bf16 tiles, 4 groups: the stages (160 KiB) fit the LDS, the
+    # other groups' sums (3 x 64 x 256 x 4 = 192 KiB) do not
+    wide = S.Cfg(SK, 64, 256, 128, 1, 1, 2, 4)
+    assert S.lds_bytes(wide, S.BF16) == 160 * 1024 <= d.lds_block
+    assert S.check_static(S.BF16, wide) == S.R_LDS
+    # one launch of one workgroup per tile, the whole K range in each
+    assert S.grid(1000, 1000, c, d, 8192) == (32 * 16, 32 * 16)
+    assert S.k_per_split(c, 8192) == 8192 and S.k_per_split(c, 1000) == 1024
+    # no split-K rule, no partial-sum slabs, no second pass
+    assert S._splitk_slabs(1000, 1000, c) == 0.0
+    assert S._splitk_pass(1000, 1000, 2, c, d) == 0.0
+    # transfers are spread over every wave of the workgroup: (32 + 64) x 128 x 2 / 1 KiB = 24 over 8
+    assert S.transfers_per_wave(c, S.BF16) == 3
+
+
+def test_sliced_k_in_the_per_cu_model():
+    # MFMA work alone (LDS, L2, latency and stores negligible, no lone-wave
+    # penalty): a block's step is its flops over the SIMDs its waves occupy, so
+    # four K groups of one wave run a one-wave tile's step four times as fast
+    d = dataclasses.replace(S.MI355X, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0, bw=1e30)
+    one = S.Cfg(S.KIND_TILED, 32, 32, 64, 1, 1, 2, 1)
+    four = S.Cfg(S.KIND_SLICEDK, 32, 32, 64, 1, 1, 2, 4)
+    M = Nn = 256
+    K = 1024
+    t1 = S.model_time(M, Nn, K, S.F32, one, d) - d.t0
+    t4 = S.model_time(M, Nn, K, S.F32, four, d) - d.t0
+    # 64 tiles, one per CU (64 CUs busy): the K loop is 16 steps of 2 x 32 x 32 x 64 flops
+    step_flops = 2.0 * 32 * 32 * 64
+    simd = d.peak_f32 / (d.n_cu * d.simds)
+    assert t1 == pytest.approx(16 * step_flops / simd)
+    assert t4 == pytest.approx(16 * step_flops / (4 * simd))
+    # the cross-group sum: (g - 1) bm bn fp32 values written and read once in LDS, per tile
+    dl = dataclasses.replace(d, lds_bw_cu=1e12)
+    red = 8.0 * 3 * 32 * 32 / 1e12
+    lds_steps = 16 * (64 * 4 * (1 * (32 + 32) + 32 + 32)) / 1e12   # fragment reads of one group + transfer writes
+    t4l = S.model_time(M, Nn, K, S.F32, four, dl) - d.t0
+    assert t4l == pytest.approx(max(16 * step_flops / (4 * simd), lds_steps) + red)

@@ -121,9 +121,13 @@ def test_missing_results_raise(tmp_path):
 
 
 def test_kernel_names_match_the_template_instances():
-    assert R.kernel_name((0, 64, 128, 64, 2, 4, 2, 4)) == "gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2, false>"
+    assert R.kernel_name((0, 64, 128, 64, 2, 4, 2, 4)) == "gemm_tiled_dma_kernel<64, 128, 64, 2, 4, 2, false, false, 1>"
     assert R.kernel_name((0, 32, 256, 32, 1, 2, 4, 2), stream_b=True) == \
-        "gemm_tiled_dma_kernel<32, 256, 32, 1, 2, 4, true>"
+        "gemm_tiled_dma_kernel<32, 256, 32, 1, 2, 4, true, false, 1>"
+    assert R.kernel_name((0, 32, 32, 32, 2, 2, 4, 1), in_bf16=False) == \
+        "gemm_tiled_dma_kernel<32, 32, 32, 2, 2, 4, false, true, 1>"
+    assert R.kernel_name((4, 16, 32, 64, 1, 1, 2, 4), in_bf16=False) == \
+        "gemm_tiled_dma_kernel<16, 32, 64, 1, 1, 2, false, true, 4>"
     assert R.kernel_name((1, 32, 128, 32, 4, 1, 2, 8)) == "gemm_skinny_kernel<2, 4, 2>"
 
 
@@ -194,8 +198,8 @@ def test_workload_launch_picks_the_dispatches_of_a_workload():
     from tile_shape_autotuning_amd import rocprof_report as R
     # 8192^3 at 256 x 256 with 8 waves: 1024 workgroups of 512 lanes, no second pass
     assert R.workload_launch(3, (0, 256, 256, 64, 2, 4, 2, 1)) == (
-        "gemm_tiled_dma_kernel<256, 256, 64, 2, 4, 2, false>", 1024 * 512, None)
+        "gemm_tiled_dma_kernel<256, 256, 64, 2, 4, 2, false, false, 1>", 1024 * 512, None)
     # the decode with split 2 streams B (one tile row) and adds a second pass over 16 x 28672 outputs
     name, grid, second = R.workload_launch(4, (0, 64, 256, 32, 2, 4, 4, 2))
-    assert name.endswith("true>") and grid == 112 * 2 * 512
+    assert name.endswith("true, false, 1>") and grid == 112 * 2 * 512
     assert second == ("splitk_reduce_kernel<2>", 448 * 256)

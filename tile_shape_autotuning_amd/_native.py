@@ -64,7 +64,7 @@ class DeviceDesc(ctypes.Structure):
                                               "waves_max", "blocks_max", "vgpr_max", "acc_max", "r0", "reserved")] + \
                [(n, ctypes.c_double) for n in ("peak_bf16", "peak_f32", "bw", "a_ref", "c_fill", "t0",
                                                "unaligned_eff", "lat_mem", "cu_bw", "lds_bw_cu", "lat_step", "lat_l2",
-                                               "l2_bytes", "w1_eff", "skinny_eff", "hbm_eff")]
+                                               "l2_bytes", "w1_eff", "skinny_eff", "hbm_eff", "sliced_eff")]
 
 
 class TuneRow(ctypes.Structure):

@@ -12,10 +12,12 @@ the held-out tables before and after the fit.
 The model's form stays the analytical one; only calibration constants of the
 MI355X description are fitted (effective LDS and L2-to-CU bandwidth per CU,
 the memory latency a K step waits for from HBM and from L2, the issue
-efficiency of a lone wave on a SIMD, the achievable HBM fraction), by grid
-search: most training tables whose measured best is the model's first
-choice, then most whose best is in the model's top k, then the smallest mean
-squared log error of predicted against measured times.  The model is
+efficiency of a lone wave on a SIMD and of the sliced-K kind, the achievable
+HBM fraction), by grid
+search: fewest training tables whose measured best is outside the model's
+top k (the hybrid tuner measures the top k), then the smallest geometric
+mean of the measured time of the model's first choice over the best, then
+the smallest mean squared log error of predicted against measured times.  The model is
 evaluated by the library (tg_model_times under a device-description
 override), so a fitted set can be written into the built-in description as
 it is.
@@ -25,7 +27,7 @@ one per shape: configuration, model time, measured median).  The split is
 fixed: the five benchmark workloads and the even-numbered calibration shapes
 train, the odd-numbered ones are held out.
 
-    python -m tile_shape_autotuning_amd.calibrate DIR [--topk 16] [--out FILE]
+    python -m tile_shape_autotuning_amd.calibrate DIR [--topk 16] [--out FILE] [--jobs N]
 """
 from __future__ import annotations
 
@@ -48,6 +50,7 @@ GRID = {
     "lat_l2": [0.25e-6, 0.3e-6, 0.4e-6, 0.5e-6],
     "w1_eff": [0.35, 0.4, 0.5, 0.55],
     "hbm_eff": [0.9125],
+    "sliced_eff": [0.4, 0.55, 0.7, 1.0],
 }
 
 
@@ -122,28 +125,50 @@ def _desc(base, vals):
     return d
 
 
-def fit(train, topk=16, grid=None, base=None):
-    """Grid search on the training tables; returns (constants, training score)."""
-    grid = grid or GRID
-    base = base if base is not None else N.builtin_device_desc(0)
-    best = None
+_FIT = {}
+
+
+def _score(cand):
+    """Score of one candidate set on the training tables (smaller is better):
+    fewest tables whose measured best is outside the model's top k (the
+    hybrid tuner measures the top k, so that is what the model has to get
+    right), then the geometric mean of the measured time of the model's first
+    choice over the best, then the mean squared log error."""
+    train, topk, base = _FIT["train"], _FIT["topk"], _FIT["base"]
     try:
-        for vals in itertools.product(*grid.values()):
-            cand = dict(zip(grid, vals))
-            d = _desc(base, cand)
-            stats = [table_stats(t, d, topk) for t in train]
-            key = (-sum(s[4] for s in stats), -sum(s[1] for s in stats), sum(s[0] for s in stats) / len(stats))
-            if best is None or key < best[0]:
-                best = (key, cand)
+        stats = [table_stats(t, _desc(base, cand), topk) for t in train]
     finally:
         N.set_device_override(None)
-    return best[1]
+    return (-sum(s[1] for s in stats), round(sum(math.log(s[2]) for s in stats) / len(stats), 9),
+            sum(s[0] for s in stats) / len(stats))
 
 
-def calibrate(tabs, topk=16, grid=None):
+def fit(train, topk=16, grid=None, base=None, jobs=None):
+    """Grid search on the training tables; returns the best constants (ties:
+    the first in grid order).  jobs > 1 scores the grid in that many forked
+    processes, with the same result."""
+    grid = grid or GRID
+    base = base if base is not None else N.builtin_device_desc(0)
+    cands = [dict(zip(grid, vals)) for vals in itertools.product(*grid.values())]
+    _FIT.update(train=train, topk=topk, base=N.DeviceDesc.from_buffer_copy(base))
+    try:
+        if jobs and jobs > 1 and len(cands) > 1:
+            import multiprocessing as mp
+            with mp.get_context("fork").Pool(jobs) as pool:
+                keys = pool.map(_score, cands, chunksize=max(1, len(cands) // (4 * jobs)))
+        else:
+            keys = [_score(c) for c in cands]
+    finally:
+        _FIT.clear()
+        N.set_device_override(None)
+    i = min(range(len(cands)), key=lambda i: (keys[i], i))
+    return cands[i]
+
+
+def calibrate(tabs, topk=16, grid=None, jobs=None):
     base = N.builtin_device_desc(0)
     train, test = split(tabs)
-    fitted = fit(train, topk, grid, base)
+    fitted = fit(train, topk, grid, base, jobs)
     after = _desc(base, fitted)
     try:
         rep = {"split": {"train": [t["workload"] for t in train], "held_out": [t["workload"] for t in test]},
@@ -162,8 +187,9 @@ def main(argv=None):
     ap.add_argument("dir")
     ap.add_argument("--topk", type=int, default=16)
     ap.add_argument("--out", default="")
+    ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
     a = ap.parse_args(argv)
-    rep = calibrate(load_tables(a.dir), a.topk)
+    rep = calibrate(load_tables(a.dir), a.topk, jobs=a.jobs)
     text = json.dumps(rep, indent=1)
     if a.out:
         with open(a.out, "w") as f:

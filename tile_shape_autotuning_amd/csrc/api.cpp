@@ -198,7 +198,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     p.N = (int)N;
     p.K = (int)K;
     p.kps = (int)k_per_split(c, K);
-    p.split = c.split_k;
+    p.split = (int)cta_splits(c);
     if (c.kind == TG_KIND_SKINNY) {
         p.tiles_m = 1;
         p.tiles_n = (int)((N + 127) / 128);
@@ -225,7 +225,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     }
     // held until both kernels of a split-K call are queued (see ensure_workspace)
     std::unique_lock<std::mutex> ws_hold;
-    if (c.split_k > 1 || fixup) {
+    if (cta_splits(c) > 1 || fixup) {
         const size_t need = workspace_bytes_for(M, N, K, c);
         if (ext) {
             if (need > ext->bytes)
@@ -243,7 +243,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     hipError_t e = launch_fn(*ke, p)(p, (int)blocks, stream);
     if (e != hipSuccess)
         return set_hip_error(e, "kernel launch");
-    if (c.split_k > 1) {
+    if (cta_splits(c) > 1) {
         e = splitk_reduce(p.ws, c.split_k, M, N, bias, C, p.out_bf16, act, stream);
         if (e != hipSuccess)
             return set_hip_error(e, "split-K reduction launch");

@@ -58,21 +58,31 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ST>
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool F32 = false, int WK = 1>
 struct TiledDma {
-    static constexpr int W = WGM * WGN;
+    // WK groups of WGM x WGN waves: group kg multiplies slices kg KKW ..
+    // (kg + 1) KKW - 1 of every stage into its own sums, which are added
+    // through LDS after the K loop (K split among the waves of one workgroup,
+    // so no second launch); every wave takes part in the transfers
+    static constexpr int WO = WGM * WGN;                // waves per K group
+    static constexpr int W = WO * WK;
     static constexpr int T = 64 * W;
     static constexpr int WM = BM / WGM, WN = BN / WGN;
     static constexpr int FM = WM / 16, FN = WN / 16;
-    static constexpr int KK = BK / 32;                  // 32-wide k slices per step
-    static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int ROWB = BK * 2;                 // bytes of one A row in LDS (all KK slices)
+    static constexpr int EB = F32 ? 4 : 2;              // bytes per input element
+    static constexpr int EPS = 16 / EB;                 // elements per 16-byte slot
+    static constexpr int KSL = 64 / EB;                 // k per slice: 64 bytes of an A row
+    static constexpr int KK = BK / KSL;                 // slices per step
+    static constexpr int KKW = KK / WK;                 // slices per step of one wave
+    static constexpr int MPS = F32 ? 4 : 1;             // MFMAs per (A, B) fragment pair
+    static constexpr int A_BYTES = BM * BK * EB;
+    static constexpr int ROWB = BK * EB;                // bytes of one A row in LDS (all KK slices)
     static constexpr int RPA = 1024 / ROWB;             // A rows per transfer (16, 8 or 4)
     static constexpr int LPR = ROWB / 16;               // lanes per A row
     static constexpr int QW = BN < 64 ? BN : 64;        // columns per B block
     static constexpr int U = QW / 16;                   // 16-column units per B row
-    static constexpr int RB = QW * 2;                   // bytes per B block row
-    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int RB = QW * EB;                  // bytes per B block row
+    static constexpr int B_BYTES = BK * BN * EB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int A_INST = A_BYTES / 1024;       // wave-wide 1 KiB transfers
     static constexpr int B_INST = B_BYTES / 1024;
@@ -84,10 +94,16 @@ struct TiledDma {
     // landed (tiles t+2 .. t+ST-1), and after the prologue (tiles 1 .. ST-1)
     static constexpr int WAIT_N = cap63((ST - 2) * LPW_MIN);
     static constexpr int WAIT_P = cap63((ST - 1) * LPW_MIN);
-    static constexpr int PPI = 1024 / RB;               // B rows per transfer (8 or 16)
+    static constexpr int PPI = 1024 / RB;               // B rows per transfer (4, 8 or 16)
     static constexpr int SLOTS_PER_ROW = RB / 16;       // 16-byte slots per B block row
-    static constexpr int NMF = FM * FN;                 // MFMAs per wave per slice
-    static constexpr int NRD = FM + 2 * FN;             // LDS reads per wave per slice
+    static constexpr int NMF = FM * FN;                 // fragment pairs per wave per slice
+    static constexpr int RDB = F32 ? 4 : 2;             // LDS reads per B fragment
+    static constexpr int NRD = FM + RDB * FN;           // LDS reads per wave per slice
+    // fp32 waves with fewer than four output tiles keep KA partial sums per
+    // tile (MFMA e of a slice adds into partial e % KA), so that consecutive
+    // MFMAs never wait for each other's result; the partials are added in a
+    // fixed order after the K loop
+    static constexpr int KA = F32 && NMF < 4 ? 4 / NMF : 1;
     // every wave's transfers split into A and B ones the same way: which
     // operand a transfer loads is then known at compile time
     static constexpr bool STATIC_AB = A_INST % W == 0 && B_INST % W == 0;
@@ -95,24 +111,29 @@ struct TiledDma {
     static constexpr bool EPI_LDS = W * 16 * (WN + 4) * 4 <= ST * STAGE_BYTES;
 
     static_assert(BM % (16 * WGM) == 0 && BN % (16 * WGN) == 0, "whole 16x16 tiles per wave");
-    static_assert(BK % 32 == 0, "BK is a multiple of the MFMA K (32)");
+    static_assert(BK % KSL == 0, "BK is a multiple of the slice (32 bf16 or 16 fp32 k)");
     static_assert(BM % 16 == 0 && BN % 32 == 0, "tile sizes");
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KiB transfers");
     static_assert(ST >= 2 && ST <= 8, "pipeline depth");
+    static_assert(WK >= 1 && KK % WK == 0, "whole slices per K group");
+    static_assert(W <= 16, "at most 1024 threads");
+    // the K groups' sums meet in the stage buffers
+    static_assert(WK == 1 || (WK - 1) * BM * BN * 4 <= ST * STAGE_BYTES, "LDS for the cross-group sums");
 };
 
-// A: rows of 2 BK bytes (all k of the stage, 4 KK chunks of 8 k); chunk c of
-// row r sits at c ^ swz_a<KK>(r).  16 consecutive rows reading one logical
+// A: rows of BK elements (all k of the stage: KK slices of 64 bytes, each
+// four 16-byte chunks of 8 bf16 or 4 fp32 k); chunk c of row r sits at
+// c ^ swz_a<KK>(r).  16 consecutive rows reading one logical
 // chunk land in 16 distinct 16-byte slots of a 256-byte window (no bank
 // conflicts): with 64- and 128-byte rows (BK = 32, 64) two or four rows share
-// a window and the swizzle uses row bits 1..3; a 256-byte row (BK = 128) is a
-// window of its own and the swizzle is the row within its 16-row group.  With
-// BK >= 64 a row is one or two whole 128-byte lines, so every A transfer
-// requests whole lines (half-line requests halve what the L2 delivers per
-// request).
+// a window and the swizzle uses row bits 1..3; a 256-byte row (bf16 BK = 128,
+// fp32 BK = 64) is a window of its own and the swizzle is the row within its
+// 16-row group.  With rows of 128 bytes or more every A transfer requests
+// whole lines (half-line requests halve what the L2 delivers per request).
 template <int KK>
 __device__ __forceinline__ int swz_a(int r)
 {
-    static_assert(KK == 1 || KK == 2 || KK == 4, "BK is 32, 64 or 128");
+    static_assert(KK == 1 || KK == 2 || KK == 4, "rows of 64, 128 or 256 bytes");
     r &= 15;   // a function of the row within its 16-row group (what a fragment read sees)
     return KK == 1 ? (((r >> 1) ^ (r >> 3)) & 3) : KK == 2 ? ((r >> 1) & 7) : r;
 }
@@ -124,7 +145,19 @@ __device__ __forceinline__ int swz_b(int p)
     return RB == 128 ? ((p >> 1) & 3) : ((p >> 2) & 1);
 }
 
-// B block rows are stored in the order the transposed reads consume them:
+// fp32 B: 64-byte unit u (16 columns) of block row r sits at u ^ swz_bf<U>(r).
+// A fragment read takes one float per lane from rows 4g + e of a slice (g =
+// lane group, e = 0..3): with 256-byte rows the four groups then read four
+// different 64-byte windows (row bits 2..3 pick the unit), with 128-byte rows
+// two (a two-way conflict; only 32-column tiles have them).
+template <int U>
+__device__ __forceinline__ int swz_bf(int r)
+{
+    static_assert(U == 2 || U == 4, "32 or 64 columns per B block");
+    return (r >> 2) & (U - 1);
+}
+
+// bf16 B block rows are stored in the order the transposed reads consume them:
 // within each 32-row slice, row 8g + 4h + q (g, h, q = lane group, read half,
 // row in the group of four) goes to position 16h + 4g + q.
 __device__ __forceinline__ int b_pos_to_row(int p)
@@ -201,6 +234,11 @@ __device__ __forceinline__ u32x4_t lds_read_b128(unsigned addr)
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(addr);
 }
 
+__device__ __forceinline__ unsigned lds_read_b32(unsigned addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) unsigned*>(addr);
+}
+
 __device__ __forceinline__ u32x2_t lds_read_tr(unsigned addr)
 {
     const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -210,14 +248,18 @@ __device__ __forceinline__ u32x2_t lds_read_tr(unsigned addr)
 
 // One output tile (tm, tn) over the K range [kbeg, kend): the transfers, the
 // pipelined MFMA loop and the epilogue into `out`.  `lds` is the workgroup's
-// ST * STAGE_BYTES of LDS.  Every lane of the workgroup calls it.
-template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB>
+// ST * STAGE_BYTES of LDS.  Every lane of the workgroup calls it.  F32: fp32
+// operands on v_mfma_f32_16x16x4_f32 (a slice is 16 k: each lane's 16-byte A
+// chunk holds k = 4g .. 4g+3 of its row, and MFMA e of the slice takes
+// element e of it, with the B values of the same four k read one float at a
+// time); otherwise bf16 on v_mfma_f32_16x16x32_bf16.
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB, bool F32 = false, int WK = 1>
 __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int tm, int tn, int kbeg, int kend,
                                          const OutSpec& out)
 {
-    using Cf = TiledDma<BM, BN, BK, WGM, WGN, ST>;
-    constexpr int T = Cf::T, FM = Cf::FM, FN = Cf::FN, W = Cf::W, KK = Cf::KK;
-    constexpr int RB = Cf::RB, U = Cf::U, QW = Cf::QW;
+    using Cf = TiledDma<BM, BN, BK, WGM, WGN, ST, F32, WK>;
+    constexpr int T = Cf::T, FM = Cf::FM, FN = Cf::FN, W = Cf::W, KK = Cf::KK, KKW = Cf::KKW, WO = Cf::WO;
+    constexpr int RB = Cf::RB, U = Cf::U, QW = Cf::QW, EB = Cf::EB, EPS = Cf::EPS;
 
     // an opaque copy of the thread index: where the tile body is used more
     // than once in a kernel, nothing derived from it is shared between the
@@ -229,7 +271,9 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     // that the transfer schedule below is resolved at compile time
     const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int kg = WK == 1 ? 0 : wave / WO;       // K group: slices kg KKW .. of every stage
+    const int wo = WK == 1 ? wave : wave % WO;
+    const int wm = wo / WGN, wn = wo % WGN;
 
     const int M = p.M, N = p.N, K = p.K;
     const int m0 = tm * BM, n0 = tn * BN;
@@ -241,17 +285,19 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     const int cols_left = N - n0;      // valid B columns in this tile
 
     // ---- per-lane parts of the transfers (fixed for the whole K loop)
-    // A transfer: RPA whole rows (2 BK bytes each); lane -> row lane / LPR,
+    // A transfer: RPA whole rows (ROWB bytes each); lane -> row lane / LPR,
     // physical chunk lane % LPR holding logical chunk (lane % LPR) ^ swz_a(row).
     const int a_row = lane / Cf::LPR;
     const int a_p = lane % Cf::LPR;
-    // B transfer: PPI block rows x RB bytes; lane -> block row p_l, 16-byte slot
-    // s16 (unit s16/2 ^ swz_b, half s16%2).
+    // B transfer: PPI block rows x RB bytes; lane -> block row p_l, 16-byte
+    // slot s16.  bf16: unit s16/2 ^ swz_b(p_l), half s16%2, rows permuted
+    // (b_pos_to_row); fp32: unit s16/4 ^ swz_bf(row), quarter s16%4, rows in
+    // order (the swizzle then depends on the transfer's rows, see below).
     const int b_pl = lane / Cf::SLOTS_PER_ROW;
     const int b_s16 = lane % Cf::SLOTS_PER_ROW;
-    const int b_col = (((b_s16 >> 1) ^ swz_b<RB>(b_pl)) * 16) + (b_s16 & 1) * 8;   // column within the block
-    const int b_krow_lane = b_pos_to_row(b_pl);       // row bits coming from the lane
-    const int voB = b_krow_lane * N * 2 + b_col * 2;
+    const int b_col = F32 ? 0 : (((b_s16 >> 1) ^ swz_b<RB>(b_pl)) * 16) + (b_s16 & 1) * 8;   // column within the block
+    const int b_krow_lane = F32 ? b_pl : b_pos_to_row(b_pl);       // row bits coming from the lane
+    const int voB = b_krow_lane * N * EB + b_col * EB;
 
     // Transfer q of this wave is number j = wave + q W of the stage: A
     // transfers first (rows j RPA ..), then B (block blk, row group pblk).  Its
@@ -260,6 +306,7 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     // first k of the lane's A chunk).
     auto is_a = [&](int q) { return Cf::STATIC_AB ? q < Cf::A_INST / W : wave + q * W < Cf::A_INST; };
     auto exists = [&](int q) { return Cf::STATIC_AB || wave + q * W < Cf::INST; };
+    auto krow_of = [&](int pblk) { return F32 ? pblk * Cf::PPI : b_pos_to_row(pblk * Cf::PPI); };
     int vo[Cf::LPW_MAX], ak8[Cf::LPW_MAX];
 #pragma unroll
     for (int q = 0; q < Cf::LPW_MAX; ++q) {
@@ -268,13 +315,18 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
         if (is_a(q)) {
             const int row = j * Cf::RPA + a_row;
             const int c = a_p ^ swz_a<KK>(row);
-            ak8[q] = c * 8;
-            vo[q] = (row < rows_left) ? (row * K + c * 8) * 2 : kOOB;
+            ak8[q] = c * EPS;
+            vo[q] = (row < rows_left) ? (row * K + c * EPS) * EB : kOOB;
         } else {
             const int jb = j - Cf::A_INST;
             const int blk = jb / (BK / Cf::PPI), pblk = jb % (BK / Cf::PPI);
-            const int krow_unif = b_pos_to_row(pblk * Cf::PPI);    // disjoint from the lane's row bits
-            vo[q] = (blk * QW + b_col < cols_left) ? voB + (krow_unif * N + blk * QW) * 2 : kOOB;
+            const int krow_unif = krow_of(pblk);    // disjoint from the lane's row bits
+            if constexpr (F32) {
+                const int col = (((b_s16 >> 2) ^ swz_bf<U>(krow_unif + b_pl)) * 16) + (b_s16 & 3) * 4;
+                vo[q] = (blk * QW + col < cols_left) ? ((krow_unif + b_pl) * N + blk * QW + col) * EB : kOOB;
+            } else {
+                vo[q] = (blk * QW + b_col < cols_left) ? voB + (krow_unif * N + blk * QW) * EB : kOOB;
+            }
         }
     }
 
@@ -294,8 +346,8 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
         d.klim = kend - k0;
         const int64_t a_off = (int64_t)m0 * K + k0;
         const int64_t b_off = (int64_t)k0 * N + n0;
-        d.rA = rsrc_words(Ab + a_off * 2, (a_total - a_off) * 2);
-        d.rB = rsrc_words(Bb + b_off * 2, (b_total - b_off) * 2);
+        d.rA = rsrc_words(Ab + a_off * EB, (a_total - a_off) * EB);
+        d.rB = rsrc_words(Bb + b_off * EB, (b_total - b_off) * EB);
         d.dst = lds_base + (unsigned)(buf * Cf::STAGE_BYTES);
         return d;
     };
@@ -307,74 +359,99 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
             dma16(d.rA, (ak8[q] < d.klim) ? vo[q] : kOOB, d.dst + (unsigned)(j * 1024));
         } else {
             const int jb = j - Cf::A_INST;
-            const int krow_unif = b_pos_to_row((jb % (BK / Cf::PPI)) * Cf::PPI);
+            const int krow_unif = krow_of(jb % (BK / Cf::PPI));
             dma16<NTB>(d.rB, (b_krow_lane < d.klim - krow_unif) ? vo[q] : kOOB,
                   d.dst + (unsigned)(Cf::A_BYTES + jb * 1024));
         }
     };
 
     // ---- per-lane LDS read bases (bytes within a stage)
-    // A fragment (row-tile i, k slice kk): row wm*WM + 16 i + l16, logical
-    // chunk 4 kk + g; the swizzle only sees row bits 1..3, i.e. l16.
-    unsigned rdA[KK];
+    // A fragment (row-tile i, the wave's k slice kk = slice kg KKW + kk of the
+    // stage): row wm*WM + 16 i + l16, logical chunk 4 (kg KKW + kk) + g; the
+    // swizzle only sees row bits 1..3, i.e. l16.
+    unsigned rdA[KKW];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        rdA[kk] = (unsigned)((wm * Cf::WM + l16) * Cf::ROWB + (((kk * 4 + g) ^ swz_a<KK>(l16)) * 16));
-    // B fragment (column tile j, k slice kk, half h): block row 16h + 4g + l16/4
-    // of slice kk, columns 4 (l16 % 4) .. +3 of the 16-column unit.
-    const int b_prow = 4 * g + (l16 >> 2);
+    for (int kk = 0; kk < KKW; ++kk)
+        rdA[kk] = (unsigned)((wm * Cf::WM + l16) * Cf::ROWB + ((((kg * KKW + kk) * 4 + g) ^ swz_a<KK>(l16)) * 16));
+    // B fragment (column tile j, k slice kk).  bf16, read half h: block row
+    // 16h + 4g + l16/4 of slice kk, columns 4 (l16 % 4) .. +3 of the 16-column
+    // unit.  fp32, read e: block row 4g + e of slice kk, column l16 of the
+    // unit (the unit's swizzle sees row bits 2..3, i.e. g only).
+    // (+ the rows of the slices before the wave's first: KSL rows a slice)
+    const int b_prow = (F32 ? 4 * g : 4 * g + (l16 >> 2)) + kg * KKW * Cf::KSL;
     unsigned rdB[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const int J = wn * (Cf::WN / 16) + j;          // 16-column unit index within the tile
         const int blk = J / U, jj = J % U;
-        rdB[j] = (unsigned)(Cf::A_BYTES + blk * BK * RB + b_prow * RB + ((jj ^ swz_b<RB>(b_prow)) * 32) +
-                            (l16 & 3) * 8);
+        if constexpr (F32)
+            rdB[j] = (unsigned)(Cf::A_BYTES + blk * BK * RB + b_prow * RB + ((jj ^ swz_bf<U>(b_prow)) * 64) +
+                                l16 * 4);
+        else
+            rdB[j] = (unsigned)(Cf::A_BYTES + blk * BK * RB + b_prow * RB + ((jj ^ swz_b<RB>(b_prow)) * 32) +
+                                (l16 & 3) * 8);
     }
 
     // Accumulators live in AGPRs from here to the end of the K loop: the
     // empty asm statements pin them there at both ends (left alone, the
     // register allocator splits them between AGPRs and VGPRs and shuffles
     // them on every iteration).
-    f32x4_t acc[FM][FN];
+    constexpr int KA = Cf::KA;
+    f32x4_t acc[KA][FM][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int ka = 0; ka < KA; ++ka)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            __asm__ __volatile__("" : "+a"(acc[i][j]));
-        }
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[ka][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                __asm__ __volatile__("" : "+a"(acc[ka][i][j]));
+            }
 
     // fragment registers of two slices
     u32x4_t a[2][FM], b[2][FN];
     // read o of a slice, in the order its MFMAs first need them: A row-tile 0,
-    // the B halves, then the other A row-tiles
+    // the B parts (bf16 halves, fp32 floats), then the other A row-tiles
     auto read_op = [&](unsigned st, int kk, int par, int o) {
         if (o == 0) {
             a[par][0] = lds_read_b128(st + rdA[kk]);
-        } else if (o <= 2 * FN) {
-            const int j = (o - 1) >> 1, h = (o - 1) & 1;
-            const u32x2_t w = lds_read_tr(st + rdB[j] + (unsigned)((kk * 32 + h * 16) * RB));
-            b[par][j][2 * h] = w.x;
-            b[par][j][2 * h + 1] = w.y;
+        } else if (o <= Cf::RDB * FN) {
+            const int j = (o - 1) / Cf::RDB, h = (o - 1) % Cf::RDB;
+            if constexpr (F32) {
+                b[par][j][h] = lds_read_b32(st + rdB[j] + (unsigned)((kk * 16 + h) * RB));
+            } else {
+                const u32x2_t w = lds_read_tr(st + rdB[j] + (unsigned)((kk * 32 + h * 16) * RB));
+                b[par][j][2 * h] = w.x;
+                b[par][j][2 * h + 1] = w.y;
+            }
         } else {
-            const int i = o - 2 * FN;
+            const int i = o - Cf::RDB * FN;
             a[par][i] = lds_read_b128(st + rdA[kk] + (unsigned)(i * 16 * Cf::ROWB));
         }
     };
     // The MFMAs of one slice with NOPS other instructions spread among them.
-    // Op o goes right after MFMA (o NMF) / NOPS.
+    // Op o goes right after MFMA (o NS) / NOPS.  fp32: MFMA x takes element
+    // x / NMF of its fragments, so consecutive MFMAs add into different
+    // accumulators wherever the wave has more than one.
     auto slice = [&](int par, auto NOPS, auto&& op) {
         constexpr int nops = decltype(NOPS)::value;
+        constexpr int NS = Cf::NMF * Cf::MPS;
 #pragma unroll
-        for (int m = 0; m < Cf::NMF; ++m) {
+        for (int x = 0; x < NS; ++x) {
+            const int m = x % Cf::NMF, e = x / Cf::NMF;
             const int i = m / FN, j = m % FN;
-            acc[i][j] = mfma_bf16(a[par][i], b[par][j], acc[i][j]);
+            // element first, then reinterpret: a bit cast applied to a vector
+            // element lvalue reads element 0 whatever the index
+            if constexpr (F32)
+                acc[e % KA][i][j] = mfma_f32(__uint_as_float((unsigned)a[par][i][e]),
+                                             __uint_as_float((unsigned)b[par][j][e]), acc[e % KA][i][j]);
+            else
+                acc[0][i][j] = mfma_bf16(a[par][i], b[par][j], acc[0][i][j]);
             // the MFMA goes first: a read hoisted above it would make the
             // MFMA's own wait for older fragments wait for this read as well
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int o = (m * nops + Cf::NMF - 1) / Cf::NMF; o < ((m + 1) * nops + Cf::NMF - 1) / Cf::NMF; ++o)
+            for (int o = (x * nops + NS - 1) / NS; o < ((x + 1) * nops + NS - 1) / NS; ++o)
                 op(o);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -385,9 +462,9 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
         constexpr int par0 = decltype(PAR0)::value;
         const unsigned st = lds_base + (unsigned)(buf * Cf::STAGE_BYTES);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < KKW; ++kk) {
             const int par = (par0 + kk) & 1;
-            if (kk + 1 < KK) {
+            if (kk + 1 < KKW) {
                 slice(par, IntC<Cf::NRD>{}, [&](int o) { read_op(st, kk + 1, par ^ 1, o); });
             } else {
                 // all reads of this buffer have returned, tile t+1 has landed
@@ -426,9 +503,9 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     for (int o = 0; o < Cf::NRD; ++o)
         read_op(lds_base, 0, 0, o);
 
-    // ---- main loop; with an odd number of slices per stage the fragment set
-    // of a stage's first slice alternates, so stages go in pairs
-    if constexpr (KK % 2 == 0) {
+    // ---- main loop; with an odd number of slices per stage (of one wave) the
+    // fragment set of a stage's first slice alternates, so stages go in pairs
+    if constexpr (KKW % 2 == 0) {
         int buf = 0;
         for (int t = 0; t < nk; ++t) {
             stage(t, buf, IntC<0>{});
@@ -449,10 +526,44 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     // they must land before LDS is reused or released
     wait_vm_all();
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int ka = 0; ka < KA; ++ka)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            __asm__ __volatile__("" : "+a"(acc[i][j]));
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                __asm__ __volatile__("" : "+a"(acc[ka][i][j]));
+    f32x4_t (&res)[FM][FN] = acc[0];
+#pragma unroll
+    for (int ka = 1; ka < KA; ++ka)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                res[i][j] += acc[ka][i][j];
+    if constexpr (WK > 1) {
+        // the K groups' sums meet in LDS (every transfer has landed, and the
+        // barrier waits for every read): groups 1 .. WK-1 store theirs, group
+        // 0 adds them in group order
+        __syncthreads();
+        f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    part[(((kg - 1) * WO + wo) * Cf::NMF + i * FN + j) * 64 + lane] = res[i][j];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int kq = 1; kq < WK; ++kq)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        res[i][j] += part[(((kq - 1) * WO + wo) * Cf::NMF + i * FN + j) * 64 + lane];
+        }
+    }
 
     // ---- epilogue: bias, activation, convert, store.  The lane coordinates
     // are derived afresh from an opaque copy of the thread index, so that
@@ -463,7 +574,9 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     const int lane_e = tid_e & 63;
     const int l16e = lane_e & 15, ge = lane_e >> 4;
     const int wave_e = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid_e >> 6);
-    const int wme = wave_e / WGN, wne = wave_e % WGN;
+    // with K groups only group 0 (waves 0 .. WO-1) holds the finished sums
+    const bool owner = WK == 1 || wave_e < WO;
+    const int wme = wave_e / WGN % WGM, wne = wave_e % WGN;
     const int row_w = m0 + wme * Cf::WM;          // first output row of the wave tile
     const int col_w = n0 + wne * Cf::WN;          // first output column
 
@@ -480,19 +593,24 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
         float* slab = reinterpret_cast<float*>(lds) + wave_e * 16 * RS;
         const int c8 = lane_e % CPR;                   // the lane's column chunk
         const int col0 = col_w + c8 * 8;
-        const bool col_ok = col0 < N;                  // N is a multiple of 8
+        // N is a multiple of 8 with bf16 operands and of 4 with fp32 ones, so a
+        // chunk is whole or (fp32) its first half is
+        const bool col_ok = col0 < N;
+        const bool hi_ok = col0 + 4 < N;
         float bias8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            bias8[e] = (out.bias && col_ok) ? out.bias[col0 + e] : 0.0f;
+            bias8[e] = (out.bias && (e < 4 ? col_ok : hi_ok)) ? out.bias[col0 + e] : 0.0f;
         __syncthreads();   // every wave's last transfers and reads are done: LDS is free
+        if (!owner)
+            return;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    slab[(ge * 4 + r) * RS + j * 16 + l16e] = acc[i][j][r];
+                    slab[(ge * 4 + r) * RS + j * 16 + l16e] = res[i][j][r];
 #pragma unroll
             for (int ps = 0; ps < PASSES; ++ps) {
                 const int c = ps * 64 + lane_e;
@@ -515,12 +633,15 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
                     } else {
                         f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(out.dst) + idx);
                         dst[0] = f32x4_t{o[0], o[1], o[2], o[3]};
-                        dst[1] = f32x4_t{o[4], o[5], o[6], o[7]};
+                        if (hi_ok)
+                            dst[1] = f32x4_t{o[4], o[5], o[6], o[7]};
                     }
                 }
             }
         }
     } else {
+        if (!owner)
+            return;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = col_w + j * 16 + l16e;
@@ -532,7 +653,7 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
                 for (int r = 0; r < 4; ++r) {
                     const int row = row_w + i * 16 + ge * 4 + r;
                     if (cv && row < M) {
-                        const float v = apply_act(acc[i][j][r] + bj, out.act);
+                        const float v = apply_act(res[i][j][r] + bj, out.act);
                         const int64_t idx = (int64_t)(row - out.row0) * out.ld + (col - out.col0);
                         if (out.bf16)
                             static_cast<unsigned short*>(out.dst)[idx] = f32_to_bf16_rne(v);
@@ -552,16 +673,16 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
 // non-temporal policy.  Measured on the 16 x 28672 x 8192 decode it lifts the
 // weight stream by 3-5 %; where tiles of other rows re-read B through L2 the
 // same policy costs 6-19 %, so it is never used there.
-template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB>
-__global__ void __launch_bounds__(64 * WGM * WGN)
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB, bool F32, int WK>
+__global__ void __launch_bounds__(64 * WGM * WGN * WK)
 gemm_tiled_dma_kernel(GemmParams p)
 {
-    __shared__ u32x4_t lds[ST * TiledDma<BM, BN, BK, WGM, WGN, ST>::STAGE_BYTES / 16];
+    __shared__ u32x4_t lds[ST * TiledDma<BM, BN, BK, WGM, WGN, ST, F32, WK>::STAGE_BYTES / 16];
     int tile, tm, tn, split;
     map_block(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tile, tm, tn, split);
     const int kbeg = split * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
-    dma_tile<BM, BN, BK, WGM, WGN, ST, NTB>(p, lds, tm, tn, kbeg, kend, out_spec(p, split));
+    dma_tile<BM, BN, BK, WGM, WGN, ST, NTB, F32, WK>(p, lds, tm, tn, kbeg, kend, out_spec(p, split));
 }
 
 // Data-parallel tiles plus a stream-K tail (page "Compilers and Kernel

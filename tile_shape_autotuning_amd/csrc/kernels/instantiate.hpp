@@ -7,10 +7,11 @@
 
 namespace tg {
 
-template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB>
+template <int BM, int BN, int BK, int WGM, int WGN, int ST, bool NTB, bool F32, int WK = 1>
 hipError_t launch_tiled_dma(const GemmParams& p, int blocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tiled_dma_kernel<BM, BN, BK, WGM, WGN, ST, NTB>), dim3(blocks), dim3(64 * WGM * WGN),
+    hipLaunchKernelGGL((gemm_tiled_dma_kernel<BM, BN, BK, WGM, WGN, ST, NTB, F32, WK>), dim3(blocks),
+                       dim3(64 * WGM * WGN * WK),
                        0, stream, p);
     return hipGetLastError();
 }

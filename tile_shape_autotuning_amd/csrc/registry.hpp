@@ -17,7 +17,7 @@ struct KernelResources {
 
 struct KernelEntry {
     int in_bf16;        // 1: bf16 operands, 0: fp32 operands
-    tg_cfg cfg;         // split_k is 0 here: it is a run-time value
+    tg_cfg cfg;         // split_k: the compiled K-group count of a sliced-K kernel, else 0 (a run-time value)
     LaunchFn launch;
     int threads;
     KernelResources res;

@@ -51,14 +51,15 @@ tg_device_desc mi355x_desc()
     d.t0 = 4.0e-6;
     d.unaligned_eff = 0.25;
     d.lat_mem = 2.0e-6;
-    d.cu_bw = 60.0e9;
+    d.cu_bw = 50.0e9;
     d.lds_bw_cu = 192.0e9;
     d.lat_step = 1.0e-6;
-    d.lat_l2 = 0.4e-6;
+    d.lat_l2 = 0.3e-6;
     d.l2_bytes = 32.0e6;
-    d.w1_eff = 0.5;
+    d.w1_eff = 0.35;
     d.skinny_eff = 0.75;
     d.hbm_eff = 0.9125;
+    d.sliced_eff = 1.0;
     return d;
 }
 
@@ -90,6 +91,7 @@ tg_device_desc h100_replica_desc()
     d.w1_eff = 1.0;
     d.skinny_eff = 1.0;
     d.hbm_eff = 1.0;
+    d.sliced_eff = 1.0;
     return d;
 }
 
@@ -117,11 +119,16 @@ bool shape_aligned(int64_t N, int64_t K, int dtype)
     return K % vec == 0 && N % vec == 0;
 }
 
-// the bf16 kernels that move panels straight into LDS (tiled and stream-K)
+// the kernels that move panels straight into LDS: the tiled and sliced-K
+// kinds (fp32 and bf16) and stream-K (bf16 only)
 static bool dma_kind(const tg_cfg& c, int dtype)
 {
-    return (c.kind == TG_KIND_TILED || c.kind == TG_KIND_STREAMK) && dtype != TG_F32;
+    return c.kind == TG_KIND_TILED || c.kind == TG_KIND_SLICEDK || (c.kind == TG_KIND_STREAMK && dtype != TG_F32);
 }
+
+int64_t cta_splits(const tg_cfg& c) { return c.kind == TG_KIND_SLICEDK ? 1 : c.split_k; }
+int64_t k_groups(const tg_cfg& c) { return c.kind == TG_KIND_SLICEDK ? c.split_k : 1; }
+int64_t waves_per_block(const tg_cfg& c) { return (int64_t)c.wgm * c.wgn * k_groups(c); }
 
 // ------------------------------------------------------------------ space
 static const int kWaveGrids[6][2] = {{1, 1}, {1, 2}, {2, 1}, {2, 2}, {2, 4}, {4, 2}};
@@ -139,17 +146,19 @@ static std::vector<tg_cfg> build_space(int dtype, int mode)
         return out;
     }
     std::vector<int> ms, ns, bks, sts;
+    // 16-row tiles: a 16-row decode wastes no MFMA rows; the reduction step
+    // spans 64, 128 or 256 bytes of an A row; the direct-to-LDS kernel keeps
+    // 2 to 8 stages in flight
     if (dtype == TG_F32) {
-        ms = {32, 64, 128};
+        ms = {16, 32, 64, 128};
         ns = {32, 64, 128};
-        bks = {8, 16, 32};
-        sts = {1, 2};               // register-staged kernel: 1 or 2 LDS buffers
+        bks = {16, 32, 64};
     } else {
-        ms = {16, 32, 64, 128, 256};   // 16-row tiles: a 16-row decode wastes no MFMA rows
+        ms = {16, 32, 64, 128, 256};
         ns = {32, 64, 128, 256};
         bks = {32, 64, 128};
-        sts = {2, 3, 4, 6, 8};      // direct-to-LDS kernel: stages in flight
     }
+    sts = {2, 3, 4, 6, 8};
     for (int bm : ms)
         for (int bn : ns)
             for (int bk : bks)
@@ -178,6 +187,20 @@ static std::vector<tg_cfg> build_space(int dtype, int mode)
                 for (const auto& w : wg)
                     for (int st : sts)
                         out.push_back(tg_cfg{TG_KIND_STREAMK, bm, bn, 64, w[0], w[1], st, 1});
+    }
+    {
+        // sliced-K: small tiles whose K loop is a chain of short steps; 2 or 4
+        // K groups per workgroup, each at least one slice of every stage
+        const int sms[3] = {16, 32, 64}, sws[3][2] = {{1, 1}, {1, 2}, {2, 2}}, ssts[3] = {2, 3, 4}, sgs[2] = {2, 4};
+        const std::vector<int> sns = dtype == TG_F32 ? std::vector<int>{32, 64} : std::vector<int>{64, 128};
+        const std::vector<int> sbks = dtype == TG_F32 ? std::vector<int>{32, 64} : std::vector<int>{64, 128};
+        for (int bm : sms)
+            for (int bn : sns)
+                for (int bk : sbks)
+                    for (const auto& w : sws)
+                        for (int st : ssts)
+                            for (int g : sgs)
+                                out.push_back(tg_cfg{TG_KIND_SLICEDK, bm, bn, bk, w[0], w[1], st, g});
     }
     return out;
 }
@@ -208,7 +231,8 @@ int64_t lds_bytes(const tg_cfg& c, int dtype)
     const int64_t eb = in_bytes(dtype);
     if (c.kind == TG_KIND_SKINNY)
         return c.wgm > 1 ? (int64_t)c.wgm * c.bm * 128 * 4 : 0;
-    const int64_t pad_b = dtype == TG_F32 ? 4 : 0;
+    // the register-staged fp32 kernel pads B rows by 4 floats
+    const int64_t pad_b = dtype == TG_F32 && !dma_kind(c, dtype) ? 4 : 0;
     return (int64_t)c.stages * ((int64_t)c.bm * c.bk + (int64_t)c.bk * (c.bn + pad_b)) * eb;
 }
 
@@ -248,7 +272,7 @@ int64_t waves_per_simd(const tg_cfg& c, int dtype, const tg_device_desc& d)
 
 int64_t blocks_per_cu(const tg_cfg& c, int dtype, const tg_device_desc& d)
 {
-    const int64_t w = (int64_t)c.wgm * c.wgn;
+    const int64_t w = waves_per_block(c);
     int64_t b = std::min<int64_t>(d.blocks_max, (d.simds * waves_per_simd(c, dtype, d)) / w);
     const int64_t lds = lds_bytes(c, dtype);
     if (lds > 0)
@@ -267,7 +291,7 @@ int64_t resident_blocks(const tg_cfg& c, int dtype, const tg_device_desc& d)
     Alloc a;
     if (d.mode != 0 || !compiled_alloc(dtype, c, &a) || a.vgpr < 0 || a.agpr < 0 || a.lds < 0)
         return blocks_per_cu(c, dtype, d);
-    const int64_t w = (int64_t)c.wgm * c.wgn;
+    const int64_t w = waves_per_block(c);
     int64_t b = std::min<int64_t>(d.blocks_max, (d.simds * waves_per_simd_alloc(a.vgpr, a.agpr, d)) / w);
     if (a.lds > 0)
         b = std::min<int64_t>(b, d.lds_cu / a.lds);
@@ -277,26 +301,30 @@ int64_t resident_blocks(const tg_cfg& c, int dtype, const tg_device_desc& d)
 int64_t transfers_per_wave(const tg_cfg& c, int dtype)
 {
     const int64_t inst = ((int64_t)c.bm + c.bn) * c.bk * in_bytes(dtype) / 1024;
-    return cdiv(inst, (int64_t)c.wgm * c.wgn);
+    return cdiv(inst, waves_per_block(c));
 }
 
 int64_t k_per_split(const tg_cfg& c, int64_t K)
 {
     const int64_t unit = c.kind == TG_KIND_SKINNY ? 32 : c.bk;
-    return cdiv(cdiv(K, c.split_k), unit) * unit;
+    return cdiv(cdiv(K, cta_splits(c)), unit) * unit;
 }
 
 int check_static(int dtype, const tg_cfg& c, const tg_device_desc& d)
 {
-    const int64_t w = (int64_t)c.wgm * c.wgn;
+    const int64_t w = waves_per_block(c);
     if (64 * w > d.max_threads)
         return R_WAVES;
     if (c.kind != TG_KIND_SKINNY) {
-        const int kstep = dtype == TG_F32 ? 16 : 32;
+        // each K group takes whole MFMA slices of every stage
+        const int64_t kstep = (dtype == TG_F32 ? 16 : 32) * k_groups(c);
         if (c.bm % (16 * c.wgm) || c.bn % (16 * c.wgn) || c.bk % kstep)
             return R_DIV;
     }
     if (lds_bytes(c, dtype) > d.lds_block)
+        return R_LDS;
+    // the sliced-K kind's groups add their sums through the stage buffers
+    if (k_groups(c) > 1 && (k_groups(c) - 1) * c.bm * c.bn * 4 > lds_bytes(c, dtype))
         return R_LDS;
     // the direct-to-LDS kernel keeps ST stages of transfers in flight after its
     // prologue; a wave's memory counter tracks at most 63 (MI355X only)
@@ -347,7 +375,7 @@ int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_
     // without a partial last round the stream-K kind is the data-parallel one
     if (c.kind == TG_KIND_STREAMK && streamk_plan(M, N, K, c, d).tail == 0)
         return R_SHAPE;
-    if (c.split_k > 1) {
+    if (cta_splits(c) > 1) {
         if (K == 0 || cdiv(K, k_per_split(c, K)) != c.split_k)
             return R_SPLIT;
     }
@@ -372,7 +400,7 @@ void grid(int64_t M, int64_t N, int64_t K, const tg_cfg& c, int64_t* tiles, int6
         *blocks = streamk_plan(M, N, K, c, d ? *d : mi355x_desc()).blocks;
         return;
     }
-    *blocks = t * c.split_k;
+    *blocks = t * cta_splits(c);
 }
 
 int64_t sk_owner_host(int64_t x, int64_t I, int64_t G) { return ((x + 1) * G - 1) / I; }
@@ -425,7 +453,7 @@ static double model_page(int64_t K, int dtype, const tg_cfg& c, const tg_device_
     const double t_c = flops / (peak * eff);
     const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
     const double g = std::sqrt((double)std::min<int64_t>(units, (int64_t)d.n_cu * bcu));
-    const double ws = c.split_k > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
+    const double ws = cta_splits(c) > 1 ? 8.0 * (double)tiles * (double)c.bm * (double)c.bn * (double)c.split_k : 0.0;
     const double t_m = (std::max(compulsory, raw / g) + ws) / d.bw;
     return std::max(t_c, t_m) + d.t0;
 }
@@ -434,14 +462,14 @@ static double model_page(int64_t K, int dtype, const tg_cfg& c, const tg_device_
 // different shape"): the fp32 partial-sum slabs, one M x N slab per split ...
 static double splitk_slabs(int64_t M, int64_t N, const tg_cfg& c)
 {
-    return c.split_k > 1 ? 4.0 * (double)c.split_k * (double)M * (double)N : 0.0;
+    return cta_splits(c) > 1 ? 4.0 * (double)c.split_k * (double)M * (double)N : 0.0;
 }
 
 // ... and the second pass: one more launch reading every slab once and
 // writing C at the HBM rate.
 static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, const tg_device_desc& d)
 {
-    if (c.split_k <= 1)
+    if (cta_splits(c) <= 1)
         return 0.0;
     return (splitk_slabs(M, N, c) + (double)ec * (double)M * (double)N) / (d.bw * d.hbm_eff) + d.t0;
 }
@@ -466,7 +494,10 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
     const int64_t wm = c.bm / c.wgm, wn = c.bn / c.wgn;
     const double simd_peak = peak / (double)((int64_t)d.n_cu * d.simds);
     const double f_step = 2.0 * (double)c.bm * (double)c.bn * (double)c.bk;
-    const double lds_step = (double)(c.bk * eb * (w * (wm + wn) + c.bm + c.bn));
+    // fragment reads (each K group reads only its own slices, so the reads of a
+    // step are those of one group's wgm x wgn waves) plus the transfers' writes
+    const int64_t wo = (int64_t)c.wgm * c.wgn;
+    const double lds_step = (double)(c.bk * eb * (wo * (wm + wn) + c.bm + c.bn));
     const int64_t qw = dma_kind(c, dtype) ? std::min<int64_t>(c.bn, 64) : c.bn;
     double l2_step = (double)(c.bm * line_bytes(c.bk * eb) + c.bk * (c.bn / qw) * line_bytes(qw * eb));
     if (c.kind == TG_KIND_UNALIGNED)
@@ -480,6 +511,8 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
         issue = std::max(issue, (double)res * lds_step / d.lds_bw_cu);
         if (res * w <= d.simds)
             issue = issue / d.w1_eff;
+        if (c.kind == TG_KIND_SLICEDK)
+            issue = issue / d.sliced_eff;
         double t = std::max(issue, (double)res * l2_step / d.cu_bw);
         return std::max(t, lat / (double)depth);
     };
@@ -510,12 +543,17 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
         t_cu = t_cu + (double)ktiles * step(cdiv(rem, (int64_t)d.n_cu));
     const int64_t rounds = full + (rem > 0 ? 1 : 0);
     t_cu = t_cu + (double)rounds * lat;
+    // sliced-K: after its K loop a tile's groups 1 .. g-1 write their sums to
+    // LDS and group 0 reads them back
+    const double red = k_groups(c) > 1 ? 8.0 * (double)(k_groups(c) - 1) * (double)c.bm * (double)c.bn / d.lds_bw_cu
+                                       : 0.0;
+    t_cu = t_cu + (double)(full * bcu + (rem > 0 ? cdiv(rem, (int64_t)d.n_cu) : 0)) * red;
     const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
     const double g = std::sqrt((double)std::min<int64_t>(units, slots));
     const double t_hbm = (std::max(compulsory, raw / g) + splitk_slabs(M, N, c)) / (d.bw * d.hbm_eff);
     // every block stores its outputs (C, or its split-K slab) after its K
     // loop: those stores do not overlap the loop
-    const double stores = c.split_k > 1 ? splitk_slabs(M, N, c) : (double)ec * (double)M * (double)N;
+    const double stores = cta_splits(c) > 1 ? splitk_slabs(M, N, c) : (double)ec * (double)M * (double)N;
     t_cu = t_cu + stores / (d.bw * d.hbm_eff);
     return std::max(t_cu, t_hbm) + splitk_pass(M, N, ec, c, d) + d.t0;
 }
@@ -529,7 +567,7 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     const double compulsory = (double)(eb * (M * K + K * N) + ec * M * N);
     int64_t tiles, units;
     grid(M, N, K, c, &tiles, &units, &d);
-    const int64_t w = (int64_t)c.wgm * c.wgn;
+    const int64_t w = waves_per_block(c);
     const int64_t bcu = resident_blocks(c, dtype, d);
 
     if (c.kind == TG_KIND_SKINNY) {

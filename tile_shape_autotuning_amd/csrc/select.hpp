@@ -29,6 +29,13 @@ bool shape_aligned(int64_t N, int64_t K, int dtype);
 const std::vector<tg_cfg>& space(int dtype, const tg_device_desc& d);
 bool in_space(int dtype, const tg_device_desc& d, const tg_cfg& c);
 
+// Workgroups that share one tile's K range (split_k, except for the sliced-K
+// kind, whose split_k groups live inside one workgroup), the K groups inside
+// a workgroup (split_k for the sliced-K kind, else 1), and waves per workgroup.
+int64_t cta_splits(const tg_cfg& c);
+int64_t k_groups(const tg_cfg& c);
+int64_t waves_per_block(const tg_cfg& c);
+
 int64_t lds_bytes(const tg_cfg& c, int dtype);
 int64_t acc_regs(const tg_cfg& c);
 int64_t vgpr_estimate(const tg_cfg& c, int dtype, const tg_device_desc& d);

@@ -202,7 +202,7 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, int act, bool has_bias,
         // only candidates with a compiled kernel can be measured (kernels the
         // compiler had to spill are already out: the filter's spill rule)
         const int max_split = env_int("TILEGEMM_TUNE_MAX_SPLIT", 1 << 30);
-        auto runnable = [&](const tg_cfg& c) { return find_kernel(dtype, c) != nullptr && c.split_k <= max_split; };
+        auto runnable = [&](const tg_cfg& c) { return find_kernel(dtype, c) != nullptr && cta_splits(c) <= max_split; };
         std::vector<Timed> cands;
         const size_t take = mode == "exhaustive" ? ranked.size() : (size_t)topk;
         std::vector<char> picked(ranked.size(), 0);

@@ -37,7 +37,7 @@ size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, const tg_cfg& c)
             return 0;
         return (size_t)sp.tail * (size_t)sp.smax * (size_t)c.bm * (size_t)c.bn * sizeof(float);
     }
-    if (c.split_k <= 1)
+    if (cta_splits(c) <= 1)
         return 0;
     return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
 }

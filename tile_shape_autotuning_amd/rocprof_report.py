@@ -195,9 +195,11 @@ def kernel_name(cfg, in_bf16=True, stream_b=False):
     """The template name rocprofv3 prints for a configuration's kernel
     (stream_b: the instantiation that reads B with the non-temporal policy,
     which launches with a single row of tiles use)."""
-    kind, bm, bn, bk, wgm, wgn, st, _ = cfg
-    if kind == 0 and in_bf16:
-        return f"gemm_tiled_dma_kernel<{bm}, {bn}, {bk}, {wgm}, {wgn}, {st}, {'true' if stream_b else 'false'}>"
+    kind, bm, bn, bk, wgm, wgn, st, split = cfg
+    if kind in (0, 4):
+        # the sliced-K kind is the same kernel with its K groups compiled in
+        return (f"gemm_tiled_dma_kernel<{bm}, {bn}, {bk}, {wgm}, {wgn}, {st}, {'true' if stream_b else 'false'}, "
+                f"{'false' if in_bf16 else 'true'}, {split if kind == 4 else 1}>")
     if kind == 1:
         return f"gemm_skinny_kernel<{bm // 16}, {wgm}, {st}>"
     return f"gemm_tiled_kernel<{'true' if in_bf16 else 'false'}, {bm}, {bn}, {bk}, {wgm}, {wgn}, {st}"
@@ -272,6 +274,9 @@ def workload_launch(index, cfg):
     else:
         threads = 64 * wgm * wgn
     name = kernel_name(cfg, in_bf16, stream_b)
+    if kind == 4:
+        # sliced-K: split groups of waves inside each tile's one workgroup
+        return name, tiles * threads * split, None
     second = None
     if split > 1:
         blocks = min(-(-w.M * w.N // 1024), 65536)
