@@ -35,6 +35,7 @@ exactly --steps timed ones.
                                   # RMS normalisation (16384 x 8192 bf16) against
                                   # the HBM roofline, reported under "rmsnorm"
                   [--rmsnorm]     # report it also with --only
+                  [--order]       # also: the headline at six tile scheduling orders
 
 The per-shape configurations come from the persisted tuning cache when it is
 present (the exhaustive measured autotune of every workload on MI355X, in the
@@ -546,7 +547,9 @@ def main():
                     help="report the occupancy-tuned RMS normalisation also with --only")
     ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMS normalisation report")
     ap.add_argument("--streamk", action="store_true", help="report the stream-K study also with --only")
-    ap.add_argument("--no-order", action="store_true", help="skip the tile-order study of the headline workload")
+    ap.add_argument("--order", action="store_true",
+                    help="also time the headline call at six tile scheduling orders (tile_order_study); off by "
+                         "default, so that a kernel trace of the default run holds the headline's own launches only")
     ap.add_argument("--no-streamk", action="store_true",
                     help="skip the stream-K study (4352 x 4352 x 8192: data-parallel against stream-K tail)")
     ap.add_argument("--cfg", type=str, default="",
@@ -683,7 +686,7 @@ def main():
         line["rmsnorm"] = rmsnorm_report(torch, 50)
     if (a.streamk or not a.only) and not a.no_streamk:
         line["streamk_study"] = streamk_study(torch)
-    if not a.only and not a.no_order and forced is None:
+    if a.order and forced is None:
         line["tile_order_study"] = tile_order_study(p, torch)
     if not a.no_cpu:
         log("cpu baseline (oracle) ...")
