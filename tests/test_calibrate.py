@@ -98,12 +98,10 @@ def test_committed_report_matches_the_committed_tables_and_built_in_constants():
     for k in ("model_hits", "best_in_topk", "geomean_choice_over_best", "mean_rank_corr", "msle"):
         assert got[k] == rep["held_out_after"][k], k
     # the constants before the fit are a point of the grid, so the fit is at
-    # least as good on the training tables by its own objective; on the
-    # held-out tables the committed fit's first choice costs less than before
+    # least as good on the training tables by its own objective (the held-out
+    # tables may go either way: that is what the report is for)
     tb, ta = rep["train_before"], rep["train_after"]
     assert (-ta["best_in_topk"], ta["geomean_choice_over_best"]) <= (-tb["best_in_topk"], tb["geomean_choice_over_best"])
-    assert rep["held_out_after"]["geomean_choice_over_best"] < rep["held_out_before"]["geomean_choice_over_best"]
-    assert rep["held_out_after"]["best_in_topk"] >= rep["held_out_before"]["best_in_topk"]
 
 
 def test_parallel_grid_search_gives_the_serial_result():

@@ -190,9 +190,16 @@ def test_empty_and_k_zero():
         A, B, bias = _int_inputs(37, 24, 0, dtype, 6)
         A_d = torch.zeros((37, 0), device="cuda", dtype=torch.float32 if dtype == wl.F32 else torch.bfloat16)
         B_d = torch.zeros((0, 24), device="cuda", dtype=A_d.dtype)
+        want = np.maximum(np.broadcast_to(bias.astype(np.float64), (37, 24)), 0.0)
         C = _run(A_d, B_d, to_dev(bias), "relu", dtype)
         torch.cuda.synchronize()
-        _exact_check(C, np.maximum(np.broadcast_to(bias.astype(np.float64), (37, 24)), 0.0), dtype, "K=0")
+        _exact_check(C, want, dtype, "K=0")
+        # the sliced-K kind with no K step: every group's sums are zero
+        sliced = (4, 16, 32, 64, 1, 1, 2, 4) if dtype == wl.F32 else (4, 16, 64, 128, 1, 1, 2, 4)
+        assert tg.has_kernel(dtype, sliced), sliced
+        C = _run(A_d, B_d, to_dev(bias), "relu", dtype, sliced)
+        torch.cuda.synchronize()
+        _exact_check(C, want, dtype, "K=0 sliced-K")
         mark(f"M=0 dt{dtype}")
         C = _run(torch.zeros((0, 8), device="cuda", dtype=A_d.dtype),
                  torch.zeros((8, 16), device="cuda", dtype=A_d.dtype), None, "none", dtype)

@@ -595,3 +595,28 @@ def test_sliced_k_in_the_per_cu_model():
     lds_steps = 16 * (64 * 4 * (1 * (32 + 32) + 32 + 32)) / 1e12   # fragment reads of one group + transfer writes
     t4l = S.model_time(M, Nn, K, S.F32, four, dl) - d.t0
     assert t4l == pytest.approx(max(16 * step_flops / (4 * simd), lds_steps) + red)
+
+
+def test_transfers_past_the_k_range_are_priced():
+    # everything but the L2-to-CU rate made negligible: a K step costs its
+    # L2-to-CU bytes, and a direct-to-LDS block also pays for the ST stages of
+    # zero-filling transfers it issues past its K range
+    d = dataclasses.replace(S.MI355X, peak_bf16=1e30, lds_bw_cu=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0,
+                            bw=1e30, t0=0.0)
+    two = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 2, 1)
+    four = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 2, 4, 1)
+    # 64 tiles: one block on each of 64 CUs; a step is 128 A rows and two
+    # 64-column B blocks of 64 rows, each row one 128-byte line
+    l2_step = 128 * 128 + 64 * 2 * 128
+    M, Nn, K = 1024, 1024, 256
+    for c in (two, four):
+        assert S.check(M, Nn, K, S.BF16, c, d) == S.OK
+        t = S.model_time(M, Nn, K, S.BF16, c, d)
+        assert t == pytest.approx((K // 64 + c.stages) * l2_step / d.cu_bw)
+    # the register-staged kernel of the unaligned kind issues none: eight
+    # 32-k steps of 128 A rows (one line each) and 32 B rows of 256 bytes, at
+    # the element-load efficiency
+    u = S.Cfg(S.KIND_UNALIGNED, 128, 128, 32, 2, 2, 2, 1)
+    assert S.check(M, Nn - 4, K - 4, S.BF16, u, d) == S.OK
+    u_step = (128 * 128 + 32 * 256) / d.unaligned_eff
+    assert S.model_time(M, Nn - 4, K - 4, S.BF16, u, d) == pytest.approx(8 * u_step / d.cu_bw)

@@ -53,7 +53,7 @@ tg_device_desc mi355x_desc()
     d.lat_mem = 2.0e-6;
     d.cu_bw = 50.0e9;
     d.lds_bw_cu = 192.0e9;
-    d.lat_step = 1.0e-6;
+    d.lat_step = 1.25e-6;
     d.lat_l2 = 0.3e-6;
     d.l2_bytes = 32.0e6;
     d.w1_eff = 0.35;
@@ -543,11 +543,19 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
         t_cu = t_cu + (double)ktiles * step(cdiv(rem, (int64_t)d.n_cu));
     const int64_t rounds = full + (rem > 0 ? 1 : 0);
     t_cu = t_cu + (double)rounds * lat;
+    // blocks a CU runs over all rounds
+    const int64_t per_cu = full * bcu + (rem > 0 ? cdiv(rem, (int64_t)d.n_cu) : 0);
+    // the direct-to-LDS kernels keep every stage the same: each block also
+    // issues the transfers of the ST tiles past the end of its K range, which
+    // the range check turns into zeros -- address-unit time at the L2-to-CU
+    // rate, no traffic (they matter where the K loop is short)
+    if (dma_kind(c, dtype))
+        t_cu = t_cu + (double)per_cu * (double)c.stages * l2_step / d.cu_bw;
     // sliced-K: after its K loop a tile's groups 1 .. g-1 write their sums to
     // LDS and group 0 reads them back
     const double red = k_groups(c) > 1 ? 8.0 * (double)(k_groups(c) - 1) * (double)c.bm * (double)c.bn / d.lds_bw_cu
                                        : 0.0;
-    t_cu = t_cu + (double)(full * bcu + (rem > 0 ? cdiv(rem, (int64_t)d.n_cu) : 0)) * red;
+    t_cu = t_cu + (double)per_cu * red;
     const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
     const double g = std::sqrt((double)std::min<int64_t>(units, slots));
     const double t_hbm = (std::max(compulsory, raw / g) + splitk_slabs(M, N, c)) / (d.bw * d.hbm_eff);
