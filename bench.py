@@ -486,6 +486,34 @@ def streamk_study(torch):
     return out
 
 
+def sliced_k_study(p, torch):
+    """The sliced-K kind where it pays: the fp32 workload's tuned call (K
+    split among the wave groups of each workgroup) against the best
+    configuration without K groups in the committed exhaustive table of the
+    same shape, both timed here, interleaved, with the same warm-up."""
+    import gzip
+    path = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "tables", f"table_{p.w.name}.json.gz")
+    if not os.path.exists(path):
+        return None
+    with gzip.open(path, "rt") as f:
+        rows = [r for r in json.load(f)["rows"] if r[2] is not None and r[2] > 0 and r[0][0] != 4]
+    plain = tuple(min(rows, key=lambda r: r[2])[0])
+    tuned = tuple(p.tuned()[0].astuple())
+    res = {}
+    for rnd in range(3):
+        for name, cfg in (("tuned", tuned), ("without_k_groups", plain)):
+            step = p.bind(cfg)
+            warm_up(step, 10, torch, 0.05)
+            sec, _ = time_steps(step, 2000, torch)
+            res[name] = min(res.get(name, 1e9), sec)
+    out = {"workload": p.w.name, "tuned": {"cfg": list(tuned), "us": round(res["tuned"] * 1e6, 3)},
+           "without_k_groups": {"cfg": list(plain), "us": round(res["without_k_groups"] * 1e6, 3),
+                                "picked_from": os.path.relpath(path, ROOT)},
+           "without_over_tuned": round(res["without_k_groups"] / res["tuned"], 3)}
+    log(f"sliced-K study: {out}")
+    return out
+
+
 def rmsnorm_report(torch, steps, rows=16384, n=8192):
     """The second workload: RMS normalisation of rows x n bf16 with
     occupancy-only tuning.  Time per call at each occupancy and with the
@@ -686,6 +714,8 @@ def main():
         line["rmsnorm"] = rmsnorm_report(torch, 50)
     if (a.streamk or not a.only) and not a.no_streamk:
         line["streamk_study"] = streamk_study(torch)
+    if 1 in prepared and not a.only and forced is None:
+        line["sliced_k_study"] = sliced_k_study(prepared[1], torch)
     if a.order and forced is None:
         line["tile_order_study"] = tile_order_study(p, torch)
     if not a.no_cpu:
