@@ -1,4 +1,7 @@
-// Block-tiled GEMM with a fused bias + activation epilogue:
+// Block-tiled GEMM with a fused bias + activation epilogue, loading every
+// element on its own: the kernel of the unaligned kind, for pointers or
+// shapes (N, K) that are not 16-byte aligned (aligned shapes run the
+// direct-to-LDS kernel of gemm_tiled_dma.hpp).
 //     C = act(A . B + bias),  A [M][K], B [K][N], C [M][N] row-major.
 //
 // The decomposition is the one the page "Tile Selection: Cost Models Against
@@ -15,9 +18,8 @@
 // slabs in split order and runs the epilogue (deterministic results).
 //
 // gfx950 specifics:
-//   * global loads are 16-byte buffer loads (out-of-range lanes read zero, so
-//     M, N and K edges need no branches); with VEC = false every element is
-//     loaded on its own, for shapes whose rows are not 16-byte aligned;
+//   * global loads are 2- or 4-byte buffer loads, one per element
+//     (out-of-range lanes read zero, so M, N and K edges need no branches);
 //   * bf16: A is kept K-contiguous in LDS; B is transposed in registers (8x8
 //     blocks of 16-bit values) on its way to LDS so that both MFMA operands
 //     are read with one ds_read_b128 each; 16-byte chunks are XOR-swizzled;
@@ -32,7 +34,7 @@
 
 namespace tg {
 
-template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST, bool VEC>
+template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST>
 struct Tiled {
     static constexpr int W = WGM * WGN;
     static constexpr int T = 64 * W;
@@ -58,12 +60,12 @@ struct Tiled {
     static_assert(W <= 16, "at most 1024 threads");
 };
 
-template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST, bool VEC>
+template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_tiled_kernel(GemmParams p)
 {
-    using Cf = Tiled<BF, BM, BN, BK, WGM, WGN, ST, VEC>;
-    constexpr int T = Cf::T, CPR = Cf::CPR, EB = Cf::EB, EPC = Cf::EPC;
+    using Cf = Tiled<BF, BM, BN, BK, WGM, WGN, ST>;
+    constexpr int T = Cf::T, CPR = Cf::CPR, EB = Cf::EB;
     constexpr int FM = Cf::FM, FN = Cf::FN;
     __shared__ u32x4_t lds[ST * Cf::STAGE_SLOTS];
 
@@ -98,10 +100,7 @@ gemm_tiled_kernel(GemmParams p)
             if (Cf::A_CH % T == 0 || q < Cf::A_CH) {
                 const int row = q / CPR, c = q % CPR;
                 const bool rv = m0 + row < M;
-                if constexpr (VEC) {
-                    const bool v = rv && (k0 + c * EPC < kend);
-                    ra[i] = load16(rA, v ? row * K * EB + c * 16 : kOOB);
-                } else if constexpr (BF) {
+                if constexpr (BF) {
                     unsigned h[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -132,33 +131,23 @@ gemm_tiled_kernel(GemmParams p)
                     for (int r = 0; r < 8; ++r) {
                         const int krow = kb * 8 + r;
                         const bool kv = k0 + krow < kend;
-                        if constexpr (VEC) {
-                            const bool v = kv && (n0 + nb * 8 < N);
-                            rb[i][r] = load16(rB, v ? krow * N * 2 + nb * 16 : kOOB);
-                        } else {
-                            unsigned h[8];
+                        unsigned h[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const bool v = kv && (n0 + nb * 8 + e < N);
-                                h[e] = load2(rB, v ? (krow * N + nb * 8 + e) * 2 : kOOB);
-                            }
-#pragma unroll
-                            for (int d = 0; d < 4; ++d)
-                                rb[i][r][d] = h[2 * d] | (h[2 * d + 1] << 16);
+                        for (int e = 0; e < 8; ++e) {
+                            const bool v = kv && (n0 + nb * 8 + e < N);
+                            h[e] = load2(rB, v ? (krow * N + nb * 8 + e) * 2 : kOOB);
                         }
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+                            rb[i][r][d] = h[2 * d] | (h[2 * d + 1] << 16);
                     }
                 } else {
                     const int cc = u % (BN / 4), krow = u / (BN / 4);
                     const bool kv = k0 + krow < kend;
-                    if constexpr (VEC) {
-                        const bool v = kv && (n0 + cc * 4 < N);
-                        rb[i][0] = load16(rB, v ? krow * N * 4 + cc * 16 : kOOB);
-                    } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const bool v = kv && (n0 + cc * 4 + e < N);
-                            rb[i][0][e] = load4(rB, v ? (krow * N + cc * 4 + e) * 4 : kOOB);
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        const bool v = kv && (n0 + cc * 4 + e < N);
+                        rb[i][0][e] = load4(rB, v ? (krow * N + cc * 4 + e) * 4 : kOOB);
                     }
                 }
             }

@@ -1,5 +1,6 @@
-// Block-tiled bf16 GEMM with an asynchronous multi-stage LDS pipeline:
-//     C = act(A . B + bias),  A [M][K], B [K][N] row-major, bf16 in, fp32 accumulate.
+// Block-tiled GEMM with an asynchronous multi-stage LDS pipeline:
+//     C = act(A . B + bias),  A [M][K], B [K][N] row-major, bf16 or fp32 in,
+//     fp32 accumulate.
 //
 // Same decomposition as gemm_tiled.hpp (page "Tile Selection: Cost Models
 // Against Measurement", "The structure of the search space": BM x BN block
@@ -10,7 +11,8 @@
 // and a latency-bound tile wants more than two stages; on MI355X one K step
 // of even a 256 x 256 tile is shorter than the memory latency under load).
 //
-// Schedule.  A stage (one BK step) is KK = BK/32 slices of 32 k; a wave's
+// Schedule.  A stage (one BK step) is KK slices of 64 bytes of an A row (32
+// bf16 or 16 fp32 k); with K groups (WK > 1) a wave takes KK/WK of them.  A wave's
 // fragment registers are double buffered per slice, and while the matrix
 // core works through the FM x FN MFMAs of slice s the wave reads slice s+1's
 // fragments and, in the last slice of a stage, issues the transfers of the
@@ -33,19 +35,22 @@
 //     plain s_barrier: no fence, so loads of later stages stay in flight (the
 //     loads are issued as inline assembly so that the compiler does not add
 //     its own full drain before the LDS reads);
-//   * A sits in LDS as whole rows [BM][2 BK bytes], K-contiguous (a transfer
-//     carries 16, 8 or 4 complete rows, so BK >= 64 requests whole 128-byte
-//     lines),
-//     and is read with ds_read_b128 (8 k values of one row per lane = the A
-//     operand of v_mfma_f32_16x16x32_bf16);
-//   * B stays N-contiguous in 64-column blocks [BN/64][BK][128 B] whose rows
-//     are permuted so that a ds_read_b64_tr_b16 (within each 16-lane group,
-//     lane L names 4 consecutive columns of row base + L/4 and lane i receives
-//     column i of those four rows) touches 16 consecutive LDS rows; two such
-//     reads give the 8 k values of one column that the B operand wants;
+//   * A sits in LDS as whole rows [BM][BK elements], K-contiguous (a transfer
+//     carries 16, 8 or 4 complete rows, so rows of 128 bytes or more request
+//     whole lines), and is read with ds_read_b128 (8 bf16 k of one row per
+//     lane = the A operand of v_mfma_f32_16x16x32_bf16; 4 fp32 k, one per
+//     v_mfma_f32_16x16x4_f32 of the slice);
+//   * bf16 B stays N-contiguous in 64-column blocks [BN/64][BK][128 B] whose
+//     rows are permuted so that a ds_read_b64_tr_b16 (within each 16-lane
+//     group, lane L names 4 consecutive columns of row base + L/4 and lane i
+//     receives column i of those four rows) touches 16 consecutive LDS rows;
+//     two such reads give the 8 k values of one column that the B operand
+//     wants; fp32 B sits in 64-column blocks of 256-byte rows (32 columns of
+//     128 bytes for 32-wide tiles) in K order and
+//     is read one float per lane and MFMA;
 //   * 16-byte chunks are XOR-swizzled by row bits 1..3, which for fragment
 //     reads come from the lane index only: every fragment read is a per-lane
-//     base register (one per 32-k slice) plus an immediate offset, and the
+//     base register (one per slice) plus an immediate offset, and the
 //     reads of a half-wave hit 64 distinct banks; every transfer is a per-lane
 //     offset register fixed for the whole K loop.
 #pragma once

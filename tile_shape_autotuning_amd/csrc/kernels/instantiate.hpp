@@ -24,10 +24,10 @@ hipError_t launch_streamk(const GemmParams& p, int blocks, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST, bool VEC>
+template <bool BF, int BM, int BN, int BK, int WGM, int WGN, int ST>
 hipError_t launch_tiled(const GemmParams& p, int blocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BF, BM, BN, BK, WGM, WGN, ST, VEC>), dim3(blocks),
+    hipLaunchKernelGGL((gemm_tiled_kernel<BF, BM, BN, BK, WGM, WGN, ST>), dim3(blocks),
                        dim3(64 * WGM * WGN), 0, stream, p);
     return hipGetLastError();
 }
