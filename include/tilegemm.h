@@ -153,7 +153,9 @@ int tg_set_stream(void *hip_stream);
  * Errors: TG_E_INVAL (NULL pointer with a non-empty operand, bad code,
  * negative size, misaligned pointer for the chosen kind), TG_E_INFEASIBLE
  * (cfg fails the filter: nothing is launched), TG_E_HIP, TG_E_NOMEM.
- * Split-K configurations run two kernels on the stream: the GEMM writes one
+ * Split-K configurations (split_k > 1, except the sliced-K kind, whose
+ * groups add their sums inside the workgroup) run two kernels on the
+ * stream: the GEMM writes one
  * fp32 slab of partial sums per split (split_k x M x N floats) to a
  * library-owned workspace, then a second kernel adds the slabs in split order
  * and applies bias, activation and conversion.  There is one workspace per
@@ -289,9 +291,10 @@ int tg_model_times(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg *cfg
 int tg_model_choice(int64_t M, int64_t N, int64_t K, int dtype, tg_cfg *out, double *us);
 /* Launch geometry (page "Tile Selection: Cost Models Against Measurement",
  * "The structure of the search space": ceil(M/bm) * ceil(N/bn) blocks): output
- * tiles and launched workgroups (tiles * split_k; for the stream-K kind the
- * data-parallel tiles plus min(CUs x resident workgroups, tail tiles x K
- * steps) workgroups for the tail, on the device description in force).
+ * tiles and launched workgroups (tiles * split_k; tiles for the sliced-K
+ * kind; for the stream-K kind the data-parallel tiles plus min(CUs x
+ * resident workgroups, tail tiles x K steps) workgroups for the tail, on the
+ * device description in force).
  * TG_E_INVAL for NULL pointers, non-positive tile sizes, K step or split, and
  * negative M, N or K. */
 int tg_grid(int64_t M, int64_t N, int64_t K, const tg_cfg *cfg, int64_t *tiles, int64_t *blocks);
