@@ -472,16 +472,22 @@ def streamk_plan(M: int, N: int, K: int, c: Cfg, dev: Device = MI355X) -> dict:
     # never more stream-K workgroups than tail iterations: each then has at
     # least one, and a tile's pieces come from consecutive workgroups
     wgs = min(G, tail * ks)
-    smax = pieces = 0
+    smax = pieces = segmax = 0
     if tail > 0 and ks > 0:
         I = tail * ks
+        segmax = 1
         for j in range(tail):
-            n = sk_owner((j + 1) * ks - 1, I, wgs) - sk_owner(j * ks, I, wgs) + 1
+            first = sk_owner(j * ks, I, wgs)
+            n = sk_owner((j + 1) * ks - 1, I, wgs) - first + 1
             smax = max(smax, n)
             if n >= 2:
                 pieces += n
+            # tile j starts inside the range of the workgroup holding its first
+            # step: that workgroup also ran the end of tile j - 1
+            if j > 0 and first * I // wgs != j * ks:
+                segmax = 2
     return {"tiles": tiles, "G": G, "dp": tiles - tail, "tail": tail, "ks": ks, "wgs": wgs, "smax": smax,
-            "pieces": pieces, "blocks": tiles - tail + (wgs if tail > 0 else 0)}
+            "pieces": pieces, "segmax": segmax, "blocks": tiles - tail + (wgs if tail > 0 else 0)}
 
 
 # ---------------------------------------------------------------- cost model
@@ -613,11 +619,16 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
         # full rounds of whole tiles, then the tail's K steps spread over a
         # round of workgroups; pieces of split tiles stored as fp32 and read
         # back once by the second pass
+        # each piece runs the tile loop afresh: one latency to start, and the
+        # stages of zero-filling transfers past its K range; a stream-K
+        # workgroup runs up to segmax pieces
         sp = streamk_plan(M, N, K, c, dev)
         dp_rounds = sp["dp"] // slots
         sk_steps = cdiv(sp["tail"] * sp["ks"], sp["wgs"]) if sp["tail"] > 0 else 0
         t_cu = (dp_rounds * ktiles + sk_steps) * step(bcu)
-        t_cu = t_cu + (dp_rounds + (1 if sp["tail"] > 0 else 0)) * lat
+        t_cu = t_cu + (dp_rounds + sp["segmax"]) * lat
+        runs_cu = dp_rounds * bcu + (cdiv(sp["wgs"], dev.n_cu) * sp["segmax"] if sp["tail"] > 0 else 0)
+        t_cu = t_cu + runs_cu * c.stages * l2_step / dev.cu_bw
         pieces = 4.0 * c.bm * c.bn * sp["pieces"]
         raw = float(tiles) * eb * K * (c.bm + c.bn)
         g = math.sqrt(min(tiles, slots))

@@ -521,6 +521,7 @@ def test_streamk_partition_against_brute_force(tail, ks, G):
     plan = S.streamk_plan(M, Nn, 64 * ks, c, dev)
     assert (plan["G"], plan["dp"], plan["tail"], plan["ks"]) == (G, G, tail, ks)
     assert plan["wgs"] == wgs and plan["smax"] == smax and plan["pieces"] == total
+    assert plan["segmax"] == max(len(v) for v in per_g.values())
     assert plan["blocks"] == G + wgs and S.grid(M, Nn, c, dev, 64 * ks) == (G + tail, G + wgs)
 
 
@@ -539,6 +540,34 @@ def test_streamk_model_closed_form():
     # K = 0 has nothing to spread; fp32 has no stream-K kernel
     assert S.check(4096, 4096, 0, S.BF16, sk) == S.R_SHAPE
     assert S.check(4096, 4096, 64, S.F32, sk) != S.OK
+
+
+def test_streamk_pieces_restart_the_tile_loop():
+    # Every piece a stream-K workgroup runs is a run of the tile loop of its
+    # own: it starts with one latency and issues the stages of zero-filling
+    # transfers past its K range, as a whole tile does.  289 tiles of 256 x 256
+    # (one round of 256 and a tail of 33; 33 x 128 steps over 256 workgroups
+    # cross tile boundaries, so some run two pieces) against 288 (a tail of 32:
+    # 16 steps each, 8 to a tile, one piece per workgroup).
+    sk = S.Cfg(S.KIND_STREAMK, 256, 256, 64, 2, 4, 2, 1)
+    K = 8192
+    two, one = (256 * 289, 256), (256 * 288, 256)
+    assert S.streamk_plan(*two, K, sk)["segmax"] == 2 and S.streamk_plan(*one, K, sk)["segmax"] == 1
+    # the L2-to-CU rate alone: a step moves 256 A rows of one 128-byte line and
+    # four 64-column B blocks of 64 rows; the data-parallel round pays 2 stages
+    # past its range, the stream-K one 2 per piece
+    d = dataclasses.replace(S.MI355X, peak_bf16=1e30, lds_bw_cu=1e30, lat_step=0.0, lat_l2=0.0, w1_eff=1.0,
+                            bw=1e30, t0=0.0)
+    l2 = (256 * 128 + 64 * 4 * 128) / d.cu_bw
+    assert S.model_time(*two, K, S.BF16, sk, d) == pytest.approx((128 + 17 + 2 + 2 * 2) * l2, rel=1e-12)
+    assert S.model_time(*one, K, S.BF16, sk, d) == pytest.approx((128 + 16 + 2 + 2 * 1) * l2, rel=1e-12)
+    # latency alone: every step waits latency / (stages - 1), every run of the
+    # loop one latency more (the round of whole tiles, then each piece)
+    lat = 1e-6
+    d = dataclasses.replace(S.MI355X, peak_bf16=1e30, lds_bw_cu=1e30, cu_bw=1e30, lat_step=lat, lat_l2=lat,
+                            w1_eff=1.0, bw=1e30, t0=0.0)
+    assert S.model_time(*two, K, S.BF16, sk, d) == pytest.approx((128 + 17) * lat + (1 + 2) * lat, rel=1e-12)
+    assert S.model_time(*one, K, S.BF16, sk, d) == pytest.approx((128 + 16) * lat + (1 + 1) * lat, rel=1e-12)
 
 
 def test_sliced_k_rules_closed_forms():

@@ -419,11 +419,17 @@ SkPlan streamk_plan(int64_t M, int64_t N, int64_t K, const tg_cfg& c, const tg_d
     p.blocks = p.dp + (p.tail > 0 ? p.wgs : 0);
     if (p.tail > 0 && p.ks > 0) {
         const int64_t I = p.tail * p.ks;
+        p.segmax = 1;
         for (int64_t j = 0; j < p.tail; ++j) {
-            const int64_t n = sk_owner_host((j + 1) * p.ks - 1, I, p.wgs) - sk_owner_host(j * p.ks, I, p.wgs) + 1;
+            const int64_t first = sk_owner_host(j * p.ks, I, p.wgs);
+            const int64_t n = sk_owner_host((j + 1) * p.ks - 1, I, p.wgs) - first + 1;
             p.smax = std::max(p.smax, n);
             if (n >= 2)
                 p.pieces += n;
+            // a tile that starts inside a workgroup's range: that workgroup
+            // runs the end of the previous tile and the start of this one
+            if (j > 0 && first * I / p.wgs != j * p.ks)
+                p.segmax = 2;
         }
     }
     return p;
@@ -520,12 +526,17 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
     if (c.kind == TG_KIND_STREAMK) {
         // full rounds of whole tiles, then the tail's K steps spread evenly
         // over a round of workgroups; the pieces of split tiles are stored as
-        // fp32 and read back once by the second pass
+        // fp32 and read back once by the second pass.  Every piece is a run
+        // of the tile loop of its own, like a whole tile: it starts with one
+        // latency and issues the stages of zero-filling transfers past its K
+        // range (a stream-K workgroup runs up to segmax pieces)
         const SkPlan sp = streamk_plan(M, N, K, c, d);
         const int64_t dp_rounds = sp.dp / slots;
         const int64_t sk_steps = sp.tail > 0 ? cdiv(sp.tail * sp.ks, sp.wgs) : 0;
         double t_cu = (double)(dp_rounds * ktiles + sk_steps) * step(bcu);
-        t_cu = t_cu + (double)(dp_rounds + (sp.tail > 0 ? 1 : 0)) * lat;
+        t_cu = t_cu + (double)(dp_rounds + sp.segmax) * lat;
+        const int64_t runs_cu = dp_rounds * bcu + (sp.tail > 0 ? cdiv(sp.wgs, (int64_t)d.n_cu) * sp.segmax : 0);
+        t_cu = t_cu + (double)runs_cu * (double)c.stages * l2_step / d.cu_bw;
         const double pieces = 4.0 * (double)c.bm * (double)c.bn * (double)sp.pieces;
         const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
         const double g = std::sqrt((double)std::min<int64_t>(tiles, slots));

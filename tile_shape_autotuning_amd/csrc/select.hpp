@@ -79,7 +79,9 @@ void grid(int64_t M, int64_t N, int64_t K, const tg_cfg& c, int64_t* tiles, int6
 // tile is split into; pieces: slots written (pieces of the tiles split in two
 // or more).
 struct SkPlan {
-    int64_t tiles, G, dp, tail, ks, wgs, smax, pieces, blocks;
+    // segmax: most pieces one stream-K workgroup runs (1, or 2 when its range
+    // crosses a tile boundary)
+    int64_t tiles, G, dp, tail, ks, wgs, smax, pieces, blocks, segmax;
 };
 SkPlan streamk_plan(int64_t M, int64_t N, int64_t K, const tg_cfg& c, const tg_device_desc& d);
 // the workgroup that holds iteration x of I over G workgroups
