@@ -486,11 +486,12 @@ def streamk_study(torch):
     return out
 
 
-def sliced_k_study(p, torch):
+def sliced_k_study(p, tuned_cfg, torch):
     """The sliced-K kind where it pays: the fp32 workload's tuned call (K
-    split among the wave groups of each workgroup) against the best
-    configuration without K groups in the committed exhaustive table of the
-    same shape, both timed here, interleaved, with the same warm-up."""
+    split among the wave groups of each workgroup; `tuned_cfg`, the
+    configuration its timed call used) against the best configuration
+    without K groups in the committed exhaustive table of the same shape,
+    both timed here, interleaved, with the same warm-up."""
     import gzip
     path = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "tables", f"table_{p.w.name}.json.gz")
     if not os.path.exists(path):
@@ -498,7 +499,7 @@ def sliced_k_study(p, torch):
     with gzip.open(path, "rt") as f:
         rows = [r for r in json.load(f)["rows"] if r[2] is not None and r[2] > 0 and r[0][0] != 4]
     plain = tuple(min(rows, key=lambda r: r[2])[0])
-    tuned = tuple(p.tuned()[0].astuple())
+    tuned = tuple(tuned_cfg)
     res = {}
     for rnd in range(3):
         for name, cfg in (("tuned", tuned), ("without_k_groups", plain)):
@@ -715,7 +716,7 @@ def main():
     if (a.streamk or not a.only) and not a.no_streamk:
         line["streamk_study"] = streamk_study(torch)
     if 1 in prepared and not a.only and forced is None:
-        line["sliced_k_study"] = sliced_k_study(prepared[1], torch)
+        line["sliced_k_study"] = sliced_k_study(prepared[1], shapes[prepared[1].w.name]["cfg"], torch)
     if a.order and forced is None:
         line["tile_order_study"] = tile_order_study(p, torch)
     if not a.no_cpu:
