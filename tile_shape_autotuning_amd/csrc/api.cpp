@@ -164,14 +164,14 @@ static LaunchFn launch_fn(const KernelEntry& ke, const GemmParams& p)
 }
 
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias, void* C,
-               int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked,
+               int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool from_selection,
                const ExternalWorkspace* ext)
 {
     const tg_device_desc d = current_desc();
     tg_cfg c = cfg;
     bool misaligned = !(aligned16(A) && aligned16(B) && aligned16(C));
     if (c.kind != TG_KIND_UNALIGNED && misaligned) {
-        if (!pointers_checked)
+        if (!from_selection)
             return set_error(TG_E_INVAL, "A, B and C must be 16-byte aligned for the tiled and skinny kinds");
         // selection ran without knowing the pointers: fall back to the element-load kernel
         c = tg_cfg{TG_KIND_UNALIGNED, 64, 64, dtype == TG_F32 ? 16 : 32, 2, 2, 2, 1};

@@ -36,12 +36,13 @@ struct ExternalWorkspace {
 };
 
 // Validates arguments and launches one configuration (no selection).
-// `pointers_checked` = false: the configuration came from selection, which did
-// not see the pointers; misaligned pointers then run the element-load kernel.
+// `from_selection` = true: the configuration came from selection, which did
+// not see the pointers, so misaligned pointers run the element-load kernel
+// instead; false (a configuration the caller named): they are refused.
 // `ext`: split-K slabs go there (nothing is allocated; a call needing more
 // than ext->bytes is refused), else into the (device, stream) workspace.
 int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, const float* bias,
-               void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool pointers_checked,
+               void* C, int dtype, int act, const tg_cfg& cfg, hipStream_t stream, bool from_selection,
                const ExternalWorkspace* ext = nullptr);
 
 // The configuration a call without cfg uses: the cache entry of M's shape

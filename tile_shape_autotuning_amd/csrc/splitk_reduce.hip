@@ -61,13 +61,26 @@ splitk_reduce_kernel(const float* ws, int split, int64_t slab, int64_t mn, int n
                 v[e] = s;
             }
         }
-        int col = (int)(i % n);
+        // the column of each element is only needed for the bias (a 64-bit
+        // remainder on the path to the stores); without one the sums get
+        // + 0.0f, as in the single-pass epilogue
+        if (bias) {
+            int col = (int)(i % n);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (e < cnt)
-                v[e] = apply_act(v[e] + (bias ? bias[col] : 0.0f), act);
-            col = col + 1 == n ? 0 : col + 1;
+            for (int e = 0; e < 4; ++e) {
+                if (e < cnt)
+                    v[e] = v[e] + bias[col];
+                col = col + 1 == n ? 0 : col + 1;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = v[e] + 0.0f;
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < cnt)
+                v[e] = apply_act(v[e], act);
         if (out_bf16) {
             unsigned short* c = static_cast<unsigned short*>(C) + i;
             if (cnt == 4 && vec_out) {
