@@ -10,6 +10,9 @@
   inputs, 1e-2 for bf16 inputs), on the full output of every workload
   (8192^3 included: the oracle's product takes about 10 s on the host).
 * Edge shapes, empty and K = 0 problems, determinism, maximum sizes.
+* 48 seeded random problems (ragged or aligned, every dtype, with and
+  without bias) with the cost model's choice and random feasible
+  configurations of every kind the shape admits, integer-exact.
 """
 import numpy as np
 import pytest
@@ -109,6 +112,52 @@ def test_unaligned_shapes_integer_exact(M, N, K, dtype):
     C = _run(A_d, B_d, b_d, "relu", dtype)
     torch.cuda.synchronize()
     _exact_check(C, ref, dtype, f"{M}x{N}x{K} autotuned")
+
+
+def _random_problem(rng):
+    """A seeded random problem: M from 1 to 1500, N and K mostly on the
+    16-byte alignment the tiled kinds need (else only the element-load kind
+    is feasible), any dtype, ReLU or none, bias or none."""
+    dtype = int(rng.choice([wl.BF16, wl.F32, wl.BF16_F32OUT]))
+    unit = 4 if dtype == wl.F32 else 8
+    M = int(rng.integers(1, 1501))
+    if rng.random() < 0.8:
+        N, K = unit * int(rng.integers(1, 1501 // unit + 1)), unit * int(rng.integers(1, 2049 // unit + 1))
+    else:
+        N, K = int(rng.integers(1, 1501)), int(rng.integers(1, 2049))
+    act = str(rng.choice(["none", "relu"]))
+    return M, N, K, dtype, act, bool(rng.random() < 0.7)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_problems_random_cfgs_integer_exact(seed):
+    """Random shapes (ragged or aligned, every dtype) with the cost model's
+    choice and up to six random feasible configurations, at least one of each
+    kind the shape admits (data-parallel, split-K, sliced-K, stream-K, skinny,
+    element-load), all integer-exact against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    M, N, K, dtype, act, with_bias = _random_problem(rng)
+    A, B, bias = _int_inputs(M, N, K, dtype, 10 + seed)
+    if not with_bias:
+        bias = None
+    ref = gemm_ref.gemm(A, B, bias, act)
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    feas = [c for c in tg.enumerate_feasible(M, N, K, dtype) if tg.has_kernel(dtype, c)]
+    assert feas
+    picks = {}
+    for c in feas:                                   # one of each kind, then random others
+        key = (c.kind, c.split_k > 1)
+        picks.setdefault(key, c)
+    chosen = list(picks.values())
+    rest = [c for c in feas if c not in chosen]
+    for i in rng.permutation(len(rest))[:max(0, 6 - len(chosen))]:
+        chosen.append(rest[int(i)])
+    chosen.append(tg.model_choice(M, N, K, dtype)[0])
+    for c in chosen:
+        mark(f"random {seed}: {M}x{N}x{K} dt{dtype} {act} bias={with_bias} {c.astuple()}")
+        C = _run(A_d, B_d, b_d, act, dtype, c)
+        torch.cuda.synchronize()
+        _exact_check(C, ref, dtype, f"{M}x{N}x{K} dt{dtype} {act} {c.astuple()}")
 
 
 @pytest.mark.parametrize("M", [1, 3, 16, 17, 31, 48, 64])
