@@ -232,7 +232,8 @@ def calibration_summary():
     (offline: tile_shape_autotuning_amd.calibrate on the committed tables)."""
     with open(CALIBRATION_REPORT) as f:
         r = json.load(f)
-    keep = ("tables", "model_hits", "best_in_topk", "geomean_choice_over_best", "mean_rank_corr", "msle")
+    keep = ("tables", "model_hits", "best_in_topk", "near_best_in_topk", "geomean_choice_over_best",
+            "mean_rank_corr", "msle")
     return {"measured_in_this_run": False, "source": r.get("source", ""),
             "train": r["split"]["train"], "held_out": r["split"]["held_out"],
             "constants_fitted": r["constants_fitted"],

@@ -61,7 +61,7 @@ def test_fit_recovers_known_constants_and_scores_held_out_tables():
     assert rep["constants_fitted"] == TRUTH
     for part in ("train_after", "held_out_after"):
         r = rep[part]
-        assert r["model_hits"] == r["tables"] and r["best_in_topk"] == r["tables"]
+        assert r["model_hits"] == r["tables"] and r["best_in_topk"] == r["tables"] == r["near_best_in_topk"]
         assert r["msle"] == 0.0 and r["geomean_choice_over_best"] == 1.0
         assert all(math.isclose(v["rank_corr"], 1.0) for v in r["per_table"].values())
     # before the fit the model (other constants) is off the synthetic truth
@@ -95,7 +95,8 @@ def test_committed_report_matches_the_committed_tables_and_built_in_constants():
     assert [t["workload"] for t in test] == rep["split"]["held_out"]
     got = C.evaluate(test, base, rep["topk"])
     N.set_device_override(None)
-    for k in ("model_hits", "best_in_topk", "geomean_choice_over_best", "mean_rank_corr", "msle"):
+    for k in ("model_hits", "best_in_topk", "near_best_in_topk", "geomean_choice_over_best", "mean_rank_corr",
+              "msle"):
         assert got[k] == rep["held_out_after"][k], k
     # the constants before the fit are a point of the grid, so the fit is at
     # least as good on the training tables by its own objective (the held-out

@@ -17,7 +17,10 @@ HBM fraction), by grid
 search: fewest training tables whose measured best is outside the model's
 top k (the hybrid tuner measures the top k), then the smallest geometric
 mean of the measured time of the model's first choice over the best, then
-the smallest mean squared log error of predicted against measured times.  The model is
+the smallest mean squared log error of predicted against measured times.  The
+report also counts the tables with a configuration within 2 % of the
+measured best in the model's top k, which box-to-box noise of that size
+does not move.  The model is
 evaluated by the library (tg_model_times under a device-description
 override), so a fitted set can be written into the built-in description as
 it is.
@@ -84,10 +87,16 @@ def _spearman(x, y):
     return 1 - 6 * sum((rx[i] - ry[i]) ** 2 for i in range(n)) / (n * (n * n - 1))
 
 
+# a configuration measured within this fraction of the best counts as
+# near-best: boxes differ by about that much between runs, so which of two
+# such configurations is "the" best is not a property of the shape
+NEAR = 0.02
+
+
 def table_stats(tab, desc, topk):
     """Model quality on one table: (msle, best in top k, measured time of the
     model's first choice over the best measured, Spearman rank correlation,
-    first choice is the measured best)."""
+    first choice is the measured best, a near-best configuration in top k)."""
     N.set_device_override(desc)
     rows = tab["rows"]
     pred_all = N.model_times_us(tab["M"], tab["N"], tab["K"], tab["dtype"], [r[0] for r in rows])
@@ -98,7 +107,9 @@ def table_stats(tab, desc, topk):
     # ties in model time keep the first configuration in canonical order
     order = sorted(range(len(pred)), key=lambda i: (pred[i], rows[keep[i]][0]))
     best = min(range(len(meas)), key=lambda i: meas[i])
-    return err, best in set(order[:topk]), meas[order[0]] / meas[best], _spearman(pred, meas), order[0] == best
+    near = any(meas[i] <= (1.0 + NEAR) * meas[best] for i in order[:topk])
+    return (err, best in set(order[:topk]), meas[order[0]] / meas[best], _spearman(pred, meas), order[0] == best,
+            near)
 
 
 def evaluate(tabs, desc, topk):
@@ -110,10 +121,12 @@ def evaluate(tabs, desc, topk):
             "msle": round(sum(s[0] for s in stats) / n, 5),
             "model_hits": sum(s[4] for s in stats),
             "best_in_topk": sum(s[1] for s in stats),
+            "near_best_in_topk": sum(s[5] for s in stats),
             "geomean_choice_over_best": round(math.exp(sum(math.log(s[2]) for s in stats) / n), 4),
             "mean_rank_corr": round(sum(s[3] for s in stats if s[3] == s[3]) / max(1, sum(s[3] == s[3] for s in stats)),
                                     4),
-            "per_table": {t["workload"]: {"hit": s[4], "in_topk": s[1], "choice_over_best": round(s[2], 4),
+            "per_table": {t["workload"]: {"hit": s[4], "in_topk": s[1], "near_in_topk": s[5],
+                                          "choice_over_best": round(s[2], 4),
                                           "rank_corr": round(s[3], 4), "msle": round(s[0], 5)}
                           for t, s in zip(tabs, stats)}}
 
