@@ -170,6 +170,24 @@ def shape_aligned(N: int, K: int, dtype: int) -> bool:
     return K % vec == 0 and N % vec == 0
 
 
+def pad_extent(x: int, dtype: int) -> int:
+    """x rounded up to a whole 16-byte vector of elements."""
+    vec = 4 if dtype == F32 else 8
+    return cdiv(x, vec) * vec
+
+
+def padded_path(N: int, K: int, dtype: int, c: "Cfg", dev: "Device") -> bool:
+    """The tiled kind on a shape that is not aligned (MI355X rules): it runs on
+    copies of A and B zero-padded to K and N rounded up to whole vectors
+    (zeros add nothing to a sum), writes its sums as fp32 slabs with any split
+    and finishes in an output pass.  My reading of page "Compilers and Kernel
+    Languages", "A different tile for every shape" (ragged shapes are where a
+    fixed kernel loses) together with page "Tile Selection: Cost Models
+    Against Measurement", "The structure of the search space" (the tile grid
+    covers the extents, here the padded ones)."""
+    return dev.mode == 0 and c.kind == KIND_TILED and not shape_aligned(N, K, dtype)
+
+
 # ---------------------------------------------------------------- space
 WAVE_GRIDS = ((1, 1), (1, 2), (2, 1), (2, 2), (2, 4), (4, 2))
 SPLITS = (1, 2, 4, 8, 16)
@@ -399,8 +417,10 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
     if dev.mode == 0:
         if c.kind == KIND_UNALIGNED and aligned:
             return R_ALIGN
-        if c.kind != KIND_UNALIGNED and not aligned:
+        # the tiled kind takes an unaligned shape through the padded path
+        if c.kind not in (KIND_UNALIGNED, KIND_TILED) and not aligned:
             return R_ALIGN
+    Ke = pad_extent(K, dtype) if padded_path(N, K, dtype, c, dev) else K
     if c.kind == KIND_SKINNY and (M > 64 or c.bm != 16 * cdiv(M, 16)):
         return R_SHAPE
     r = check_static(dtype, c, dev)
@@ -417,7 +437,7 @@ def check(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X) -> i
     if c.kind == KIND_STREAMK and streamk_plan(M, N, K, c, dev)["tail"] == 0:
         return R_SHAPE
     if cta_splits(c) > 1:
-        if K == 0 or cdiv(K, k_per_split(c, K)) != c.split_k:
+        if Ke == 0 or cdiv(Ke, k_per_split(c, Ke)) != c.split_k:
             return R_SPLIT
     return OK
 
@@ -526,23 +546,33 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
         return t + dev.t0
     if dev.mode == 1:
         return _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, units, w, bcu)
+    if padded_path(N, K, dtype, c, dev):
+        # copying A and B into their padded forms (each read once and written
+        # once at the HBM rate, one launch), then the tiled kind on the padded
+        # problem with its sums in slabs, then the output pass (priced as the
+        # split-K second pass)
+        Np, Kp = pad_extent(N, dtype), pad_extent(K, dtype)
+        comp_p = float(eb * (M * Kp + Kp * Np) + ec * M * Np)
+        copies = float(eb * (M * K + K * N + M * Kp + Kp * Np)) / (dev.bw * dev.hbm_eff) + dev.t0
+        return _model_cu(M, Np, Kp, dtype, c, dev, eb, ec, peak, comp_p, tiles, units, w, bcu, True) + copies
     return _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w, bcu)
 
 
-def _splitk_slabs(M: int, N: int, c: Cfg) -> float:
+def _splitk_slabs(M: int, N: int, c: Cfg, padded: bool = False) -> float:
     """Bytes of the fp32 partial-sum slabs split-K leaves in memory: one
     M x N slab per split (my reading of split-K, page "Compilers and Kernel
     Languages", "A different tile for a different shape": the partial sums
-    of the K ranges have to meet before the non-linear epilogue)."""
-    return 4.0 * c.split_k * M * N if cta_splits(c) > 1 else 0.0
+    of the K ranges have to meet before the non-linear epilogue); the padded
+    path writes them with any split."""
+    return 4.0 * c.split_k * M * N if (cta_splits(c) > 1 or padded) else 0.0
 
 
-def _splitk_pass(M: int, N: int, ec: int, c: Cfg, dev: Device) -> float:
+def _splitk_pass(M: int, N: int, ec: int, c: Cfg, dev: Device, padded: bool = False) -> float:
     """The second split-K pass: one more launch that reads every slab once
-    and writes C, at the HBM rate."""
-    if cta_splits(c) <= 1:
+    and writes C, at the HBM rate (the padded path's output pass alike)."""
+    if cta_splits(c) <= 1 and not padded:
         return 0.0
-    return (_splitk_slabs(M, N, c) + float(ec) * M * N) / (dev.bw * dev.hbm_eff) + dev.t0
+    return (_splitk_slabs(M, N, c, padded) + float(ec) * M * N) / (dev.bw * dev.hbm_eff) + dev.t0
 
 
 def _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, units, w, bcu) -> float:
@@ -571,7 +601,7 @@ def _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, unit
     return max(t_c, t_m) + dev.t0
 
 
-def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w, bcu) -> float:
+def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w, bcu, padded=False) -> float:
     """MI355X: the roofline of "Analytical models and where they break" taken
     per CU and per K step.  The blocks resident on a CU advance together; one
     K step of all of them takes the longest of
@@ -657,12 +687,12 @@ def _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w,
     t_cu = t_cu + per_cu * red
     raw = float(tiles) * eb * K * (c.bm + c.bn)
     g = math.sqrt(min(units, slots))
-    t_hbm = (max(compulsory, raw / g) + _splitk_slabs(M, N, c)) / (dev.bw * dev.hbm_eff)
+    t_hbm = (max(compulsory, raw / g) + _splitk_slabs(M, N, c, padded)) / (dev.bw * dev.hbm_eff)
     # every block stores its outputs (C, or its split-K slab) after its K
     # loop: those stores do not overlap the loop
-    stores = _splitk_slabs(M, N, c) if cta_splits(c) > 1 else float(ec) * M * N
+    stores = _splitk_slabs(M, N, c, padded) if (cta_splits(c) > 1 or padded) else float(ec) * M * N
     t_cu = t_cu + stores / (dev.bw * dev.hbm_eff)
-    return max(t_cu, t_hbm) + _splitk_pass(M, N, ec, c, dev) + dev.t0
+    return max(t_cu, t_hbm) + _splitk_pass(M, N, ec, c, dev, padded) + dev.t0
 
 
 def rank(M: int, N: int, K: int, dtype: int, dev: Device = MI355X):

@@ -4,7 +4,7 @@ selection plans (tg_grid: ceil(M/BM) ceil(N/BN) tiles times the workgroups
 per tile, page "Tile Selection: Cost Models Against Measurement", "The
 structure of the search space"), for every kernel kind, and the second pass
 runs exactly where the plan has one (split-K across workgroups, a stream-K
-tail cut into pieces)."""
+tail cut into pieces), as do the padded path's copies and output pass."""
 import json
 
 import pytest
@@ -20,7 +20,8 @@ torch = pytest.importorskip("torch")
 tg = pytest.importorskip("tile_shape_autotuning_amd")
 
 # (M, N, K, dtype, cfg): every kind, split-K, a single row of tiles (B
-# streamed), an unaligned shape, fp32
+# streamed), an unaligned shape, fp32; K is exact in bf16 (the outputs of
+# all-ones operands are K)
 CASES = [
     (300, 264, 520, wl.BF16, (0, 64, 64, 64, 2, 2, 2, 2)),
     (200, 168, 392, wl.BF16, (0, 16, 32, 64, 1, 2, 3, 1)),
@@ -30,6 +31,10 @@ CASES = [
     (1024, 1040, 2048, wl.BF16_F32OUT, (3, 256, 256, 64, 2, 4, 2, 1)),
     (300, 264, 520, wl.BF16, (4, 32, 64, 128, 1, 2, 2, 4)),
     (256, 256, 256, wl.F32, (4, 16, 32, 64, 1, 1, 2, 4)),
+    # the tiled kind's padded path: copies, the kernel on the padded extents, output pass
+    (300, 262, 516, wl.BF16, (0, 64, 64, 64, 2, 2, 2, 1)),
+    (300, 262, 1020, wl.BF16, (0, 64, 64, 64, 2, 2, 2, 2)),
+    (130, 130, 258, wl.F32, (0, 32, 64, 32, 2, 2, 3, 1)),
 ]
 
 
@@ -40,11 +45,15 @@ def _threads(c):
     return 64 * wgm * wgn * (s if kind == S.KIND_SLICEDK else 1)
 
 
-def _second_pass(M, N, K, c):
+def _other_kernels(M, N, K, dt, c):
+    """Kernels the call runs besides the GEMM: the split-K or stream-K second
+    pass, or the padded path's copies and output pass."""
     kind, s = c[0], c[7]
+    if S.padded_path(N, K, dt, S.Cfg(*c), S.MI355X):
+        return 2
     if kind == S.KIND_STREAMK:
-        return S.streamk_plan(M, N, K, S.Cfg(*c))["smax"] >= 2
-    return kind != S.KIND_SLICEDK and s > 1
+        return int(S.streamk_plan(M, N, K, S.Cfg(*c))["smax"] >= 2)
+    return int(kind != S.KIND_SLICEDK and s > 1)
 
 
 def test_dispatched_grid_is_the_planned_one(tmp_path):
@@ -82,5 +91,7 @@ def test_dispatched_grid_is_the_planned_one(tmp_path):
             assert e["name"].rstrip(")").split("(")[0].endswith(f", {c[7]}>"), e["name"]
         if c[0] != S.KIND_SLICEDK and c[0] != S.KIND_STREAMK and c[7] > 1:
             assert blocks == tiles * c[7]
-    seconds = [e for e in kernels if "gemm_" not in e["name"]]
-    assert len(seconds) == sum(_second_pass(M, N, K, c) for M, N, K, _, c in CASES), [e["name"] for e in seconds]
+    others = [e for e in kernels if "gemm_" not in e["name"]]
+    assert len(others) == sum(_other_kernels(M, N, K, dt, c) for M, N, K, dt, c in CASES), [e["name"] for e in others]
+    assert sum("pad_operands" in e["name"] for e in others) == sum(
+        S.padded_path(N, K, dt, S.Cfg(*c), S.MI355X) for M, N, K, dt, c in CASES)

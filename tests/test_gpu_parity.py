@@ -98,11 +98,14 @@ def test_every_feasible_cfg_integer_exact(M, N, K, dtype):
     (300, 47, 129, wl.F32), (5, 1000, 77, wl.BF16),
 ])
 def test_unaligned_shapes_integer_exact(M, N, K, dtype):
+    # every configuration of the element-load kind and of the tiled kind's
+    # padded path (zero-padded copies of A and B, slabs, output pass)
     A, B, bias = _int_inputs(M, N, K, dtype, 3)
     ref = gemm_ref.gemm(A, B, bias, "relu")
     A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
-    feas = tg.enumerate_feasible(M, N, K, dtype)
-    assert feas and all(c.kind == S.KIND_UNALIGNED for c in feas)
+    feas = [c for c in tg.enumerate_feasible(M, N, K, dtype) if tg.has_kernel(dtype, c)]
+    assert {c.kind for c in feas} == {S.KIND_UNALIGNED, S.KIND_TILED}
+    assert all(S.padded_path(N, K, dtype, S.Cfg(*c.astuple()), S.MI355X) for c in feas if c.kind == S.KIND_TILED)
     for c in feas:
         mark(f"unaligned {M}x{N}x{K} dt{dtype} {c.astuple()}")
         C = _run(A_d, B_d, b_d, "relu", dtype, c)
@@ -460,15 +463,17 @@ def test_sliced_k_gelu_random_inputs_and_repeatable():
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])
 def test_split_k_second_pass_edges(dtype):
-    # an unaligned shape (N = 33) runs the element-load kind, which takes any C: the second pass
-    # then writes element by element into a C shifted off 16-byte alignment, and M x N = 2145
-    # leaves a ragged tail after the four-element groups
+    # an unaligned shape (N = 33) runs the element-load kind or the tiled kind's padded path, which
+    # take any C: the second pass then writes element by element into a C shifted off 16-byte
+    # alignment, and M x N = 2145 leaves a ragged tail after the four-element groups
     M, N, K = 65, 33, 630
     A, B, bias = _int_inputs(M, N, K, dtype, 8)
     ref = gemm_ref.gemm(A, B, bias, "relu")
     A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
     feas = [c for c in tg.enumerate_feasible(M, N, K, dtype) if c.split_k > 1 and tg.has_kernel(dtype, c)]
-    assert feas and all(c.kind == S.KIND_UNALIGNED for c in feas)
+    # the element-load kind and the tiled kind's padded path (whose output
+    # pass writes C element by element too)
+    assert {c.kind for c in feas} == {S.KIND_UNALIGNED, S.KIND_TILED}
     odt = torch.bfloat16 if dtype == wl.BF16 else torch.float32
     for shift in (0, 1):
         buf = torch.zeros(M * N + 1, dtype=odt, device="cuda")

@@ -182,7 +182,15 @@ def test_rejections_have_reasons():
     assert S.transfers_per_wave(S.Cfg(0, 16, 128, 64, 1, 2, 8, 1), S.BF16) == 9
     assert S.check(16, 28672, 8192, S.BF16, S.Cfg(0, 16, 128, 64, 1, 2, 6, 1), d) == S.OK
     assert S.check(16, 28672, 8192, S.BF16, S.Cfg(0, 16, 128, 64, 1, 2, 8, 1), d) == S.R_INFLIGHT
-    assert S.check(256, 256, 15, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
+    # an unaligned shape: the tiled kind takes it padded (K 15 -> 16), the
+    # kinds without a padded path do not
+    assert S.check(256, 256, 15, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 1), d) == S.OK
+    assert S.check(256, 256, 15, S.BF16, S.Cfg(4, 32, 64, 64, 1, 2, 2, 2), d) == S.R_ALIGN
+    assert S.check(256, 257, 4096, S.BF16, S.Cfg(3, 128, 128, 64, 2, 4, 3, 1), d) == S.R_ALIGN
+    assert S.check(16, 257, 4096, S.BF16, S.Cfg(1, 16, 128, 32, 1, 1, 1, 1), d) == S.R_ALIGN
+    # split-K on the padded K: 1025 -> 1032 = 2 x 516, so 2 splits of 544 (whole 32-k steps)
+    assert S.check(256, 256, 1025, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 2), d) == S.OK
+    assert S.check(256, 256, 15, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 2), d) == S.R_SPLIT
     assert S.check(256, 256, 256, S.BF16, S.Cfg(2, 64, 64, 32, 2, 2, 2, 1), d) == S.R_ALIGN
     assert S.check(256, 256, 64, S.BF16, S.Cfg(0, 64, 64, 32, 2, 2, 2, 4), d) == S.R_SPLIT
     assert S.check(100, 256, 256, S.BF16, S.Cfg(1, 112, 128, 32, 1, 1, 1, 1), d) == S.R_SPACE
@@ -568,6 +576,32 @@ def test_streamk_pieces_restart_the_tile_loop():
                             w1_eff=1.0, bw=1e30, t0=0.0)
     assert S.model_time(*two, K, S.BF16, sk, d) == pytest.approx((128 + 17) * lat + (1 + 2) * lat, rel=1e-12)
     assert S.model_time(*one, K, S.BF16, sk, d) == pytest.approx((128 + 16) * lat + (1 + 1) * lat, rel=1e-12)
+
+
+def test_padded_path_closed_form():
+    # an unaligned shape on the tiled kind: memory terms only (everything else
+    # made free).  The copies read A [256 x 777] and B [777 x 1001] and write
+    # A' [256 x 784] and B' [784 x 1008]; the kernel on the padded problem
+    # moves its compulsory bytes and writes one fp32 slab [256 x 1008] (split
+    # 1); the output pass reads that slab and writes 256 x 1008 outputs
+    d = dataclasses.replace(S.MI355X, peak_bf16=1e30, lds_bw_cu=1e30, cu_bw=1e30, lat_step=0.0, lat_l2=0.0,
+                            w1_eff=1.0, t0=0.0)
+    c = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 4, 2, 1)
+    M, Nn, K = 256, 1001, 777
+    assert S.padded_path(Nn, K, S.BF16, c, d) and (S.pad_extent(Nn, S.BF16), S.pad_extent(K, S.BF16)) == (1008, 784)
+    assert S.check(M, Nn, K, S.BF16, c, d) == S.OK
+    rate = d.bw * d.hbm_eff
+    copies = 2 * (256 * 777 + 777 * 1001 + 256 * 784 + 784 * 1008)
+    compulsory = 2 * (256 * 784 + 784 * 1008) + 2 * 256 * 1008
+    slab = 4 * 256 * 1008
+    want = (compulsory + slab) / rate + (slab + 2 * 256 * 1008) / rate + copies / rate
+    assert S.model_time(M, Nn, K, S.BF16, c, d) == pytest.approx(want, rel=1e-12)
+    # the same tiles on the aligned shape 256 x 1008 x 784 skip the copies,
+    # store C directly and need no output pass
+    aligned = S.model_time(M, 1008, 784, S.BF16, c, d)
+    assert aligned == pytest.approx(compulsory / rate, rel=1e-12)
+    # the H100 replica keeps the page's rules: no alignment rule, no padding
+    assert not S.padded_path(Nn, K, S.BF16, c, S.H100_REPLICA)
 
 
 def test_sliced_k_rules_closed_forms():

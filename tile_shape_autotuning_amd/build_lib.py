@@ -55,7 +55,7 @@ def kernel_source_digest() -> str:
     import hashlib
     files = sorted(os.path.join(CSRC, "kernels", f) for f in os.listdir(os.path.join(CSRC, "kernels"))
                    if f.endswith(".hpp"))
-    files += [os.path.join(CSRC, f) for f in ("api.cpp", "splitk_reduce.hip")]
+    files += [os.path.join(CSRC, f) for f in ("api.cpp", "splitk_reduce.hip", "pad.hip", "workspace.cpp")]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.relpath(f, CSRC).encode())
@@ -303,6 +303,7 @@ def build(force: bool = True, jobs: int | None = None, verbose: bool = False) ->
                  ex.submit(compile_host, os.path.join(CSRC, "tune.cpp"), True),
                  ex.submit(compile_host, os.path.join(CSRC, "tune_kernels.hip"), True),
                  ex.submit(compile_host, os.path.join(CSRC, "splitk_reduce.hip"), True),
+                 ex.submit(compile_host, os.path.join(CSRC, "pad.hip"), True),
                  ex.submit(compile_host, os.path.join(CSRC, "rmsnorm.hip"), True),
                  ex.submit(compile_host, os.path.join(CSRC, "noalloc.hip"), True)]
         unit_objs = [f.result() for f in futs]

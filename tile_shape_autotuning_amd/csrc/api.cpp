@@ -169,8 +169,11 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
 {
     const tg_device_desc d = current_desc();
     tg_cfg c = cfg;
+    // the padded path reads A and B and writes C element by element: any
+    // pointer alignment will do
+    const bool padded = padded_path(N, K, dtype, c, d);
     bool misaligned = !(aligned16(A) && aligned16(B) && aligned16(C));
-    if (c.kind != TG_KIND_UNALIGNED && misaligned) {
+    if (c.kind != TG_KIND_UNALIGNED && misaligned && !padded) {
         if (!from_selection)
             return set_error(TG_E_INVAL, "A, B and C must be 16-byte aligned for the tiled and skinny kinds");
         // selection ran without knowing the pointers: fall back to the element-load kernel
@@ -209,6 +212,16 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     p.out_bf16 = dtype == TG_BF16 ? 1 : 0;
     p.act = act;
     p.group_m = tile_order();
+    // the padded path: the kernel runs on the padded extents, its sums go to
+    // the slabs whatever the split, and the output pass writes C
+    const PaddedLayout pl = padded_layout(M, N, K, dtype, c);
+    if (pl.on) {
+        p.N = (int)pl.Np;
+        p.K = (int)pl.Kp;
+        p.kps = (int)k_per_split(c, pl.Kp);
+        p.C = nullptr;
+        p.slab_out = 1;
+    }
     int64_t tiles, blocks;
     grid(M, N, K, c, &tiles, &blocks, &d);
     if (blocks > 0x7FFFFFFF)
@@ -223,13 +236,14 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
         p.sk_smax = (int)std::max<int64_t>(1, sp.smax);
         fixup = sp.smax >= 2;
     }
-    // held until both kernels of a split-K call are queued (see ensure_workspace)
+    // held until every kernel of a call that uses the workspace is queued (see
+    // ensure_workspace)
     std::unique_lock<std::mutex> ws_hold;
-    if (cta_splits(c) > 1 || fixup) {
-        const size_t need = workspace_bytes_for(M, N, K, c);
+    if (cta_splits(c) > 1 || fixup || pl.on) {
+        const size_t need = workspace_bytes_for(M, N, K, dtype, c);
         if (ext) {
             if (need > ext->bytes)
-                return set_error(TG_E_INVAL, "split-K partial sums need " + std::to_string(need) +
+                return set_error(TG_E_INVAL, "the workspace of this call needs " + std::to_string(need) +
                                                  " bytes, more than the " + std::to_string(ext->bytes) +
                                                  " bytes of the caller-independent scratch");
             p.ws = ext->ws;
@@ -238,12 +252,25 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
             if (st != TG_OK)
                 return st;
         }
-        p.slab = splitk_slab(M, N);
+        p.slab = pl.on ? pl.slab : splitk_slab(M, N);
     }
-    hipError_t e = launch_fn(*ke, p)(p, (int)blocks, stream);
+    hipError_t e;
+    if (pl.on) {
+        char* base = reinterpret_cast<char*>(p.ws);
+        p.A = base + pl.a_off;
+        p.B = base + pl.b_off;
+        e = pad_operands(A, B, base + pl.a_off, base + pl.b_off, M, N, K, pl.Np, pl.Kp, in_bytes(dtype), stream);
+        if (e != hipSuccess)
+            return set_hip_error(e, "operand padding launch");
+    }
+    e = launch_fn(*ke, p)(p, (int)blocks, stream);
     if (e != hipSuccess)
         return set_hip_error(e, "kernel launch");
-    if (cta_splits(c) > 1) {
+    if (pl.on) {
+        e = padded_output(p.ws, c.split_k, pl.slab, pl.Np, M, N, bias, C, p.out_bf16, act, stream);
+        if (e != hipSuccess)
+            return set_hip_error(e, "padded output pass launch");
+    } else if (cta_splits(c) > 1) {
         e = splitk_reduce(p.ws, c.split_k, M, N, bias, C, p.out_bf16, act, stream);
         if (e != hipSuccess)
             return set_hip_error(e, "split-K reduction launch");

@@ -36,6 +36,7 @@ struct GemmParams {
     int out_bf16;         // 1: C is bf16, 0: C is fp32
     int act;              // 0 none, 1 ReLU, 2 GELU (erf form)
     int group_m;          // tile rows per scheduling group (>= 1)
+    int slab_out;         // 1: sums go to the split slabs even with split == 1 (the padded path)
     // stream-K kind: the first sk_dp tiles (in scheduling order) run one
     // workgroup each; the remaining sk_tail tiles' sk_ks K steps each are
     // spread evenly over sk_g further workgroups, whose pieces of a tile go to
@@ -158,6 +159,9 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float v)
 // With split > 1 a block's sums skip bias, activation and conversion and go,
 // as fp32, to its split's slab of the workspace (row-major, row stride N like
 // C); a second kernel adds the slabs in split order and applies the rest.
+// The padded path (shapes whose rows are not 16-byte multiples) does the same
+// with any split: the kernel then runs on zero-padded copies of A and B and
+// the second kernel writes the real C.
 // Kernel boundaries order the two passes, so no flags or cache control are
 // needed between them.
 // Output (row, col) of the problem goes to dst[(row - row0) * ld + col - col0].
@@ -172,7 +176,7 @@ struct OutSpec {
 
 __device__ __forceinline__ OutSpec out_spec(const GemmParams& p, int split)
 {
-    if (p.split > 1)
+    if (p.split > 1 || p.slab_out)
         return OutSpec{p.ws + (int64_t)split * p.slab, nullptr, 0, 0, 0, 0, (int64_t)p.N};
     return OutSpec{p.C, p.bias, p.act, p.out_bf16, 0, 0, (int64_t)p.N};
 }

@@ -77,10 +77,11 @@ int gemm_bias_act_noalloc(int64_t M, int64_t N, int64_t K, const void* A, const 
         if (st != TG_OK)
             return st;
     }
-    if (workspace_bytes_for(M, N, K, c) > kScratchBytes)
-        return set_error(TG_E_INVAL, "split-K partial sums of this call need " +
-                                         std::to_string(workspace_bytes_for(M, N, K, c)) + " bytes; the no-allocation "
-                                         "entry point has " + std::to_string(kScratchBytes));
+    const size_t need = workspace_bytes_for(M, N, K, dtype, c);
+    if (need > kScratchBytes)
+        return set_error(TG_E_INVAL, "the workspace of this call (split-K partial sums, padded operands) needs " +
+                                         std::to_string(need) + " bytes; the no-allocation entry point has " +
+                                         std::to_string(kScratchBytes));
     float* ws = nullptr;
     int dev = 0;
     st = scratch_for_device(&ws, &dev);

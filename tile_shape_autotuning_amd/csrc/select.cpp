@@ -119,6 +119,17 @@ bool shape_aligned(int64_t N, int64_t K, int dtype)
     return K % vec == 0 && N % vec == 0;
 }
 
+int64_t pad_extent(int64_t x, int dtype)
+{
+    const int64_t vec = dtype == TG_F32 ? 4 : 8;
+    return (x + vec - 1) / vec * vec;
+}
+
+bool padded_path(int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d)
+{
+    return d.mode == 0 && c.kind == TG_KIND_TILED && !shape_aligned(N, K, dtype);
+}
+
 // the kernels that move panels straight into LDS: the tiled and sliced-K
 // kinds (fp32 and bf16) and stream-K (bf16 only)
 static bool dma_kind(const tg_cfg& c, int dtype)
@@ -356,9 +367,11 @@ int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_
     if (d.mode == 0) {
         if (c.kind == TG_KIND_UNALIGNED && aligned)
             return R_ALIGN;
-        if (c.kind != TG_KIND_UNALIGNED && !aligned)
+        // the tiled kind takes an unaligned shape through the padded path
+        if (c.kind != TG_KIND_UNALIGNED && c.kind != TG_KIND_TILED && !aligned)
             return R_ALIGN;
     }
+    const int64_t Ke = padded_path(N, K, dtype, c, d) ? pad_extent(K, dtype) : K;
     if (c.kind == TG_KIND_SKINNY && (M > 64 || c.bm != 16 * cdiv(M, 16)))
         return R_SHAPE;
     const int st = check_static(dtype, c, d);
@@ -376,7 +389,7 @@ int check(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_
     if (c.kind == TG_KIND_STREAMK && streamk_plan(M, N, K, c, d).tail == 0)
         return R_SHAPE;
     if (cta_splits(c) > 1) {
-        if (K == 0 || cdiv(K, k_per_split(c, K)) != c.split_k)
+        if (Ke == 0 || cdiv(Ke, k_per_split(c, Ke)) != c.split_k)
             return R_SPLIT;
     }
     return OK;
@@ -465,19 +478,21 @@ static double model_page(int64_t K, int dtype, const tg_cfg& c, const tg_device_
 }
 
 // Split-K (page "Compilers and Kernel Languages", "A different tile for a
-// different shape"): the fp32 partial-sum slabs, one M x N slab per split ...
-static double splitk_slabs(int64_t M, int64_t N, const tg_cfg& c)
+// different shape"): the fp32 partial-sum slabs, one M x N slab per split
+// (the padded path writes them with any split) ...
+static double splitk_slabs(int64_t M, int64_t N, const tg_cfg& c, bool padded = false)
 {
-    return cta_splits(c) > 1 ? 4.0 * (double)c.split_k * (double)M * (double)N : 0.0;
+    return (cta_splits(c) > 1 || padded) ? 4.0 * (double)c.split_k * (double)M * (double)N : 0.0;
 }
 
 // ... and the second pass: one more launch reading every slab once and
 // writing C at the HBM rate.
-static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, const tg_device_desc& d)
+static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, const tg_device_desc& d,
+                          bool padded = false)
 {
-    if (cta_splits(c) <= 1)
+    if (cta_splits(c) <= 1 && !padded)
         return 0.0;
-    return (splitk_slabs(M, N, c) + (double)ec * (double)M * (double)N) / (d.bw * d.hbm_eff) + d.t0;
+    return (splitk_slabs(M, N, c, padded) + (double)ec * (double)M * (double)N) / (d.bw * d.hbm_eff) + d.t0;
 }
 
 // MI355X: the roofline of "Analytical models and where they break" per CU and
@@ -494,7 +509,7 @@ static double splitk_pass(int64_t M, int64_t N, int64_t ec, const tg_cfg& c, con
 // pass.
 static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d,
                        int64_t eb, int64_t ec, double peak, double compulsory, int64_t tiles, int64_t units,
-                       int64_t w, int64_t bcu)
+                       int64_t w, int64_t bcu, bool padded = false)
 {
     const int64_t ktiles = cdiv(k_per_split(c, K), c.bk);
     const int64_t wm = c.bm / c.wgm, wn = c.bn / c.wgn;
@@ -569,12 +584,13 @@ static double model_cu(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg&
     t_cu = t_cu + (double)per_cu * red;
     const double raw = (double)tiles * (double)eb * (double)K * (double)(c.bm + c.bn);
     const double g = std::sqrt((double)std::min<int64_t>(units, slots));
-    const double t_hbm = (std::max(compulsory, raw / g) + splitk_slabs(M, N, c)) / (d.bw * d.hbm_eff);
+    const double t_hbm = (std::max(compulsory, raw / g) + splitk_slabs(M, N, c, padded)) / (d.bw * d.hbm_eff);
     // every block stores its outputs (C, or its split-K slab) after its K
     // loop: those stores do not overlap the loop
-    const double stores = cta_splits(c) > 1 ? splitk_slabs(M, N, c) : (double)ec * (double)M * (double)N;
+    const double stores = (cta_splits(c) > 1 || padded) ? splitk_slabs(M, N, c, padded)
+                                                        : (double)ec * (double)M * (double)N;
     t_cu = t_cu + stores / (d.bw * d.hbm_eff);
-    return std::max(t_cu, t_hbm) + splitk_pass(M, N, ec, c, d) + d.t0;
+    return std::max(t_cu, t_hbm) + splitk_pass(M, N, ec, c, d, padded) + d.t0;
 }
 
 double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d)
@@ -607,6 +623,15 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     }
     if (d.mode == 1)
         return model_page(K, dtype, c, d, eb, peak, flops, compulsory, tiles, units, w, bcu);
+    if (padded_path(N, K, dtype, c, d)) {
+        // the padded path: copying A and B into their padded forms (read once,
+        // written once), then the tiled kind on the padded problem with its
+        // sums in slabs, then the output pass (priced as the split-K one)
+        const int64_t Np = pad_extent(N, dtype), Kp = pad_extent(K, dtype);
+        const double comp_p = (double)(eb * (M * Kp + Kp * Np) + ec * M * Np);
+        const double copies = (double)(eb * (M * K + K * N + M * Kp + Kp * Np)) / (d.bw * d.hbm_eff) + d.t0;
+        return model_cu(M, Np, Kp, dtype, c, d, eb, ec, peak, comp_p, tiles, units, w, bcu, true) + copies;
+    }
     return model_cu(M, N, K, dtype, c, d, eb, ec, peak, compulsory, tiles, units, w, bcu);
 }
 

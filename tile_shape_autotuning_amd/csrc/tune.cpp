@@ -285,7 +285,7 @@ int autotune(int64_t M, int64_t N, int64_t K, int dtype, int act, bool has_bias,
         // workspace for the largest split-K candidate, allocated before timing
         size_t wsb = 0;
         for (const Timed& t : cands)
-            wsb = std::max(wsb, workspace_bytes_for(M, N, K, t.cfg));
+            wsb = std::max(wsb, workspace_bytes_for(M, N, K, dtype, t.cfg));
         if (wsb > 0) {
             float* w;
             const int r = ensure_workspace(wsb, st, &w);

@@ -28,8 +28,11 @@ struct Workspace {
 static std::mutex g_ws_mu;   // guards the map itself
 static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, const tg_cfg& c)
+size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c)
 {
+    const PaddedLayout pl = padded_layout(M, N, K, dtype, c);
+    if (pl.on)
+        return pl.total;
     if (c.kind == TG_KIND_STREAMK) {
         // one bm x bn slot per piece: tail tiles x most pieces per tile
         const SkPlan sp = streamk_plan(M, N, K, c, current_desc());
@@ -40,6 +43,23 @@ size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, const tg_cfg& c)
     if (cta_splits(c) <= 1)
         return 0;
     return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
+}
+
+PaddedLayout padded_layout(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c)
+{
+    PaddedLayout l{};
+    if (!padded_path(N, K, dtype, c, current_desc()))
+        return l;
+    auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t eb = (size_t)in_bytes(dtype);
+    l.on = true;
+    l.Np = pad_extent(N, dtype);
+    l.Kp = pad_extent(K, dtype);
+    l.slab = splitk_slab(M, l.Np);
+    l.a_off = up256((size_t)c.split_k * (size_t)l.slab * sizeof(float));
+    l.b_off = l.a_off + up256((size_t)M * (size_t)l.Kp * eb);
+    l.total = l.b_off + up256((size_t)l.Kp * (size_t)l.Np * eb);
+    return l;
 }
 
 int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws, std::unique_lock<std::mutex>* hold)
