@@ -51,7 +51,10 @@ typedef enum {
 } tg_act;
 
 typedef enum {
-    TG_KIND_TILED = 0,     /* block-tiled MFMA kernel, 16-byte vector loads */
+    TG_KIND_TILED = 0,     /* block-tiled MFMA kernel, 16-byte transfers of
+                              rows straight into LDS; on a shape whose K or N
+                              is not a whole 16-byte vector it runs padded (see
+                              gemm_bias_act) */
     TG_KIND_SKINNY = 1,    /* M <= 64 weight-streaming kernel (bf16 only) */
     TG_KIND_UNALIGNED = 2, /* block-tiled kernel with element loads, for K or N
                               not a multiple of the 16-byte vector */
@@ -146,7 +149,10 @@ int tg_set_stream(void *hip_stream);
  * the cache is keyed on M's shape bucket (tg_dispatch_m): one tuning serves
  * every M of the bucket.
  *   M, N >= 0, K >= 0 (M or N = 0: nothing to do; K = 0: C = act(bias)).
- *   A, B, C: device pointers, 16-byte aligned for the tiled and skinny kinds.
+ *   A, B, C: device pointers, 16-byte aligned for the tiled, skinny,
+ *     stream-K and sliced-K kinds on an aligned shape (K and N multiples of 8
+ *     bf16 / 4 fp32 elements); any element alignment for the unaligned kind
+ *     and for the tiled kind's padded path.
  *   bias: device pointer to N floats, or NULL.
  *   dtype: tg_dtype; act: tg_act; cfg: explicit configuration or NULL.
  * Limits: K <= 2^21, N <= 2^21, M <= 2^31 - 1 (TG_E_UNSUPPORTED beyond).
@@ -158,10 +164,17 @@ int tg_set_stream(void *hip_stream);
  * stream: the GEMM writes one
  * fp32 slab of partial sums per split (split_k x M x N floats) to a
  * library-owned workspace, then a second kernel adds the slabs in split order
- * and applies bias, activation and conversion.  There is one workspace per
- * (device, stream), grown on demand (growth waits for that stream), so calls
- * on different streams may run concurrently; calls on one stream are ordered
- * by it.
+ * and applies bias, activation and conversion.  The tiled kind on a shape
+ * whose K or N is not a multiple of 8 bf16 / 4 fp32 elements takes the
+ * padded path (page "Compilers and Kernel Languages", "A different tile for
+ * every shape": ragged shapes): one kernel copies A and B into the workspace
+ * with K and N rounded up to whole vectors and the new rows and columns zero,
+ * the GEMM runs on the copies and writes fp32 slabs of M x Np with any
+ * split_k, and an output pass adds them, applies bias, activation and
+ * conversion and writes C -- three kernels, results as on an aligned shape.
+ * There is one workspace per (device, stream), grown on demand (growth waits
+ * for that stream), so calls on different streams may run concurrently;
+ * calls on one stream are ordered by it.
  */
 int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   const float *bias, void *C, int dtype, int act, const tg_cfg *cfg);
@@ -173,11 +186,11 @@ int gemm_bias_act(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
  * kernels run), but the call allocates nothing: no hipMalloc, no hipFree, no
  * allocating library routine, and it never tunes -- with cfg == NULL it takes
  * the cache entry of M's shape bucket, else the cost model's choice.
- * Split-K partial sums go to one fixed device array of
- * tg_noalloc_scratch_bytes() bytes (32 MiB) that each GPU the library runs on
- * holds until the process ends; a call whose slabs need more
- * (split_k x M x N floats, each slab rounded up to 64) is refused with
- * TG_E_INVAL before anything is queued.  Every call on one GPU shares that
+ * Split-K partial sums (and the padded path's operand copies) go to one
+ * fixed device array of tg_noalloc_scratch_bytes() bytes (32 MiB) that each
+ * GPU the library runs on holds until the process ends; a call that needs
+ * more (split_k x M x N floats, each slab rounded up to 64, plus the padded
+ * copies) is refused with TG_E_INVAL before anything is queued.  Every call on one GPU shares that
  * GPU's array: calls on one stream are ordered by it, but calls that overlap
  * on one GPU through different streams race on the array and may return
  * wrong results.  Other errors as gemm_bias_act.
