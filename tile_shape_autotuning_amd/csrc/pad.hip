@@ -38,27 +38,28 @@ struct PadJob {
     int64_t colsp;    // destination columns = destination row stride (a multiple of 16 bytes)
 };
 
-// blockIdx.z picks the operand; rows by blockIdx.y (grid-stride), 16-byte
-// destination chunks by thread.  T: the element's bit pattern (2 or 4 bytes).
+// blockIdx.y picks the operand; the destination's 16-byte chunks, row after
+// row, are spread over the threads (grid-stride), so short rows do not
+// leave threads idle.  T: the element's bit pattern (2 or 4 bytes).
 template <typename T>
 __global__ void __launch_bounds__(256) pad_operands_kernel(PadJob a, PadJob b)
 {
-    const PadJob j = blockIdx.z == 0 ? a : b;
+    const PadJob j = blockIdx.y == 0 ? a : b;
     constexpr int V = 16 / (int)sizeof(T);
     const T* src = static_cast<const T*>(j.src);
     T* dst = static_cast<T*>(j.dst);
-    const int64_t chunks = j.colsp / V;
-    for (int64_t r = blockIdx.y; r < j.rowsp; r += gridDim.y) {
-        for (int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x; ch < chunks; ch += (int64_t)gridDim.x * 256) {
-            const int64_t c0 = ch * V;
-            T v[V];
+    const int64_t chunks = j.colsp / V;       // per destination row
+    const int64_t total = j.rowsp * chunks;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / chunks;
+        const int64_t c0 = (i - r * chunks) * V;
+        T v[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                v[e] = (r < j.rows && c0 + e < j.cols) ? src[r * j.cols + c0 + e] : T(0);
-            u32x4_t w;
-            __builtin_memcpy(&w, v, 16);
-            *reinterpret_cast<u32x4_t*>(dst + r * j.colsp + c0) = w;
-        }
+        for (int e = 0; e < V; ++e)
+            v[e] = (r < j.rows && c0 + e < j.cols) ? src[r * j.cols + c0 + e] : T(0);
+        u32x4_t w;
+        __builtin_memcpy(&w, v, 16);
+        *reinterpret_cast<u32x4_t*>(dst + i * V) = w;
     }
 }
 
@@ -116,10 +117,8 @@ hipError_t pad_operands(const void* A, const void* B, void* Ap, void* Bp, int64_
     const PadJob a{A, Ap, M, M, K, Kp};
     const PadJob b{B, Bp, K, Kp, N, Np};
     const int64_t v = 16 / eb;
-    const int64_t cx = cdiv64(std::max(Kp, Np) / v, 256);
-    const int64_t ry = std::max(M, Kp);
-    const dim3 grid((unsigned)std::min<int64_t>(std::max<int64_t>(cx, 1), 64),
-                    (unsigned)std::min<int64_t>(std::max<int64_t>(ry, 1), 65535), 2);
+    const int64_t most = std::max(M * (Kp / v), Kp * (Np / v));   // chunks of the larger copy
+    const dim3 grid((unsigned)std::min<int64_t>(std::max<int64_t>(cdiv64(most, 256), 1), 4096), 2);
     if (eb == 2)
         hipLaunchKernelGGL(pad_operands_kernel<unsigned short>, grid, dim3(256), 0, stream, a, b);
     else
