@@ -163,6 +163,28 @@ def test_random_problems_random_cfgs_integer_exact(seed):
         _exact_check(C, ref, dtype, f"{M}x{N}x{K} dt{dtype} {act} {c.astuple()}")
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])
+def test_padded_path_gelu_random_inputs(dtype):
+    # the padded path with bias and GELU on random operands, against the fp64
+    # oracle within the dtype's tolerance, and twice in a row bit for bit
+    M, N, K = 257, 1001, 515
+    A, B, bias = wl.make_inputs(M, N, K, dtype, wl.Dist("normal", 1.0), wl.Dist("normal", 1.0 / 23.0),
+                                wl.Dist("normal", 0.1), 77)
+    ref = gemm_ref.gemm(A, B, bias, "gelu")
+    A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+    for cfg in ((0, 64, 64, 64, 2, 2, 2, 1), (0, 128, 128, 64, 2, 4, 2, 2)):
+        c = S.Cfg(*cfg)
+        if dtype == wl.F32:
+            c = S.Cfg(0, 64, 64, 32, 2, 2, 2, cfg[7])
+        assert S.padded_path(N, K, dtype, c, S.MI355X) and tg.check_cfg(M, N, K, dtype, c.astuple()) == 0
+        mark(f"padded gelu dt{dtype} {c.astuple()}")
+        C1 = _run(A_d, B_d, b_d, "gelu", dtype, c.astuple())
+        C2 = _run(A_d, B_d, b_d, "gelu", dtype, c.astuple())
+        torch.cuda.synchronize()
+        assert torch.equal(C1, C2)
+        assert_close(out_f64(C1), ref, dtype, f"padded gelu {c.astuple()}")
+
+
 @pytest.mark.parametrize("M", [1, 3, 16, 17, 31, 48, 64])
 def test_skinny_kernels_integer_exact(M):
     N, K = 1032, 1064

@@ -2,8 +2,9 @@
 C ABI, against gemm_bias_act on the same inputs: the same kernels run, so the
 outputs must be identical bit for bit; both are also checked against the
 oracle (integer-valued inputs make the fp32 sums exact).  Split-K
-configurations put their partial sums in the library's fixed scratch array;
-two calls in a row, the second smaller, share it."""
+configurations put their partial sums, and the padded path its operand
+copies too, in the library's fixed scratch array; two calls in a row, the
+second smaller, share it."""
 import numpy as np
 import pytest
 
@@ -61,6 +62,28 @@ def test_noalloc_matches_gemm_bias_act_two_calls_second_smaller(dtype):
         got = _call(N_.gemm_bias_act_noalloc_ptr, M, N, K, A_d, B_d, b_d, dtype, cfg)
         want = _call(N_.gemm_bias_act_ptr, M, N, K, A_d, B_d, b_d, dtype, cfg)
         assert np.array_equal(_bits(got), _bits(want)), f"call {i}: differs from gemm_bias_act"
+        if dtype == wl.BF16:
+            assert np.array_equal(out_bits(got), wl.f32_to_bf16_bits(ref.astype(np.float32)))
+        else:
+            assert np.array_equal(out_f64(got), ref)
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_noalloc_padded_path_two_calls_second_smaller(dtype):
+    # unaligned shapes on the tiled kind: the padded copies of A and B and the
+    # slabs all live in the fixed scratch array
+    N_ = tg._native
+    if dtype == wl.F32:
+        calls = [(130, 130, 258, (0, 32, 64, 32, 2, 2, 3, 2)), (65, 33, 63, (0, 32, 32, 32, 1, 1, 2, 1))]
+    else:
+        calls = [(513, 1001, 777, (0, 128, 64, 64, 4, 2, 3, 2)), (100, 130, 300, (0, 64, 64, 64, 2, 2, 2, 1))]
+    for i, (M, N, K, cfg) in enumerate(calls):
+        mark(f"noalloc padded call {i}: {M}x{N}x{K} dt{dtype} cfg {cfg}")
+        A, B, bias, ref = _problem(M, N, K, dtype, 60 + i)
+        A_d, B_d, b_d = to_dev(A), to_dev(B), to_dev(bias)
+        got = _call(N_.gemm_bias_act_noalloc_ptr, M, N, K, A_d, B_d, b_d, dtype, cfg)
+        want = _call(N_.gemm_bias_act_ptr, M, N, K, A_d, B_d, b_d, dtype, cfg)
+        assert np.array_equal(_bits(got), _bits(want)), f"padded call {i}: differs from gemm_bias_act"
         if dtype == wl.BF16:
             assert np.array_equal(out_bits(got), wl.f32_to_bf16_bits(ref.astype(np.float32)))
         else:
