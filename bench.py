@@ -487,6 +487,50 @@ def streamk_study(torch):
     return out
 
 
+PADDED_SHAPE = (513, 1001, 777)
+
+
+def padded_study(torch):
+    """The padded path where the shape is ragged: 513 x 1001 x 777 bf16 with
+    bias and ReLU (K and N not whole 16-byte vectors).  Times the best
+    element-load configuration and the best padded-path configuration of the
+    committed exhaustive table of that shape, interleaved, and the hybrid
+    tuner's own choice (which sees both)."""
+    import gzip
+    import tile_shape_autotuning_amd as tg
+    M, N, K = PADDED_SHAPE
+    path = os.path.join(ROOT, "tile_shape_autotuning_amd", "tuned", "tables", "table_c23_bf16_513x1001x777.json.gz")
+    if not os.path.exists(path):
+        return None
+    with gzip.open(path, "rt") as f:
+        rows = [r for r in json.load(f)["rows"] if r[2] is not None and r[2] > 0]
+    elem = tuple(min((r for r in rows if r[0][0] == 2), key=lambda r: r[2])[0])
+    padded = tuple(min((r for r in rows if r[0][0] == 0), key=lambda r: r[2])[0])
+    A, B, bias = wl.make_inputs(M, N, K, wl.BF16, wl.Dist("normal", 1.0 / np.sqrt(K)), wl.Dist("normal", 1.0),
+                                wl.Dist("uniform", 1.0), 9)
+    A_d, B_d, b_d = _dev(A, torch), _dev(B, torch), _dev(bias, torch)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for rnd in range(3):
+        for name, cfg in (("element_loads", elem), ("padded", padded)):
+            call = tg.BoundGemm(A_d, B_d, b_d, act="relu", out=C, cfg=cfg)
+            warm_up(call, 10, torch, 0.05)
+            sec, _ = time_steps(call, 2000, torch)
+            res[name] = min(res.get(name, 1e9), sec)
+    tuned = tuple(tg.gemm_autotune(M, N, K, wl.BF16, act="relu", bias=True).astuple())
+    call = tg.BoundGemm(A_d, B_d, b_d, act="relu", out=C, cfg=tuned)
+    warm_up(call, 10, torch, 0.05)
+    t_tuned, _ = time_steps(call, 2000, torch)
+    out = {"shape": f"{M} x {N} x {K} bf16, bias + ReLU",
+           "element_loads": {"cfg": list(elem), "us": round(res["element_loads"] * 1e6, 3)},
+           "padded": {"cfg": list(padded), "us": round(res["padded"] * 1e6, 3)},
+           "element_loads_over_padded": round(res["element_loads"] / res["padded"], 3),
+           "tuner_choice": {"cfg": list(tuned), "us": round(t_tuned * 1e6, 3)},
+           "picked_from": os.path.relpath(path, ROOT)}
+    log(f"padded study: {out}")
+    return out
+
+
 def sliced_k_study(p, tuned_cfg, torch):
     """The sliced-K kind where it pays: the fp32 workload's tuned call (K
     split among the wave groups of each workgroup; `tuned_cfg`, the
@@ -580,6 +624,8 @@ def main():
     ap.add_argument("--order", action="store_true",
                     help="also time the headline call at six tile scheduling orders (tile_order_study); off by "
                          "default, so that a kernel trace of the default run holds the headline's own launches only")
+    ap.add_argument("--no-padded", action="store_true",
+                    help="skip the padded-path study (513 x 1001 x 777: element loads against padded operands)")
     ap.add_argument("--no-streamk", action="store_true",
                     help="skip the stream-K study (4352 x 4352 x 8192: data-parallel against stream-K tail)")
     ap.add_argument("--cfg", type=str, default="",
@@ -718,6 +764,8 @@ def main():
         line["streamk_study"] = streamk_study(torch)
     if 1 in prepared and not a.only and forced is None:
         line["sliced_k_study"] = sliced_k_study(prepared[1], shapes[prepared[1].w.name]["cfg"], torch)
+    if not a.only and forced is None and not a.no_padded:
+        line["padded_study"] = padded_study(torch)
     if a.order and forced is None:
         line["tile_order_study"] = tile_order_study(p, torch)
     if not a.no_cpu:
