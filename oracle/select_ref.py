@@ -178,9 +178,10 @@ def pad_extent(x: int, dtype: int) -> int:
 
 def padded_path(N: int, K: int, dtype: int, c: "Cfg", dev: "Device") -> bool:
     """The tiled kind on a shape that is not aligned (MI355X rules): it runs on
-    copies of A and B zero-padded to K and N rounded up to whole vectors
-    (zeros add nothing to a sum), writes its sums as fp32 slabs with any split
-    and finishes in an output pass.  My reading of page "Compilers and Kernel
+    zero-padded copies of the operands whose rows are ragged, K and N rounded
+    up to whole vectors (zeros add nothing to a sum); with N ragged it writes
+    its sums as fp32 slabs with any split and finishes in an output pass.  My
+    reading of page "Compilers and Kernel
     Languages", "A different tile for every shape" (ragged shapes are where a
     fixed kernel loses) together with page "Tile Selection: Cost Models
     Against Measurement", "The structure of the search space" (the tile grid
@@ -547,14 +548,18 @@ def model_time(M: int, N: int, K: int, dtype: int, c: Cfg, dev: Device = MI355X)
     if dev.mode == 1:
         return _model_page(M, N, K, dtype, c, dev, eb, peak, flops, compulsory, tiles, units, w, bcu)
     if padded_path(N, K, dtype, c, dev):
-        # copying A and B into their padded forms (each read once and written
-        # once at the HBM rate, one launch), then the tiled kind on the padded
-        # problem with its sums in slabs, then the output pass (priced as the
-        # split-K second pass)
+        # one launch copies the operands whose rows are ragged (A when K is;
+        # B when N is, K rounded up -- with only K ragged B is read in place,
+        # the rows it lacks counting as zeros), each read once and written
+        # once at the HBM rate; then the tiled kind on the padded problem,
+        # whose sums go to slabs and an output pass (priced as the split-K
+        # second pass) when N is ragged: C's rows then take no 16-byte stores
         Np, Kp = pad_extent(N, dtype), pad_extent(K, dtype)
+        pad_a, pad_b = Kp != K, Np != N
         comp_p = float(eb * (M * Kp + Kp * Np) + ec * M * Np)
-        copies = float(eb * (M * K + K * N + M * Kp + Kp * Np)) / (dev.bw * dev.hbm_eff) + dev.t0
-        return _model_cu(M, Np, Kp, dtype, c, dev, eb, ec, peak, comp_p, tiles, units, w, bcu, True) + copies
+        copied = (eb * (M * K + M * Kp) if pad_a else 0) + (eb * (K * N + Kp * Np) if pad_b else 0)
+        copies = float(copied) / (dev.bw * dev.hbm_eff) + dev.t0
+        return _model_cu(M, Np, Kp, dtype, c, dev, eb, ec, peak, comp_p, tiles, units, w, bcu, pad_b) + copies
     return _model_cu(M, N, K, dtype, c, dev, eb, ec, peak, compulsory, tiles, units, w, bcu)
 
 

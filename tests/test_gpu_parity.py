@@ -95,7 +95,9 @@ def test_every_feasible_cfg_integer_exact(M, N, K, dtype):
 
 @pytest.mark.parametrize("M,N,K,dtype", [
     (17, 65, 15, wl.BF16), (63, 17, 1, wl.F32), (1, 1, 1, wl.BF16), (65, 33, 63, wl.BF16_F32OUT),
-    (300, 47, 129, wl.F32), (5, 1000, 77, wl.BF16),
+    (300, 47, 129, wl.F32), (5, 1000, 77, wl.BF16),                 # ... and K ragged only
+    (40, 1001, 512, wl.BF16), (100, 130, 128, wl.F32),               # N ragged only
+    (100, 128, 130, wl.F32), (70, 264, 515, wl.BF16_F32OUT),          # K ragged only
 ])
 def test_unaligned_shapes_integer_exact(M, N, K, dtype):
     # every configuration of the element-load kind and of the tiled kind's
@@ -161,6 +163,42 @@ def test_random_problems_random_cfgs_integer_exact(seed):
         C = _run(A_d, B_d, b_d, act, dtype, c)
         torch.cuda.synchronize()
         _exact_check(C, ref, dtype, f"{M}x{N}x{K} dt{dtype} {act} {c.astuple()}")
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_padded_path_misaligned_pointers(dtype):
+    # a shape with only K ragged reads B in place and stores C directly --
+    # unless B or C (or A) sits off 16-byte alignment, which the padded path
+    # then copies (A, B) or sends through the output pass (C)
+    M, N, K = 96, 264, 515
+    A, B, bias = _int_inputs(M, N, K, dtype, 12)
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    tdt = torch.float32 if dtype == wl.F32 else torch.bfloat16
+    odt = tdt
+    b_d = to_dev(bias)
+
+    def shifted(x, shift):
+        t = to_dev(x)
+        buf = torch.zeros(t.numel() + 1, dtype=tdt, device="cuda")
+        v = buf[shift:shift + t.numel()].view(t.shape)
+        v.copy_(t)
+        return v
+
+    cfgs = [(0, 64, 64, 64, 2, 2, 2, 1), (0, 64, 64, 64, 2, 2, 2, 2)] if dtype != wl.F32 else \
+        [(0, 64, 64, 32, 2, 2, 2, 1), (0, 64, 64, 32, 2, 2, 2, 2)]
+    for sa, sb, sc in ((0, 0, 0), (1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 1, 1)):
+        A_d, B_d = shifted(A, sa), shifted(B, sb)
+        cbuf = torch.zeros(M * N + 1, dtype=odt, device="cuda")
+        out = cbuf[sc:sc + M * N].view(M, N)
+        for cfg in cfgs:
+            assert tg.check_cfg(M, N, K, dtype, cfg) == 0
+            mark(f"padded misaligned dt{dtype} shifts {sa}{sb}{sc} {cfg}")
+            out.fill_(0)
+            tg.gemm_bias_act(A_d, B_d, b_d, act="relu", out=out, cfg=cfg)
+            torch.cuda.synchronize()
+            _exact_check(out, ref, dtype, f"shifts {sa}{sb}{sc} {cfg}")
+            if sc:
+                assert float(cbuf[0]) == 0.0, "wrote before C"
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])

@@ -580,7 +580,8 @@ def test_streamk_pieces_restart_the_tile_loop():
 
 def test_padded_path_closed_form():
     # an unaligned shape on the tiled kind: memory terms only (everything else
-    # made free).  The copies read A [256 x 777] and B [777 x 1001] and write
+    # made free).  Both K and N ragged: the copies read A [256 x 777] and
+    # B [777 x 1001] and write
     # A' [256 x 784] and B' [784 x 1008]; the kernel on the padded problem
     # moves its compulsory bytes and writes one fp32 slab [256 x 1008] (split
     # 1); the output pass reads that slab and writes 256 x 1008 outputs
@@ -600,6 +601,20 @@ def test_padded_path_closed_form():
     # store C directly and need no output pass
     aligned = S.model_time(M, 1008, 784, S.BF16, c, d)
     assert aligned == pytest.approx(compulsory / rate, rel=1e-12)
+    # only K ragged (N = 1008): A alone is copied, B is read in place and the
+    # kernel stores C itself -- no slab, no output pass
+    copies_a = 2 * (256 * 777 + 256 * 784)
+    want_k = compulsory / rate + copies_a / rate
+    assert S.model_time(M, 1008, K, S.BF16, c, d) == pytest.approx(want_k, rel=1e-12)
+    # ... and with split 2 the usual split-K slabs and second pass
+    c2 = S.Cfg(S.KIND_TILED, 128, 128, 64, 2, 4, 2, 2)
+    slabs2 = 2 * slab
+    want_k2 = (compulsory + slabs2) / rate + (slabs2 + 2 * 256 * 1008) / rate + copies_a / rate
+    assert S.model_time(M, 1008, K, S.BF16, c2, d) == pytest.approx(want_k2, rel=1e-12)
+    # only N ragged (K = 784): B alone is copied, then slab and output pass
+    copies_b = 2 * (784 * 1001 + 784 * 1008)
+    want_n = (compulsory + slab) / rate + (slab + 2 * 256 * 1008) / rate + copies_b / rate
+    assert S.model_time(M, Nn, 784, S.BF16, c, d) == pytest.approx(want_n, rel=1e-12)
     # the H100 replica keeps the page's rules: no alignment rule, no padding
     assert not S.padded_path(Nn, K, S.BF16, c, S.H100_REPLICA)
 

@@ -212,15 +212,26 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     p.out_bf16 = dtype == TG_BF16 ? 1 : 0;
     p.act = act;
     p.group_m = tile_order();
-    // the padded path: the kernel runs on the padded extents, its sums go to
-    // the slabs whatever the split, and the output pass writes C
+    // the padded path: the kernel runs on the padded extents.  It copies the
+    // operands whose rows are ragged or that are not 16-byte aligned (the
+    // kernel moves 16-byte chunks of rows); a B read in place has its rows
+    // past K read as zero.  When N is ragged (or C misaligned) the sums go to
+    // slabs whatever the split and the output pass writes C.
     const PaddedLayout pl = padded_layout(M, N, K, dtype, c);
+    bool copy_a = false, copy_b = false, out_pass = false;
     if (pl.on) {
+        copy_a = pl.Kp != K || !aligned16(A);
+        copy_b = pl.Np != N || !aligned16(B);
+        out_pass = pl.Np != N || !aligned16(C);
         p.N = (int)pl.Np;
         p.K = (int)pl.Kp;
         p.kps = (int)k_per_split(c, pl.Kp);
-        p.C = nullptr;
-        p.slab_out = 1;
+        if (!copy_b)
+            p.kb = (int)K;
+        if (out_pass) {
+            p.C = nullptr;
+            p.slab_out = 1;
+        }
     }
     int64_t tiles, blocks;
     grid(M, N, K, c, &tiles, &blocks, &d);
@@ -257,16 +268,19 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     hipError_t e;
     if (pl.on) {
         char* base = reinterpret_cast<char*>(p.ws);
-        p.A = base + pl.a_off;
-        p.B = base + pl.b_off;
-        e = pad_operands(A, B, base + pl.a_off, base + pl.b_off, M, N, K, pl.Np, pl.Kp, in_bytes(dtype), stream);
+        if (copy_a)
+            p.A = base + pl.a_off;
+        if (copy_b)
+            p.B = base + pl.b_off;
+        e = pad_operands(A, B, base + pl.a_off, base + pl.b_off, M, N, K, pl.Np, pl.Kp, in_bytes(dtype), copy_a,
+                         copy_b, stream);
         if (e != hipSuccess)
             return set_hip_error(e, "operand padding launch");
     }
     e = launch_fn(*ke, p)(p, (int)blocks, stream);
     if (e != hipSuccess)
         return set_hip_error(e, "kernel launch");
-    if (pl.on) {
+    if (out_pass) {
         e = padded_output(p.ws, c.split_k, pl.slab, pl.Np, M, N, bias, C, p.out_bf16, act, stream);
         if (e != hipSuccess)
             return set_hip_error(e, "padded output pass launch");

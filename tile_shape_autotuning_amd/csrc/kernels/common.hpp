@@ -37,6 +37,7 @@ struct GemmParams {
     int act;              // 0 none, 1 ReLU, 2 GELU (erf form)
     int group_m;          // tile rows per scheduling group (>= 1)
     int slab_out;         // 1: sums go to the split slabs even with split == 1 (the padded path)
+    int kb;               // rows of B in memory when fewer than K (rows kb .. K-1 read as zero); 0: K
     // stream-K kind: the first sk_dp tiles (in scheduling order) run one
     // workgroup each; the remaining sk_tail tiles' sk_ks K steps each are
     // spread evenly over sk_g further workgroups, whose pieces of a tile go to

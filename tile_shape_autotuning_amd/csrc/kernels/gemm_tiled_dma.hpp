@@ -285,7 +285,9 @@ __device__ __forceinline__ void dma_tile(const GemmParams& p, u32x4_t* lds, int 
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     const char* Ab = static_cast<const char*>(p.A);
     const char* Bb = static_cast<const char*>(p.B);
-    const int64_t a_total = (int64_t)M * K, b_total = (int64_t)K * N;
+    // B may hold fewer rows than K (the padded path on a ragged K only pads A):
+    // the range check then reads its missing rows as zero
+    const int64_t a_total = (int64_t)M * K, b_total = (int64_t)(p.kb > 0 ? p.kb : K) * N;
     const int rows_left = M - m0;      // valid A rows in this tile (may exceed BM)
     const int cols_left = N - n0;      // valid B columns in this tile
 

@@ -1,14 +1,16 @@
 // The padded path of the tiled kind: GEMMs whose rows are not whole 16-byte
 // chunks (K or N not a multiple of 8 bf16 / 4 fp32 elements).  The
 // direct-to-LDS kernel moves 16-byte chunks of rows, so here it runs on
-// zero-padded copies of the operands instead: A [M x K] -> A' [M x Kp] and
-// B [K x N] -> B' [Kp x Np], with Kp and Np rounded up to the chunk and the
-// extra columns and rows zero, which adds nothing to any sum.  The kernel
-// writes its fp32 sums as split slabs [M x Np] (any split, 1 included), and
-// the output pass below adds them in split order, adds the bias, applies the
-// activation and writes the real C [M x N] element by element -- the same
-// operations in the same order as the split-K second pass, so the results are
-// those of the aligned kinds (page "Compilers and Kernel Languages", "A
+// zero-padded copies of the operands whose rows are ragged (or misaligned):
+// A [M x K] -> A' [M x Kp], B [K x N] -> B' [Kp x Np], with Kp and Np
+// rounded up to the chunk and the extra columns and rows zero, which adds
+// nothing to any sum (a B read in place has the rows it lacks read as zero
+// by the kernel's range check).  When N is ragged the kernel writes its fp32
+// sums as split slabs [M x Np] (any split, 1 included), and the output pass
+// below adds them in split order, adds the bias, applies the activation and
+// writes the real C [M x N] element by element -- the same operations in the
+// same order as the split-K second pass, so the results are those of the
+// aligned kinds (page "Compilers and Kernel Languages", "A
 // different tile for every shape": ragged shapes are where a fixed kernel
 // loses; page "Tile Selection: Cost Models Against Measurement", "The
 // structure of the search space": the tile grid covers the padded extents).
@@ -112,12 +114,13 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 hipError_t pad_operands(const void* A, const void* B, void* Ap, void* Bp, int64_t M, int64_t N, int64_t K,
-                        int64_t Np, int64_t Kp, int eb, hipStream_t stream)
+                        int64_t Np, int64_t Kp, int eb, bool copy_a, bool copy_b, hipStream_t stream)
 {
-    const PadJob a{A, Ap, M, M, K, Kp};
-    const PadJob b{B, Bp, K, Kp, N, Np};
+    // an operand not copied gets a job of no rows
+    const PadJob a{A, Ap, M, copy_a ? M : 0, K, Kp};
+    const PadJob b{B, Bp, K, copy_b ? Kp : 0, N, Np};
     const int64_t v = 16 / eb;
-    const int64_t most = std::max(M * (Kp / v), Kp * (Np / v));   // chunks of the larger copy
+    const int64_t most = std::max(a.rowsp * (Kp / v), b.rowsp * (Np / v));   // chunks of the larger copy
     const dim3 grid((unsigned)std::min<int64_t>(std::max<int64_t>(cdiv64(most, 256), 1), 4096), 2);
     if (eb == 2)
         hipLaunchKernelGGL(pad_operands_kernel<unsigned short>, grid, dim3(256), 0, stream, a, b);

@@ -57,10 +57,10 @@ int validate_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 // keeps it until every kernel that uses the buffer is queued.
 int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws, std::unique_lock<std::mutex>* hold = nullptr);
 size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& cfg);
-// Workspace of the padded path (padded_path in select.hpp): `split` fp32
-// slabs of [M x Np] (slab floats apart) from offset 0, then A' [M x Kp] at
-// a_off and B' [Kp x Np] at b_off (bytes, 256-byte aligned); `on` false when
-// the call does not take the padded path.
+// Workspace of the padded path (padded_path in select.hpp): room for `split`
+// fp32 slabs of [M x Np] (slab floats apart) from offset 0, then A' [M x Kp]
+// at a_off and B' [Kp x Np] at b_off (bytes, 256-byte aligned), whichever of
+// them a call uses; `on` false when the call does not take the padded path.
 struct PaddedLayout {
     bool on;
     int64_t Np, Kp, slab;
@@ -75,11 +75,11 @@ hipError_t splitk_reduce(const float* ws, int split, int64_t M, int64_t N, const
                          int out_bf16, int act, hipStream_t stream);
 
 // The padded path (pad.hip): zero-padded copies A' [M x Kp], B' [Kp x Np] of
-// A [M x K], B [K x N] (eb bytes per element), and the output pass that adds
-// `split` slabs of row stride ldp in split order, then bias, activation,
-// conversion into C [M x N].
+// A [M x K], B [K x N] (eb bytes per element; each only if its flag is set),
+// and the output pass that adds `split` slabs of row stride ldp in split
+// order, then bias, activation, conversion into C [M x N].
 hipError_t pad_operands(const void* A, const void* B, void* Ap, void* Bp, int64_t M, int64_t N, int64_t K,
-                        int64_t Np, int64_t Kp, int eb, hipStream_t stream);
+                        int64_t Np, int64_t Kp, int eb, bool copy_a, bool copy_b, hipStream_t stream);
 hipError_t padded_output(const float* ws, int split, int64_t slab, int64_t ldp, int64_t M, int64_t N,
                          const float* bias, void* C, int out_bf16, int act, hipStream_t stream);
 

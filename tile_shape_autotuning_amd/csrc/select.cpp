@@ -624,13 +624,19 @@ double model_time(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, c
     if (d.mode == 1)
         return model_page(K, dtype, c, d, eb, peak, flops, compulsory, tiles, units, w, bcu);
     if (padded_path(N, K, dtype, c, d)) {
-        // the padded path: copying A and B into their padded forms (read once,
-        // written once), then the tiled kind on the padded problem with its
-        // sums in slabs, then the output pass (priced as the split-K one)
+        // the padded path: one launch copies the operands whose rows are
+        // ragged into their padded forms (A when K is; B when N is, with K
+        // rounded up -- a B with only K ragged is read in place, its missing
+        // rows as zeros), each read once and written once; then the tiled
+        // kind on the padded problem, its sums in slabs and an output pass
+        // (priced as the split-K one) when N is ragged, since C's rows then
+        // cannot take the kernel's 16-byte stores
         const int64_t Np = pad_extent(N, dtype), Kp = pad_extent(K, dtype);
+        const bool pad_a = Kp != K, pad_b = Np != N;
         const double comp_p = (double)(eb * (M * Kp + Kp * Np) + ec * M * Np);
-        const double copies = (double)(eb * (M * K + K * N + M * Kp + Kp * Np)) / (d.bw * d.hbm_eff) + d.t0;
-        return model_cu(M, Np, Kp, dtype, c, d, eb, ec, peak, comp_p, tiles, units, w, bcu, true) + copies;
+        const int64_t copied = (pad_a ? eb * (M * K + M * Kp) : 0) + (pad_b ? eb * (K * N + Kp * Np) : 0);
+        const double copies = (double)copied / (d.bw * d.hbm_eff) + d.t0;
+        return model_cu(M, Np, Kp, dtype, c, d, eb, ec, peak, comp_p, tiles, units, w, bcu, pad_b) + copies;
     }
     return model_cu(M, N, K, dtype, c, d, eb, ec, peak, compulsory, tiles, units, w, bcu);
 }

@@ -25,9 +25,9 @@ int in_bytes(int dtype);
 int out_bytes(int dtype);
 bool shape_aligned(int64_t N, int64_t K, int dtype);
 // The padded path: on a shape that is not shape_aligned (MI355X rules), the
-// tiled kind runs on zero-padded copies of A and B whose K and N are rounded
-// up to whole 16-byte chunks (pad_extent), writes fp32 slabs and finishes in
-// an output pass.
+// tiled kind runs on zero-padded copies of the operands whose rows are ragged,
+// K and N rounded up to whole 16-byte chunks (pad_extent); with N ragged it
+// writes fp32 slabs and finishes in an output pass.
 bool padded_path(int64_t N, int64_t K, int dtype, const tg_cfg& c, const tg_device_desc& d);
 int64_t pad_extent(int64_t x, int dtype);
 
