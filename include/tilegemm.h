@@ -152,7 +152,8 @@ int tg_set_stream(void *hip_stream);
  *   A, B, C: device pointers, 16-byte aligned for the tiled, skinny,
  *     stream-K and sliced-K kinds on an aligned shape (K and N multiples of 8
  *     bf16 / 4 fp32 elements); any element alignment for the unaligned kind
- *     and for the tiled kind's padded path.
+ *     and for the tiled kind's padded path (which copies a misaligned A or B
+ *     and writes a misaligned C through its output pass).
  *   bias: device pointer to N floats, or NULL.
  *   dtype: tg_dtype; act: tg_act; cfg: explicit configuration or NULL.
  * Limits: K <= 2^21, N <= 2^21, M <= 2^31 - 1 (TG_E_UNSUPPORTED beyond).
@@ -167,11 +168,14 @@ int tg_set_stream(void *hip_stream);
  * and applies bias, activation and conversion.  The tiled kind on a shape
  * whose K or N is not a multiple of 8 bf16 / 4 fp32 elements takes the
  * padded path (page "Compilers and Kernel Languages", "A different tile for
- * every shape": ragged shapes): one kernel copies A and B into the workspace
- * with K and N rounded up to whole vectors and the new rows and columns zero,
- * the GEMM runs on the copies and writes fp32 slabs of M x Np with any
- * split_k, and an output pass adds them, applies bias, activation and
- * conversion and writes C -- three kernels, results as on an aligned shape.
+ * every shape": ragged shapes): one kernel copies into the workspace the
+ * operands whose rows are ragged or not 16-byte aligned (A with K rounded
+ * up to a whole vector, B with N and K rounded up; new rows and columns
+ * zero; a B with only K ragged is read in place, its missing rows as
+ * zeros), the GEMM runs on the padded extents, and when N is ragged (or C
+ * misaligned) it writes fp32 slabs of M x Np with any split_k and an output
+ * pass adds them, applies bias, activation and conversion and writes C --
+ * two or three kernels, results as on an aligned shape.
  * There is one workspace per (device, stream), grown on demand (growth waits
  * for that stream), so calls on different streams may run concurrently;
  * calls on one stream are ordered by it.
