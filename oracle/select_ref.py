@@ -120,7 +120,7 @@ class Device:
 MI355X = Device(mode=0, n_cu=256, simds=4, lds_cu=163840, lds_block=163840,
                 max_threads=1024, waves_max=8, blocks_max=32, vgpr_max=512,
                 acc_max=256, peak_bf16=2516.6e12, peak_f32=157.3e12, bw=8.0e12,
-                a_ref=16384.0, c_fill=2.0, t0=4.0e-6, unaligned_eff=0.25,
+                a_ref=16384.0, c_fill=2.0, t0=4.0e-6, unaligned_eff=0.125,
                 lat_mem=2.0e-6, cu_bw=50.0e9, r0=24, lds_bw_cu=192.0e9, lat_step=1.25e-6,
                 lat_l2=0.3e-6, l2_bytes=32.0e6, w1_eff=0.35, skinny_eff=0.75, hbm_eff=0.9125,
                 sliced_eff=1.0)

@@ -13,7 +13,7 @@ The model's form stays the analytical one; only calibration constants of the
 MI355X description are fitted (effective LDS and L2-to-CU bandwidth per CU,
 the memory latency a K step waits for from HBM and from L2, the issue
 efficiency of a lone wave on a SIMD and of the sliced-K kind, the achievable
-HBM fraction), by grid
+HBM fraction, the L2-to-CU efficiency of element loads), by grid
 search: fewest training tables whose measured best is outside the model's
 top k (the hybrid tuner measures the top k), then the smallest geometric
 mean of the measured time of the model's first choice over the best, then
@@ -54,6 +54,7 @@ GRID = {
     "w1_eff": [0.35, 0.4, 0.5, 0.55],
     "hbm_eff": [0.9125],
     "sliced_eff": [0.4, 0.55, 0.7, 1.0],
+    "unaligned_eff": [0.0625, 0.125, 0.25],
 }
 
 

@@ -49,7 +49,7 @@ tg_device_desc mi355x_desc()
     d.a_ref = 16384.0;
     d.c_fill = 2.0;
     d.t0 = 4.0e-6;
-    d.unaligned_eff = 0.25;
+    d.unaligned_eff = 0.125;
     d.lat_mem = 2.0e-6;
     d.cu_bw = 50.0e9;
     d.lds_bw_cu = 192.0e9;

@@ -48,7 +48,9 @@ CALIBRATION_SHAPES = [
     ("c20_f32_128x128x128", 128, 128, 128, F32),
     ("c21_f32_512x512x512", 512, 512, 512, F32),
     ("c22_f32_384x640x256", 384, 640, 256, F32),
-    ("c23_bf16_513x1001x777", 513, 1001, 777, BF16),     # N, K not multiples of 8: element-load kind
+    ("c23_bf16_513x1001x777", 513, 1001, 777, BF16),     # N, K not multiples of 8: element loads or padded
+    ("c24_bf16_4096x256x147", 4096, 256, 147, BF16),     # K ragged only: A padded, B read in place
+    ("c25_bf16_1024x1001x1024", 1024, 1001, 1024, BF16),  # N ragged only: B padded, output pass
 ]
 
 
