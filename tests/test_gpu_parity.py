@@ -312,6 +312,17 @@ def test_empty_and_k_zero():
         C = _run(A_d, B_d, to_dev(bias), "relu", dtype, sliced)
         torch.cuda.synchronize()
         _exact_check(C, want, dtype, "K=0 sliced-K")
+        # K = 0 with a ragged N: the padded path (B's copy has no rows, the
+        # kernel sums nothing, the output pass adds the bias)
+        A0 = torch.zeros((37, 0), device="cuda", dtype=A_d.dtype)
+        B0 = torch.zeros((0, 21), device="cuda", dtype=A_d.dtype)
+        want21 = np.maximum(np.broadcast_to(bias[:21].astype(np.float64), (37, 21)), 0.0)
+        cfg = (0, 32, 32, 32, 1, 1, 2, 1)
+        assert tg.check_cfg(37, 21, 0, dtype, cfg) == 0
+        mark(f"K=0 padded dt{dtype}")
+        C = _run(A0, B0, to_dev(np.ascontiguousarray(bias[:21])), "relu", dtype, cfg)
+        torch.cuda.synchronize()
+        _exact_check(C, want21, dtype, "K=0 padded")
         mark(f"M=0 dt{dtype}")
         C = _run(torch.zeros((0, 8), device="cuda", dtype=A_d.dtype),
                  torch.zeros((8, 16), device="cuda", dtype=A_d.dtype), None, "none", dtype)
