@@ -149,11 +149,11 @@ int tg_set_stream(void *hip_stream);
  * the cache is keyed on M's shape bucket (tg_dispatch_m): one tuning serves
  * every M of the bucket.
  *   M, N >= 0, K >= 0 (M or N = 0: nothing to do; K = 0: C = act(bias)).
- *   A, B, C: device pointers, 16-byte aligned for the tiled, skinny,
- *     stream-K and sliced-K kinds on an aligned shape (K and N multiples of 8
- *     bf16 / 4 fp32 elements); any element alignment for the unaligned kind
- *     and for the tiled kind's padded path (which copies a misaligned A or B
- *     and writes a misaligned C through its output pass).
+ *   A, B, C: device pointers, 16-byte aligned for the skinny, stream-K and
+ *     sliced-K kinds; any element alignment for the unaligned kind and for
+ *     the tiled kind, whose padded path copies an A or B off 16-byte
+ *     alignment and writes such a C through its output pass (a call without
+ *     cfg whose selection picked another kind runs the unaligned kind then).
  *   bias: device pointer to N floats, or NULL.
  *   dtype: tg_dtype; act: tg_act; cfg: explicit configuration or NULL.
  * Limits: K <= 2^21, N <= 2^21, M <= 2^31 - 1 (TG_E_UNSUPPORTED beyond).

@@ -166,11 +166,13 @@ def test_random_problems_random_cfgs_integer_exact(seed):
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
-def test_padded_path_misaligned_pointers(dtype):
-    # a shape with only K ragged reads B in place and stores C directly --
-    # unless B or C (or A) sits off 16-byte alignment, which the padded path
-    # then copies (A, B) or sends through the output pass (C)
-    M, N, K = 96, 264, 515
+@pytest.mark.parametrize("K", [515, 512])
+def test_padded_path_misaligned_pointers(dtype, K):
+    # a shape with only K ragged reads B in place and stores C directly, and
+    # an aligned shape reads both in place -- unless B or C (or A) sits off
+    # 16-byte alignment, which the tiled kind's padded path then copies (A, B)
+    # or sends through the output pass (C)
+    M, N = 96, 264
     A, B, bias = _int_inputs(M, N, K, dtype, 12)
     ref = gemm_ref.gemm(A, B, bias, "relu")
     tdt = torch.float32 if dtype == wl.F32 else torch.bfloat16
@@ -192,13 +194,21 @@ def test_padded_path_misaligned_pointers(dtype):
         out = cbuf[sc:sc + M * N].view(M, N)
         for cfg in cfgs:
             assert tg.check_cfg(M, N, K, dtype, cfg) == 0
-            mark(f"padded misaligned dt{dtype} shifts {sa}{sb}{sc} {cfg}")
+            mark(f"padded misaligned dt{dtype} K {K} shifts {sa}{sb}{sc} {cfg}")
             out.fill_(0)
             tg.gemm_bias_act(A_d, B_d, b_d, act="relu", out=out, cfg=cfg)
             torch.cuda.synchronize()
             _exact_check(out, ref, dtype, f"shifts {sa}{sb}{sc} {cfg}")
             if sc:
                 assert float(cbuf[0]) == 0.0, "wrote before C"
+        if (sa, sb, sc) == (1, 1, 1):
+            # without a configuration: the tuned choice, whatever its kind
+            mark(f"padded misaligned dt{dtype} K {K} tuned")
+            out.fill_(0)
+            tg.gemm_bias_act(A_d, B_d, b_d, act="relu", out=out)
+            torch.cuda.synchronize()
+            _exact_check(out, ref, dtype, "misaligned, tuned")
+            assert float(cbuf[0]) == 0.0, "wrote before C"
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])

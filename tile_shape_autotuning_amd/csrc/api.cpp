@@ -169,10 +169,11 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
 {
     const tg_device_desc d = current_desc();
     tg_cfg c = cfg;
-    // the padded path reads A and B and writes C element by element: any
-    // pointer alignment will do
-    const bool padded = padded_path(N, K, dtype, c, d);
+    // the padded path copies the operands it cannot read in place and writes
+    // a C it cannot store into through its output pass: the tiled kind takes
+    // it for a ragged shape and for operands off 16-byte alignment
     bool misaligned = !(aligned16(A) && aligned16(B) && aligned16(C));
+    const bool padded = padded_path(N, K, dtype, c, d) || (d.mode == 0 && c.kind == TG_KIND_TILED && misaligned);
     if (c.kind != TG_KIND_UNALIGNED && misaligned && !padded) {
         if (!from_selection)
             return set_error(TG_E_INVAL, "A, B and C must be 16-byte aligned for the tiled and skinny kinds");
@@ -217,7 +218,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     // kernel moves 16-byte chunks of rows); a B read in place has its rows
     // past K read as zero.  When N is ragged (or C misaligned) the sums go to
     // slabs whatever the split and the output pass writes C.
-    const PaddedLayout pl = padded_layout(M, N, K, dtype, c);
+    const PaddedLayout pl = padded_layout(M, N, K, dtype, c, padded);
     bool copy_a = false, copy_b = false, out_pass = false;
     if (pl.on) {
         copy_a = pl.Kp != K || !aligned16(A);
@@ -251,7 +252,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     // ensure_workspace)
     std::unique_lock<std::mutex> ws_hold;
     if (cta_splits(c) > 1 || fixup || pl.on) {
-        const size_t need = workspace_bytes_for(M, N, K, dtype, c);
+        const size_t need = pl.on ? pl.total : workspace_bytes_for(M, N, K, dtype, c);
         if (ext) {
             if (need > ext->bytes)
                 return set_error(TG_E_INVAL, "the workspace of this call needs " + std::to_string(need) +

@@ -57,16 +57,17 @@ int validate_call(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
 // keeps it until every kernel that uses the buffer is queued.
 int ensure_workspace(size_t ws_bytes, hipStream_t stream, float** ws, std::unique_lock<std::mutex>* hold = nullptr);
 size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& cfg);
-// Workspace of the padded path (padded_path in select.hpp): room for `split`
+// Workspace of the padded path (a ragged shape, padded_path in select.hpp,
+// or operands off 16-byte alignment on the tiled kind): room for `split`
 // fp32 slabs of [M x Np] (slab floats apart) from offset 0, then A' [M x Kp]
 // at a_off and B' [Kp x Np] at b_off (bytes, 256-byte aligned), whichever of
-// them a call uses; `on` false when the call does not take the padded path.
+// them a call uses; `on` (the call takes the padded path) false: all zero.
 struct PaddedLayout {
     bool on;
     int64_t Np, Kp, slab;
     size_t a_off, b_off, total;
 };
-PaddedLayout padded_layout(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c);
+PaddedLayout padded_layout(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, bool on);
 
 // Split-K second pass (splitk_reduce.hip): C = act(sum of the split slabs +
 // bias), slabs `splitk_slab(M, N)` floats apart.

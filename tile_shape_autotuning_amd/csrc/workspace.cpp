@@ -30,7 +30,7 @@ static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c)
 {
-    const PaddedLayout pl = padded_layout(M, N, K, dtype, c);
+    const PaddedLayout pl = padded_layout(M, N, K, dtype, c, padded_path(N, K, dtype, c, current_desc()));
     if (pl.on)
         return pl.total;
     if (c.kind == TG_KIND_STREAMK) {
@@ -45,10 +45,10 @@ size_t workspace_bytes_for(int64_t M, int64_t N, int64_t K, int dtype, const tg_
     return (size_t)c.split_k * (size_t)splitk_slab(M, N) * sizeof(float);
 }
 
-PaddedLayout padded_layout(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c)
+PaddedLayout padded_layout(int64_t M, int64_t N, int64_t K, int dtype, const tg_cfg& c, bool on)
 {
     PaddedLayout l{};
-    if (!padded_path(N, K, dtype, c, current_desc()))
+    if (!on)
         return l;
     auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t eb = (size_t)in_bytes(dtype);
