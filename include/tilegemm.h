@@ -153,7 +153,8 @@ int tg_set_stream(void *hip_stream);
  *     sliced-K kinds; any element alignment for the unaligned kind and for
  *     the tiled kind, whose padded path copies an A or B off 16-byte
  *     alignment and writes such a C through its output pass (a call without
- *     cfg whose selection picked another kind runs the unaligned kind then).
+ *     cfg whose selection picked another kind runs the same tile on the
+ *     tiled kind then, or the unaligned kind where that tile does not fit).
  *   bias: device pointer to N floats, or NULL.
  *   dtype: tg_dtype; act: tg_act; cfg: explicit configuration or NULL.
  * Limits: K <= 2^21, N <= 2^21, M <= 2^31 - 1 (TG_E_UNSUPPORTED beyond).

@@ -211,6 +211,34 @@ def test_padded_path_misaligned_pointers(dtype, K):
             assert float(cbuf[0]) == 0.0, "wrote before C"
 
 
+def test_misaligned_operands_of_a_selected_sliced_k_call(monkeypatch):
+    # a call without a configuration whose selection (here the cost model's
+    # choice: the sliced-K kind) cannot take operands off 16-byte alignment
+    # runs the same tile on the tiled kind, padded
+    monkeypatch.setenv("TILEGEMM_DISABLE_AUTOTUNE", "1")
+    tg.cache_clear()
+    M = N = K = 256
+    dtype = wl.F32
+    assert tg.model_choice(M, N, K, dtype)[0].kind == S.KIND_SLICEDK
+    A, B, bias = _int_inputs(M, N, K, dtype, 13)
+    ref = gemm_ref.gemm(A, B, bias, "relu")
+    bufs = []
+    for x in (A, B):
+        t = to_dev(x)
+        buf = torch.zeros(t.numel() + 1, dtype=torch.float32, device="cuda")
+        v = buf[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        bufs.append(v)
+    cbuf = torch.zeros(M * N + 1, dtype=torch.float32, device="cuda")
+    out = cbuf[1:].view(M, N)
+    mark("misaligned operands, selected sliced-K")
+    tg.gemm_bias_act(bufs[0], bufs[1], to_dev(bias), act="relu", out=out)
+    torch.cuda.synchronize()
+    _exact_check(out, ref, dtype, "misaligned, selected sliced-K")
+    assert float(cbuf[0]) == 0.0
+    tg.cache_clear()
+
+
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32, wl.BF16_F32OUT])
 def test_padded_path_gelu_random_inputs(dtype):
     # the padded path with bias and GELU on random operands, against the fp64

@@ -173,12 +173,20 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
     // a C it cannot store into through its output pass: the tiled kind takes
     // it for a ragged shape and for operands off 16-byte alignment
     bool misaligned = !(aligned16(A) && aligned16(B) && aligned16(C));
-    const bool padded = padded_path(N, K, dtype, c, d) || (d.mode == 0 && c.kind == TG_KIND_TILED && misaligned);
+    bool padded = padded_path(N, K, dtype, c, d) || (d.mode == 0 && c.kind == TG_KIND_TILED && misaligned);
     if (c.kind != TG_KIND_UNALIGNED && misaligned && !padded) {
         if (!from_selection)
-            return set_error(TG_E_INVAL, "A, B and C must be 16-byte aligned for the tiled and skinny kinds");
-        // selection ran without knowing the pointers: fall back to the element-load kernel
-        c = tg_cfg{TG_KIND_UNALIGNED, 64, 64, dtype == TG_F32 ? 16 : 32, 2, 2, 2, 1};
+            return set_error(TG_E_INVAL, "A, B and C must be 16-byte aligned for the skinny, stream-K and sliced-K kinds");
+        // selection ran without knowing the pointers: the same tile as the
+        // tiled kind, which takes misaligned operands padded, else the
+        // element-load kernel
+        const tg_cfg t{TG_KIND_TILED, c.bm, c.bn, c.bk, c.wgm, c.wgn, c.stages, 1};
+        if (d.mode == 0 && check(M, N, K, dtype, t, d) == OK && find_kernel(dtype, t)) {
+            c = t;
+            padded = true;
+        } else {
+            c = tg_cfg{TG_KIND_UNALIGNED, 64, 64, dtype == TG_F32 ? 16 : 32, 2, 2, 2, 1};
+        }
     } else {
         const int r = check(M, N, K, dtype, c, d);
         if (r != OK)
@@ -267,7 +275,7 @@ int launch_cfg(int64_t M, int64_t N, int64_t K, const void* A, const void* B, co
         p.slab = pl.on ? pl.slab : splitk_slab(M, N);
     }
     hipError_t e;
-    if (pl.on) {
+    if (copy_a || copy_b) {
         char* base = reinterpret_cast<char*>(p.ws);
         if (copy_a)
             p.A = base + pl.a_off;
