@@ -39,7 +39,8 @@ def _inputs(M, N, K, seed):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M,N,K,seed", [(200, 136, 520, 3), (16, 1000, 1064, 5)])
+@pytest.mark.parametrize("M,N,K,seed", [(200, 136, 520, 3), (16, 1000, 1064, 5),
+                                        (130, 264, 515, 9), (61, 1001, 515, 4)])   # ragged K; ragged N and K
 def test_c_program_matches_oracle(tmp_path, M, N, K, seed):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
