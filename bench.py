@@ -624,6 +624,7 @@ def main():
     ap.add_argument("--order", action="store_true",
                     help="also time the headline call at six tile scheduling orders (tile_order_study); off by "
                          "default, so that a kernel trace of the default run holds the headline's own launches only")
+    ap.add_argument("--padded", action="store_true", help="report the padded-path study also with --only")
     ap.add_argument("--no-padded", action="store_true",
                     help="skip the padded-path study (513 x 1001 x 777: element loads against padded operands)")
     ap.add_argument("--no-streamk", action="store_true",
@@ -764,7 +765,7 @@ def main():
         line["streamk_study"] = streamk_study(torch)
     if 1 in prepared and not a.only and forced is None:
         line["sliced_k_study"] = sliced_k_study(prepared[1], shapes[prepared[1].w.name]["cfg"], torch)
-    if not a.only and forced is None and not a.no_padded:
+    if (a.padded or not a.only) and forced is None and not a.no_padded:
         line["padded_study"] = padded_study(torch)
     if a.order and forced is None:
         line["tile_order_study"] = tile_order_study(p, torch)
