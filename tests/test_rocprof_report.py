@@ -42,6 +42,9 @@ def test_kernel_times_average_per_name(tmp_path):
     assert t[GEMM] == (2, 35000.0)
     assert t[COPY] == (1, 1000.0)
     assert "gemm_tiled_dma_kernel" in R.kernel_table(d)
+    # the name filter keeps only the matching kernels, with their own averages
+    only = R.kernel_table(d, match=("gemm_tiled_dma_kernel",)).splitlines()
+    assert len(only) == 2 and "35.000" in only[1] and COPY not in "\n".join(only)
 
 
 def test_kernel_times_split_one_template_by_grid(tmp_path):

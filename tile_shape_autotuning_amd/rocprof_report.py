@@ -175,13 +175,16 @@ def hbm_traffic(fetch_dir, write_dir, copy_bytes, kernel="gemm"):
     return res
 
 
-def kernel_table(trace_dir, top=12):
+def kernel_table(trace_dir, top=12, match=()):
     """Text table of the kernels in a trace (one row per kernel and grid
-    size), by total time."""
+    size), by total time; with `match`, only kernels whose name contains one
+    of those strings."""
     acc = collections.defaultdict(lambda: [0, 0.0])
     for db in _dbs(trace_dir):
         c = sqlite3.connect(db)
         for name, dur, gx in c.execute("select name, duration, grid_x from kernels"):
+            if match and not any(m in name for m in match):
+                continue
             acc[(name, int(gx))][0] += 1
             acc[(name, int(gx))][1] += float(dur)
     rows = sorted(acc.items(), key=lambda kv: -kv[1][1])[:top]
@@ -315,6 +318,10 @@ def main(argv=None):
     r.add_argument("--out", default="")
     c = sub.add_parser("commands")
     c.add_argument("bench_args", nargs=argparse.REMAINDER)
+    k = sub.add_parser("kernels", help="the kernel table of a trace, by total time")
+    k.add_argument("--trace", required=True)
+    k.add_argument("--top", type=int, default=12)
+    k.add_argument("--match", action="append", default=[], help="keep kernels whose name contains this (repeatable)")
     s = sub.add_parser("summary")
     s.add_argument("--trace", required=True)
     s.add_argument("--pmc", action="append", default=[])
@@ -329,6 +336,9 @@ def main(argv=None):
         cfg = tuple(int(x) for x in a.cfg.split(","))
         text, _ = render(a.workload, cfg, a.trace, a.pmc, a.fetch, a.write, a.command, a.out or None)
         print(text)
+        return 0
+    if a.cmd == "kernels":
+        print(kernel_table(a.trace, a.top, tuple(a.match)))
         return 0
     if a.cmd == "commands":
         print("\n".join(commands(a.bench_args)))
